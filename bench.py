@@ -1,0 +1,189 @@
+"""Benchmark of the chunked KDA forward on one MI355X.
+
+One step = one kda_fwd call (scheduler + chunk-prep + chunk-recurrence kernels)
+over one batch of seeded synthetic input already resident in HBM.  Workloads:
+  * headline: T = 8192, H = 96, K = V = 128, one fixed-length sequence, bf16
+    initial and final state, lower_bound = -5;
+  * also timed: the same shape as 8 varlen sequences of 1024 tokens.
+Prints ONE JSON line (rank 0).  Per-kernel times come from HIP events that
+kda_fwd_profiled records on the launch stream; the roofline is computed for
+the kernel that takes the most time, with algorithmic bytes only (inputs and
+outputs of the method that kernel is responsible for), and for the whole path.
+The fp64 oracle is timed on a bounded sample of the headline workload on the
+host cores (cpu_baseline).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16/fp16 matrix, TFLOP/s
+METRIC = "KDA fwd ms + token·heads/s at T=8192,D=128,H=96 (fixed, varlen 8x1024)"
+
+# Algorithmic bytes per token-head (q, k, v, g: 4 x 256 B; beta 2 B; out 256 B),
+# split by the kernel that moves them.
+PREP_BYTES_PER_TH = 3 * 256 + 2      # q, k, g, beta
+RECUR_BYTES_PER_TH = 256 + 256       # v in, out
+PATH_BYTES_PER_TH = PREP_BYTES_PER_TH + RECUR_BYTES_PER_TH   # = 1282
+FLOPS_PER_TH = 6 * 128 * 128 + (6 * 128 + 4 * 128) * 16     # chunked form at C = 16
+
+
+def state_bytes(inp):
+    if inp.state_dtype is None:
+        return 0
+    per = 2 if inp.state_dtype == "bf16" else 4
+    n = inp.N * inp.H * inp.V * inp.K * per
+    return n * ((inp.initial_state is not None) + int(inp.output_final_state))
+
+
+def param_bytes(inp):
+    return inp.H * 4 + inp.H * inp.K * 4
+
+
+def run_workload(cfg, steps, warmup, torch, kda, device_inputs):
+    inp = cfg.make()
+    d = device_inputs(inp, "cuda")
+    out = torch.empty((inp.B, inp.T, inp.H, inp.V), dtype=torch.bfloat16, device="cuda")
+    fin = torch.empty((inp.N, inp.H, inp.V, inp.K),
+                      dtype=torch.bfloat16 if inp.state_dtype == "bf16" else torch.float32, device="cuda")
+    ws = kda.alloc_workspace(inp.B, inp.T, inp.H, inp.N, inp.cu_seqlens is not None, "cuda")
+
+    def step(events=None):
+        kda.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], inp.scale, out, d["A_log"], d["dt_bias"],
+                inp.lower_bound, initial_state=d["initial_state"], final_state=fin,
+                cu_seqlens=d["cu_seqlens"], workspace=ws, events=events)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+
+    # per-kernel durations, HIP events recorded by the library on its stream
+    n_prof = max(steps, 5)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_prof)]
+    for row in ev:
+        for e in row:
+            e.record()          # creates the underlying HIP event
+    torch.cuda.synchronize()
+    for row in ev:
+        step(events=row)
+    torch.cuda.synchronize()
+    k_ms = np.array([[row[i].elapsed_time(row[i + 1]) for i in range(3)] for row in ev]).mean(axis=0)
+    status = kda.check_status(ws)
+    th = inp.B * inp.T * inp.H
+    return dict(inp=inp, ms=ms, sched_ms=float(k_ms[0]), prep_ms=float(k_ms[1]), recur_ms=float(k_ms[2]),
+                token_heads=th, status=status)
+
+
+def roofline(res):
+    inp, th = res["inp"], res["token_heads"]
+    prep_bytes = th * PREP_BYTES_PER_TH + param_bytes(inp)
+    recur_bytes = th * RECUR_BYTES_PER_TH + state_bytes(inp)
+    path_bytes = prep_bytes + recur_bytes
+    if res["recur_ms"] >= res["prep_ms"]:
+        name, kbytes, kms = "kda::recur_kernel", recur_bytes, res["recur_ms"]
+    else:
+        name, kbytes, kms = "kda::prep_kernel", prep_bytes, res["prep_ms"]
+    ach = kbytes / (kms * 1e-3) / 1e9
+    path_ms = res["ms"]
+    path_ach = path_bytes / (path_ms * 1e-3) / 1e9
+    return dict(kernel=name, bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                frac=round(ach / HBM_PEAK_GBS, 4), traffic=None, kernel_ms=round(kms, 4),
+                algorithmic_bytes_per_launch=int(kbytes)), \
+        dict(bound="hbm", achieved=round(path_ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+             frac=round(path_ach / HBM_PEAK_GBS, 4), algorithmic_bytes=int(path_bytes),
+             mfma_frac=round(th * FLOPS_PER_TH / (path_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4))
+
+
+def cpu_baseline(cfg, heads: int):
+    """The fp64 oracle on the first `heads` heads of the workload (all tokens)."""
+    import oracle
+    inp = cfg.make()
+    hs = list(range(heads))
+    sl = lambda x: np.ascontiguousarray(x[:, :, hs])
+    s0 = inp.initial_state_f64()
+    threads = len(os.sched_getaffinity(0))
+    t = time.perf_counter()
+    oracle.kda_fwd(sl(inp.q), sl(inp.k), sl(inp.v), sl(inp.g), sl(inp.beta), inp.scale, inp.A_log[hs].copy(),
+                   inp.dt_bias[hs].copy(), inp.lower_bound,
+                   initial_state=None if s0 is None else np.ascontiguousarray(s0[:, hs]),
+                   cu_seqlens=inp.cu_seqlens, threads=threads)
+    dt = time.perf_counter() - t
+    th = inp.B * inp.T * heads
+    return dict(value=round(th / dt, 1), unit="token·heads/s", cores=threads, kind="oracle",
+                sample="%s, heads 0..%d of %d, all %d tokens (%d token-heads), fp64 token-by-token, %.2f s wall"
+                % (cfg.name, heads - 1, inp.H, inp.T, th, dt))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle cpu_baseline leg")
+    ap.add_argument("--cpu-heads", type=int, default=24)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build measures one GPU only; run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from gated_delta_rule_prep_amd import kda
+    from gated_delta_rule_prep_amd.inputs import configs
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    from tests.kda_gpu import device_inputs
+
+    cfgs = configs()
+    fixed = run_workload(cfgs[2], args.steps, args.warmup, torch, kda, device_inputs)
+    varlen = run_workload(cfgs[3], args.steps, args.warmup, torch, kda, device_inputs)
+    rl, path = roofline(fixed)
+    rl_v, path_v = roofline(varlen)
+    cpu = None if args.no_cpu else cpu_baseline(cfgs[2], args.cpu_heads)
+    value = fixed["token_heads"] / (fixed["ms"] * 1e-3)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "token·heads/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(fixed["ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 in/out, fp16/fp32 MFMA, fp32 state on chip",
+        "data": "synthetic (seeded normal q/k/v/g/beta, A_log=log U[1,16], dt_bias~N(0,0.1), state~N(0,0.05))",
+        "config": {"workload": cfgs[2].name, "B": 1, "T": 8192, "H": 96, "K": 128, "V": 128,
+                   "state": "bf16", "lower_bound": -5.0, "chunk": 16},
+        "roofline": rl,
+        "path_roofline": path,
+        "kernels_ms": {"sched": round(fixed["sched_ms"], 4), "prep": round(fixed["prep_ms"], 4),
+                       "recur": round(fixed["recur_ms"], 4)},
+        "varlen_8x1024": {"workload": cfgs[3].name, "ms_per_step": round(varlen["ms"], 4),
+                          "value": round(varlen["token_heads"] / (varlen["ms"] * 1e-3), 1),
+                          "kernels_ms": {"sched": round(varlen["sched_ms"], 4), "prep": round(varlen["prep_ms"], 4),
+                                         "recur": round(varlen["recur_ms"], 4)},
+                          "roofline": rl_v, "path_roofline": path_v},
+        "status_ok": fixed["status"] == 0 and varlen["status"] == 0,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,286 @@
+// kda_api.cpp -- the C ABI declared in include/kda.h: host-side validation,
+// workspace layout and the three kernel launches.
+//
+// Argument rules follow the kernel API notes of the FlashKDA README mirror
+// (section "内核 API"): K = V = 128; states may be absent, bf16 or fp32 and must
+// share a dtype when both are given; with cu_seqlens B must be 1 and states are
+// [N, H, V, K]; without it each batch row is a sequence.  lower_bound lies in
+// [-5, 0] (the same table).  Every check runs on the host before any HIP call.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "../../include/kda.h"
+#include "kda_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+// The kernels move q, k, g, v, out and the states in 16-byte vectors.
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) != 0; }
+
+// Device capability cache: -1 unknown, 0 unsupported, 1 gfx950.
+constexpr int kMaxDevices = 64;
+int g_dev_ok[kMaxDevices];
+std::once_flag g_dev_once;
+
+int check_device() {
+  std::call_once(g_dev_once, [] {
+    for (int i = 0; i < kMaxDevices; ++i) g_dev_ok[i] = -1;
+  });
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(KDA_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(KDA_EUNSUPPORTED, "device index %d out of range", dev);
+  int ok = __atomic_load_n(&g_dev_ok[dev], __ATOMIC_ACQUIRE);
+  if (ok < 0) {
+    hipDeviceProp_t p;
+    e = hipGetDeviceProperties(&p, dev);
+    if (e != hipSuccess) return fail(KDA_EHIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+    ok = std::strncmp(p.gcnArchName, "gfx950", 6) == 0 ? 1 : 0;
+    __atomic_store_n(&g_dev_ok[dev], ok, __ATOMIC_RELEASE);
+  }
+  if (!ok) return fail(KDA_EUNSUPPORTED, "kda: device %d is not gfx950 (MI355X)", dev);
+  return KDA_OK;
+}
+
+// Size checks shared by kda_fwd and the layout query.  N is the sequence count.
+int check_sizes(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V, const int64_t* cu,
+                int64_t num_seqs, int has_cu, int64_t* N_out) {
+  if (B < 1 || T < 0 || H < 1)
+    return fail(KDA_EINVAL, "kda: need B >= 1, T >= 0, H >= 1 (got B=%lld T=%lld H=%lld)",
+                (long long)B, (long long)T, (long long)H);
+  if (K != kda::K || V != kda::V)
+    return fail(KDA_EINVAL, "kda: K and V must both be 128 (got K=%lld V=%lld)", (long long)K, (long long)V);
+  if (H > 65535) return fail(KDA_EINVAL, "kda: H=%lld exceeds 65535", (long long)H);
+  const bool with_cu = cu != nullptr || has_cu;
+  if (with_cu && B != 1) return fail(KDA_EINVAL, "kda: B must be 1 with cu_seqlens (got B=%lld)", (long long)B);
+  if (with_cu && num_seqs < 1)
+    return fail(KDA_EINVAL, "kda: num_seqs must be >= 1 with cu_seqlens (got %lld)", (long long)num_seqs);
+  const int64_t N = with_cu ? num_seqs : B;
+  // int32 token rows and chunk indices inside the kernels
+  if (B * T >= (int64_t(1) << 31) || N >= (int64_t(1) << 30))
+    return fail(KDA_EINVAL, "kda: B*T=%lld or N=%lld too large", (long long)(B * T), (long long)N);
+  if (N * H >= (int64_t(1) << 31)) return fail(KDA_EINVAL, "kda: N*H too large");
+  *N_out = N;
+  return KDA_OK;
+}
+
+}  // namespace
+
+namespace kda {
+
+bool layout_for(int64_t B, int64_t T, int64_t H, int64_t N, Layout* L) {
+  if (B < 1 || T < 0 || H < 1 || N < 0) return false;
+  const int64_t max_chunks = (B * T) / C + N;   // sum_n ceil(len_n / C) <= B*T/C + N
+  int64_t off = sizeof(WsHeader);
+  L->chunk_table = off;
+  off = align_up(off + max_chunks * (int64_t)sizeof(ChunkEntry), 256);
+  L->seq_table = off;
+  off = align_up(off + N * (int64_t)sizeof(SeqEntry), 256);
+  L->order = off;
+  off = align_up(off + N * 4, 256);
+  L->records = off;
+  L->rec_bytes = REC_BYTES;
+  L->max_chunks = max_chunks;
+  off += H * max_chunks * REC_BYTES;
+  L->total = align_up(off, 256);
+  return true;
+}
+
+}  // namespace kda
+
+extern "C" {
+
+int kda_version(void) { return 100; }  // 0.1.0
+
+const char* kda_get_last_error(void) { return g_last_error.c_str(); }
+
+size_t kda_fwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t num_seqs, int has_cu_seqlens) {
+  int64_t N = 0;
+  if (check_sizes(B, T, H, kda::K, kda::V, nullptr, num_seqs, has_cu_seqlens, &N) != KDA_OK) return 0;
+  kda::Layout L;
+  if (!kda::layout_for(B, T, H, N, &L)) return 0;
+  return (size_t)L.total;
+}
+
+int kda_workspace_layout(int64_t B, int64_t T, int64_t H, int64_t num_seqs, int has_cu_seqlens,
+                         int64_t offsets[7]) {
+  int64_t N = 0;
+  if (offsets == nullptr) return fail(KDA_EINVAL, "kda: offsets is NULL");
+  int rc = check_sizes(B, T, H, kda::K, kda::V, nullptr, num_seqs, has_cu_seqlens, &N);
+  if (rc != KDA_OK) return rc;
+  kda::Layout L;
+  if (!kda::layout_for(B, T, H, N, &L)) return fail(KDA_EINVAL, "kda: bad sizes");
+  offsets[0] = L.chunk_table;
+  offsets[1] = L.seq_table;
+  offsets[2] = L.order;
+  offsets[3] = L.records;
+  offsets[4] = L.rec_bytes;
+  offsets[5] = L.max_chunks;
+  offsets[6] = L.total;
+  return KDA_OK;
+}
+
+static int validate_common(const void* q, const void* k, const void* g, const void* beta, float scale,
+                           const float* A_log, const float* dt_bias, float lower_bound,
+                           const int64_t* cu, int64_t num_seqs, int64_t B, int64_t T, int64_t H,
+                           int64_t K, int64_t V, void* workspace, size_t workspace_bytes,
+                           kda::Layout* L, int64_t* N) {
+  int rc = check_sizes(B, T, H, K, V, cu, num_seqs, cu != nullptr, N);
+  if (rc != KDA_OK) return rc;
+  // With no tokens (B * T == 0) the token tensors are empty and may be NULL.
+  if (B * T > 0 && (!q || !k || !g || !beta))
+    return fail(KDA_EINVAL, "kda: a required input pointer is NULL");
+  if (!A_log || !dt_bias) return fail(KDA_EINVAL, "kda: A_log or dt_bias is NULL");
+  if (misaligned(q) || misaligned(k) || misaligned(g))
+    return fail(KDA_EINVAL, "kda: q, k and g must be 16-byte aligned");
+  if (!std::isfinite(scale)) return fail(KDA_EINVAL, "kda: scale is not finite");
+  if (!std::isfinite(lower_bound) || lower_bound < -5.0f || lower_bound > 0.0f)
+    return fail(KDA_EINVAL, "kda: lower_bound must lie in [-5, 0] (got %g)", (double)lower_bound);
+  if (!kda::layout_for(B, T, H, *N, L)) return fail(KDA_EINVAL, "kda: bad sizes");
+  if (!workspace) return fail(KDA_EINVAL, "kda: workspace is NULL");
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+    return fail(KDA_EINVAL, "kda: workspace must be 256-byte aligned");
+  if ((int64_t)workspace_bytes < L->total)
+    return fail(KDA_EWORKSPACE, "kda: workspace has %zu bytes, needs %lld", workspace_bytes,
+                (long long)L->total);
+  return KDA_OK;
+}
+
+static int fwd_impl(const void* q, const void* k, const void* v, const void* g, const void* beta, float scale,
+                    void* out, const float* A_log, const float* dt_bias, float lower_bound,
+                    const void* initial_state, int initial_state_dtype, void* final_state,
+                    int final_state_dtype, const int64_t* cu_seqlens, int64_t num_seqs, int64_t B,
+                    int64_t T, int64_t H, int64_t K, int64_t V, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream, hipEvent_t* ev) {
+  try {
+    if ((!v || !out) && B * T > 0) return fail(KDA_EINVAL, "kda: v or out is NULL");
+    auto dtype_ok = [](int d) { return d == KDA_DTYPE_NONE || d == KDA_DTYPE_BF16 || d == KDA_DTYPE_FP32; };
+    if (!dtype_ok(initial_state_dtype) || !dtype_ok(final_state_dtype))
+      return fail(KDA_EDTYPE, "kda: state dtype codes must be KDA_DTYPE_NONE/BF16/FP32");
+    if ((initial_state == nullptr) != (initial_state_dtype == KDA_DTYPE_NONE))
+      return fail(KDA_EDTYPE, "kda: initial_state pointer and dtype disagree");
+    if ((final_state == nullptr) != (final_state_dtype == KDA_DTYPE_NONE))
+      return fail(KDA_EDTYPE, "kda: final_state pointer and dtype disagree");
+    if (initial_state && final_state && initial_state_dtype != final_state_dtype)
+      return fail(KDA_EDTYPE, "kda: initial_state and final_state dtypes differ");
+    kda::Layout L;
+    int64_t N = 0;
+    int rc = validate_common(q, k, g, beta, scale, A_log, dt_bias, lower_bound, cu_seqlens, num_seqs, B, T,
+                             H, K, V, workspace, workspace_bytes, &L, &N);
+    if (rc != KDA_OK) return rc;
+    if (misaligned(v) || misaligned(out) || misaligned(initial_state) || misaligned(final_state))
+      return fail(KDA_EINVAL, "kda: v, out and the states must be 16-byte aligned");
+    rc = check_device();
+    if (rc != KDA_OK) return rc;
+
+    auto mark = [&](int i) -> hipError_t { return ev ? hipEventRecord(ev[i], stream) : hipSuccess; };
+    char* ws = static_cast<char*>(workspace);
+    hipError_t e = mark(0);
+    if (e != hipSuccess) return fail(KDA_EHIP, "kda: hipEventRecord: %s", hipGetErrorString(e));
+    kda::SchedArgs sa{cu_seqlens, N, B, T, ws, L};
+    e = kda::launch_sched(sa, stream);
+    if (e != hipSuccess) return fail(KDA_EHIP, "kda: scheduler launch: %s", hipGetErrorString(e));
+    e = mark(1);
+    if (e != hipSuccess) return fail(KDA_EHIP, "kda: hipEventRecord: %s", hipGetErrorString(e));
+    kda::PrepArgs pa{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                     static_cast<const uint16_t*>(g), static_cast<const uint16_t*>(beta), A_log, dt_bias,
+                     scale, lower_bound, H, ws, L};
+    e = kda::launch_prep(pa, stream);
+    if (e != hipSuccess) return fail(KDA_EHIP, "kda: prep launch: %s", hipGetErrorString(e));
+    e = mark(2);
+    if (e != hipSuccess) return fail(KDA_EHIP, "kda: hipEventRecord: %s", hipGetErrorString(e));
+    const int sdt = initial_state ? initial_state_dtype : final_state_dtype;
+    kda::RecurArgs ra{static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out), initial_state, final_state,
+                      sdt, N, H, ws, L};
+    e = kda::launch_recur(ra, stream);
+    if (e != hipSuccess) return fail(KDA_EHIP, "kda: recurrence launch: %s", hipGetErrorString(e));
+    e = mark(3);
+    if (e != hipSuccess) return fail(KDA_EHIP, "kda: hipEventRecord: %s", hipGetErrorString(e));
+    return KDA_OK;
+  } catch (...) {
+    return fail(KDA_EHIP, "kda: unexpected C++ exception");
+  }
+}
+
+int kda_fwd(const void* q, const void* k, const void* v, const void* g, const void* beta, float scale,
+            void* out, const float* A_log, const float* dt_bias, float lower_bound,
+            const void* initial_state, int initial_state_dtype, void* final_state,
+            int final_state_dtype, const int64_t* cu_seqlens, int64_t num_seqs, int64_t B,
+            int64_t T, int64_t H, int64_t K, int64_t V, void* workspace, size_t workspace_bytes,
+            hipStream_t stream) {
+  return fwd_impl(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
+                  initial_state_dtype, final_state, final_state_dtype, cu_seqlens, num_seqs, B, T, H, K, V,
+                  workspace, workspace_bytes, stream, nullptr);
+}
+
+int kda_fwd_profiled(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                     float scale, void* out, const float* A_log, const float* dt_bias, float lower_bound,
+                     const void* initial_state, int initial_state_dtype, void* final_state,
+                     int final_state_dtype, const int64_t* cu_seqlens, int64_t num_seqs, int64_t B,
+                     int64_t T, int64_t H, int64_t K, int64_t V, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream, hipEvent_t events[4]) {
+  if (events == nullptr || !events[0] || !events[1] || !events[2] || !events[3])
+    return fail(KDA_EINVAL, "kda: kda_fwd_profiled needs four events");
+  return fwd_impl(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
+                  initial_state_dtype, final_state, final_state_dtype, cu_seqlens, num_seqs, B, T, H, K, V,
+                  workspace, workspace_bytes, stream, events);
+}
+
+int kda_debug_prep(const void* q, const void* k, const void* g, const void* beta, float scale,
+                   const float* A_log, const float* dt_bias, float lower_bound, const int64_t* cu_seqlens,
+                   int64_t num_seqs, int64_t B, int64_t T, int64_t H, int64_t K, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream) {
+  try {
+    kda::Layout L;
+    int64_t N = 0;
+    int rc = validate_common(q, k, g, beta, scale, A_log, dt_bias, lower_bound, cu_seqlens, num_seqs, B, T,
+                             H, K, kda::V, workspace, workspace_bytes, &L, &N);
+    if (rc != KDA_OK) return rc;
+    rc = check_device();
+    if (rc != KDA_OK) return rc;
+    char* ws = static_cast<char*>(workspace);
+    kda::SchedArgs sa{cu_seqlens, N, B, T, ws, L};
+    hipError_t e = kda::launch_sched(sa, stream);
+    if (e != hipSuccess) return fail(KDA_EHIP, "kda: scheduler launch: %s", hipGetErrorString(e));
+    kda::PrepArgs pa{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                     static_cast<const uint16_t*>(g), static_cast<const uint16_t*>(beta), A_log, dt_bias,
+                     scale, lower_bound, H, ws, L};
+    e = kda::launch_prep(pa, stream);
+    if (e != hipSuccess) return fail(KDA_EHIP, "kda: prep launch: %s", hipGetErrorString(e));
+    return KDA_OK;
+  } catch (...) {
+    return fail(KDA_EHIP, "kda: unexpected C++ exception");
+  }
+}
+
+int kda_fwd_check_status(const void* workspace, hipStream_t stream, int* status) {
+  if (!workspace || !status) return fail(KDA_EINVAL, "kda: workspace or status is NULL");
+  hipError_t e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return fail(KDA_EHIP, "kda: hipStreamSynchronize: %s", hipGetErrorString(e));
+  int32_t st = 0;
+  e = hipMemcpy(&st, workspace, sizeof st, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return fail(KDA_EHIP, "kda: hipMemcpy: %s", hipGetErrorString(e));
+  *status = st;
+  return KDA_OK;
+}
+
+}  // extern "C"

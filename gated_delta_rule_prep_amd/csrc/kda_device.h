@@ -1,0 +1,66 @@
+// kda_device.h -- gfx950 device helpers: vector types, MFMA wrappers, bf16/fp16
+// conversions.  Lane layouts of the MFMA wrappers (wave64, l = lane, g = l / 16):
+//   16x16x32 (A 16xK=32, B 32x16):  A lane l holds row l%16, k = 8g..8g+7;
+//                                   B lane l holds col l%16, k = 8g..8g+7;
+//   16x16x16 (A 16x16, B 16x16):    A lane l holds row l%16, k = 4g..4g+3;
+//                                   B lane l holds col l%16, k = 4g..4g+3;
+//   accumulator (16x16):            lane l holds col l%16, rows 4g..4g+3.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x4 mfma_f16_k32(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f16_k16(f16x4 a, f16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_bf16_k32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// fp32 16x16x4: A lane l holds row l%16, k = l/16; B lane l holds col l%16, k = l/16.
+__device__ __forceinline__ f32x4 mfma_f32_k4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// bf16 bit pattern -> fp32 (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (hardware conversion).
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
+  __bf16 b = (__bf16)x;
+  return *reinterpret_cast<uint16_t*>(&b);
+}
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Stored position p (0..31) within a 32-channel block of the Qhat / -W record
+// rows holds channel kPermCh(p); kPermPos is the inverse.  This order lets a
+// lane of the recurrence feed its 16x16x32 operand straight from the two
+// accumulator tiles of the state it owns (rows 4g..4g+3 of both 16-row tiles).
+__host__ __device__ constexpr int kPermCh(int p) {
+  return ((p & 7) < 4) ? 4 * (p >> 3) + (p & 7) : 16 + 4 * (p >> 3) + (p & 7) - 4;
+}
+__host__ __device__ constexpr int kPermPos(int c) {
+  return (c < 16) ? 8 * (c >> 2) + (c & 3) : 8 * ((c - 16) >> 2) + 4 + ((c - 16) & 3);
+}
+
+}  // namespace kda

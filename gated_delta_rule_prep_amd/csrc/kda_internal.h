@@ -1,0 +1,92 @@
+// kda_internal.h -- types, constants and launchers shared by the gfx950 KDA
+// kernels and the C-ABI layer.  Not part of the public ABI (include/kda.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+constexpr int C = 16;     // chunk size (tokens per chunk)
+constexpr int K = 128;    // key channels
+constexpr int V = 128;    // value channels
+
+// Chunk record, one per (head, chunk), head-major.  Offsets in bytes.
+constexpr int REC_QH = 0;        // Qhat  fp16 [16][128], 32-block channel order (see kPerm)
+constexpr int REC_NW = 4096;     // -W    fp16 [16][128], same channel order
+constexpr int REC_KBT = 8192;    // Kbar^T fp16 [128][16]
+constexpr int REC_T = 12288;     // T     fp16 [16][16]
+constexpr int REC_MQK = 12800;   // Mqk   fp16 [16][16]
+constexpr int REC_GAM = 13312;   // gamma fp32 [128]
+constexpr int REC_BYTES = 13824;
+
+// Workspace header (first 256 bytes).
+struct WsHeader {
+  int32_t status;       // KDA_STATUS_*
+  int32_t chunk_count;  // number of valid chunk-table entries
+  int32_t pad[62];
+};
+
+struct ChunkEntry {     // chunk table entry
+  int32_t seq;          // sequence index n
+  int32_t row0;         // first flattened token row (b * T + t) of the chunk
+  int32_t len;          // tokens in the chunk (1..16)
+};
+
+struct SeqEntry {
+  int32_t first_chunk;
+  int32_t nchunks;
+  int32_t slot;         // position in the longest-first work order
+  int32_t pad;
+};
+
+struct Layout {
+  int64_t chunk_table;  // byte offsets into the workspace
+  int64_t seq_table;
+  int64_t order;
+  int64_t records;
+  int64_t rec_bytes;
+  int64_t max_chunks;
+  int64_t total;
+};
+
+// Returns false if the sizes are invalid.
+bool layout_for(int64_t B, int64_t T, int64_t H, int64_t N, Layout* out);
+
+struct SchedArgs {
+  const int64_t* cu;    // device, N + 1 entries, or nullptr
+  int64_t N, B, T;
+  char* ws;
+  Layout lay;
+};
+
+struct PrepArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* g;
+  const uint16_t* beta;
+  const float* A_log;
+  const float* dt_bias;
+  float scale;
+  float lower_bound;
+  int64_t H;
+  char* ws;
+  Layout lay;
+};
+
+struct RecurArgs {
+  const uint16_t* v;
+  uint16_t* out;
+  const void* s_in;
+  void* s_out;
+  int state_dtype;      // KDA_DTYPE_*
+  int64_t N, H;
+  char* ws;
+  Layout lay;
+};
+
+hipError_t launch_sched(const SchedArgs& a, hipStream_t s);
+hipError_t launch_prep(const PrepArgs& a, hipStream_t s);
+hipError_t launch_recur(const RecurArgs& a, hipStream_t s);
+
+}  // namespace kda

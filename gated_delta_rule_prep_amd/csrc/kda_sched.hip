@@ -1,0 +1,123 @@
+// kda_sched.hip -- cu_seqlens work scheduler (one workgroup, integer work only).
+//
+// Turns the sequence boundaries into
+//   * a chunk table: chunk i -> {sequence n, first flattened token row, length},
+//     chunks of at most 16 tokens that restart at every sequence start (so a
+//     chunk never straddles two sequences; the pages batch variable-length
+//     sequences through cu_seqlens: README mirror "内核 API", cu_seqlens row);
+//   * a per-sequence table {first chunk, chunk count, work-order slot};
+//   * a work order of the sequences, longest first, so that the chunk
+//     recurrence starts its longest serial chains first;
+//   * a status word: KDA_STATUS_BAD_CU_SEQLENS when cu_seqlens[0] != 0, the
+//     boundaries decrease, or cu_seqlens[N] != T.  Then every sequence gets zero
+//     chunks, so no later kernel touches a token.
+// Without cu_seqlens sequence n is batch row n: rows [n*T, (n+1)*T).
+#include "kda_internal.h"
+#include "../../include/kda.h"
+
+namespace kda {
+namespace {
+
+constexpr int kThreads = 1024;
+constexpr int kRankSortMax = 2048;   // longest-first order by rank sort up to this N
+
+__global__ __launch_bounds__(kThreads) void sched_kernel(SchedArgs a) {
+  WsHeader* hdr = reinterpret_cast<WsHeader*>(a.ws);
+  ChunkEntry* chunks = reinterpret_cast<ChunkEntry*>(a.ws + a.lay.chunk_table);
+  SeqEntry* seqs = reinterpret_cast<SeqEntry*>(a.ws + a.lay.seq_table);
+  int32_t* order = reinterpret_cast<int32_t*>(a.ws + a.lay.order);
+  const int tid = threadIdx.x;
+  const int64_t N = a.N;
+
+  __shared__ int s_bad;
+  __shared__ int32_t s_scan[kThreads];
+  __shared__ int32_t s_carry;
+  __shared__ int32_t s_nch[kRankSortMax];
+  if (tid == 0) {
+    s_bad = 0;
+    s_carry = 0;
+  }
+  __syncthreads();
+
+  // 1. validate the boundaries
+  if (a.cu) {
+    if (tid == 0 && (a.cu[0] != 0 || a.cu[N] != a.T)) s_bad = 1;
+    for (int64_t n = tid; n < N; n += kThreads)
+      if (a.cu[n + 1] < a.cu[n]) s_bad = 1;
+  }
+  __syncthreads();
+  const bool bad = s_bad != 0;
+
+  // 2. chunk counts and their exclusive prefix sum, one tile of kThreads at a time
+  for (int64_t base = 0; base < N; base += kThreads) {
+    const int64_t n = base + tid;
+    int32_t nch = 0;
+    if (n < N && !bad) {
+      const int64_t len = a.cu ? a.cu[n + 1] - a.cu[n] : a.T;
+      nch = (int32_t)((len + C - 1) / C);
+    }
+    s_scan[tid] = nch;
+    __syncthreads();
+    for (int off = 1; off < kThreads; off <<= 1) {  // Hillis-Steele inclusive scan
+      const int32_t x = tid >= off ? s_scan[tid - off] : 0;
+      __syncthreads();
+      s_scan[tid] += x;
+      __syncthreads();
+    }
+    if (n < N) {
+      seqs[n].first_chunk = s_carry + s_scan[tid] - nch;
+      seqs[n].nchunks = nch;
+      seqs[n].pad = 0;
+    }
+    __syncthreads();
+    if (tid == kThreads - 1) s_carry += s_scan[tid];
+    __syncthreads();
+  }
+  const int32_t total = s_carry;
+
+  // 3. chunk table: each thread fills the chunks of its sequences
+  for (int64_t n = tid; n < N; n += kThreads) {
+    const int64_t row0 = a.cu ? a.cu[n] : n * a.T;
+    const int64_t len = a.cu ? a.cu[n + 1] - a.cu[n] : a.T;
+    const int32_t first = seqs[n].first_chunk, nch = seqs[n].nchunks;
+    for (int32_t c = 0; c < nch; ++c) {
+      const int64_t rem = len - (int64_t)c * C;
+      chunks[first + c].seq = (int32_t)n;
+      chunks[first + c].row0 = (int32_t)(row0 + (int64_t)c * C);
+      chunks[first + c].len = (int32_t)(rem < C ? rem : C);
+    }
+  }
+  __syncthreads();
+
+  // 4. work order, longest first (ties by index); identity beyond kRankSortMax
+  const bool sort = N <= kRankSortMax;
+  if (sort)
+    for (int64_t n = tid; n < N; n += kThreads) s_nch[n] = seqs[n].nchunks;
+  __syncthreads();
+  for (int64_t n = tid; n < N; n += kThreads) {
+    int64_t rank = n;
+    if (sort) {
+      const int32_t mine = s_nch[n];
+      rank = 0;
+      for (int m = 0; m < (int)N; ++m) {
+        const int32_t o = s_nch[m];
+        rank += (o > mine) || (o == mine && m < n);
+      }
+    }
+    order[rank] = (int32_t)n;
+    seqs[n].slot = (int32_t)rank;
+  }
+  if (tid == 0) {
+    hdr->status = bad ? KDA_STATUS_BAD_CU_SEQLENS : KDA_STATUS_OK;
+    hdr->chunk_count = total;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_sched(const SchedArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(sched_kernel, dim3(1), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace kda

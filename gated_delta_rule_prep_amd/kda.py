@@ -1,0 +1,210 @@
+"""Thin ctypes binding of libkda.so (include/kda.h).
+
+Argument marshalling only: every step of the forward pass runs in the HIP
+kernels behind ``kda_fwd``.  torch supplies device memory (the tensors and the
+workspace) and the current HIP stream.  Importing this module loads the
+library and raises ImportError when it has not been built; there is no other
+code path.
+
+``fwd`` keeps the argument list and order of ``flash_kda.fwd`` in the FlashKDA
+README mirror (section "内核 API").
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkda.so")
+
+KDA_OK, KDA_EINVAL, KDA_EDTYPE, KDA_EWORKSPACE, KDA_EUNSUPPORTED, KDA_EHIP = range(6)
+KDA_DTYPE_NONE, KDA_DTYPE_BF16, KDA_DTYPE_FP32 = 0, 1, 2
+KDA_STATUS_OK, KDA_STATUS_BAD_CU_SEQLENS = 0, 1
+CHUNK = 16
+
+EXPORTS = ("kda_fwd", "kda_fwd_profiled", "kda_fwd_workspace_bytes", "kda_get_last_error", "kda_version",
+           "kda_fwd_check_status", "kda_workspace_layout", "kda_debug_prep")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError("libkda.so is not built (run gated_delta_rule_prep_amd/build.py or "
+                      "__graft_entry__.build()); there is no fallback path")
+
+_lib = ctypes.CDLL(LIB_PATH)
+_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_lib.kda_fwd.argtypes = [_p, _p, _p, _p, _p, ctypes.c_float, _p, _p, _p, ctypes.c_float,
+                         _p, ctypes.c_int, _p, ctypes.c_int, _p, _i64, _i64, _i64, _i64, _i64, _i64,
+                         _p, ctypes.c_size_t, _p]
+_lib.kda_fwd.restype = ctypes.c_int
+_lib.kda_fwd_profiled.argtypes = _lib.kda_fwd.argtypes + [ctypes.POINTER(ctypes.c_void_p)]
+_lib.kda_fwd_profiled.restype = ctypes.c_int
+_lib.kda_fwd_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int]
+_lib.kda_fwd_workspace_bytes.restype = ctypes.c_size_t
+_lib.kda_get_last_error.restype = ctypes.c_char_p
+_lib.kda_version.restype = ctypes.c_int
+_lib.kda_fwd_check_status.argtypes = [_p, _p, ctypes.POINTER(ctypes.c_int)]
+_lib.kda_fwd_check_status.restype = ctypes.c_int
+_lib.kda_workspace_layout.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.POINTER(ctypes.c_int64)]
+_lib.kda_workspace_layout.restype = ctypes.c_int
+_lib.kda_debug_prep.argtypes = [_p, _p, _p, _p, ctypes.c_float, _p, _p, ctypes.c_float, _p, _i64, _i64,
+                                _i64, _i64, _i64, _p, ctypes.c_size_t, _p]
+_lib.kda_debug_prep.restype = ctypes.c_int
+
+
+class KDAError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__("%s (code %d)" % (msg, code))
+        self.code = code
+
+
+class KDAValueError(KDAError, ValueError):
+    pass
+
+
+def lib() -> ctypes.CDLL:
+    return _lib
+
+
+def last_error() -> str:
+    return _lib.kda_get_last_error().decode()
+
+
+def version() -> int:
+    return _lib.kda_version()
+
+
+def _raise(code: int):
+    msg = last_error()
+    if code in (KDA_EINVAL, KDA_EDTYPE):
+        raise KDAValueError(code, msg)
+    raise KDAError(code, msg)
+
+
+def workspace_bytes(B: int, T: int, H: int, num_seqs: int = 0, has_cu_seqlens: bool = False) -> int:
+    return int(_lib.kda_fwd_workspace_bytes(B, T, H, num_seqs, int(has_cu_seqlens)))
+
+
+def workspace_layout(B: int, T: int, H: int, num_seqs: int = 0, has_cu_seqlens: bool = False) -> dict:
+    off = (ctypes.c_int64 * 7)()
+    rc = _lib.kda_workspace_layout(B, T, H, num_seqs, int(has_cu_seqlens), off)
+    if rc != KDA_OK:
+        _raise(rc)
+    keys = ("chunk_table", "seq_table", "order", "records", "rec_bytes", "max_chunks", "total")
+    return dict(zip(keys, [int(x) for x in off]))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _state_code(t: Optional[torch.Tensor]) -> int:
+    if t is None:
+        return KDA_DTYPE_NONE
+    if t.dtype == torch.bfloat16:
+        return KDA_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return KDA_DTYPE_FP32
+    raise KDAValueError(KDA_EDTYPE, "state tensors must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def _check(name, t, dtype, shape=None):
+    if t.dtype != dtype:
+        raise KDAValueError(KDA_EDTYPE, "%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise KDAValueError(KDA_EINVAL, "%s must be contiguous" % name)
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise KDAValueError(KDA_EINVAL, "%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def alloc_workspace(B: int, T: int, H: int, num_seqs: int, has_cu: bool, device) -> torch.Tensor:
+    n = workspace_bytes(B, T, H, num_seqs, has_cu)
+    if n == 0:
+        raise KDAValueError(KDA_EINVAL, "bad sizes for the workspace: B=%d T=%d H=%d" % (B, T, H))
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state=None, final_state=None,
+        cu_seqlens=None, workspace: Optional[torch.Tensor] = None, events=None):
+    """Chunked KDA forward into the caller's ``out`` (and ``final_state``).
+
+    Shapes and dtypes as in include/kda.h.  Runs on the current stream of the
+    tensors' device.  Returns ``out``.  ``events``: optional list of four
+    torch.cuda.Event (created with enable_timing=True); when given, the call
+    goes through kda_fwd_profiled, which records them around each kernel.
+    """
+    if q.dim() != 4:
+        raise KDAValueError(KDA_EINVAL, "q must be [B, T, H, K]")
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    dev = q.device
+    _check("q", q, torch.bfloat16)
+    _check("k", k, torch.bfloat16, (B, T, H, K))
+    _check("g", g, torch.bfloat16, (B, T, H, K))
+    _check("v", v, torch.bfloat16, (B, T, H, V))
+    _check("beta", beta, torch.bfloat16, (B, T, H))
+    _check("out", out, torch.bfloat16, (B, T, H, V))
+    _check("A_log", A_log, torch.float32, (H,))
+    _check("dt_bias", dt_bias, torch.float32, (H, K))
+    if cu_seqlens is not None:
+        _check("cu_seqlens", cu_seqlens, torch.int64)
+        if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+            raise KDAValueError(KDA_EINVAL, "cu_seqlens must be a 1-D int64 tensor of N + 1 >= 2 entries")
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    for name, t in (("initial_state", initial_state), ("final_state", final_state)):
+        if t is not None:
+            _state_code(t)
+            _check(name, t, t.dtype, (N, H, V, K))
+    tensors = [q, k, v, g, beta, out, A_log, dt_bias, initial_state, final_state, cu_seqlens]
+    for t in tensors:
+        if t is not None and t.device != dev:
+            raise KDAValueError(KDA_EINVAL, "all tensors must be on %s" % dev)
+    if dev.type != "cuda":
+        raise KDAValueError(KDA_EINVAL, "tensors must be on a HIP device, got %s" % dev)
+    if workspace is None:
+        workspace = alloc_workspace(B, T, H, N, cu_seqlens is not None, dev)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(out),
+            _ptr(A_log), _ptr(dt_bias), float(lower_bound), _ptr(initial_state),
+            _state_code(initial_state), _ptr(final_state), _state_code(final_state),
+            _ptr(cu_seqlens), N, B, T, H, K, V, _ptr(workspace), workspace.numel())
+    with torch.cuda.device(dev):
+        if events is None:
+            rc = _lib.kda_fwd(*args, _stream(dev))
+        else:
+            ev = (ctypes.c_void_p * 4)(*[e.cuda_event for e in events])
+            rc = _lib.kda_fwd_profiled(*args, _stream(dev), ev)
+    if rc != KDA_OK:
+        _raise(rc)
+    return out
+
+
+def check_status(workspace: torch.Tensor) -> int:
+    st = ctypes.c_int(-1)
+    with torch.cuda.device(workspace.device):
+        rc = _lib.kda_fwd_check_status(_ptr(workspace), _stream(workspace.device), ctypes.byref(st))
+    if rc != KDA_OK:
+        _raise(rc)
+    return st.value
+
+
+def debug_prep(q, k, g, beta, scale, A_log, dt_bias, lower_bound, cu_seqlens=None, workspace=None):
+    """Test-only: run the scheduler and prep kernels; returns the workspace tensor."""
+    B, T, H, K = q.shape
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    if workspace is None:
+        workspace = alloc_workspace(B, T, H, N, cu_seqlens is not None, q.device)
+    with torch.cuda.device(q.device):
+        rc = _lib.kda_debug_prep(_ptr(q), _ptr(k), _ptr(g), _ptr(beta), float(scale), _ptr(A_log),
+                                 _ptr(dt_bias), float(lower_bound), _ptr(cu_seqlens), N, B, T, H, K,
+                                 _ptr(workspace), workspace.numel(), _stream(q.device))
+    if rc != KDA_OK:
+        _raise(rc)
+    return workspace

@@ -1,0 +1,185 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) chunked Kimi Delta Attention forward.
+ *
+ * Citation key:
+ *   P1 = blog post "FlashKDA：月之暗面开源的 Kimi Delta Attention 高性能内核"
+ *        (guancyxx.cn), §一 (the gated delta-rule state update) and §二 2.1-2.4
+ *        (chunk size 16, the token-parallel / chunk-recurrent split, the 16 x 16
+ *        inverse, base-2 exponentials).
+ *   P2 = FlashKDA README mirror (ai-feeds.com), section "内核 API" (Kernel API):
+ *        the argument table of flash_kda.fwd and its four usage notes.
+ *
+ * What kda_fwd computes, for every sequence n and head h, with a K x V state S
+ * per (n, h) kept in math layout S[k][v]:
+ *   a_t[k] = lower_bound * sigmoid(exp(A_log[h]) * (g_t[k] + dt_bias[h][k]))
+ *   beta_t = sigmoid(beta_t logit)
+ *   kn_t   = k_t / sqrt(|k_t|^2 + 1e-6),  qn_t = scale * q_t / sqrt(|q_t|^2 + 1e-6)
+ *   S      = diag(exp(a_t)) S;   S += beta_t kn_t (v_t - S^T kn_t)^T;   o_t = S^T qn_t
+ * (P1 §一 gives a simplified scalar-gate form of this update; the per-channel
+ * gate shape and the in-kernel gate / L2-norm / sigmoid activations come from
+ * P2's argument table and its chunk_kda call.  The exact gate activation is not
+ * printed on the pages: the bounded sigmoid form above is this library's
+ * reading, chosen because it maps any raw gate into (lower_bound, 0).)
+ *
+ * All tensor pointers are DEVICE pointers to contiguous row-major buffers on
+ * the current HIP device; q, k, g, v, out and the states must be 16-byte aligned.  The caller owns every buffer, including the
+ * workspace; the library never allocates or frees device memory.  kda_fwd only
+ * enqueues work on `stream` (no host synchronisation, no device reads on the
+ * host); buffers must stay alive until the stream has passed the call.
+ *
+ * Shapes (P2 Kernel API), with N = B without cu_seqlens, len(cu_seqlens) - 1 with:
+ *   q, k, g        bf16  [B, T, H, K]
+ *   v              bf16  [B, T, H, V]
+ *   beta           bf16  [B, T, H]          (logits; sigmoid applied inside)
+ *   out            bf16  [B, T, H, V]       (written; rounded to nearest even)
+ *   A_log          fp32  [H]
+ *   dt_bias        fp32  [H, K]
+ *   initial_state  bf16 | fp32 | none  [N, H, V, K]   (stored [n,h,v,k] = S[k][v])
+ *   final_state    bf16 | fp32 | none  [N, H, V, K]   (written)
+ *   cu_seqlens     int64 [N + 1] or NULL  (then B must be 1 and T is the total)
+ * K = V = 128 is required (P2 Kernel API notes).
+ *
+ * Numerical range: the chunk recurrence multiplies fp16 operands with fp32
+ * accumulation.  Values derived from v and the state (the state itself, the
+ * per-chunk residuals) must stay below 65504 in magnitude; inputs drawn from
+ * activations of O(1..1000) scale satisfy this with a wide margin.
+ */
+#ifndef KDA_MI355X_H
+#define KDA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define KDA_OK 0
+#define KDA_EINVAL 1       /* null required pointer, misaligned tensor, bad size, K or V != 128,
+                              B != 1 with cu_seqlens, lower_bound outside [-5, 0], non-finite
+                              scale */
+#define KDA_EDTYPE 2       /* bad state dtype code, pointer/dtype mismatch, or initial and
+                              final state dtypes differ (P2 Kernel API notes) */
+#define KDA_EWORKSPACE 3   /* workspace too small (see kda_fwd_workspace_bytes) */
+#define KDA_EUNSUPPORTED 4 /* current device is not gfx950 */
+#define KDA_EHIP 5         /* a HIP runtime call or kernel launch failed */
+
+/* State dtype codes. */
+#define KDA_DTYPE_NONE 0
+#define KDA_DTYPE_BF16 1
+#define KDA_DTYPE_FP32 2
+
+/* Device-side status word values (kda_fwd_check_status). */
+#define KDA_STATUS_OK 0
+#define KDA_STATUS_BAD_CU_SEQLENS 1 /* cu_seqlens[0] != 0, not monotone, or cu_seqlens[N] != T;
+                                       then no token was processed and out is not written */
+
+/* Chunk size of the chunked form (P1 §二 2.1 uses 16). */
+#define KDA_CHUNK 16
+
+/*
+ * kda_fwd -- enqueue the chunked KDA forward pass on `stream`.
+ *
+ * Work is done by three kernels on `stream`: a scheduler that turns
+ * cu_seqlens into a chunk table and a longest-first work order, a
+ * token-parallel chunk-prep kernel (gate activation, L2 norm, in-chunk decay,
+ * the L / Mqk matrices and the 16 x 16 unit-lower-triangular inverse; P1 §二
+ * 2.2 first stage) and a chunk-recurrence kernel (the chunk-by-chunk delta-rule
+ * state update and the output; P1 §二 2.2 second stage).
+ *
+ * initial_state / final_state: NULL with dtype KDA_DTYPE_NONE, or a pointer
+ * with KDA_DTYPE_BF16 / KDA_DTYPE_FP32.  When both are given their dtypes must
+ * match.  A NULL initial state means a zero state; a NULL final state is not
+ * written.  final_state == initial_state (the same buffer) is allowed; any
+ * other overlap between inputs and outputs is undefined.
+ * cu_seqlens: NULL, or num_seqs + 1 int64 prefix sums on the device (B == 1).
+ * Its contents are checked on the device (see kda_fwd_check_status).
+ * workspace: at least kda_fwd_workspace_bytes(B, T, H, num_seqs, cu != NULL)
+ * bytes of device memory, 256-byte aligned.  Its contents are scratch between
+ * calls except for the status word.
+ * stream: a hipStream_t (NULL = the default stream).
+ *
+ * With no tokens (B * T == 0) the token tensors q, k, v, g, beta and out are
+ * empty and may be NULL; the final state is then the initial state.
+ * Every argument error is detected on the host before any HIP call is made.
+ * Returns KDA_OK or one of the codes above; kda_get_last_error() describes a
+ * nonzero return.  No exception crosses this boundary.
+ */
+int kda_fwd(const void* q, const void* k, const void* v, const void* g, const void* beta,
+            float scale, void* out, const float* A_log, const float* dt_bias, float lower_bound,
+            const void* initial_state, int initial_state_dtype, void* final_state,
+            int final_state_dtype, const int64_t* cu_seqlens, int64_t num_seqs, int64_t B,
+            int64_t T, int64_t H, int64_t K, int64_t V, void* workspace, size_t workspace_bytes,
+            hipStream_t stream);
+
+/*
+ * kda_fwd_profiled -- kda_fwd that also records events[0..3] on `stream`
+ * before the scheduler, before the prep kernel, before the recurrence kernel
+ * and after it, so a caller can time each kernel with hipEventElapsedTime.
+ * Same arguments, checks and results as kda_fwd; the four events are created
+ * and owned by the caller.
+ */
+int kda_fwd_profiled(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                     float scale, void* out, const float* A_log, const float* dt_bias, float lower_bound,
+                     const void* initial_state, int initial_state_dtype, void* final_state,
+                     int final_state_dtype, const int64_t* cu_seqlens, int64_t num_seqs, int64_t B,
+                     int64_t T, int64_t H, int64_t K, int64_t V, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream, hipEvent_t events[4]);
+
+/*
+ * Workspace bytes kda_fwd needs for these sizes (0 if the sizes are invalid).
+ * num_seqs is ignored when has_cu_seqlens is 0 (then N = B).
+ */
+size_t kda_fwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t num_seqs,
+                               int has_cu_seqlens);
+
+/* Thread-local description of the last nonzero return on this thread. */
+const char* kda_get_last_error(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int kda_version(void);
+
+/*
+ * kda_fwd_check_status -- read the device status word that the last kda_fwd
+ * using `workspace` wrote (KDA_STATUS_*).  Synchronises `stream` first; meant
+ * for tests and debugging, not for the hot loop.
+ */
+int kda_fwd_check_status(const void* workspace, hipStream_t stream, int* status);
+
+/*
+ * Workspace layout, for tests that decode the chunk records:
+ * offsets[0] = chunk table (int32 triples {sequence, first token row, length}),
+ * offsets[1] = per-sequence table (int32 quadruples {first chunk, chunk count,
+ *              work-order slot, unused}),
+ * offsets[2] = work order (int32 [N], sequences longest first),
+ * offsets[3] = chunk records, head-major: record (h, c) at
+ *              offsets[3] + (h * offsets[5] + c) * offsets[4],
+ * offsets[4] = bytes per record, offsets[5] = chunk capacity (floor(B*T/16) + N),
+ * offsets[6] = total bytes.  Returns KDA_OK or KDA_EINVAL.
+ * Record layout (bytes): [0, 4096) Qhat fp16 [16][128]; [4096, 8192) -W fp16
+ * [16][128]; both with the channels of each 32-block stored in the order
+ * {0-3, 16-19, 4-7, 20-23, 8-11, 24-27, 12-15, 28-31}; [8192, 12288) Kbar^T fp16
+ * [128][16]; [12288, 12800) T fp16 [16][16]; [12800, 13312) Mqk fp16 [16][16];
+ * [13312, 13824) gamma fp32 [128].
+ */
+int kda_workspace_layout(int64_t B, int64_t T, int64_t H, int64_t num_seqs, int has_cu_seqlens,
+                         int64_t offsets[7]);
+
+/*
+ * kda_debug_prep -- test-only: enqueue the scheduler and chunk-prep kernels
+ * alone (same arguments as kda_fwd minus v, out and the states), leaving the
+ * chunk table and records in `workspace` for inspection.
+ */
+int kda_debug_prep(const void* q, const void* k, const void* g, const void* beta, float scale,
+                   const float* A_log, const float* dt_bias, float lower_bound,
+                   const int64_t* cu_seqlens, int64_t num_seqs, int64_t B, int64_t T, int64_t H,
+                   int64_t K, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_MI355X_H */

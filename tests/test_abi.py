@@ -1,0 +1,144 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/kda.h declares, sizes its workspace, and rejects every bad argument on
+the host before making any HIP call (failure injection from the host)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+kda = pytest.importorskip("gated_delta_rule_prep_amd.kda")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert "kda_fwd" in names and len(names) >= 6
+    for n in names:
+        assert hasattr(kda.lib(), n), n
+    assert set(names) == set(kda.EXPORTS)
+
+
+def test_header_codes_match_binding():
+    src = open(HEADER).read()
+    for name, val in [("KDA_OK", 0), ("KDA_EINVAL", 1), ("KDA_EDTYPE", 2), ("KDA_EWORKSPACE", 3),
+                      ("KDA_EUNSUPPORTED", 4), ("KDA_EHIP", 5), ("KDA_DTYPE_NONE", 0), ("KDA_DTYPE_BF16", 1),
+                      ("KDA_DTYPE_FP32", 2), ("KDA_STATUS_BAD_CU_SEQLENS", 1), ("KDA_CHUNK", 16)]:
+        m = re.search(r"#define\s+%s\s+(\d+)" % name, src)
+        assert m and int(m.group(1)) == val, name
+        if hasattr(kda, name):
+            assert getattr(kda, name) == val
+
+
+def test_version():
+    assert kda.version() >= 100
+
+
+def test_workspace_sizes_and_layout():
+    lay = kda.workspace_layout(1, 8192, 96)
+    assert lay["max_chunks"] == 8192 // 16 + 1
+    assert lay["rec_bytes"] == 13824
+    assert lay["records"] % 256 == 0 and lay["total"] % 256 == 0
+    assert lay["total"] >= lay["records"] + 96 * lay["max_chunks"] * lay["rec_bytes"]
+    assert kda.workspace_bytes(1, 8192, 96) == lay["total"]
+    # varlen capacity: floor(T/16) + N chunks covers every split into N sequences
+    lay2 = kda.workspace_layout(1, 8192, 96, 12, True)
+    assert lay2["max_chunks"] == 512 + 12
+    assert kda.workspace_bytes(1, 0, 4) > 0
+    assert kda.workspace_bytes(1, 10, 4, 0, True) == 0      # no sequences with cu_seqlens
+    assert kda.workspace_bytes(0, 10, 4) == 0
+
+
+def test_chunk_capacity_bound_is_tight():
+    """sum ceil(l_n / 16) <= floor(T / 16) + N for every split of T into N parts."""
+    import itertools
+    for T in range(0, 40):
+        for N in range(1, 4):
+            for cuts in itertools.combinations_with_replacement(range(T + 1), N - 1):
+                b = [0, *cuts, T]
+                lens = [b[i + 1] - b[i] for i in range(N)]
+                assert sum((l + 15) // 16 for l in lens) <= T // 16 + N
+
+
+FAKE = ctypes.c_void_p(0x1000)        # never dereferenced: validation fails first
+WS = ctypes.c_void_p(0x100000)        # 256-byte aligned fake workspace
+
+
+def call(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, scale=0.088, out=FAKE, A_log=FAKE, dt_bias=FAKE,
+             lb=-5.0, s0=None, s0_dt=0, s1=None, s1_dt=0, cu=None, N=0, B=1, T=64, H=2, K=128, V=128,
+             ws=WS, ws_bytes=1 << 40, stream=None)
+    a.update(over)
+    return kda.lib().kda_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["scale"], a["out"], a["A_log"],
+                             a["dt_bias"], a["lb"], a["s0"], a["s0_dt"], a["s1"], a["s1_dt"], a["cu"], a["N"],
+                             a["B"], a["T"], a["H"], a["K"], a["V"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), kda.KDA_EINVAL),
+    (dict(k=None), kda.KDA_EINVAL),
+    (dict(v=None), kda.KDA_EINVAL),
+    (dict(g=None), kda.KDA_EINVAL),
+    (dict(beta=None), kda.KDA_EINVAL),
+    (dict(out=None), kda.KDA_EINVAL),
+    (dict(A_log=None), kda.KDA_EINVAL),
+    (dict(dt_bias=None), kda.KDA_EINVAL),
+    (dict(ws=None), kda.KDA_EINVAL),
+    (dict(ws=ctypes.c_void_p(0x100010)), kda.KDA_EINVAL),     # misaligned workspace
+    (dict(q=ctypes.c_void_p(0x1002)), kda.KDA_EINVAL),        # misaligned tensor
+    (dict(out=ctypes.c_void_p(0x1008)), kda.KDA_EINVAL),
+    (dict(K=64), kda.KDA_EINVAL),
+    (dict(V=256), kda.KDA_EINVAL),
+    (dict(B=0), kda.KDA_EINVAL),
+    (dict(T=-1), kda.KDA_EINVAL),
+    (dict(H=0), kda.KDA_EINVAL),
+    (dict(H=70000), kda.KDA_EINVAL),
+    (dict(cu=FAKE, N=2, B=2), kda.KDA_EINVAL),                # B != 1 with cu_seqlens
+    (dict(cu=FAKE, N=0), kda.KDA_EINVAL),
+    (dict(lb=-5.5), kda.KDA_EINVAL),
+    (dict(lb=0.25), kda.KDA_EINVAL),
+    (dict(lb=float("nan")), kda.KDA_EINVAL),
+    (dict(scale=float("inf")), kda.KDA_EINVAL),
+    (dict(B=1 << 20, T=1 << 12), kda.KDA_EINVAL),            # token rows overflow int32
+    (dict(s0=FAKE, s0_dt=3), kda.KDA_EDTYPE),
+    (dict(s0=FAKE, s0_dt=0), kda.KDA_EDTYPE),                 # pointer without dtype
+    (dict(s0=None, s0_dt=1), kda.KDA_EDTYPE),                 # dtype without pointer
+    (dict(s0=FAKE, s0_dt=1, s1=FAKE, s1_dt=2), kda.KDA_EDTYPE),  # dtypes differ
+    (dict(ws_bytes=1024), kda.KDA_EWORKSPACE),
+])
+def test_host_validation_rejects(over, code):
+    rc = call(**over)
+    assert rc == code, (rc, kda.last_error())
+    assert kda.last_error()
+
+
+def test_debug_prep_validation():
+    rc = kda.lib().kda_debug_prep(FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, FAKE, -6.0, None, 0, 1, 64, 2, 128, WS,
+                                  1 << 40, None)
+    assert rc == kda.KDA_EINVAL
+
+
+def test_python_binding_rejects_bad_tensors():
+    import torch
+    q = torch.zeros(1, 4, 2, 128, dtype=torch.bfloat16)
+    v = torch.zeros(1, 4, 2, 128, dtype=torch.bfloat16)
+    b = torch.zeros(1, 4, 2, dtype=torch.bfloat16)
+    A = torch.zeros(2)
+    dt = torch.zeros(2, 128)
+    with pytest.raises(ValueError):
+        kda.fwd(q.float(), q, v, q, b, 0.1, v.clone(), A, dt, -5.0)        # q not bf16
+    with pytest.raises(ValueError):
+        kda.fwd(q, q, v, q, b, 0.1, v.clone(), A, dt[:, :64].contiguous(), -5.0)
+    with pytest.raises(ValueError):
+        kda.fwd(q, q, v, q, b, 0.1, v.clone(), A, dt, -5.0,
+                initial_state=torch.zeros(1, 2, 128, 128, dtype=torch.float16))
+    with pytest.raises(ValueError):                                          # CPU tensors
+        kda.fwd(q, q, v, q, b, 0.1, v.clone(), A, dt, -5.0)

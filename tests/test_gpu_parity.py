@@ -1,0 +1,178 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 oracle.
+
+Small cases run the oracle on every output; the five full-size workloads run
+the oracle on a sample of heads (heads never interact, so slicing the inputs
+along H gives the oracle's exact values for those heads) and compare those
+heads' outputs and final states element by element.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gated_delta_rule_prep_amd.inputs import configs, make_inputs, ragged_lengths, f32_to_bf16_bits
+from tests.kda_gpu import assert_close, device_inputs, run_gpu, say, to_f64
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+
+def oracle_run(inp, heads=None):
+    if heads is None:
+        heads = list(range(inp.H))
+    sl = lambda x: np.ascontiguousarray(x[:, :, heads])
+    s0 = inp.initial_state_f64()
+    return oracle.kda_fwd(sl(inp.q), sl(inp.k), sl(inp.v), sl(inp.g), sl(inp.beta), inp.scale,
+                          inp.A_log[heads].copy(), inp.dt_bias[heads].copy(), inp.lower_bound,
+                          initial_state=None if s0 is None else np.ascontiguousarray(s0[:, heads]),
+                          output_final_state=True, cu_seqlens=inp.cu_seqlens)
+
+
+def check(inp, heads=None, tag=""):
+    say("case %s B=%d T=%d H=%d N=%d state=%s lb=%g" % (tag or inp.name, inp.B, inp.T, inp.H, inp.N,
+                                                      inp.state_dtype, inp.lower_bound))
+    out, fin = run_gpu(inp)
+    torch.cuda.synchronize()
+    ref_o, ref_f = oracle_run(inp, heads)
+    hs = list(range(inp.H)) if heads is None else heads
+    x = to_f64(out)[:, :, hs]
+    assert_close(x, ref_o, "out")
+    if inp.output_final_state:
+        assert_close(to_f64(fin)[:, hs], ref_f, "final_state", inp.state_dtype)
+    return out, fin
+
+
+SMALL = [
+    dict(B=1, T=37, H=2, state_dtype=None, lower_bound=-5.0, seed=100),
+    dict(B=1, T=64, H=1, state_dtype="fp32", initial_state=False, lower_bound=-5.0, seed=101),
+    dict(B=2, T=100, H=3, state_dtype="fp32", lower_bound=-5.0, seed=102),
+    dict(B=1, T=300, H=2, state_dtype="bf16", lower_bound=-5.0, seed=103),
+    dict(B=1, T=257, H=4, state_dtype="fp32", lower_bound=-0.5, seed=104, g_std=2.0),
+    dict(B=3, T=16, H=2, state_dtype="bf16", lower_bound=0.0, seed=105),
+    dict(B=1, T=1, H=5, state_dtype="fp32", lower_bound=-5.0, seed=106),
+    dict(B=1, T=113, H=2, state_dtype="fp32", lower_bound=-2.0, seed=107, seq_lens=[1, 15, 17, 0, 40, 16, 24]),
+    dict(B=1, T=300, H=3, state_dtype="bf16", lower_bound=-5.0, seed=108, seq_lens=ragged_lengths(300, 7)),
+]
+
+
+@pytest.mark.parametrize("i", range(len(SMALL)))
+def test_small_parity(i):
+    kw = dict(SMALL[i])
+    inp = make_inputs(**kw)
+    check(inp, tag="small%d" % i)
+
+
+@pytest.mark.parametrize("ci", range(5))
+def test_config_parity(ci):
+    cfg = configs()[ci]
+    inp = cfg.make()
+    heads = None if inp.H <= 4 else sorted({0, 1, inp.H // 2, inp.H - 1})
+    check(inp, heads, tag="config%d %s" % (ci, cfg.name))
+
+
+def test_deterministic_bitwise():
+    inp = make_inputs(1, 500, 4, seed=200, state_dtype="fp32")
+    say("case determinism T=500 H=4")
+    o1, f1 = run_gpu(inp)
+    o2, f2 = run_gpu(inp)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(f1, f2)
+
+
+def test_varlen_equals_separate_calls_bitwise():
+    lens = [1, 15, 17, 33, 130, 60]
+    inp = make_inputs(1, sum(lens), 3, seed=201, state_dtype="bf16", seq_lens=lens)
+    say("case varlen-vs-separate lens=%s" % lens)
+    out, fin = run_gpu(inp)
+    cu = inp.cu_seqlens
+    for n in range(len(lens)):
+        a, b = int(cu[n]), int(cu[n + 1])
+        sub = make_inputs(1, b - a, 3, seed=201, state_dtype="bf16")
+        for f in ("q", "k", "v", "g", "beta"):
+            setattr(sub, f, np.ascontiguousarray(getattr(inp, f)[:, a:b]))
+        sub.A_log, sub.dt_bias = inp.A_log, inp.dt_bias
+        sub.initial_state = np.ascontiguousarray(inp.initial_state[n:n + 1])
+        o, f = run_gpu(sub)
+        torch.cuda.synchronize()
+        assert torch.equal(o.view(torch.int16), out[:, a:b].view(torch.int16)), n
+        assert torch.equal(f[0].view(torch.int16), fin[n].view(torch.int16)), n
+
+
+def test_resume_split_matches_one_call():
+    inp = make_inputs(1, 400, 2, seed=202, state_dtype="fp32")
+    say("case resume T=400 split at 163")
+    out, fin = run_gpu(inp)
+    t1 = 163
+    d = device_inputs(inp)
+    from gated_delta_rule_prep_amd import kda
+    o = torch.empty_like(out)
+    mid = torch.empty_like(fin)
+    f2 = torch.empty_like(fin)
+    sl = lambda t, a, b: t[:, a:b].contiguous()
+    kda.fwd(sl(d["q"], 0, t1), sl(d["k"], 0, t1), sl(d["v"], 0, t1), sl(d["g"], 0, t1), sl(d["beta"], 0, t1),
+            inp.scale, o[:, :t1], d["A_log"], d["dt_bias"], inp.lower_bound, initial_state=d["initial_state"],
+            final_state=mid)
+    o2 = torch.empty_like(out[:, t1:])
+    kda.fwd(sl(d["q"], t1, 400), sl(d["k"], t1, 400), sl(d["v"], t1, 400), sl(d["g"], t1, 400),
+            sl(d["beta"], t1, 400), inp.scale, o2, d["A_log"], d["dt_bias"], inp.lower_bound,
+            initial_state=mid, final_state=f2)
+    torch.cuda.synchronize()
+    ref_o, ref_f = oracle_run(inp)
+    assert_close(np.concatenate([to_f64(o[:, :t1]), to_f64(o2)], axis=1), ref_o, "out(split)")
+    assert_close(to_f64(f2), ref_f, "final(split)", "fp32")
+
+
+def test_inplace_state():
+    inp = make_inputs(1, 90, 2, seed=203, state_dtype="fp32")
+    say("case in-place state")
+    d = device_inputs(inp)
+    out = torch.empty(1, 90, 2, 128, dtype=torch.bfloat16, device="cuda")
+    st = d["initial_state"].clone()
+    from gated_delta_rule_prep_amd import kda
+    kda.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], inp.scale, out, d["A_log"], d["dt_bias"],
+            inp.lower_bound, initial_state=st, final_state=st)
+    o_ref, f_ref = run_gpu(inp, d=d)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), o_ref.view(torch.int16))
+    assert torch.equal(st, f_ref)
+
+
+def test_identity_lower_bound_zero_beta_zero():
+    inp = make_inputs(1, 50, 2, seed=204, state_dtype="fp32", lower_bound=0.0)
+    inp.beta[:] = f32_to_bf16_bits(np.array([-1e4], np.float32))[0]
+    say("case identity lb=0 beta=0")
+    out, fin = run_gpu(inp)
+    torch.cuda.synchronize()
+    assert torch.equal(fin.cpu(), torch.from_numpy(inp.initial_state))
+    ref_o, _ = oracle_run(inp)
+    assert_close(to_f64(out), ref_o, "out")
+
+
+def test_zero_tokens_passes_state_through():
+    inp = make_inputs(1, 0, 3, seed=205, state_dtype="bf16")
+    say("case T=0")
+    out, fin = run_gpu(inp)
+    torch.cuda.synchronize()
+    assert torch.equal(fin.cpu().view(torch.int16), torch.from_numpy(inp.initial_state.view(np.int16)))
+
+
+def test_bad_cu_seqlens_sets_status_and_touches_nothing():
+    from gated_delta_rule_prep_amd import kda
+    inp = make_inputs(1, 64, 2, seed=206, state_dtype="fp32", seq_lens=[30, 34])
+    d = device_inputs(inp)
+    for bad in ([0, 40, 30], [1, 30, 64], [0, 30, 63]):
+        say("case bad cu_seqlens %s" % bad)
+        cu = torch.tensor(bad, dtype=torch.int64, device="cuda")
+        out = torch.zeros(1, 64, 2, 128, dtype=torch.bfloat16, device="cuda")
+        fin = torch.zeros(2, 2, 128, 128, dtype=torch.float32, device="cuda")
+        ws = kda.alloc_workspace(1, 64, 2, 2, True, "cuda")
+        kda.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], inp.scale, out, d["A_log"], d["dt_bias"],
+                inp.lower_bound, initial_state=d["initial_state"], final_state=fin, cu_seqlens=cu, workspace=ws)
+        assert kda.check_status(ws) == kda.KDA_STATUS_BAD_CU_SEQLENS
+        assert torch.count_nonzero(out.view(torch.int16)) == 0
+    ws = kda.alloc_workspace(1, 64, 2, 2, True, "cuda")
+    run_gpu(inp, d=d, workspace=ws)
+    assert kda.check_status(ws) == kda.KDA_STATUS_OK

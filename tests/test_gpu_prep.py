@@ -1,0 +1,96 @@
+"""GPU unit test of the scheduler and chunk-prep kernels alone: the chunk table
+and every chunk record are decoded from the workspace and compared with the
+fp64 chunked-form intermediates of tests/chunked_ref.py."""
+import numpy as np
+import pytest
+import torch
+
+from gated_delta_rule_prep_amd.inputs import make_inputs
+from tests import chunked_ref
+from tests.kda_gpu import device_inputs, say
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+EPS = 1e-6
+
+
+def perm_ch(p):
+    j, g = p % 8, p // 8
+    return 4 * g + j if j < 4 else 16 + 4 * g + j - 4
+
+
+PERM = np.array([(p // 32) * 32 + perm_ch(p % 32) for p in range(128)])
+
+
+def unpermute(x):
+    y = np.empty_like(x)
+    y[..., PERM] = x
+    return y
+
+
+def test_chunk_table_and_records_match_chunked_form():
+    from gated_delta_rule_prep_amd import kda
+    lens = [1, 15, 17, 40, 0, 33]
+    T = sum(lens)
+    H = 3
+    inp = make_inputs(1, T, H, seed=300, lower_bound=-5.0, seq_lens=lens)
+    say("case prep records lens=%s H=%d" % (lens, H))
+    d = device_inputs(inp)
+    ws = kda.debug_prep(d["q"], d["k"], d["g"], d["beta"], inp.scale, d["A_log"], d["dt_bias"], inp.lower_bound,
+                        cu_seqlens=d["cu_seqlens"])
+    torch.cuda.synchronize()
+    lay = kda.workspace_layout(1, T, H, len(lens), True)
+    buf = ws.cpu().numpy()
+    hdr = buf[:8].view(np.int32)
+    assert hdr[0] == kda.KDA_STATUS_OK
+    nch = sum((l + 15) // 16 for l in lens)
+    assert hdr[1] == nch
+    table = buf[lay["chunk_table"]:lay["chunk_table"] + 12 * nch].view(np.int32).reshape(nch, 3)
+    want = []
+    cu = inp.cu_seqlens
+    for n, l in enumerate(lens):
+        for c in range(0, l, 16):
+            want.append((n, int(cu[n]) + c, min(16, l - c)))
+    assert [tuple(r) for r in table] == want
+    seqs = buf[lay["seq_table"]:lay["seq_table"] + 16 * len(lens)].view(np.int32).reshape(-1, 4)
+    order = buf[lay["order"]:lay["order"] + 4 * len(lens)].view(np.int32)
+    assert list(seqs[:, 1]) == [(l + 15) // 16 for l in lens]
+    assert sorted(order) == list(range(len(lens)))
+    counts = [seqs[n, 1] for n in order]
+    assert counts == sorted(counts, reverse=True)               # longest first
+
+    f = chunked_ref.decode_bf16
+    qf, kf, gf, bf = f(inp.q)[0], f(inp.k)[0], f(inp.g)[0], f(inp.beta)[0]
+    R = lay["rec_bytes"]
+    worst = {}
+    for h in range(H):
+        A = np.exp(np.float64(inp.A_log[h]))
+        for ci, (n, r0, ln) in enumerate(want):
+            sl = slice(r0, r0 + ln)
+            a = inp.lower_bound / (1 + np.exp(-A * (gf[sl, h] + inp.dt_bias[h].astype(np.float64))))
+            kk, qq = kf[sl, h], qf[sl, h]
+            kn = kk / np.sqrt((kk * kk).sum(-1, keepdims=True) + EPS)
+            qn = inp.scale * qq / np.sqrt((qq * qq).sum(-1, keepdims=True) + EPS)
+            P = chunked_ref.chunk_pieces(qn, kn, a, 1 / (1 + np.exp(-bf[sl, h])))
+            off = lay["records"] + (h * lay["max_chunks"] + ci) * R
+            rec = buf[off:off + R]
+            f16 = lambda o, shape: rec[o:o + 2 * int(np.prod(shape))].view(np.float16).astype(np.float64).reshape(shape)
+            got = dict(Qh=unpermute(f16(0, (16, 128)))[:ln], W=-unpermute(f16(4096, (16, 128)))[:ln],
+                       Kb=f16(8192, (128, 16)).T[:ln], T=f16(12288, (16, 16))[:ln, :ln],
+                       M=f16(12800, (16, 16))[:ln, :ln], gamma=rec[13312:13824].view(np.float32).astype(np.float64))
+            ref = dict(Qh=P["Qh"], W=P["T"] @ P["Kh"], Kb=P["Kb"], T=P["T"], M=P["M"], gamma=P["gamma"])
+            # padded rows / columns of a partial chunk are exactly zero
+            assert np.all(f16(0, (16, 128))[ln:] == 0) and np.all(f16(4096, (16, 128))[ln:] == 0)
+            assert np.all(f16(8192, (128, 16))[:, ln:] == 0)
+            assert np.all(f16(12288, (16, 16))[ln:] == 0) and np.all(f16(12800, (16, 16))[ln:] == 0)
+            # structure: T lower triangular, Mqk lower triangular incl. diagonal
+            assert np.all(np.triu(got["T"], 1) == 0) and np.all(np.triu(got["M"], 1) == 0)
+            for key in ref:
+                e = np.abs(got[key] - ref[key]).max() / max(np.abs(ref[key]).max(), 1e-30)
+                worst[key] = max(worst.get(key, 0.0), e)
+    say("  worst relative max error per record field: %s" % {k: "%.2e" % v for k, v in worst.items()})
+    assert worst["Qh"] < 2e-3 and worst["Kb"] < 2e-3 and worst["gamma"] < 1e-5
+    assert worst["T"] < 1e-2 and worst["M"] < 1e-2 and worst["W"] < 1e-2
