@@ -136,7 +136,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle cpu_baseline leg")
-    ap.add_argument("--cpu-heads", type=int, default=24)
+    ap.add_argument("--cpu-heads", type=int, default=96, help="heads of the headline workload the oracle runs")
+    ap.add_argument("--only", choices=["both", "fixed", "varlen"], default="both",
+                    help="time only one workload (for profiler runs); the JSON line needs both")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this build measures one GPU only; run it with --gpus 1", file=sys.stderr)
@@ -149,6 +151,12 @@ def main():
     from tests.kda_gpu import device_inputs
 
     cfgs = configs()
+    if args.only != "both":
+        res = run_workload(cfgs[2] if args.only == "fixed" else cfgs[3], args.steps, args.warmup, torch, kda,
+                           device_inputs)
+        print(json.dumps({"workload": res["inp"].name, "ms_per_step": round(res["ms"], 4),
+                          "kernels_ms": {k: round(res[k + "_ms"], 4) for k in ("sched", "prep", "recur")}}))
+        return
     fixed = run_workload(cfgs[2], args.steps, args.warmup, torch, kda, device_inputs)
     varlen = run_workload(cfgs[3], args.steps, args.warmup, torch, kda, device_inputs)
     rl, path = roofline(fixed)
