@@ -18,8 +18,12 @@ OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkda.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
+# -amdgpu-mfma-vgpr-form keeps MFMA accumulators in ordinary VGPRs: the
+# recurrence scales and converts its state accumulators with VALU instructions
+# every chunk, and accumulators placed in AGPRs cost a copy each way.
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-Wall", "-Wno-unused-function",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-mfma-vgpr-form=1",
          "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 SOURCES = ["kda_api.cpp", "kda_sched.hip", "kda_prep.hip", "kda_recur.hip"]
 

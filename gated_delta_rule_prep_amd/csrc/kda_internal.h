@@ -36,8 +36,8 @@ struct ChunkEntry {     // chunk table entry
 struct SeqEntry {
   int32_t first_chunk;
   int32_t nchunks;
-  int32_t slot;         // position in the longest-first work order
-  int32_t pad;
+  int32_t row0;         // first flattened token row of the sequence
+  int32_t len;          // tokens in the sequence
 };
 
 struct Layout {

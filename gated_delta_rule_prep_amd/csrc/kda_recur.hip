@@ -20,6 +20,12 @@
 // itself stays fp32.  The channel order of Qhat / -W in the record matches the
 // rows a lane holds in its two accumulator tiles (kPermCh), so the conversion
 // needs no lane exchange.
+//
+// Memory pipeline: the record and the value rows of chunk c+2 are loaded into
+// registers while chunk c is computed (two register sets, the loop unrolled by
+// two), then written to one of two LDS buffers; one barrier per chunk.  Values
+// are staged transposed and already in fp16; the output tile goes through LDS
+// so that it leaves as 16-byte row stores, one chunk behind.
 #include "kda_device.h"
 #include "kda_internal.h"
 #include "../../include/kda.h"
@@ -28,17 +34,157 @@ namespace kda {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int SV = V + 8;   // bf16 [16][SV] staged values
+constexpr int kRecPieces = REC_BYTES / 16;   // 864 16-byte pieces per record
+constexpr int SVT = C + 4;                   // fp16 [128][SVT] transposed values
+constexpr int SO = V + 8;                    // bf16 [16][SO] output tile
+
+// LDS copy of one record, rows padded so that the 16 lanes that read one
+// operand row each land on distinct banks (a 256-byte row stride maps every
+// row onto the same banks): Qhat / -W rows 272 B, Kbar^T / T / Mqk rows 48 B.
+constexpr int SQ = K + 8;                    // fp16 row stride of Qhat and -W
+constexpr int SK = C + 8;                    // fp16 row stride of Kbar^T, T, Mqk
+
+struct __align__(16) Stage {
+  __align__(16) _Float16 qh[C][SQ];
+  __align__(16) _Float16 nw[C][SQ];
+  __align__(16) _Float16 kbt[K][SK];
+  __align__(16) _Float16 tm[C][SK];
+  __align__(16) _Float16 mq[C][SK];
+  __align__(16) float gam[K];
+  __align__(16) _Float16 vt[V][SVT];
+};
 
 struct __align__(16) RecurSmem {
-  __align__(16) char rec[REC_BYTES];
-  __align__(16) uint16_t v[C][SV];
+  Stage buf[2];
+  __align__(16) uint16_t ot[2][C][SO];
 };
+
+// One chunk's worth of global data held in registers.
+struct Prefetch {
+  u32x4 rec[4];
+  u32x4 v;
+};
+
+// Chunk j of a sequence: first flattened token row and length (1..16).
+struct Rows {
+  int64_t row0;
+  int len;
+};
+__device__ __forceinline__ Rows chunk_rows(const SeqEntry& se, int j) {
+  const int rem = se.len - C * j;
+  return Rows{(int64_t)se.row0 + C * j, rem < C ? rem : C};
+}
 
 __device__ __forceinline__ f16x4 f16x4_of(f32x4 x) {
   f16x4 r;
   r[0] = (_Float16)x[0]; r[1] = (_Float16)x[1]; r[2] = (_Float16)x[2]; r[3] = (_Float16)x[3];
   return r;
+}
+
+// Every load is unconditional (indices clamped into range) so that the
+// compiler can count outstanding loads exactly and wait only for the chunk it
+// stages, not for the prefetch issued after it.
+__device__ __forceinline__ void load_chunk(Prefetch& p, const char* recs, const SeqEntry& se,
+                                           const uint16_t* v, int chunk, int64_t H, int h, int tid) {
+  chunk = min(chunk, se.nchunks - 1);
+  const Rows cr = chunk_rows(se, chunk);
+  const char* rec = recs + (int64_t)chunk * REC_BYTES;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int piece = min(tid + kThreads * j, kRecPieces - 1);
+    p.rec[j] = *reinterpret_cast<const u32x4*>(rec + 16 * piece);
+  }
+  const int r = min(tid >> 4, cr.len - 1), c8 = (tid & 15) * 8;
+  p.v = *reinterpret_cast<const u32x4*>(v + ((cr.row0 + r) * H + h) * V + c8);
+}
+
+// Thread tid stages record pieces tid + 256 j (16 bytes each): j = 0 is a
+// piece of Qhat, j = 1 of -W, j = 2 of Kbar^T, and j = 3 (tid < 96) of T, Mqk
+// or gamma.  Value rows past the end of a partial chunk are staged as zeros.
+__device__ __forceinline__ void stage_chunk(const Prefetch& p, Stage& st, int len, int tid) {
+  const int r16 = tid >> 4, c16 = (tid & 15) * 8;        // Qhat / -W: row, first fp16 column
+  *reinterpret_cast<u32x4*>(&st.qh[r16][c16]) = p.rec[0];
+  *reinterpret_cast<u32x4*>(&st.nw[r16][c16]) = p.rec[1];
+  *reinterpret_cast<u32x4*>(&st.kbt[tid >> 1][(tid & 1) * 8]) = p.rec[2];
+  if (tid < 32) {
+    *reinterpret_cast<u32x4*>(&st.tm[tid >> 1][(tid & 1) * 8]) = p.rec[3];
+  } else if (tid < 64) {
+    *reinterpret_cast<u32x4*>(&st.mq[(tid - 32) >> 1][(tid & 1) * 8]) = p.rec[3];
+  } else if (tid < 96) {
+    *reinterpret_cast<u32x4*>(&st.gam[4 * (tid - 64)]) = p.rec[3];
+  }
+  const bool live = r16 < len;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t w = live ? p.v[j] : 0u;
+    st.vt[c16 + 2 * j][r16] = (_Float16)bf16_lo(w);
+    st.vt[c16 + 2 * j + 1][r16] = (_Float16)bf16_hi(w);
+  }
+}
+
+// Output rows of a chunk from the LDS tile: 16 rows x 256 B, 16 B per thread.
+__device__ __forceinline__ void store_out(const uint16_t (*ot)[SO], const Rows& cr, uint16_t* out, int64_t H,
+                                          int h, int tid) {
+  const int r = tid >> 4, c8 = (tid & 15) * 8;
+  if (r < cr.len)
+    *reinterpret_cast<u32x4*>(out + ((cr.row0 + r) * H + h) * V + c8) =
+        *reinterpret_cast<const u32x4*>(&ot[r][c8]);
+}
+
+// One chunk step on the staged record: updates Z, writes the output tile.
+__device__ __forceinline__ void step(f32x4 (&Z)[8][2], const Stage& st, uint16_t (*ot)[SO], int wave, int lg,
+                                     int lc) {
+  // ---- U = T V
+  f32x4 E[2], O[2];
+  const f16x4 aT = *reinterpret_cast<const f16x4*>(&st.tm[lc][4 * lg]);
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const f16x4 bv = *reinterpret_cast<const f16x4*>(&st.vt[32 * wave + 16 * nt + lc][4 * lg]);
+    E[nt] = mfma_f16_k16(aT, bv, f32x4{0.f, 0.f, 0.f, 0.f});
+    O[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // ---- E += (-W) Z ; O = Qhat Z
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const f16x8 aw = *reinterpret_cast<const f16x8*>(&st.nw[lc][32 * s + 8 * lg]);
+    const f16x8 aq = *reinterpret_cast<const f16x8*>(&st.qh[lc][32 * s + 8 * lg]);
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      f16x8 zb;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        zb[i] = (_Float16)Z[2 * s][nt][i];
+        zb[4 + i] = (_Float16)Z[2 * s + 1][nt][i];
+      }
+      E[nt] = mfma_f16_k32(aw, zb, E[nt]);
+      O[nt] = mfma_f16_k32(aq, zb, O[nt]);
+    }
+  }
+
+  // ---- O += Mqk E
+  f16x4 eb[2];
+  const f16x4 am = *reinterpret_cast<const f16x4*>(&st.mq[lc][4 * lg]);
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    eb[nt] = f16x4_of(E[nt]);
+    O[nt] = mfma_f16_k16(am, eb[nt], O[nt]);
+  }
+
+  // ---- Z = diag(gam) Z + Kbar^T E
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    const f32x4 gm = *reinterpret_cast<const f32x4*>(&st.gam[16 * m + 4 * lg]);
+    const f16x4 ak = *reinterpret_cast<const f16x4*>(&st.kbt[16 * m + lc][4 * lg]);
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) Z[m][nt] = mfma_f16_k16(ak, eb[nt], Z[m][nt] * gm);
+  }
+
+  // ---- output tile (rows 4lg + i, columns 32 wave + 16 nt + lc)
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ot[4 * lg + i][32 * wave + 16 * nt + lc] = f32_to_bf16(O[nt][i]);
 }
 
 __global__ __launch_bounds__(kThreads) void recur_kernel(RecurArgs a) {
@@ -49,8 +195,8 @@ __global__ __launch_bounds__(kThreads) void recur_kernel(RecurArgs a) {
   const int32_t* order = reinterpret_cast<const int32_t*>(a.ws + a.lay.order);
   const int n = order[slot];
   const SeqEntry se = reinterpret_cast<const SeqEntry*>(a.ws + a.lay.seq_table)[n];
-  const ChunkEntry* chunks = reinterpret_cast<const ChunkEntry*>(a.ws + a.lay.chunk_table);
-  const char* recs = a.ws + a.lay.records + (int64_t)h * a.lay.max_chunks * REC_BYTES;
+  const char* recs = a.ws + a.lay.records + ((int64_t)h * a.lay.max_chunks + se.first_chunk) * REC_BYTES;
+  const int nch = se.nchunks;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, lg = lane >> 4, lc = lane & 15;
@@ -73,92 +219,31 @@ __global__ __launch_bounds__(kThreads) void recur_kernel(RecurArgs a) {
       }
     }
 
-  for (int ci = 0; ci < se.nchunks; ++ci) {
-    const int chunk = se.first_chunk + ci;
-    const ChunkEntry ce = chunks[chunk];
-    const char* rec = recs + (int64_t)chunk * REC_BYTES;
-
-    // ---- stage the record and the chunk's values in LDS
-    for (int o = tid * 16; o < REC_BYTES; o += kThreads * 16)
-      *reinterpret_cast<u32x4*>(sm.rec + o) = *reinterpret_cast<const u32x4*>(rec + o);
-    {
-      const int r = tid >> 4, c8 = (tid & 15) * 8;
-      u32x4 w = {0, 0, 0, 0};
-      if (r < ce.len) w = *reinterpret_cast<const u32x4*>(a.v + (((int64_t)ce.row0 + r) * H + h) * V + c8);
-      *reinterpret_cast<u32x4*>(&sm.v[r][c8]) = w;
-    }
+  if (nch > 0) {
+    Prefetch pa, pb;
+    load_chunk(pa, recs, se, a.v, 0, H, h, tid);
+    load_chunk(pb, recs, se, a.v, 1, H, h, tid);
+    stage_chunk(pa, sm.buf[0], chunk_rows(se, 0).len, tid);
     __syncthreads();
-
-    const _Float16* nW = reinterpret_cast<const _Float16*>(sm.rec + REC_NW);
-    const _Float16* qH = reinterpret_cast<const _Float16*>(sm.rec + REC_QH);
-    const _Float16* kBt = reinterpret_cast<const _Float16*>(sm.rec + REC_KBT);
-    const _Float16* Tm = reinterpret_cast<const _Float16*>(sm.rec + REC_T);
-    const _Float16* Mq = reinterpret_cast<const _Float16*>(sm.rec + REC_MQK);
-    const float* gam = reinterpret_cast<const float*>(sm.rec + REC_GAM);
-
-    // ---- U = T V
-    f32x4 E[2], O[2];
-    const f16x4 aT = *reinterpret_cast<const f16x4*>(Tm + lc * C + 4 * lg);
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int col = 32 * wave + 16 * nt + lc;
-      f16x4 bv;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) bv[i] = (_Float16)bf16_to_f32(sm.v[4 * lg + i][col]);
-      E[nt] = mfma_f16_k16(aT, bv, f32x4{0.f, 0.f, 0.f, 0.f});
-      O[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // Step ci computes chunk ci from buf[ci & 1].  First the output tile of
+    // chunk ci - 1 is stored, then the register set that held chunk ci
+    // (already staged) fetches chunk ci + 2 (clamped: past the end it reloads
+    // the last chunk, which is never staged); after the compute the other set
+    // (chunk ci + 1) is staged into the other buffer.  PCUR / PNEXT swap every
+    // step, so the loop is unrolled by two to keep the register sets fixed.
+#define KDA_RECUR_STEP(PCUR, PNEXT, B)                                                      \
+  if (ci > 0) store_out(sm.ot[(B) ^ 1], chunk_rows(se, ci - 1), a.out, H, h, tid);         \
+  load_chunk(PCUR, recs, se, a.v, ci + 2, H, h, tid);                                      \
+  step(Z, sm.buf[B], sm.ot[B], wave, lg, lc);                                              \
+  if (ci + 1 < nch) stage_chunk(PNEXT, sm.buf[(B) ^ 1], chunk_rows(se, ci + 1).len, tid); \
+  __syncthreads();                                                                         \
+  if (++ci >= nch) break;
+    for (int ci = 0;;) {
+      KDA_RECUR_STEP(pa, pb, 0)
+      KDA_RECUR_STEP(pb, pa, 1)
     }
-
-    // ---- E += (-W) Z ; O = Qhat Z
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const f16x8 aw = *reinterpret_cast<const f16x8*>(nW + lc * K + 32 * s + 8 * lg);
-      const f16x8 aq = *reinterpret_cast<const f16x8*>(qH + lc * K + 32 * s + 8 * lg);
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        f16x8 zb;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          zb[i] = (_Float16)Z[2 * s][nt][i];
-          zb[4 + i] = (_Float16)Z[2 * s + 1][nt][i];
-        }
-        E[nt] = mfma_f16_k32(aw, zb, E[nt]);
-        O[nt] = mfma_f16_k32(aq, zb, O[nt]);
-      }
-    }
-
-    // ---- O += Mqk E
-    f16x4 eb[2];
-    const f16x4 am = *reinterpret_cast<const f16x4*>(Mq + lc * C + 4 * lg);
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      eb[nt] = f16x4_of(E[nt]);
-      O[nt] = mfma_f16_k16(am, eb[nt], O[nt]);
-    }
-
-    // ---- Z = diag(gam) Z + Kbar^T E
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      const f32x4 gm = *reinterpret_cast<const f32x4*>(gam + 16 * m + 4 * lg);
-      const f16x4 ak = *reinterpret_cast<const f16x4*>(kBt + (16 * m + lc) * C + 4 * lg);
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        f32x4 zc = Z[m][nt] * gm;
-        Z[m][nt] = mfma_f16_k16(ak, eb[nt], zc);
-      }
-    }
-
-    // ---- output rows of this chunk
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int col = 32 * wave + 16 * nt + lc;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 4 * lg + i;
-        if (r < ce.len) a.out[(((int64_t)ce.row0 + r) * H + h) * V + col] = f32_to_bf16(O[nt][i]);
-      }
-    }
-    __syncthreads();
+#undef KDA_RECUR_STEP
+    store_out(sm.ot[(nch - 1) & 1], chunk_rows(se, nch - 1), a.out, H, h, tid);
   }
 
   // ---- final state

@@ -5,7 +5,7 @@
 //     chunks of at most 16 tokens that restart at every sequence start (so a
 //     chunk never straddles two sequences; the pages batch variable-length
 //     sequences through cu_seqlens: README mirror "内核 API", cu_seqlens row);
-//   * a per-sequence table {first chunk, chunk count, work-order slot};
+//   * a per-sequence table {first chunk, chunk count, first token row, length};
 //   * a work order of the sequences, longest first, so that the chunk
 //     recurrence starts its longest serial chains first;
 //   * a status word: KDA_STATUS_BAD_CU_SEQLENS when cu_seqlens[0] != 0, the
@@ -67,7 +67,8 @@ __global__ __launch_bounds__(kThreads) void sched_kernel(SchedArgs a) {
     if (n < N) {
       seqs[n].first_chunk = s_carry + s_scan[tid] - nch;
       seqs[n].nchunks = nch;
-      seqs[n].pad = 0;
+      seqs[n].row0 = (bad || !a.cu) ? (int32_t)(n * a.T) : (int32_t)a.cu[n];
+      seqs[n].len = bad ? 0 : (int32_t)(a.cu ? a.cu[n + 1] - a.cu[n] : a.T);
     }
     __syncthreads();
     if (tid == kThreads - 1) s_carry += s_scan[tid];
@@ -105,7 +106,6 @@ __global__ __launch_bounds__(kThreads) void sched_kernel(SchedArgs a) {
       }
     }
     order[rank] = (int32_t)n;
-    seqs[n].slot = (int32_t)rank;
   }
   if (tid == 0) {
     hdr->status = bad ? KDA_STATUS_BAD_CU_SEQLENS : KDA_STATUS_OK;

@@ -153,7 +153,7 @@ int kda_fwd_check_status(const void* workspace, hipStream_t stream, int* status)
  * Workspace layout, for tests that decode the chunk records:
  * offsets[0] = chunk table (int32 triples {sequence, first token row, length}),
  * offsets[1] = per-sequence table (int32 quadruples {first chunk, chunk count,
- *              work-order slot, unused}),
+ *              first token row, length}),
  * offsets[2] = work order (int32 [N], sequences longest first),
  * offsets[3] = chunk records, head-major: record (h, c) at
  *              offsets[3] + (h * offsets[5] + c) * offsets[4],

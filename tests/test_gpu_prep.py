@@ -47,10 +47,10 @@ def test_chunk_table_and_records_match_chunked_form():
     hdr = buf[:8].view(np.int32)
     assert hdr[0] == kda.KDA_STATUS_OK
     nch = sum((l + 15) // 16 for l in lens)
+    cu = inp.cu_seqlens
     assert hdr[1] == nch
     table = buf[lay["chunk_table"]:lay["chunk_table"] + 12 * nch].view(np.int32).reshape(nch, 3)
     want = []
-    cu = inp.cu_seqlens
     for n, l in enumerate(lens):
         for c in range(0, l, 16):
             want.append((n, int(cu[n]) + c, min(16, l - c)))
@@ -58,6 +58,8 @@ def test_chunk_table_and_records_match_chunked_form():
     seqs = buf[lay["seq_table"]:lay["seq_table"] + 16 * len(lens)].view(np.int32).reshape(-1, 4)
     order = buf[lay["order"]:lay["order"] + 4 * len(lens)].view(np.int32)
     assert list(seqs[:, 1]) == [(l + 15) // 16 for l in lens]
+    assert list(seqs[:, 2]) == [int(x) for x in cu[:-1]] and list(seqs[:, 3]) == lens
+    assert list(seqs[:, 0]) == [sum((l + 15) // 16 for l in lens[:n]) for n in range(len(lens))]
     assert sorted(order) == list(range(len(lens)))
     counts = [seqs[n, 1] for n in order]
     assert counts == sorted(counts, reverse=True)               # longest first
