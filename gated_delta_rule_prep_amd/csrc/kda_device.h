@@ -47,6 +47,28 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
 }
 
+__device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  const f16x2 v = {(_Float16)lo, (_Float16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Transposing LDS read of a 16-bit matrix M stored row-major (stride in
+// elements): within each group of 16 lanes (g = lane / 16), lane i receives
+// M[4g + k][i] for k = 0..3, because lane j of the group fetches the 8 bytes at
+// M[4g + j / 4][4 (j % 4)] and ds_read_b64_tr_b16 hands element i % 4 of lane
+// 4k + i / 4's fetch to lane i as element k.  `m` points at M[0][0] (any column
+// offset is part of the pointer).  For M token-major this yields the MFMA
+// operand that holds four consecutive tokens of one column per lane.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+__device__ __forceinline__ f16x4 lds_read_tr(const _Float16* m, int stride, int lane) {
+  const int g = lane >> 4, j = lane & 15;
+  const _Float16* p = m + (4 * g + (j >> 2)) * stride + 4 * (j & 3);
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+  return __builtin_bit_cast(f16x4, v);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 

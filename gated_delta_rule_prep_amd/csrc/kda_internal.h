@@ -12,11 +12,11 @@ constexpr int K = 128;    // key channels
 constexpr int V = 128;    // value channels
 
 // Chunk record, one per (head, chunk), head-major.  Offsets in bytes.
-constexpr int REC_QH = 0;        // Qhat  fp16 [16][128], 32-block channel order (see kPerm)
+constexpr int REC_QH = 0;        // Qhat  fp16 [16][128], 32-block channel order (see kPermCh)
 constexpr int REC_NW = 4096;     // -W    fp16 [16][128], same channel order
-constexpr int REC_KBT = 8192;    // Kbar^T fp16 [128][16]
-constexpr int REC_T = 12288;     // T     fp16 [16][16]
-constexpr int REC_MQK = 12800;   // Mqk   fp16 [16][16]
+constexpr int REC_KB = 8192;     // Kbar  fp16 [16][128], token-major, natural channel order
+constexpr int REC_T = 12288;     // T^T   fp16 [16][16]
+constexpr int REC_MQK = 12800;   // Mqk^T fp16 [16][16]
 constexpr int REC_GAM = 13312;   // gamma fp32 [128]
 constexpr int REC_BYTES = 13824;
 

@@ -10,7 +10,9 @@
 //
 // P1 = blog post "FlashKDA：月之暗面开源的 Kimi Delta Attention 高性能内核".
 //
-// Per chunk (records from the prep kernel, Z = chunk-start state, K x V):
+// Per chunk (records from the prep kernel, Z = chunk-start state, K x V; T,
+// Mqk, Kbar^T and V reach their MFMA operand layouts through transposing LDS
+// reads of token-major tiles):
 //   U = T V                      fp16 MFMA 16x16x16
 //   E = U + (-W) Z               fp16 MFMA 16x16x32 chain over the 128 channels
 //   O = Qhat Z + Mqk E           fp16 MFMA (E feeds the B operand directly: the
@@ -24,8 +26,8 @@
 // Memory pipeline: the record and the value rows of chunk c+2 are loaded into
 // registers while chunk c is computed (two register sets, the loop unrolled by
 // two), then written to one of two LDS buffers; one barrier per chunk.  Values
-// are staged transposed and already in fp16; the output tile goes through LDS
-// so that it leaves as 16-byte row stores, one chunk behind.
+// are staged already in fp16; the output tile goes through LDS so that it
+// leaves as 16-byte row stores, one chunk behind.
 #include "kda_device.h"
 #include "kda_internal.h"
 #include "../../include/kda.h"
@@ -35,23 +37,25 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kRecPieces = REC_BYTES / 16;   // 864 16-byte pieces per record
-constexpr int SVT = C + 4;                   // fp16 [128][SVT] transposed values
 constexpr int SO = V + 8;                    // bf16 [16][SO] output tile
 
-// LDS copy of one record, rows padded so that the 16 lanes that read one
-// operand row each land on distinct banks (a 256-byte row stride maps every
-// row onto the same banks): Qhat / -W rows 272 B, Kbar^T / T / Mqk rows 48 B.
+// LDS copy of one record plus the chunk's values (converted to fp16), all
+// token-major and written as 16-byte rows.  Row strides are chosen per read
+// pattern so the lanes of one read fall on distinct banks: 272 B for Qhat and
+// -W (16-byte operand reads, one row per lane), 288 B for Kbar and V and 48 B
+// for T^T and Mqk^T (transposing reads, four lanes per row).
 constexpr int SQ = K + 8;                    // fp16 row stride of Qhat and -W
-constexpr int SK = C + 8;                    // fp16 row stride of Kbar^T, T, Mqk
+constexpr int SR = K + 16;                   // fp16 row stride of Kbar and V
+constexpr int ST = C + 8;                    // fp16 row stride of T^T and Mqk^T
 
 struct __align__(16) Stage {
   __align__(16) _Float16 qh[C][SQ];
   __align__(16) _Float16 nw[C][SQ];
-  __align__(16) _Float16 kbt[K][SK];
-  __align__(16) _Float16 tm[C][SK];
-  __align__(16) _Float16 mq[C][SK];
+  __align__(16) _Float16 kb[C][SR];
+  __align__(16) _Float16 v[C][SR];
+  __align__(16) _Float16 tt[C][ST];
+  __align__(16) _Float16 mt[C][ST];
   __align__(16) float gam[K];
-  __align__(16) _Float16 vt[V][SVT];
 };
 
 struct __align__(16) RecurSmem {
@@ -99,27 +103,26 @@ __device__ __forceinline__ void load_chunk(Prefetch& p, const char* recs, const 
 }
 
 // Thread tid stages record pieces tid + 256 j (16 bytes each): j = 0 is a
-// piece of Qhat, j = 1 of -W, j = 2 of Kbar^T, and j = 3 (tid < 96) of T, Mqk
-// or gamma.  Value rows past the end of a partial chunk are staged as zeros.
+// piece of Qhat, j = 1 of -W, j = 2 of Kbar, and j = 3 (tid < 96) of T^T,
+// Mqk^T or gamma; plus 8 values of token row tid / 16 converted to fp16.
+// Value rows past the end of a partial chunk are staged as zeros.
 __device__ __forceinline__ void stage_chunk(const Prefetch& p, Stage& st, int len, int tid) {
-  const int r16 = tid >> 4, c16 = (tid & 15) * 8;        // Qhat / -W: row, first fp16 column
+  const int r16 = tid >> 4, c16 = (tid & 15) * 8;
   *reinterpret_cast<u32x4*>(&st.qh[r16][c16]) = p.rec[0];
   *reinterpret_cast<u32x4*>(&st.nw[r16][c16]) = p.rec[1];
-  *reinterpret_cast<u32x4*>(&st.kbt[tid >> 1][(tid & 1) * 8]) = p.rec[2];
+  *reinterpret_cast<u32x4*>(&st.kb[r16][c16]) = p.rec[2];
   if (tid < 32) {
-    *reinterpret_cast<u32x4*>(&st.tm[tid >> 1][(tid & 1) * 8]) = p.rec[3];
+    *reinterpret_cast<u32x4*>(&st.tt[tid >> 1][(tid & 1) * 8]) = p.rec[3];
   } else if (tid < 64) {
-    *reinterpret_cast<u32x4*>(&st.mq[(tid - 32) >> 1][(tid & 1) * 8]) = p.rec[3];
+    *reinterpret_cast<u32x4*>(&st.mt[(tid - 32) >> 1][(tid & 1) * 8]) = p.rec[3];
   } else if (tid < 96) {
     *reinterpret_cast<u32x4*>(&st.gam[4 * (tid - 64)]) = p.rec[3];
   }
   const bool live = r16 < len;
+  u32x4 w;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t w = live ? p.v[j] : 0u;
-    st.vt[c16 + 2 * j][r16] = (_Float16)bf16_lo(w);
-    st.vt[c16 + 2 * j + 1][r16] = (_Float16)bf16_hi(w);
-  }
+  for (int j = 0; j < 4; ++j) w[j] = live ? pack_f16(bf16_lo(p.v[j]), bf16_hi(p.v[j])) : 0u;
+  *reinterpret_cast<u32x4*>(&st.v[r16][c16]) = w;
 }
 
 // Output rows of a chunk from the LDS tile: 16 rows x 256 B, 16 B per thread.
@@ -134,12 +137,13 @@ __device__ __forceinline__ void store_out(const uint16_t (*ot)[SO], const Rows& 
 // One chunk step on the staged record: updates Z, writes the output tile.
 __device__ __forceinline__ void step(f32x4 (&Z)[8][2], const Stage& st, uint16_t (*ot)[SO], int wave, int lg,
                                      int lc) {
+  const int lane = 16 * lg + lc;
   // ---- U = T V
   f32x4 E[2], O[2];
-  const f16x4 aT = *reinterpret_cast<const f16x4*>(&st.tm[lc][4 * lg]);
+  const f16x4 aT = lds_read_tr(&st.tt[0][0], ST, lane);   // T[lc][4lg..4lg+3]
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
-    const f16x4 bv = *reinterpret_cast<const f16x4*>(&st.vt[32 * wave + 16 * nt + lc][4 * lg]);
+    const f16x4 bv = lds_read_tr(&st.v[0][32 * wave + 16 * nt], SR, lane);
     E[nt] = mfma_f16_k16(aT, bv, f32x4{0.f, 0.f, 0.f, 0.f});
     O[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -164,7 +168,7 @@ __device__ __forceinline__ void step(f32x4 (&Z)[8][2], const Stage& st, uint16_t
 
   // ---- O += Mqk E
   f16x4 eb[2];
-  const f16x4 am = *reinterpret_cast<const f16x4*>(&st.mq[lc][4 * lg]);
+  const f16x4 am = lds_read_tr(&st.mt[0][0], ST, lane);   // Mqk[lc][4lg..4lg+3]
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     eb[nt] = f16x4_of(E[nt]);
@@ -175,7 +179,7 @@ __device__ __forceinline__ void step(f32x4 (&Z)[8][2], const Stage& st, uint16_t
 #pragma unroll
   for (int m = 0; m < 8; ++m) {
     const f32x4 gm = *reinterpret_cast<const f32x4*>(&st.gam[16 * m + 4 * lg]);
-    const f16x4 ak = *reinterpret_cast<const f16x4*>(&st.kbt[16 * m + lc][4 * lg]);
+    const f16x4 ak = lds_read_tr(&st.kb[0][16 * m], SR, lane);   // Kbar[4lg..4lg+3][16m + lc]
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) Z[m][nt] = mfma_f16_k16(ak, eb[nt], Z[m][nt] * gm);
   }

@@ -161,9 +161,9 @@ int kda_fwd_check_status(const void* workspace, hipStream_t stream, int* status)
  * offsets[6] = total bytes.  Returns KDA_OK or KDA_EINVAL.
  * Record layout (bytes): [0, 4096) Qhat fp16 [16][128]; [4096, 8192) -W fp16
  * [16][128]; both with the channels of each 32-block stored in the order
- * {0-3, 16-19, 4-7, 20-23, 8-11, 24-27, 12-15, 28-31}; [8192, 12288) Kbar^T fp16
- * [128][16]; [12288, 12800) T fp16 [16][16]; [12800, 13312) Mqk fp16 [16][16];
- * [13312, 13824) gamma fp32 [128].
+ * {0-3, 16-19, 4-7, 20-23, 8-11, 24-27, 12-15, 28-31}; [8192, 12288) Kbar fp16
+ * [16][128] (token-major, natural channel order); [12288, 12800) T^T fp16
+ * [16][16]; [12800, 13312) Mqk^T fp16 [16][16]; [13312, 13824) gamma fp32 [128].
  */
 int kda_workspace_layout(int64_t B, int64_t T, int64_t H, int64_t num_seqs, int has_cu_seqlens,
                          int64_t offsets[7]);

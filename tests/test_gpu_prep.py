@@ -81,13 +81,13 @@ def test_chunk_table_and_records_match_chunked_form():
             rec = buf[off:off + R]
             f16 = lambda o, shape: rec[o:o + 2 * int(np.prod(shape))].view(np.float16).astype(np.float64).reshape(shape)
             got = dict(Qh=unpermute(f16(0, (16, 128)))[:ln], W=-unpermute(f16(4096, (16, 128)))[:ln],
-                       Kb=f16(8192, (128, 16)).T[:ln], T=f16(12288, (16, 16))[:ln, :ln],
-                       M=f16(12800, (16, 16))[:ln, :ln], gamma=rec[13312:13824].view(np.float32).astype(np.float64))
+                       Kb=f16(8192, (16, 128))[:ln], T=f16(12288, (16, 16)).T[:ln, :ln],
+                       M=f16(12800, (16, 16)).T[:ln, :ln], gamma=rec[13312:13824].view(np.float32).astype(np.float64))
             ref = dict(Qh=P["Qh"], W=P["T"] @ P["Kh"], Kb=P["Kb"], T=P["T"], M=P["M"], gamma=P["gamma"])
             # padded rows / columns of a partial chunk are exactly zero
             assert np.all(f16(0, (16, 128))[ln:] == 0) and np.all(f16(4096, (16, 128))[ln:] == 0)
-            assert np.all(f16(8192, (128, 16))[:, ln:] == 0)
-            assert np.all(f16(12288, (16, 16))[ln:] == 0) and np.all(f16(12800, (16, 16))[ln:] == 0)
+            assert np.all(f16(8192, (16, 128))[ln:] == 0)
+            assert np.all(f16(12288, (16, 16)).T[ln:] == 0) and np.all(f16(12800, (16, 16)).T[ln:] == 0)
             # structure: T lower triangular, Mqk lower triangular incl. diagonal
             assert np.all(np.triu(got["T"], 1) == 0) and np.all(np.triu(got["M"], 1) == 0)
             for key in ref:
