@@ -139,6 +139,9 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=96, help="heads of the headline workload the oracle runs")
     ap.add_argument("--only", choices=["both", "fixed", "varlen"], default="both",
                     help="time only one workload (for profiler runs); the JSON line needs both")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="with --only: afterwards run 3 device-to-device copies of this many MiB, a plain copy "
+                         "kernel of known size that scales the HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this build measures one GPU only; run it with --gpus 1", file=sys.stderr)
@@ -156,6 +159,14 @@ def main():
                            device_inputs)
         print(json.dumps({"workload": res["inp"].name, "ms_per_step": round(res["ms"], 4),
                           "kernels_ms": {k: round(res[k + "_ms"], 4) for k in ("sched", "prep", "recur")}}))
+        if args.copy_mib > 0:
+            n = args.copy_mib << 20
+            src = torch.ones(n, dtype=torch.uint8, device="cuda")
+            dst = torch.empty_like(src)
+            for _ in range(3):
+                dst.copy_(src)
+            torch.cuda.synchronize()
+            print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copies": 3}))
         return
     fixed = run_workload(cfgs[2], args.steps, args.warmup, torch, kda, device_inputs)
     varlen = run_workload(cfgs[3], args.steps, args.warmup, torch, kda, device_inputs)

@@ -88,5 +88,6 @@ struct RecurArgs {
 hipError_t launch_sched(const SchedArgs& a, hipStream_t s);
 hipError_t launch_prep(const PrepArgs& a, hipStream_t s);
 hipError_t launch_recur(const RecurArgs& a, hipStream_t s);
+int recur_waves_per_group(int64_t pairs);   // waves per recurrence workgroup (2 or 4)
 
 }  // namespace kda
