@@ -17,8 +17,16 @@ constexpr int REC_NW = 4096;     // -W    fp16 [16][128], same channel order
 constexpr int REC_KB = 8192;     // Kbar  fp16 [16][128], token-major, natural channel order
 constexpr int REC_T = 12288;     // T^T   fp16 [16][16]
 constexpr int REC_MQK = 12800;   // Mqk^T fp16 [16][16]
-constexpr int REC_GAM = 13312;   // gamma fp32 [128]
+constexpr int REC_GAM = 13312;   // gamma fp32 [128], channel c at slot kGamSlot(c)
 constexpr int REC_BYTES = 13824;
+
+// Slot of channel c = 64 r + 16 a + 4 b + i in the stored gamma: lane
+// L = 16 b + 4 a + i of a recurrence wave reads slots 2L and 2L + 1 (r = 0, 1),
+// i.e. exactly the decay factors that its 16-lane row (lanes with the same b)
+// hands out by row broadcast.
+__host__ __device__ constexpr int kGamSlot(int c) {
+  return 2 * (16 * ((c >> 2) & 3) + 4 * ((c >> 4) & 3) + (c & 3)) + (c >> 6);
+}
 
 // Workspace header (first 256 bytes).
 struct WsHeader {
@@ -88,6 +96,6 @@ struct RecurArgs {
 hipError_t launch_sched(const SchedArgs& a, hipStream_t s);
 hipError_t launch_prep(const PrepArgs& a, hipStream_t s);
 hipError_t launch_recur(const RecurArgs& a, hipStream_t s);
-int recur_waves_per_group(int64_t pairs);   // waves per recurrence workgroup (2 or 4)
+int recur_tile_cols(int64_t pairs);   // value columns per recurrence workgroup (32, 64 or 128)
 
 }  // namespace kda

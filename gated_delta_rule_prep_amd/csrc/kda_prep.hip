@@ -164,8 +164,8 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
     *reinterpret_cast<u32x2*>(rec_qh + p0) = wq0;
     *reinterpret_cast<u32x2*>(rec_qh + p1) = wq1;
     if (r == 15) {   // gam = P of the last token (padded tokens keep G constant)
-      *reinterpret_cast<f32x4*>(rec_gam + c0) = f32x4{gm[0], gm[1], gm[2], gm[3]};
-      *reinterpret_cast<f32x4*>(rec_gam + c0 + 4) = f32x4{gm[4], gm[5], gm[6], gm[7]};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) rec_gam[kGamSlot(c0 + e)] = gm[e];
     }
   }
 

@@ -3,13 +3,14 @@
 // The second stage of the split the pages describe (P1 §二 2.2: chunk-by-chunk
 // delta-rule recurrence, output projection, rolling state).  The state's value
 // columns never interact (every step acts on each value column of the state
-// separately), so a (sequence, head) pair is cut into V-tiles of 32 * NW
-// columns, one workgroup of NW waves per tile, and wave w of a tile owns 32 of
-// its columns.  Nothing is exchanged between waves or workgroups.  The 128 x 32
-// fp32 state slice of a wave lives in registers as 8 x 2 MFMA accumulator tiles
-// for the whole sequence.  NW = 4 (one workgroup per pair) when there are
-// enough pairs to fill the chip; with few pairs (one long sequence, 64-96
-// heads) NW = 2 spreads the same columns over 2 workgroups.
+// separately), so a (sequence, head) pair is cut into V-tiles, one workgroup
+// of four waves per tile, and each wave owns 16 or 32 of the tile's columns.
+// Nothing is exchanged between workgroups.  The 128 x 16 (or 32) fp32 state
+// slice of a wave lives in registers as 8 x 1 (or 8 x 2) MFMA accumulator
+// tiles for the whole sequence.  With enough pairs to fill the chip a
+// workgroup takes all 128 columns of a pair (32 per wave); with few pairs (one
+// long sequence, 64-96 heads) it takes 64 (16 per wave), so two workgroups
+// share a pair and each wave's serial per-chunk work is halved.
 //
 // P1 = blog post "FlashKDA：月之暗面开源的 Kimi Delta Attention 高性能内核".
 //
@@ -18,21 +19,28 @@
 // reads of token-major tiles):
 //   U = T V                      fp16 MFMA 16x16x16
 //   E = U + (-W) Z               fp16 MFMA 16x16x32 chain over the 128 channels
-//   O = Qhat Z + Mqk E           fp16 MFMA (E feeds the B operand directly: the
-//                                accumulator layout of E is the B-operand layout)
+//   O^T = Z^T Qhat^T + E^T Mqk^T fp16 MFMA; the same register operands as
+//                                O = Qhat Z + Mqk E with A and B swapped, so
+//                                each lane ends up with four consecutive value
+//                                columns of one token and stores them directly
 //   Z = diag(gam) Z + Kbar^T E   fp16 MFMA 16x16x16, accumulating onto gam * Z
 // Z is converted to fp16 per step for the two products that read it; the state
 // itself stays fp32.  The channel order of Qhat / -W in the record matches the
 // rows a lane holds in its two accumulator tiles (kPermCh), so the conversion
-// needs no lane exchange.
+// needs no lane exchange.  The decay factors reach the lanes by DPP row
+// broadcast from a permuted copy of gamma (kGamSlot): two LDS words per lane
+// instead of 32.
 //
-// Memory pipeline: the record and the tile's value rows of chunk c+2 are loaded
-// into registers while chunk c is computed (two register sets, the loop
-// unrolled by two), then written to one of two LDS buffers; one barrier per
-// chunk.  Values are staged already in fp16; the output tile goes through LDS
-// so that it leaves as 16-byte row stores, one chunk behind.  Every operand of
-// a step is read from LDS before its first product, so the LDS latency is paid
-// once per step rather than once per product.
+// Memory pipeline: a ring of kDepth chunk slots in LDS, filled by direct
+// buffer-to-LDS loads (buffer_load_dwordx4 ... lds) issued kDepth - 1 chunks
+// ahead, so no VGPRs or LDS write instructions are spent on staging and up to
+// kDepth - 1 chunks are in flight from HBM.  Each slot holds the tile's value
+// rows (raw bf16) and the chunk record.  Every 16-byte piece of a slot may come
+// from any 16-byte piece of HBM, so the pieces are stored XOR-swizzled by row
+// (rather than padded), which keeps the operand reads free of bank conflicts.
+// One barrier per chunk: a wave waits for its own loads of the chunk (vmcnt),
+// then the barrier makes every wave's loads visible, and only then is the slot
+// of the previous chunk (read by every wave before the barrier) refilled.
 //
 // Work placement: consecutive workgroup ids go round-robin to the 8 XCDs, and
 // the V-tiles of one pair are given ids that land on the same XCD, so the
@@ -45,54 +53,28 @@ namespace kda {
 namespace {
 
 constexpr int kRecPieces = REC_BYTES / 16;   // 864 16-byte pieces per record
-#ifndef KDA_RECUR_DEPTH
-#define KDA_RECUR_DEPTH 2
-#endif
-constexpr int kDepth = KDA_RECUR_DEPTH;      // chunks in flight from HBM
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBufWord3 = 0x00020000;        // raw buffer descriptor, dword 3 (gfx9 family)
 
-// LDS row strides (fp16 elements), chosen per read pattern so that the lanes
-// of one read fall on distinct banks: 272 B for Qhat and -W (16-byte operand
-// reads, one row per lane), 288 B for Kbar and 48 B for T^T and Mqk^T
-// (transposing reads, four lanes per row, 32 B apart in bank space).
-constexpr int SQ = K + 8;
-constexpr int SR = K + 16;
-constexpr int ST = C + 8;
-
-template <int NW>
-struct Tile {
-  static constexpr int kThreads = 64 * NW;
-  static constexpr int kCols = 32 * NW;                 // value columns per workgroup
+template <int NT, int D>
+struct Cfg {
+  static constexpr int kWaveCols = 16 * NT;             // value columns per wave
+  static constexpr int kCols = kWaveCols * kWaves;      // value columns per workgroup
   static constexpr int kTiles = V / kCols;              // workgroups per (sequence, head)
-  static constexpr int kRecLoads = (kRecPieces + kThreads - 1) / kThreads;
-  static constexpr int SV = kCols + 16;                 // value tile stride (transposing reads)
-  static constexpr int SO = kCols + 8;                  // bf16 output tile stride
-  static_assert(256 % kThreads == 0, "record fields are 256 pieces long");
-};
-
-// LDS copy of one record plus the tile's values (converted to fp16), all
-// token-major and written as 16-byte rows.
-template <int NW>
-struct __align__(16) Stage {
-  __align__(16) _Float16 qh[C][SQ];
-  __align__(16) _Float16 nw[C][SQ];
-  __align__(16) _Float16 kb[C][SR];
-  __align__(16) _Float16 v[C][Tile<NW>::SV];
-  __align__(16) _Float16 tt[C][ST];
-  __align__(16) _Float16 mt[C][ST];
-  __align__(16) float gam[K];
-};
-
-template <int NW>
-struct __align__(16) RecurSmem {
-  Stage<NW> buf[2];
-  __align__(16) uint16_t ot[2][C][Tile<NW>::SO];
-};
-
-// One chunk's worth of global data held in registers.
-template <int NW>
-struct Prefetch {
-  u32x4 rec[Tile<NW>::kRecLoads];
-  u32x4 v;
+  static constexpr int kRowPieces = kCols / 8;          // 16-byte pieces per value row of the tile
+  static constexpr int kValBlocks = C * kRowPieces / 64;             // 64-piece blocks of values
+  static constexpr int kBlocks = (kValBlocks + (kRecPieces + 63) / 64 + kWaves - 1) / kWaves * kWaves;
+  static constexpr int kLoads = kBlocks / kWaves;       // load instructions per wave per chunk
+  static constexpr int kSlotBytes = kBlocks * 1024;     // one ring slot
+  // byte offsets of the fields inside a slot
+  static constexpr int kVal = 0;
+  static constexpr int kRec = kValBlocks * 1024;
+  static constexpr int kQh = kRec + REC_QH, kNw = kRec + REC_NW, kKb = kRec + REC_KB;
+  static constexpr int kTt = kRec + REC_T, kMt = kRec + REC_MQK, kGam = kRec + REC_GAM;
+  static_assert(C * kRowPieces % 64 == 0, "value rows fill whole blocks");
+  static_assert(D >= 3 && (D - 2) * kLoads <= 63, "ring depth within the vmcnt range");
+  static_assert(V % kCols == 0, "tile shape");
 };
 
 // Chunk j of a sequence: first flattened token row and length (1..16).
@@ -111,160 +93,242 @@ __device__ __forceinline__ f16x4 f16x4_of(f32x4 x) {
   return r;
 }
 
-// Every load is unconditional (indices clamped into range) so that the
-// compiler can count outstanding loads exactly and wait only for the chunk it
-// stages, not for the prefetch issued after it.  Thread tid loads record
-// pieces tid + kThreads * j and one 16-byte piece of the tile's values.
-template <int NW>
-__device__ __forceinline__ void load_chunk(Prefetch<NW>& p, const char* recs, const SeqEntry& se,
-                                           const uint16_t* v, int chunk, int64_t H, int h, int v0, int tid) {
-  using Tl = Tile<NW>;
-  chunk = min(chunk, se.nchunks - 1);
-  const Rows cr = chunk_rows(se, chunk);
-  const char* rec = recs + (int64_t)chunk * REC_BYTES;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
+
+// ---- swizzled slot layout -------------------------------------------------
+// Qhat and -W: token row r, 16-byte piece p (8 channels in record order) at
+// piece position p ^ r of the row.  Kbar and the value tile: piece p of row r
+// at position p ^ 2 (r % 4).  T^T, Mqk^T and gamma are stored as in the record.
+
+// Byte offset (within the record) of the piece that record piece position `s`
+// of a slot holds.
+__device__ __forceinline__ int rec_source(int s) {
+  if (s >= kRecPieces) return 0;   // padding: any valid piece
+  const int r = (s >> 4) & 15, p = s & 15;
+  if (s < 512) return 16 * ((s & ~15) | (p ^ r));
+  if (s < 768) return 16 * ((s & ~15) | (p ^ (2 * (r & 3))));
+  return 16 * s;
+}
+
+// Transposing read of the 16 x 16 block of a swizzled token-major 16-bit tile
+// (row stride `rowb` bytes) whose first column is `col` (a multiple of 16):
+// lane (lc, lg) receives M[4lg..4lg+3][col + lc] (see lds_read_tr).
+__device__ __forceinline__ s16x4 tr_swz(const char* tile, int rowb, int col, int lane) {
+  const int g = lane >> 4, j = lane & 15;
+  const int r = 4 * g + (j >> 2);
+  const int c = col + 4 * (j & 3);                 // first of the 4 elements this lane fetches
+  const int p = (c >> 3) ^ (2 * (r & 3));
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tile + r * rowb + 16 * p + 2 * (c & 7)));
+}
+
+// The MFMA operands of one chunk step.
+template <int NT>
+struct Ops {
+  f16x4 aT, am;          // T[lc][4lg..4lg+3], Mqk[lc][4lg..4lg+3]
+  f16x4 bv[NT];          // V[4lg..4lg+3][wc + 16nt + lc] (converted from bf16)
+  f16x8 aw[4], aq[4];    // -W, Qhat row lc, channels of 32-block s at the lane's 8 positions
+  f16x4 ak[8];           // Kbar[4lg..4lg+3][16m + lc]
+  f32x2 g2;              // gamma of the rows that this lane hands to its 16-lane row
+};
+
+template <int NT, int D>
+__device__ __forceinline__ void read_ops(Ops<NT>& o, const char* slot, int wc, int lane) {
+  using Cf = Cfg<NT, D>;
+  const int lg = lane >> 4, lc = lane & 15;
+  o.aT = lds_read_tr(reinterpret_cast<const _Float16*>(slot + Cf::kTt), C, lane);
+  o.am = lds_read_tr(reinterpret_cast<const _Float16*>(slot + Cf::kMt), C, lane);
 #pragma unroll
-  for (int j = 0; j < Tl::kRecLoads; ++j) {
-    const int piece = min(tid + Tl::kThreads * j, kRecPieces - 1);
-    p.rec[j] = *reinterpret_cast<const u32x4*>(rec + 16 * piece);
+  for (int nt = 0; nt < NT; ++nt) {
+    const s16x4 raw = tr_swz(slot + Cf::kVal, 2 * Cf::kCols, wc + 16 * nt, lane);
+    f16x4 b;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) b[i] = (_Float16)bf16_to_f32((uint16_t)raw[i]);
+    o.bv[nt] = b;
   }
-  constexpr int kRowPieces = Tl::kCols / 8;
-  const int r = min(tid / kRowPieces, cr.len - 1), c8 = (tid % kRowPieces) * 8;
-  p.v = *reinterpret_cast<const u32x4*>(v + ((cr.row0 + r) * H + h) * V + v0 + c8);
-}
-
-// Record piece p (16 bytes) to its LDS place: pieces 0-255 are Qhat, 256-511
-// -W, 512-767 Kbar (16 pieces per token row), 768-799 T^T, 800-831 Mqk^T and
-// 832-863 gamma.  For p < 768 the field is known at compile time after the
-// loop below is unrolled (kThreads divides 256).
-template <int NW>
-__device__ __forceinline__ void stage_chunk(const Prefetch<NW>& p, Stage<NW>& st, int len, int tid) {
-  using Tl = Tile<NW>;
-#pragma unroll
-  for (int j = 0; j < Tl::kRecLoads; ++j) {
-    const int first = Tl::kThreads * j;                 // compile-time after unrolling
-    if (first < 768) {
-      const int field = first >> 8;
-      const int loc = (first & 255) + tid, r = loc >> 4, c = (loc & 15) * 8;
-      _Float16* dst = field == 0 ? &st.qh[r][c] : field == 1 ? &st.nw[r][c] : &st.kb[r][c];
-      *reinterpret_cast<u32x4*>(dst) = p.rec[j];
-    } else {
-      const int sub = first - 768 + tid;
-      if (sub < 32) {
-        *reinterpret_cast<u32x4*>(&st.tt[sub >> 1][(sub & 1) * 8]) = p.rec[j];
-      } else if (sub < 64) {
-        *reinterpret_cast<u32x4*>(&st.mt[(sub - 32) >> 1][(sub & 1) * 8]) = p.rec[j];
-      } else if (sub < 96) {
-        *reinterpret_cast<u32x4*>(&st.gam[4 * (sub - 64)]) = p.rec[j];
-      }
-    }
-  }
-  constexpr int kRowPieces = Tl::kCols / 8;
-  const int r = tid / kRowPieces, c8 = (tid % kRowPieces) * 8;
-  const bool live = r < len;
-  u32x4 w;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) w[j] = live ? pack_f16(bf16_lo(p.v[j]), bf16_hi(p.v[j])) : 0u;
-  *reinterpret_cast<u32x4*>(&st.v[r][c8]) = w;
-}
-
-// Output rows of a chunk from the LDS tile: 16 rows x kCols bf16, 16 B per
-// thread.
-template <int NW>
-__device__ __forceinline__ void store_out(const uint16_t (*ot)[Tile<NW>::SO], const Rows& cr, uint16_t* out,
-                                          int64_t H, int h, int v0, int tid) {
-  constexpr int kRowPieces = Tile<NW>::kCols / 8;
-  const int r = tid / kRowPieces, c8 = (tid % kRowPieces) * 8;
-  if (r < cr.len)
-    *reinterpret_cast<u32x4*>(out + ((cr.row0 + r) * H + h) * V + v0 + c8) =
-        *reinterpret_cast<const u32x4*>(&ot[r][c8]);
-}
-
-// One chunk step on the staged record: updates Z, writes the output tile.
-template <int NW>
-__device__ __forceinline__ void step(f32x4 (&Z)[8][2], const Stage<NW>& st, uint16_t (*ot)[Tile<NW>::SO],
-                                     int wave, int lg, int lc) {
-  constexpr int SV = Tile<NW>::SV;
-  const int lane = 16 * lg + lc;
-
-  // ---- every operand of the step, read before the first product
-  const f16x4 aT = lds_read_tr(&st.tt[0][0], ST, lane);   // T[lc][4lg..4lg+3]
-  const f16x4 am = lds_read_tr(&st.mt[0][0], ST, lane);   // Mqk[lc][4lg..4lg+3]
-  f16x4 bv[2];
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) bv[nt] = lds_read_tr(&st.v[0][32 * wave + 16 * nt], SV, lane);
-  f16x8 aw[4], aq[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    aw[s] = *reinterpret_cast<const f16x8*>(&st.nw[lc][32 * s + 8 * lg]);
-    aq[s] = *reinterpret_cast<const f16x8*>(&st.qh[lc][32 * s + 8 * lg]);
+    const int p = (4 * s + lg) ^ lc;
+    o.aw[s] = *reinterpret_cast<const f16x8*>(slot + Cf::kNw + 256 * lc + 16 * p);
+    o.aq[s] = *reinterpret_cast<const f16x8*>(slot + Cf::kQh + 256 * lc + 16 * p);
   }
-  f16x4 ak[8];
-  f32x4 gm[8];
 #pragma unroll
-  for (int m = 0; m < 8; ++m) {
-    ak[m] = lds_read_tr(&st.kb[0][16 * m], SR, lane);     // Kbar[4lg..4lg+3][16m + lc]
-    gm[m] = *reinterpret_cast<const f32x4*>(&st.gam[16 * m + 4 * lg]);
-  }
+  for (int m = 0; m < 8; ++m) o.ak[m] = __builtin_bit_cast(f16x4, tr_swz(slot + Cf::kKb, 2 * K, 16 * m, lane));
+  o.g2 = *reinterpret_cast<const f32x2*>(slot + Cf::kGam + 8 * lane);
+}
 
-  // ---- U = T V ; E = U + (-W) Z ; O = Qhat Z
-  f32x4 E[2], O[2];
+// x from lane L of this lane's 16-lane row.
+template <int L>
+__device__ __forceinline__ float row_bcast(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + L, 0xF, 0xF, false));
+}
+
+// Row 16M + 4lg + i decays by gamma[16M + 4lg + i], held by lane 4 (M % 4) + i
+// of the 16-lane row in register M / 4 (see kGamSlot).
+template <int M>
+__device__ __forceinline__ f32x4 decay(f32x4 z, f32x2 g2) {
+  const float g = g2[M >> 2];
+  return f32x4{z[0] * row_bcast<4 * (M & 3) + 0>(g), z[1] * row_bcast<4 * (M & 3) + 1>(g),
+               z[2] * row_bcast<4 * (M & 3) + 2>(g), z[3] * row_bcast<4 * (M & 3) + 3>(g)};
+}
+
+// One chunk step from operands in registers: updates Z and returns the output
+// tile as O^T (lane (lc, lg): token lc, value columns 16nt + 4lg .. +3 of the
+// wave), rounded to bf16 and packed.
+template <int NT>
+__device__ __forceinline__ void compute(f32x4 (&Z)[8][NT], const Ops<NT>& o, u32x2 (&out)[NT]) {
+  // ---- U = T V ; E = U + (-W) Z ; O^T = Z^T Qhat^T
+  f32x4 E[NT], O[NT];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    E[nt] = mfma_f16_k16(aT, bv[nt], f32x4{0.f, 0.f, 0.f, 0.f});
+  for (int nt = 0; nt < NT; ++nt) {
+    E[nt] = mfma_f16_k16(o.aT, o.bv[nt], f32x4{0.f, 0.f, 0.f, 0.f});
     O[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
+    for (int nt = 0; nt < NT; ++nt) {
       f16x8 zb;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         zb[i] = (_Float16)Z[2 * s][nt][i];
         zb[4 + i] = (_Float16)Z[2 * s + 1][nt][i];
       }
-      E[nt] = mfma_f16_k32(aw[s], zb, E[nt]);
-      O[nt] = mfma_f16_k32(aq[s], zb, O[nt]);
+      E[nt] = mfma_f16_k32(o.aw[s], zb, E[nt]);
+      O[nt] = mfma_f16_k32(zb, o.aq[s], O[nt]);
     }
   }
 
-  // ---- O += Mqk E
-  f16x4 eb[2];
+  // ---- O^T += E^T Mqk^T
+  f16x4 eb[NT];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
+  for (int nt = 0; nt < NT; ++nt) {
     eb[nt] = f16x4_of(E[nt]);
-    O[nt] = mfma_f16_k16(am, eb[nt], O[nt]);
+    O[nt] = mfma_f16_k16(eb[nt], o.am, O[nt]);
   }
 
   // ---- Z = diag(gam) Z + Kbar^T E
 #pragma unroll
-  for (int m = 0; m < 8; ++m)
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) Z[m][nt] = mfma_f16_k16(ak[m], eb[nt], Z[m][nt] * gm[m]);
+  for (int nt = 0; nt < NT; ++nt) {
+    Z[0][nt] = mfma_f16_k16(o.ak[0], eb[nt], decay<0>(Z[0][nt], o.g2));
+    Z[1][nt] = mfma_f16_k16(o.ak[1], eb[nt], decay<1>(Z[1][nt], o.g2));
+    Z[2][nt] = mfma_f16_k16(o.ak[2], eb[nt], decay<2>(Z[2][nt], o.g2));
+    Z[3][nt] = mfma_f16_k16(o.ak[3], eb[nt], decay<3>(Z[3][nt], o.g2));
+    Z[4][nt] = mfma_f16_k16(o.ak[4], eb[nt], decay<4>(Z[4][nt], o.g2));
+    Z[5][nt] = mfma_f16_k16(o.ak[5], eb[nt], decay<5>(Z[5][nt], o.g2));
+    Z[6][nt] = mfma_f16_k16(o.ak[6], eb[nt], decay<6>(Z[6][nt], o.g2));
+    Z[7][nt] = mfma_f16_k16(o.ak[7], eb[nt], decay<7>(Z[7][nt], o.g2));
+  }
 
-  // ---- output tile (rows 4lg + i, columns 32 wave + 16 nt + lc)
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ot[4 * lg + i][32 * wave + 16 * nt + lc] = f32_to_bf16(O[nt][i]);
+  for (int nt = 0; nt < NT; ++nt) out[nt] = u32x2{pack_bf16(O[nt][0], O[nt][1]), pack_bf16(O[nt][2], O[nt][3])};
 }
 
-template <int NW>
-__global__ __launch_bounds__(64 * NW) void recur_kernel(RecurArgs a) {
-  using Tl = Tile<NW>;
-  __shared__ RecurSmem<NW> sm;
+// Where this lane's load instruction j of a chunk reads from.  Slot block
+// b = kWaves j + wave (64 pieces, one per lane); blocks below kValBlocks hold
+// the value tile, the rest the record.
+template <int NT, int D>
+struct LoadPlan {
+  int32_t off[Cfg<NT, D>::kLoads];   // record byte offset, or value byte offset within the token row
+  int32_t row[Cfg<NT, D>::kLoads];   // value token row (value blocks)
+};
+
+template <int NT, int D>
+__device__ __forceinline__ void make_plan(LoadPlan<NT, D>& pl, int wave, int lane) {
+  using Cf = Cfg<NT, D>;
+#pragma unroll
+  for (int j = 0; j < Cf::kLoads; ++j) {
+    const int b = kWaves * j + wave;
+    if (b < Cf::kValBlocks) {
+      const int s = 64 * b + lane, r = s / Cf::kRowPieces, p = s % Cf::kRowPieces;
+      pl.row[j] = r;
+      pl.off[j] = 16 * (p ^ (2 * (r & 3)));
+    } else {
+      pl.row[j] = 0;
+      pl.off[j] = rec_source(64 * (b - Cf::kValBlocks) + lane);
+    }
+  }
+}
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor over `bytes` bytes at `base` (stride 0, no swizzle),
+// made wave-uniform so that it can live in scalar registers.
+__device__ __forceinline__ i32x4 buf_rsrc(const void* base, int bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return i32x4{__builtin_amdgcn_readfirstlane((int32_t)(uint32_t)a),
+               __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)(a >> 32) & 0xffff),
+               __builtin_amdgcn_readfirstlane(bytes), kBufWord3};
+}
+
+// buffer_load_dwordx4 ... lds: lane i's 16 bytes at rsrc + voff land at LDS
+// byte address lds + 16 i (lds wave-uniform).  Written as inline assembly so
+// that the compiler does not treat it as an LDS store of unknown extent (it
+// would then wait for every outstanding load before each LDS read); the waits
+// are explicit in the kernel.  M0 carries the LDS address (one wait state
+// between setting it and the load) and is restored afterwards.
+__device__ __forceinline__ void load_lds16(const i32x4& rsrc, uint32_t lds, int voff) {
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(__builtin_amdgcn_readfirstlane((int)lds)), "s"(rsrc)
+      : "memory");
+}
+
+// Issue the loads of chunk c into ring slot `slot` (all lanes, no waits).
+// Value rows past the end of a partial chunk repeat the last row: the
+// record gives them zero weight (their T rows and columns and their -W, Qhat
+// and Kbar rows are exactly zero), so any finite values are harmless.
+template <int NT, int D>
+__device__ __forceinline__ void issue_chunk(char* slot, const LoadPlan<NT, D>& pl, const char* recs,
+                                            const uint16_t* v, const SeqEntry& se, int c, int64_t H, int h,
+                                            int v0, int wave) {
+  using Cf = Cfg<NT, D>;
+  c = min(c, se.nchunks - 1);
+  const Rows cr = chunk_rows(se, c);
+  const i32x4 rrec = buf_rsrc(recs + (int64_t)c * REC_BYTES, REC_BYTES);
+  const int row_bytes = (int)(H * V * 2);
+  const i32x4 rval = buf_rsrc(v + (cr.row0 * H + h) * V + v0, (cr.len - 1) * row_bytes + 2 * Cf::kCols);
+  const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>((lds_void*)slot);
+#pragma unroll
+  for (int j = 0; j < Cf::kLoads; ++j) {
+    const int b = kWaves * j + wave;   // wave-uniform
+    if (b < Cf::kValBlocks) {
+      load_lds16(rval, lds0 + 1024 * b, min(pl.row[j], cr.len - 1) * row_bytes + pl.off[j]);
+    } else {
+      load_lds16(rrec, lds0 + 1024 * b, pl.off[j]);
+    }
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+template <int NT, int D>
+__global__ __launch_bounds__(kThreads) void recur_kernel(RecurArgs a) {
+  using Cf = Cfg<NT, D>;
+  __shared__ __align__(1024) char ring[D][Cf::kSlotBytes];
   const int64_t H = a.H;
   // XCD-aware placement: id b runs on XCD b % 8; the kTiles tiles of pair
   // 8 * g + x get ids 8 * (kTiles * g + tile) + x.
-  const int64_t b = blockIdx.x, x = b & 7, q = b >> 3;
-  const int64_t pair = 8 * (q / Tl::kTiles) + x;
-  const int tile = (int)(q % Tl::kTiles);
+  const int64_t bid = blockIdx.x, x = bid & 7, q = bid >> 3;
+  const int64_t pair = 8 * (q / Cf::kTiles) + x;
+  const int tile = (int)(q % Cf::kTiles);
   if (pair >= a.N * H) return;
-  const int64_t slot = pair / H;
-  const int h = (int)(pair - slot * H);
-  const int v0 = tile * Tl::kCols;
+  const int64_t slot_id = pair / H;
+  const int h = (int)(pair - slot_id * H);
+  const int v0 = tile * Cf::kCols;
   const int32_t* order = reinterpret_cast<const int32_t*>(a.ws + a.lay.order);
-  const int n = order[slot];
+  const int n = order[slot_id];
   const SeqEntry se = reinterpret_cast<const SeqEntry*>(a.ws + a.lay.seq_table)[n];
   const char* recs = a.ws + a.lay.records + ((int64_t)h * a.lay.max_chunks + se.first_chunk) * REC_BYTES;
   const int nch = se.nchunks;
@@ -272,14 +336,15 @@ __global__ __launch_bounds__(64 * NW) void recur_kernel(RecurArgs a) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, lg = lane >> 4, lc = lane & 15;
   const int64_t sbase = ((int64_t)n * H + h) * V * K;   // state [n][h][v][k]
-  const int col0 = v0 + 32 * wave;                      // first state column of this wave
+  const int wc = Cf::kWaveCols * wave;                   // first tile column of this wave
+  const int col0 = v0 + wc;                              // first state column of this wave
 
   // ---- state slice: Z[m][nt] holds rows 16m + 4lg + i, column col0 + 16nt + lc
-  f32x4 Z[8][2];
+  f32x4 Z[8][NT];
 #pragma unroll
   for (int m = 0; m < 8; ++m)
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
+    for (int nt = 0; nt < NT; ++nt) {
       const int64_t idx = sbase + (int64_t)(col0 + 16 * nt + lc) * K + 16 * m + 4 * lg;
       if (a.s_in == nullptr) {
         Z[m][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -292,32 +357,44 @@ __global__ __launch_bounds__(64 * NW) void recur_kernel(RecurArgs a) {
     }
 
   if (nch > 0) {
-    // kDepth register sets: step ci computes chunk ci from LDS buffer ci & 1
-    // while set ci % kDepth, whose chunk is already staged, fetches chunk
-    // ci + kDepth (clamped: past the end it reloads the last chunk, which is
-    // never staged).  First the output tile of chunk ci - 1 is stored; after
-    // the compute, set (ci + 1) % kDepth is staged into the other buffer.  The
-    // loop is unrolled by 2 * kDepth so that every set and buffer index is a
-    // compile-time constant.
-    Prefetch<NW> pf[kDepth];
+    LoadPlan<NT, D> pl;
+    make_plan<NT, D>(pl, wave, lane);
+    // Chunks 0 .. D-2 in flight before the first step.  Loads past the last
+    // chunk repeat it into slots that are never read.
 #pragma unroll
-    for (int j = 0; j < kDepth; ++j) load_chunk<NW>(pf[j], recs, se, a.v, j, H, h, v0, tid);
-    stage_chunk<NW>(pf[0], sm.buf[0], chunk_rows(se, 0).len, tid);
-    __syncthreads();
-    for (int ci = 0;;) {
+    for (int c = 0; c < D - 1; ++c) issue_chunk<NT, D>(ring[c], pl, recs, a.v, se, c, H, h, v0, wave);
+    u32x2 o_prev[NT];
+    int slot = 0;   // ring slot of chunk ci
+    for (int ci = 0; ci < nch; ++ci) {
+      // At most the D - 2 chunks issued after chunk ci may still be in flight
+      // (loads complete in issue order); the output stores of the step
+      // before, also counted, have had a whole step to complete.
+      wait_vmcnt<(D - 2) * Cf::kLoads>();
+      wait_lgkm0();
+      barrier();
+      // Every wave is done with chunk ci - 1, whose slot is refilled now, and
+      // every wave's loads of chunk ci have landed.
+      const int refill = slot == 0 ? D - 1 : slot - 1;
+      issue_chunk<NT, D>(ring[refill], pl, recs, a.v, se, ci + D - 1, H, h, v0, wave);
+      if (ci > 0) {   // output of chunk ci - 1
+        const Rows pr = chunk_rows(se, ci - 1);
+        if (lc < pr.len) {
 #pragma unroll
-      for (int u = 0; u < 2 * kDepth; ++u) {
-        const int cur = u % kDepth, nxt = (u + 1) % kDepth, B = u & 1;
-        if (ci > 0) store_out<NW>(sm.ot[B ^ 1], chunk_rows(se, ci - 1), a.out, H, h, v0, tid);
-        load_chunk<NW>(pf[cur], recs, se, a.v, ci + kDepth, H, h, v0, tid);
-        step<NW>(Z, sm.buf[B], sm.ot[B], wave, lg, lc);
-        if (ci + 1 < nch) stage_chunk<NW>(pf[nxt], sm.buf[B ^ 1], chunk_rows(se, ci + 1).len, tid);
-        __syncthreads();
-        if (++ci >= nch) goto chunks_done;
+          for (int nt = 0; nt < NT; ++nt)
+            *reinterpret_cast<u32x2*>(a.out + ((pr.row0 + lc) * H + h) * V + col0 + 16 * nt + 4 * lg) = o_prev[nt];
+        }
       }
+      Ops<NT> ops;
+      read_ops<NT, D>(ops, ring[slot], wc, lane);
+      compute<NT>(Z, ops, o_prev);
+      slot = slot == D - 1 ? 0 : slot + 1;
     }
-  chunks_done:
-    store_out<NW>(sm.ot[(nch - 1) & 1], chunk_rows(se, nch - 1), a.out, H, h, v0, tid);
+    const Rows pr = chunk_rows(se, nch - 1);
+    if (lc < pr.len) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        *reinterpret_cast<u32x2*>(a.out + ((pr.row0 + lc) * H + h) * V + col0 + 16 * nt + 4 * lg) = o_prev[nt];
+    }
   }
 
   // ---- final state
@@ -325,7 +402,7 @@ __global__ __launch_bounds__(64 * NW) void recur_kernel(RecurArgs a) {
 #pragma unroll
     for (int m = 0; m < 8; ++m)
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
+      for (int nt = 0; nt < NT; ++nt) {
         const int64_t idx = sbase + (int64_t)(col0 + 16 * nt + lc) * K + 16 * m + 4 * lg;
         if (a.state_dtype == KDA_DTYPE_FP32) {
           *reinterpret_cast<f32x4*>(static_cast<float*>(a.s_out) + idx) = Z[m][nt];
@@ -339,36 +416,45 @@ __global__ __launch_bounds__(64 * NW) void recur_kernel(RecurArgs a) {
   }
 }
 
-template <int NW>
-hipError_t launch_nw(const RecurArgs& a, hipStream_t s) {
+template <int NT, int D>
+hipError_t launch_tiles(const RecurArgs& a, hipStream_t s) {
   const int64_t pairs = a.N * a.H;
-  const int64_t grid = 8 * Tile<NW>::kTiles * ((pairs + 7) / 8);
-  hipLaunchKernelGGL(recur_kernel<NW>, dim3((unsigned)grid), dim3(Tile<NW>::kThreads), 0, s, a);
+  const int64_t grid = 8 * Cfg<NT, D>::kTiles * ((pairs + 7) / 8);
+  hipLaunchKernelGGL((recur_kernel<NT, D>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-// Waves per workgroup from the number of (sequence, head) pairs: one
-// workgroup per pair while that fills the 256 CUs, otherwise the value
-// columns are split over 2 workgroups per pair.  (Four single-wave workgroups
-// per pair measured slower at 96 pairs: each of them stages the whole record.)
-int recur_waves_per_group(int64_t pairs) {
-#ifdef KDA_RECUR_FORCE_NW
+// Value columns per recurrence workgroup from the number of (sequence, head)
+// pairs.  With enough pairs to fill the 256 CUs, one workgroup of four waves
+// takes a whole pair, 32 columns per wave, with a 3-chunk ring (60 KB of LDS,
+// two workgroups per CU).  With fewer, each wave takes 16 columns and a pair
+// is split over two workgroups: the per-step VALU work (state conversion and
+// decay) and MFMA work of a wave are halved, twice as many SIMDs carry the
+// serial chains, and a 4-chunk ring (64 KB) hides the HBM latency (deeper
+// rings measured no faster).
+int recur_tile_cols(int64_t pairs) {
+#ifdef KDA_RECUR_FORCE_COLS
   (void)pairs;
-  return KDA_RECUR_FORCE_NW;
+  return KDA_RECUR_FORCE_COLS;
 #else
-  return pairs >= 256 ? 4 : 2;
+  return pairs >= 256 ? 128 : 64;
 #endif
 }
+
+#ifndef KDA_RECUR_DEPTH64
+#define KDA_RECUR_DEPTH64 4
+#endif
+#ifndef KDA_RECUR_DEPTH128
+#define KDA_RECUR_DEPTH128 3
+#endif
 
 hipError_t launch_recur(const RecurArgs& a, hipStream_t s) {
   const int64_t pairs = a.N * a.H;
   if (pairs == 0) return hipSuccess;
-  switch (recur_waves_per_group(pairs)) {
-    case 2: return launch_nw<2>(a, s);
-    default: return launch_nw<4>(a, s);
-  }
+  if (recur_tile_cols(pairs) == 64) return launch_tiles<1, KDA_RECUR_DEPTH64>(a, s);
+  return launch_tiles<2, KDA_RECUR_DEPTH128>(a, s);
 }
 
 }  // namespace kda

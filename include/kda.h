@@ -163,7 +163,8 @@ int kda_fwd_check_status(const void* workspace, hipStream_t stream, int* status)
  * [16][128]; both with the channels of each 32-block stored in the order
  * {0-3, 16-19, 4-7, 20-23, 8-11, 24-27, 12-15, 28-31}; [8192, 12288) Kbar fp16
  * [16][128] (token-major, natural channel order); [12288, 12800) T^T fp16
- * [16][16]; [12800, 13312) Mqk^T fp16 [16][16]; [13312, 13824) gamma fp32 [128].
+ * [16][16]; [12800, 13312) Mqk^T fp16 [16][16]; [13312, 13824) gamma fp32 [128],
+ * channel c = 64 r + 16 a + 4 b + i stored at slot 2 (16 b + 4 a + i) + r.
  */
 int kda_workspace_layout(int64_t B, int64_t T, int64_t H, int64_t num_seqs, int has_cu_seqlens,
                          int64_t offsets[7]);

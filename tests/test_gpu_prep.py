@@ -15,6 +15,8 @@ if not torch.cuda.is_available():
     pytest.skip("no GPU", allow_module_level=True)
 
 EPS = 1e-6
+# stored gamma slot of channel c = 64 r + 16 a + 4 b + i (record layout in include/kda.h)
+GAM_SLOT = np.array([2 * (16 * ((c >> 2) & 3) + 4 * ((c >> 4) & 3) + (c & 3)) + (c >> 6) for c in range(128)])
 
 
 def perm_ch(p):
@@ -82,7 +84,7 @@ def test_chunk_table_and_records_match_chunked_form():
             f16 = lambda o, shape: rec[o:o + 2 * int(np.prod(shape))].view(np.float16).astype(np.float64).reshape(shape)
             got = dict(Qh=unpermute(f16(0, (16, 128)))[:ln], W=-unpermute(f16(4096, (16, 128)))[:ln],
                        Kb=f16(8192, (16, 128))[:ln], T=f16(12288, (16, 16)).T[:ln, :ln],
-                       M=f16(12800, (16, 16)).T[:ln, :ln], gamma=rec[13312:13824].view(np.float32).astype(np.float64))
+                       M=f16(12800, (16, 16)).T[:ln, :ln], gamma=rec[13312:13824].view(np.float32).astype(np.float64)[GAM_SLOT])
             ref = dict(Qh=P["Qh"], W=P["T"] @ P["Kh"], Kb=P["Kb"], T=P["T"], M=P["M"], gamma=P["gamma"])
             # padded rows / columns of a partial chunk are exactly zero
             assert np.all(f16(0, (16, 128))[ln:] == 0) and np.all(f16(4096, (16, 128))[ln:] == 0)
