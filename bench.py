@@ -90,7 +90,24 @@ def run_workload(cfg, steps, warmup, torch, kda, device_inputs):
                 token_heads=th, status=status)
 
 
-def roofline(res):
+TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "hbm_traffic_T8192_H96.md")
+
+
+def load_traffic():
+    """Per-kernel HBM bytes per dispatch from the committed counter summary,
+    keyed by workload, or {} when the kernels changed since it was taken (the
+    summary records a hash of the kernel sources)."""
+    from gated_delta_rule_prep_amd import prof_summary
+    try:
+        with open(TRAFFIC_FILE) as f:
+            entries = [json.loads(l.split("traffic-json:", 1)[1]) for l in f if l.startswith("traffic-json:")]
+    except OSError:
+        return {}
+    cur = prof_summary.source_hash()
+    return {e["workload"]: e["kernels"] for e in entries if e.get("source_hash") == cur}
+
+
+def roofline(res, traffic=None):
     inp, th = res["inp"], res["token_heads"]
     prep_bytes = th * PREP_BYTES_PER_TH + param_bytes(inp)
     recur_bytes = th * RECUR_BYTES_PER_TH + state_bytes(inp)
@@ -100,10 +117,12 @@ def roofline(res):
     else:
         name, kbytes, kms = "kda::prep_kernel", prep_bytes, res["prep_ms"]
     ach = kbytes / (kms * 1e-3) / 1e9
+    t = (traffic or {}).get(name.split("::")[1])
+    tbytes = None if t is None else int(t["fetch_bytes"] + t["write_bytes"])
     path_ms = res["ms"]
     path_ach = path_bytes / (path_ms * 1e-3) / 1e9
     return dict(kernel=name, bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                frac=round(ach / HBM_PEAK_GBS, 4), traffic=None, kernel_ms=round(kms, 4),
+                frac=round(ach / HBM_PEAK_GBS, 4), traffic=tbytes, kernel_ms=round(kms, 4),
                 algorithmic_bytes_per_launch=int(kbytes)), \
         dict(bound="hbm", achieved=round(path_ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
              frac=round(path_ach / HBM_PEAK_GBS, 4), algorithmic_bytes=int(path_bytes),
@@ -170,8 +189,9 @@ def main():
         return
     fixed = run_workload(cfgs[2], args.steps, args.warmup, torch, kda, device_inputs)
     varlen = run_workload(cfgs[3], args.steps, args.warmup, torch, kda, device_inputs)
-    rl, path = roofline(fixed)
-    rl_v, path_v = roofline(varlen)
+    traffic = load_traffic()
+    rl, path = roofline(fixed, traffic.get("fixed"))
+    rl_v, path_v = roofline(varlen, traffic.get("varlen"))
     cpu = None if args.no_cpu else cpu_baseline(cfgs[2], args.cpu_heads)
     value = fixed["token_heads"] / (fixed["ms"] * 1e-3)
     line = {

@@ -76,16 +76,30 @@ __global__ __launch_bounds__(kThreads) void sched_kernel(SchedArgs a) {
   }
   const int32_t total = s_carry;
 
-  // 3. chunk table: each thread fills the chunks of its sequences
-  for (int64_t n = tid; n < N; n += kThreads) {
-    const int64_t row0 = a.cu ? a.cu[n] : n * a.T;
-    const int64_t len = a.cu ? a.cu[n + 1] - a.cu[n] : a.T;
-    const int32_t first = seqs[n].first_chunk, nch = seqs[n].nchunks;
-    for (int32_t c = 0; c < nch; ++c) {
-      const int64_t rem = len - (int64_t)c * C;
-      chunks[first + c].seq = (int32_t)n;
-      chunks[first + c].row0 = (int32_t)(row0 + (int64_t)c * C);
-      chunks[first + c].len = (int32_t)(rem < C ? rem : C);
+  // 3. chunk table.  Up to kThreads sequences (one scan tile, still in LDS)
+  // the threads fill each sequence's chunks together, so that one long
+  // sequence does not leave a single thread writing all of its entries;
+  // beyond that each thread fills the chunks of its own sequences.
+  if (N <= kThreads) {
+    for (int64_t n = 0; n < N; ++n) {
+      const int32_t nch = bad ? 0 : s_scan[n] - (n > 0 ? s_scan[n - 1] : 0);
+      const int32_t first = s_scan[n] - nch;
+      const int64_t row0 = a.cu ? a.cu[n] : n * a.T;
+      const int64_t len = a.cu ? a.cu[n + 1] - a.cu[n] : a.T;
+      for (int32_t c = tid; c < nch; c += kThreads) {
+        const int64_t rem = len - (int64_t)c * C;
+        chunks[first + c] = ChunkEntry{(int32_t)n, (int32_t)(row0 + (int64_t)c * C), (int32_t)(rem < C ? rem : C)};
+      }
+    }
+  } else {
+    for (int64_t n = tid; n < N; n += kThreads) {
+      const int64_t row0 = a.cu ? a.cu[n] : n * a.T;
+      const int64_t len = a.cu ? a.cu[n + 1] - a.cu[n] : a.T;
+      const int32_t first = seqs[n].first_chunk, nch = seqs[n].nchunks;
+      for (int32_t c = 0; c < nch; ++c) {
+        const int64_t rem = len - (int64_t)c * C;
+        chunks[first + c] = ChunkEntry{(int32_t)n, (int32_t)(row0 + (int64_t)c * C), (int32_t)(rem < C ? rem : C)};
+      }
     }
   }
   __syncthreads();

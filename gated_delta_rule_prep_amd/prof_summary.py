@@ -1,0 +1,116 @@
+"""Turn rocprofv3 output into the short summaries kept under profiles/.
+
+  python -m gated_delta_rule_prep_amd.prof_summary stats <kernel_stats.csv> [title]
+      markdown table of the --stats kernel summary.
+  python -m gated_delta_rule_prep_amd.prof_summary traffic <workload> <fetch_dir> <write_dir> <copy_bytes>
+      per-kernel HBM bytes per dispatch from a FETCH_SIZE pass and a WRITE_SIZE
+      pass (counter_collection.csv under each directory).  Both counters are in
+      KiB per dispatch; each is scaled by what it reads for the plain copy of
+      copy_bytes bytes that bench.py --copy-mib runs after the workload (the
+      copy reads and writes exactly copy_bytes), so that the figures are bytes.
+      Prints one JSON object: {"workload", "scale", "kernels": {name: {fetch,
+      write}}, "source_hash"}.
+
+The source hash covers the HIP sources and headers of the kernels, so a
+reader (bench.py) can tell whether the counters still describe the current
+kernels.
+"""
+from __future__ import annotations
+
+import csv
+import glob
+import hashlib
+import json
+import os
+import re
+import statistics
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCES = ["csrc/kda_device.h", "csrc/kda_internal.h", "csrc/kda_sched.hip", "csrc/kda_prep.hip",
+                  "csrc/kda_recur.hip"]
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(HERE, rel), "rb") as f:
+            h.update(rel.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def short_name(name: str) -> str:
+    m = re.search(r"(sched_kernel|prep_kernel|recur_kernel|copyBuffer|elementwise_kernel)", name)
+    return m.group(1) if m else name[:40]
+
+
+def counter_rows(d: str):
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit("no counter_collection.csv under %s" % d)
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    return rows
+
+
+def per_dispatch(rows, counter):
+    out = {}
+    for r in rows:
+        if r["Counter_Name"] != counter:
+            continue
+        out.setdefault(short_name(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+    return out
+
+
+def copy_value(vals, expect_kib):
+    """The copy dispatches are the copyBuffer ones whose counter is within a
+    factor 4 of the copy size (input uploads are far smaller)."""
+    c = [v for v in vals.get("copyBuffer", []) if expect_kib / 4 <= v <= expect_kib * 4]
+    if not c:
+        raise SystemExit("no copy dispatch of the expected size")
+    return statistics.median(c)
+
+
+def traffic(workload, fetch_dir, write_dir, copy_bytes):
+    f = per_dispatch(counter_rows(fetch_dir), "FETCH_SIZE")
+    w = per_dispatch(counter_rows(write_dir), "WRITE_SIZE")
+    kib = copy_bytes / 1024.0
+    fs = copy_bytes / copy_value(f, kib)   # bytes per counter unit
+    ws = copy_bytes / copy_value(w, kib)
+    kernels = {}
+    for k in ("sched_kernel", "prep_kernel", "recur_kernel"):
+        if k in f and k in w:
+            kernels[k] = {"fetch_bytes": int(statistics.median(f[k]) * fs),
+                          "write_bytes": int(statistics.median(w[k]) * ws), "dispatches": len(f[k])}
+    return {"workload": workload, "scale": {"fetch_bytes_per_unit": fs, "write_bytes_per_unit": ws},
+            "kernels": kernels, "source_hash": source_hash()}
+
+
+def stats(path, title=""):
+    with open(path) as fh:
+        rows = list(csv.DictReader(fh))
+    lines = ["| kernel | calls | avg us | min us | max us | share |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append("| %s | %s | %.1f | %.1f | %.1f | %.1f %% |" % (
+            short_name(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+            float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    return ("### " + title + "\n\n" if title else "") + "\n".join(lines)
+
+
+def main(argv):
+    if len(argv) >= 2 and argv[1] == "stats":
+        print(stats(argv[2], argv[3] if len(argv) > 3 else ""))
+    elif len(argv) == 6 and argv[1] == "traffic":
+        print(json.dumps(traffic(argv[2], argv[3], argv[4], int(argv[5]))))
+    elif len(argv) == 2 and argv[1] == "hash":
+        print(source_hash())
+    else:
+        print(__doc__)
+        return 2
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main(sys.argv))
