@@ -6,7 +6,7 @@ over one batch of seeded synthetic input already resident in HBM.  Workloads:
     initial and final state, lower_bound = -5;
   * also timed: the same shape as 8 varlen sequences of 1024 tokens.
 Prints ONE JSON line (rank 0).  Per-kernel times come from HIP events that
-kda_fwd_profiled records on the launch stream; the roofline is computed for
+kda_fwd_ex records around every kernel on the stream it runs on; the roofline is computed for
 the kernel that takes the most time, with algorithmic bytes only (inputs and
 outputs of the method that kernel is responsible for), and for the whole path.
 The fp64 oracle is timed on a bounded sample of the headline workload on the
@@ -73,9 +73,11 @@ def run_workload(cfg, steps, warmup, torch, kda, device_inputs):
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / steps
 
-    # per-kernel durations, HIP events recorded by the library on its stream
+    # per-kernel durations: kda_fwd_ex records HIP events before and after
+    # every kernel on the stream it launches that kernel on
     n_prof = max(steps, 5)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_prof)]
+    P = kda.parts(inp.B, inp.T)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2 + 4 * P)] for _ in range(n_prof)]
     for row in ev:
         for e in row:
             e.record()          # creates the underlying HIP event
@@ -83,7 +85,9 @@ def run_workload(cfg, steps, warmup, torch, kda, device_inputs):
     for row in ev:
         step(events=row)
     torch.cuda.synchronize()
-    k_ms = np.array([[row[i].elapsed_time(row[i + 1]) for i in range(3)] for row in ev]).mean(axis=0)
+    span = lambda row, i: row[i].elapsed_time(row[i + 1])
+    k_ms = np.array([[span(row, 0), sum(span(row, 2 + 2 * p) for p in range(P)),
+                      sum(span(row, 2 + 2 * P + 2 * p) for p in range(P))] for row in ev]).mean(axis=0)
     status = kda.check_status(ws)
     th = inp.B * inp.T * inp.H
     return dict(inp=inp, ms=ms, sched_ms=float(k_ms[0]), prep_ms=float(k_ms[1]), recur_ms=float(k_ms[2]),

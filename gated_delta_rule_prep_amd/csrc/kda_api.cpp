@@ -9,6 +9,8 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <algorithm>
+#include <cstdint>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -41,7 +43,7 @@ constexpr int kMaxDevices = 64;
 int g_dev_ok[kMaxDevices];
 std::once_flag g_dev_once;
 
-int check_device() {
+int check_device(int* dev_out = nullptr) {
   std::call_once(g_dev_once, [] {
     for (int i = 0; i < kMaxDevices; ++i) g_dev_ok[i] = -1;
   });
@@ -58,6 +60,35 @@ int check_device() {
     __atomic_store_n(&g_dev_ok[dev], ok, __ATOMIC_RELEASE);
   }
   if (!ok) return fail(KDA_EUNSUPPORTED, "kda: device %d is not gfx950 (MI355X)", dev);
+  if (dev_out) *dev_out = dev;
+  return KDA_OK;
+}
+
+// Per-device side stream and events for the overlapped path: the recurrence
+// of part p runs on the side stream while the main stream computes the chunk
+// records of part p + 1.  Created on first use, kept until the process ends;
+// the mutex also keeps concurrent callers on one device from interleaving
+// their use of the shared stream and events.
+struct SideRes {
+  std::mutex mu;
+  bool ready = false;
+  hipStream_t side = nullptr;
+  hipEvent_t prep_done[kda::kMaxParts];
+  hipEvent_t join;
+};
+SideRes g_side[kMaxDevices];
+
+int side_resources(int dev, SideRes** out) {
+  SideRes& r = g_side[dev];
+  if (!r.ready) {
+    hipError_t e = hipStreamCreateWithFlags(&r.side, hipStreamNonBlocking);
+    for (int i = 0; e == hipSuccess && i < kda::kMaxParts; ++i)
+      e = hipEventCreateWithFlags(&r.prep_done[i], hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&r.join, hipEventDisableTiming);
+    if (e != hipSuccess) return fail(KDA_EHIP, "kda: side stream or event creation: %s", hipGetErrorString(e));
+    r.ready = true;
+  }
+  *out = &r;
   return KDA_OK;
 }
 
@@ -100,10 +131,19 @@ bool layout_for(int64_t B, int64_t T, int64_t H, int64_t N, Layout* L) {
   L->records = off;
   L->rec_bytes = REC_BYTES;
   L->max_chunks = max_chunks;
-  off += H * max_chunks * REC_BYTES;
+  off = align_up(off + H * max_chunks * REC_BYTES, 256);
+  L->state = off;
+  off += N * H * V * K * (int64_t)sizeof(float);
   L->total = align_up(off, 256);
   return true;
 }
+
+// Parts used when the caller leaves the choice to the library: one.  On
+// MI355X the two kernels slow each other down by about as much as running
+// them side by side saves (measured at T = 8192, H = 64 / 96, fixed and
+// varlen: 2 to 8 parts change the step time by -2 % to +50 %), so overlap is
+// left to callers that measure a gain at their own shapes.
+int parts_for(int64_t) { return 1; }
 
 }  // namespace kda
 
@@ -165,12 +205,20 @@ static int validate_common(const void* q, const void* k, const void* g, const vo
   return KDA_OK;
 }
 
+// Parts the call uses: `requested` (clamped to 1 .. kMaxParts) or, for 0, the
+// library's choice for B*T rows.
+static int parts_used(int64_t B, int64_t T, int requested) {
+  if (B * T == 0) return 1;
+  if (requested > 0) return requested < kda::kMaxParts ? requested : kda::kMaxParts;
+  return kda::parts_for(B * T);
+}
+
 static int fwd_impl(const void* q, const void* k, const void* v, const void* g, const void* beta, float scale,
                     void* out, const float* A_log, const float* dt_bias, float lower_bound,
                     const void* initial_state, int initial_state_dtype, void* final_state,
                     int final_state_dtype, const int64_t* cu_seqlens, int64_t num_seqs, int64_t B,
                     int64_t T, int64_t H, int64_t K, int64_t V, void* workspace, size_t workspace_bytes,
-                    hipStream_t stream, hipEvent_t* ev) {
+                    hipStream_t stream, int parts_req, hipEvent_t* ev, int n_ev, hipEvent_t* ev4) {
   try {
     if ((!v || !out) && B * T > 0) return fail(KDA_EINVAL, "kda: v or out is NULL");
     auto dtype_ok = [](int d) { return d == KDA_DTYPE_NONE || d == KDA_DTYPE_BF16 || d == KDA_DTYPE_FP32; };
@@ -182,6 +230,7 @@ static int fwd_impl(const void* q, const void* k, const void* v, const void* g, 
       return fail(KDA_EDTYPE, "kda: final_state pointer and dtype disagree");
     if (initial_state && final_state && initial_state_dtype != final_state_dtype)
       return fail(KDA_EDTYPE, "kda: initial_state and final_state dtypes differ");
+    if (parts_req < 0) return fail(KDA_EINVAL, "kda: parts must be >= 0 (got %d)", parts_req);
     kda::Layout L;
     int64_t N = 0;
     int rc = validate_common(q, k, g, beta, scale, A_log, dt_bias, lower_bound, cu_seqlens, num_seqs, B, T,
@@ -189,32 +238,68 @@ static int fwd_impl(const void* q, const void* k, const void* v, const void* g, 
     if (rc != KDA_OK) return rc;
     if (misaligned(v) || misaligned(out) || misaligned(initial_state) || misaligned(final_state))
       return fail(KDA_EINVAL, "kda: v, out and the states must be 16-byte aligned");
-    rc = check_device();
+    const int P = parts_used(B, T, parts_req);
+    if (ev && n_ev != 2 + 4 * P)
+      return fail(KDA_EINVAL, "kda: %d events given, this call needs %d (2 + 4 x %d parts)", n_ev, 2 + 4 * P, P);
+    int dev = 0;
+    rc = check_device(&dev);
     if (rc != KDA_OK) return rc;
+    SideRes* side = nullptr;
+    std::unique_lock<std::mutex> lock;
+    if (P > 1) {
+      lock = std::unique_lock<std::mutex>(g_side[dev].mu);
+      rc = side_resources(dev, &side);
+      if (rc != KDA_OK) return rc;
+    }
+    hipStream_t rstream = P > 1 ? side->side : stream;   // where the recurrence runs
 
-    auto mark = [&](int i) -> hipError_t { return ev ? hipEventRecord(ev[i], stream) : hipSuccess; };
+    hipError_t e = hipSuccess;
+    auto rec = [&](int i, hipStream_t st) {
+      if (e == hipSuccess && ev) e = hipEventRecord(ev[i], st);
+    };
+    auto rec4 = [&](int i) {
+      if (e == hipSuccess && ev4) e = hipEventRecord(ev4[i], stream);
+    };
     char* ws = static_cast<char*>(workspace);
-    hipError_t e = mark(0);
-    if (e != hipSuccess) return fail(KDA_EHIP, "kda: hipEventRecord: %s", hipGetErrorString(e));
-    kda::SchedArgs sa{cu_seqlens, N, B, T, ws, L};
-    e = kda::launch_sched(sa, stream);
-    if (e != hipSuccess) return fail(KDA_EHIP, "kda: scheduler launch: %s", hipGetErrorString(e));
-    e = mark(1);
-    if (e != hipSuccess) return fail(KDA_EHIP, "kda: hipEventRecord: %s", hipGetErrorString(e));
-    kda::PrepArgs pa{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                     static_cast<const uint16_t*>(g), static_cast<const uint16_t*>(beta), A_log, dt_bias,
-                     scale, lower_bound, H, ws, L};
-    e = kda::launch_prep(pa, stream);
-    if (e != hipSuccess) return fail(KDA_EHIP, "kda: prep launch: %s", hipGetErrorString(e));
-    e = mark(2);
-    if (e != hipSuccess) return fail(KDA_EHIP, "kda: hipEventRecord: %s", hipGetErrorString(e));
+    const int64_t rows = B * T;
+    const int64_t part_rows = P > 1 ? (rows + P - 1) / P : (rows > 0 ? rows : 1);
+    rec(0, stream);
+    rec4(0);
+    if (e == hipSuccess) {
+      kda::SchedArgs sa{cu_seqlens, N, B, T, P, part_rows, ws, L};
+      e = kda::launch_sched(sa, stream);
+    }
+    rec(1, stream);
+    rec4(1);
     const int sdt = initial_state ? initial_state_dtype : final_state_dtype;
-    kda::RecurArgs ra{static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out), initial_state, final_state,
-                      sdt, N, H, ws, L};
-    e = kda::launch_recur(ra, stream);
-    if (e != hipSuccess) return fail(KDA_EHIP, "kda: recurrence launch: %s", hipGetErrorString(e));
-    e = mark(3);
-    if (e != hipSuccess) return fail(KDA_EHIP, "kda: hipEventRecord: %s", hipGetErrorString(e));
+    for (int p = 0; p < P && e == hipSuccess; ++p) {
+      // chunks whose first row lies in the part's rows: at most one per 16 rows
+      // plus one per sequence start
+      const int64_t bound = P == 1 ? L.max_chunks : std::min(L.max_chunks, part_rows / kda::C + N + 1);
+      kda::PrepArgs pa{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                       static_cast<const uint16_t*>(g), static_cast<const uint16_t*>(beta), A_log, dt_bias,
+                       scale, lower_bound, H, p, bound, ws, L};
+      rec(2 + 2 * p, stream);
+      if (e == hipSuccess) e = kda::launch_prep(pa, stream);
+      rec(3 + 2 * p, stream);
+      if (P > 1 && e == hipSuccess) {
+        e = hipEventRecord(side->prep_done[p], stream);
+        if (e == hipSuccess) e = hipStreamWaitEvent(rstream, side->prep_done[p], 0);
+      }
+      const int64_t lo = p * part_rows, hi = p == P - 1 ? (INT64_MAX / 2) : (p + 1) * part_rows;
+      kda::RecurArgs ra{static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out), initial_state, final_state,
+                        sdt, N, H, p, lo, hi, ws, L};
+      rec(2 + 2 * P + 2 * p, rstream);
+      if (e == hipSuccess) e = kda::launch_recur(ra, rstream);
+      rec(3 + 2 * P + 2 * p, rstream);
+    }
+    rec4(2);
+    if (P > 1 && e == hipSuccess) {
+      e = hipEventRecord(side->join, rstream);
+      if (e == hipSuccess) e = hipStreamWaitEvent(stream, side->join, 0);
+    }
+    rec4(3);
+    if (e != hipSuccess) return fail(KDA_EHIP, "kda: launch or event call: %s", hipGetErrorString(e));
     return KDA_OK;
   } catch (...) {
     return fail(KDA_EHIP, "kda: unexpected C++ exception");
@@ -229,7 +314,7 @@ int kda_fwd(const void* q, const void* k, const void* v, const void* g, const vo
             hipStream_t stream) {
   return fwd_impl(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
                   initial_state_dtype, final_state, final_state_dtype, cu_seqlens, num_seqs, B, T, H, K, V,
-                  workspace, workspace_bytes, stream, nullptr);
+                  workspace, workspace_bytes, stream, 0, nullptr, 0, nullptr);
 }
 
 int kda_fwd_profiled(const void* q, const void* k, const void* v, const void* g, const void* beta,
@@ -242,7 +327,26 @@ int kda_fwd_profiled(const void* q, const void* k, const void* v, const void* g,
     return fail(KDA_EINVAL, "kda: kda_fwd_profiled needs four events");
   return fwd_impl(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
                   initial_state_dtype, final_state, final_state_dtype, cu_seqlens, num_seqs, B, T, H, K, V,
-                  workspace, workspace_bytes, stream, events);
+                  workspace, workspace_bytes, stream, 0, nullptr, 0, events);
+}
+
+int kda_fwd_parts(int64_t B, int64_t T, int parts) {
+  if (B < 0 || T < 0 || parts < 0) return 0;
+  return parts_used(B, T, parts);
+}
+
+int kda_fwd_ex(const void* q, const void* k, const void* v, const void* g, const void* beta, float scale,
+               void* out, const float* A_log, const float* dt_bias, float lower_bound,
+               const void* initial_state, int initial_state_dtype, void* final_state, int final_state_dtype,
+               const int64_t* cu_seqlens, int64_t num_seqs, int64_t B, int64_t T, int64_t H, int64_t K,
+               int64_t V, void* workspace, size_t workspace_bytes, hipStream_t stream, int parts,
+               hipEvent_t* events, int num_events) {
+  if (events != nullptr)
+    for (int i = 0; i < num_events; ++i)
+      if (!events[i]) return fail(KDA_EINVAL, "kda: event %d is NULL", i);
+  return fwd_impl(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
+                  initial_state_dtype, final_state, final_state_dtype, cu_seqlens, num_seqs, B, T, H, K, V,
+                  workspace, workspace_bytes, stream, parts, events, num_events, nullptr);
 }
 
 int kda_debug_prep(const void* q, const void* k, const void* g, const void* beta, float scale,
@@ -258,12 +362,12 @@ int kda_debug_prep(const void* q, const void* k, const void* g, const void* beta
     rc = check_device();
     if (rc != KDA_OK) return rc;
     char* ws = static_cast<char*>(workspace);
-    kda::SchedArgs sa{cu_seqlens, N, B, T, ws, L};
+    kda::SchedArgs sa{cu_seqlens, N, B, T, 1, B * T > 0 ? B * T : 1, ws, L};
     hipError_t e = kda::launch_sched(sa, stream);
     if (e != hipSuccess) return fail(KDA_EHIP, "kda: scheduler launch: %s", hipGetErrorString(e));
     kda::PrepArgs pa{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(g), static_cast<const uint16_t*>(beta), A_log, dt_bias,
-                     scale, lower_bound, H, ws, L};
+                     scale, lower_bound, H, 0, L.max_chunks, ws, L};
     e = kda::launch_prep(pa, stream);
     if (e != hipSuccess) return fail(KDA_EHIP, "kda: prep launch: %s", hipGetErrorString(e));
     return KDA_OK;

@@ -28,12 +28,18 @@ __host__ __device__ constexpr int kGamSlot(int c) {
   return 2 * (16 * ((c >> 2) & 3) + 4 * ((c >> 4) & 3) + (c & 3)) + (c >> 6);
 }
 
+// The token rows are cut into at most kMaxParts consecutive ranges ("parts");
+// the prep kernel of part p + 1 runs while the recurrence works on part p.
+constexpr int kMaxParts = 8;
+
 // Workspace header (first 256 bytes).
 struct WsHeader {
-  int32_t status;       // KDA_STATUS_*
-  int32_t chunk_count;  // number of valid chunk-table entries
-  int32_t pad[62];
+  int32_t status;                   // KDA_STATUS_*
+  int32_t chunk_count;              // number of valid chunk-table entries
+  int32_t part_first[kMaxParts + 1];  // chunk-table index of the first chunk of each part; [parts] = count
+  int32_t pad[53];
 };
+static_assert(sizeof(WsHeader) == 256, "header size");
 
 struct ChunkEntry {     // chunk table entry
   int32_t seq;          // sequence index n
@@ -55,15 +61,19 @@ struct Layout {
   int64_t records;
   int64_t rec_bytes;
   int64_t max_chunks;
+  int64_t state;        // fp32 [N][H][V][K]: the state handed from one part to the next
   int64_t total;
 };
 
 // Returns false if the sizes are invalid.
 bool layout_for(int64_t B, int64_t T, int64_t H, int64_t N, Layout* out);
+int parts_for(int64_t rows);   // parts used for B*T token rows when the caller does not choose
 
 struct SchedArgs {
   const int64_t* cu;    // device, N + 1 entries, or nullptr
   int64_t N, B, T;
+  int parts;            // 1 .. kMaxParts
+  int64_t part_rows;    // token rows per part (the last part takes the rest)
   char* ws;
   Layout lay;
 };
@@ -78,6 +88,8 @@ struct PrepArgs {
   float scale;
   float lower_bound;
   int64_t H;
+  int part;             // chunks part_first[part] .. part_first[part + 1] - 1
+  int64_t grid_chunks;  // workgroup columns launched (a bound on the part's chunk count)
   char* ws;
   Layout lay;
 };
@@ -89,6 +101,8 @@ struct RecurArgs {
   void* s_out;
   int state_dtype;      // KDA_DTYPE_*
   int64_t N, H;
+  int part;             // chunks whose first token row lies in [row_lo, row_hi)
+  int64_t row_lo, row_hi;
   char* ws;
   Layout lay;
 };

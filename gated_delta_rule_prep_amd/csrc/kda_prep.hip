@@ -66,9 +66,9 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
   const int wave = tid >> 6, lane = tid & 63;
   const int64_t H = a.H;
   const int h = blockIdx.y * kWaves + wave;
-  const int chunk = blockIdx.x;
   const WsHeader* hdr = reinterpret_cast<const WsHeader*>(a.ws);
-  if (chunk >= hdr->chunk_count || h >= H) return;   // whole waves only; no barriers below
+  const int chunk = hdr->part_first[a.part] + (int)blockIdx.x;   // this launch covers one part
+  if (chunk >= hdr->part_first[a.part + 1] || h >= H) return;   // whole waves only; no barriers below
   WaveSmem& sm = wsm[wave];
   const ChunkEntry ce = reinterpret_cast<const ChunkEntry*>(a.ws + a.lay.chunk_table)[chunk];
   const int r = lane & 15, cq = lane >> 4;
@@ -232,9 +232,9 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
 }  // namespace
 
 hipError_t launch_prep(const PrepArgs& a, hipStream_t s) {
-  if (a.lay.max_chunks == 0) return hipSuccess;
+  if (a.grid_chunks == 0) return hipSuccess;
   const unsigned hx = (unsigned)((a.H + kWaves - 1) / kWaves);
-  hipLaunchKernelGGL(prep_kernel, dim3((unsigned)a.lay.max_chunks, hx), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(prep_kernel, dim3((unsigned)a.grid_chunks, hx), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

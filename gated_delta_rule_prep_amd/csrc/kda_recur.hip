@@ -280,16 +280,18 @@ __device__ __forceinline__ void load_lds16(const i32x4& rsrc, uint32_t lds, int 
       : "memory");
 }
 
-// Issue the loads of chunk c into ring slot `slot` (all lanes, no waits).
+// Issue the loads of chunk min(c, clast) into ring slot `slot` (all lanes, no
+// waits); clast is the last chunk of the part, so loads never run ahead into
+// records that the next part's prep may still be writing.
 // Value rows past the end of a partial chunk repeat the last row: the
 // record gives them zero weight (their T rows and columns and their -W, Qhat
 // and Kbar rows are exactly zero), so any finite values are harmless.
 template <int NT, int D>
 __device__ __forceinline__ void issue_chunk(char* slot, const LoadPlan<NT, D>& pl, const char* recs,
-                                            const uint16_t* v, const SeqEntry& se, int c, int64_t H, int h,
-                                            int v0, int wave) {
+                                            const uint16_t* v, const SeqEntry& se, int c, int clast, int64_t H,
+                                            int h, int v0, int wave) {
   using Cf = Cfg<NT, D>;
-  c = min(c, se.nchunks - 1);
+  c = min(c, clast);
   const Rows cr = chunk_rows(se, c);
   const i32x4 rrec = buf_rsrc(recs + (int64_t)c * REC_BYTES, REC_BYTES);
   const int row_bytes = (int)(H * V * 2);
@@ -332,6 +334,20 @@ __global__ __launch_bounds__(kThreads) void recur_kernel(RecurArgs a) {
   const SeqEntry se = reinterpret_cast<const SeqEntry*>(a.ws + a.lay.seq_table)[n];
   const char* recs = a.ws + a.lay.records + ((int64_t)h * a.lay.max_chunks + se.first_chunk) * REC_BYTES;
   const int nch = se.nchunks;
+  // This launch covers the chunks whose first token row lies in [row_lo,
+  // row_hi): chunks ci_lo .. ci_hi - 1 of the sequence.  The state comes from
+  // the caller's initial state when the part starts the sequence, otherwise
+  // from the previous part (fp32 in the workspace), and goes to the caller's
+  // final state when the part ends the sequence, otherwise to the next part.
+  // An empty sequence passes its state through in part 0.
+  const auto first_at = [&](int64_t row) -> int {
+    const int64_t d = row - se.row0;
+    return d <= 0 ? 0 : (int)min((d + C - 1) / C, (int64_t)nch);
+  };
+  const int ci_lo = first_at(a.row_lo), ci_hi = first_at(a.row_hi);
+  if (nch > 0 ? ci_lo >= ci_hi : a.part != 0) return;
+  const bool from_caller = ci_lo == 0, to_caller = ci_hi == nch;
+  float* const ws_state = reinterpret_cast<float*>(a.ws + a.lay.state);
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, lg = lane >> 4, lc = lane & 15;
@@ -346,7 +362,9 @@ __global__ __launch_bounds__(kThreads) void recur_kernel(RecurArgs a) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const int64_t idx = sbase + (int64_t)(col0 + 16 * nt + lc) * K + 16 * m + 4 * lg;
-      if (a.s_in == nullptr) {
+      if (!from_caller) {
+        Z[m][nt] = *reinterpret_cast<const f32x4*>(ws_state + idx);
+      } else if (a.s_in == nullptr) {
         Z[m][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
       } else if (a.state_dtype == KDA_DTYPE_FP32) {
         Z[m][nt] = *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.s_in) + idx);
@@ -356,16 +374,18 @@ __global__ __launch_bounds__(kThreads) void recur_kernel(RecurArgs a) {
       }
     }
 
-  if (nch > 0) {
+  if (ci_lo < ci_hi) {
     LoadPlan<NT, D> pl;
     make_plan<NT, D>(pl, wave, lane);
-    // Chunks 0 .. D-2 in flight before the first step.  Loads past the last
-    // chunk repeat it into slots that are never read.
+    const int clast = ci_hi - 1;
+    // Chunks ci_lo .. ci_lo + D-2 in flight before the first step.  Loads past
+    // the part's last chunk repeat it into slots that are never read.
 #pragma unroll
-    for (int c = 0; c < D - 1; ++c) issue_chunk<NT, D>(ring[c], pl, recs, a.v, se, c, H, h, v0, wave);
+    for (int c = 0; c < D - 1; ++c)
+      issue_chunk<NT, D>(ring[c], pl, recs, a.v, se, ci_lo + c, clast, H, h, v0, wave);
     u32x2 o_prev[NT];
     int slot = 0;   // ring slot of chunk ci
-    for (int ci = 0; ci < nch; ++ci) {
+    for (int ci = ci_lo; ci < ci_hi; ++ci) {
       // At most the D - 2 chunks issued after chunk ci may still be in flight
       // (loads complete in issue order); the output stores of the step
       // before, also counted, have had a whole step to complete.
@@ -375,8 +395,8 @@ __global__ __launch_bounds__(kThreads) void recur_kernel(RecurArgs a) {
       // Every wave is done with chunk ci - 1, whose slot is refilled now, and
       // every wave's loads of chunk ci have landed.
       const int refill = slot == 0 ? D - 1 : slot - 1;
-      issue_chunk<NT, D>(ring[refill], pl, recs, a.v, se, ci + D - 1, H, h, v0, wave);
-      if (ci > 0) {   // output of chunk ci - 1
+      issue_chunk<NT, D>(ring[refill], pl, recs, a.v, se, ci + D - 1, clast, H, h, v0, wave);
+      if (ci > ci_lo) {   // output of chunk ci - 1
         const Rows pr = chunk_rows(se, ci - 1);
         if (lc < pr.len) {
 #pragma unroll
@@ -389,7 +409,7 @@ __global__ __launch_bounds__(kThreads) void recur_kernel(RecurArgs a) {
       compute<NT>(Z, ops, o_prev);
       slot = slot == D - 1 ? 0 : slot + 1;
     }
-    const Rows pr = chunk_rows(se, nch - 1);
+    const Rows pr = chunk_rows(se, clast);
     if (lc < pr.len) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
@@ -397,14 +417,16 @@ __global__ __launch_bounds__(kThreads) void recur_kernel(RecurArgs a) {
     }
   }
 
-  // ---- final state
-  if (a.s_out != nullptr) {
+  // ---- state out
+  if (!to_caller || a.s_out != nullptr) {
 #pragma unroll
     for (int m = 0; m < 8; ++m)
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const int64_t idx = sbase + (int64_t)(col0 + 16 * nt + lc) * K + 16 * m + 4 * lg;
-        if (a.state_dtype == KDA_DTYPE_FP32) {
+        if (!to_caller) {
+          *reinterpret_cast<f32x4*>(ws_state + idx) = Z[m][nt];
+        } else if (a.state_dtype == KDA_DTYPE_FP32) {
           *reinterpret_cast<f32x4*>(static_cast<float*>(a.s_out) + idx) = Z[m][nt];
         } else {
           u32x2 w;

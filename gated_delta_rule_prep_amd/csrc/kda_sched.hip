@@ -8,6 +8,8 @@
 //   * a per-sequence table {first chunk, chunk count, first token row, length};
 //   * a work order of the sequences, longest first, so that the chunk
 //     recurrence starts its longest serial chains first;
+//   * the first chunk of each part (parts cut the token rows into consecutive
+//     ranges of part_rows rows, so that prep and recurrence can overlap);
 //   * a status word: KDA_STATUS_BAD_CU_SEQLENS when cu_seqlens[0] != 0, the
 //     boundaries decrease, or cu_seqlens[N] != T.  Then every sequence gets zero
 //     chunks, so no later kernel touches a token.
@@ -104,7 +106,20 @@ __global__ __launch_bounds__(kThreads) void sched_kernel(SchedArgs a) {
   }
   __syncthreads();
 
-  // 4. work order, longest first (ties by index); identity beyond kRankSortMax
+  // 4. parts: part_first[p] = index of the first chunk whose first token row is
+  // at or past p * part_rows (the chunk table is in token order)
+  auto part_of = [&](int32_t row0) { return (int)min((int64_t)row0 / a.part_rows, (int64_t)a.parts - 1); };
+  for (int32_t i = tid; i < total; i += kThreads) {
+    const int pi = part_of(chunks[i].row0);
+    const int pprev = i > 0 ? part_of(chunks[i - 1].row0) : -1;
+    for (int p = pprev + 1; p <= pi; ++p) hdr->part_first[p] = i;
+  }
+  if (tid == 0) {
+    const int plast = total > 0 ? part_of(chunks[total - 1].row0) : -1;
+    for (int p = plast + 1; p <= a.parts; ++p) hdr->part_first[p] = total;
+  }
+
+  // 5. work order, longest first (ties by index); identity beyond kRankSortMax
   const bool sort = N <= kRankSortMax;
   if (sort)
     for (int64_t n = tid; n < N; n += kThreads) s_nch[n] = seqs[n].nchunks;

@@ -25,8 +25,8 @@ KDA_DTYPE_NONE, KDA_DTYPE_BF16, KDA_DTYPE_FP32 = 0, 1, 2
 KDA_STATUS_OK, KDA_STATUS_BAD_CU_SEQLENS = 0, 1
 CHUNK = 16
 
-EXPORTS = ("kda_fwd", "kda_fwd_profiled", "kda_fwd_workspace_bytes", "kda_get_last_error", "kda_version",
-           "kda_fwd_check_status", "kda_workspace_layout", "kda_debug_prep")
+EXPORTS = ("kda_fwd", "kda_fwd_profiled", "kda_fwd_ex", "kda_fwd_parts", "kda_fwd_workspace_bytes",
+           "kda_get_last_error", "kda_version", "kda_fwd_check_status", "kda_workspace_layout", "kda_debug_prep")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError("libkda.so is not built (run gated_delta_rule_prep_amd/build.py or "
@@ -41,6 +41,10 @@ _lib.kda_fwd.argtypes = [_p, _p, _p, _p, _p, ctypes.c_float, _p, _p, _p, ctypes.
 _lib.kda_fwd.restype = ctypes.c_int
 _lib.kda_fwd_profiled.argtypes = _lib.kda_fwd.argtypes + [ctypes.POINTER(ctypes.c_void_p)]
 _lib.kda_fwd_profiled.restype = ctypes.c_int
+_lib.kda_fwd_ex.argtypes = _lib.kda_fwd.argtypes + [ctypes.c_int, ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
+_lib.kda_fwd_ex.restype = ctypes.c_int
+_lib.kda_fwd_parts.argtypes = [_i64, _i64, ctypes.c_int]
+_lib.kda_fwd_parts.restype = ctypes.c_int
 _lib.kda_fwd_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int]
 _lib.kda_fwd_workspace_bytes.restype = ctypes.c_size_t
 _lib.kda_get_last_error.restype = ctypes.c_char_p
@@ -130,14 +134,21 @@ def alloc_workspace(B: int, T: int, H: int, num_seqs: int, has_cu: bool, device)
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
+def parts(B: int, T: int, requested: int = 0) -> int:
+    """Parts (overlapped prep / recurrence ranges) a call uses; see kda_fwd_ex."""
+    return _lib.kda_fwd_parts(B, T, requested)
+
+
 def fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state=None, final_state=None,
-        cu_seqlens=None, workspace: Optional[torch.Tensor] = None, events=None):
+        cu_seqlens=None, workspace: Optional[torch.Tensor] = None, events=None, parts: Optional[int] = None):
     """Chunked KDA forward into the caller's ``out`` (and ``final_state``).
 
     Shapes and dtypes as in include/kda.h.  Runs on the current stream of the
-    tensors' device.  Returns ``out``.  ``events``: optional list of four
-    torch.cuda.Event (created with enable_timing=True); when given, the call
-    goes through kda_fwd_profiled, which records them around each kernel.
+    tensors' device.  Returns ``out``.  ``parts``: None for kda_fwd's own
+    choice, or the number of overlapped ranges (kda_fwd_ex).  ``events``:
+    optional torch.cuda.Event list (enable_timing=True): four go through
+    kda_fwd_profiled; 2 + 4 P (P = ``parts(B, T, parts or 0)``) go through
+    kda_fwd_ex, which records them around every kernel.
     """
     if q.dim() != 4:
         raise KDAValueError(KDA_EINVAL, "q must be [B, T, H, K]")
@@ -176,11 +187,15 @@ def fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state
             _state_code(initial_state), _ptr(final_state), _state_code(final_state),
             _ptr(cu_seqlens), N, B, T, H, K, V, _ptr(workspace), workspace.numel())
     with torch.cuda.device(dev):
-        if events is None:
+        if events is None and parts is None:
             rc = _lib.kda_fwd(*args, _stream(dev))
-        else:
+        elif parts is None and len(events) == 4:
             ev = (ctypes.c_void_p * 4)(*[e.cuda_event for e in events])
             rc = _lib.kda_fwd_profiled(*args, _stream(dev), ev)
+        else:
+            n = 0 if events is None else len(events)
+            ev = None if events is None else (ctypes.c_void_p * n)(*[e.cuda_event for e in events])
+            rc = _lib.kda_fwd_ex(*args, _stream(dev), int(parts or 0), ev, n)
     if rc != KDA_OK:
         _raise(rc)
     return out

@@ -98,8 +98,9 @@ extern "C" {
  * cu_seqlens: NULL, or num_seqs + 1 int64 prefix sums on the device (B == 1).
  * Its contents are checked on the device (see kda_fwd_check_status).
  * workspace: at least kda_fwd_workspace_bytes(B, T, H, num_seqs, cu != NULL)
- * bytes of device memory, 256-byte aligned.  Its contents are scratch between
- * calls except for the status word.
+ * bytes of device memory, 256-byte aligned (chunk tables, chunk records and an
+ * fp32 state per (sequence, head) for the hand-over between parts).  Its
+ * contents are scratch between calls except for the status word.
  * stream: a hipStream_t (NULL = the default stream).
  *
  * With no tokens (B * T == 0) the token tensors q, k, v, g, beta and out are
@@ -116,11 +117,13 @@ int kda_fwd(const void* q, const void* k, const void* v, const void* g, const vo
             hipStream_t stream);
 
 /*
- * kda_fwd_profiled -- kda_fwd that also records events[0..3] on `stream`
- * before the scheduler, before the prep kernel, before the recurrence kernel
- * and after it, so a caller can time each kernel with hipEventElapsedTime.
- * Same arguments, checks and results as kda_fwd; the four events are created
- * and owned by the caller.
+ * kda_fwd_profiled -- kda_fwd that also records events[0..3] on `stream`:
+ * before the scheduler, before the first prep kernel, after the last prep
+ * kernel is enqueued (when the recurrence runs on the second stream, parts
+ * still being computed there are not covered), and after the whole call, so a
+ * caller can time the stages with hipEventElapsedTime.  Same arguments,
+ * checks and results as kda_fwd; the four events are created and owned by
+ * the caller.  kda_fwd_ex gives per-kernel events.
  */
 int kda_fwd_profiled(const void* q, const void* k, const void* v, const void* g, const void* beta,
                      float scale, void* out, const float* A_log, const float* dt_bias, float lower_bound,
@@ -128,6 +131,41 @@ int kda_fwd_profiled(const void* q, const void* k, const void* v, const void* g,
                      int final_state_dtype, const int64_t* cu_seqlens, int64_t num_seqs, int64_t B,
                      int64_t T, int64_t H, int64_t K, int64_t V, void* workspace,
                      size_t workspace_bytes, hipStream_t stream, hipEvent_t events[4]);
+
+/*
+ * kda_fwd_ex -- kda_fwd with the overlap of its two stages under the caller's
+ * control, and optional per-kernel events.
+ *
+ * The token rows (B * T, flattened) are cut into `parts` consecutive ranges of
+ * equal size.  The chunk-prep kernel of range p + 1 runs on `stream` while the
+ * chunk recurrence of range p runs on a second stream that the library keeps
+ * per device (created on first use, default priority); the recurrence hands
+ * the state of every (sequence, head) from one range to the next through the
+ * workspace in fp32, so the result equals the one-range result.  The call
+ * still only enqueues work: `stream` waits for the second stream before
+ * anything enqueued after the call.  parts = 0 lets the library choose
+ * (kda_fwd does that; it chooses 1, since on MI355X the two kernels slow each
+ * other down about as much as the overlap saves); values above 8 are clamped
+ * to 8.  The split into two stages and their roles follow P1 §二
+ * 2.2; overlapping them is this library's addition.
+ *
+ * events: NULL (num_events ignored) or num_events = 2 + 4 P caller-owned
+ * events, P = kda_fwd_parts(B, T, parts): [0] before the scheduler, [1] after
+ * it, [2 + 2p] / [3 + 2p] before / after the prep kernel of part p (on
+ * `stream`), [2 + 2P + 2p] / [3 + 2P + 2p] before / after the recurrence of
+ * part p (on the stream it runs on).  A wrong count returns KDA_EINVAL.
+ * Calls on one device that use the second stream are serialised on the host
+ * by a per-device lock while they enqueue.
+ */
+int kda_fwd_ex(const void* q, const void* k, const void* v, const void* g, const void* beta, float scale,
+               void* out, const float* A_log, const float* dt_bias, float lower_bound,
+               const void* initial_state, int initial_state_dtype, void* final_state, int final_state_dtype,
+               const int64_t* cu_seqlens, int64_t num_seqs, int64_t B, int64_t T, int64_t H, int64_t K,
+               int64_t V, void* workspace, size_t workspace_bytes, hipStream_t stream, int parts,
+               hipEvent_t* events, int num_events);
+
+/* Number of parts kda_fwd_ex uses for these sizes and `parts` request (0 on bad input). */
+int kda_fwd_parts(int64_t B, int64_t T, int parts);
 
 /*
  * Workspace bytes kda_fwd needs for these sizes (0 if the sizes are invalid).

@@ -142,3 +142,32 @@ def test_python_binding_rejects_bad_tensors():
                 initial_state=torch.zeros(1, 2, 128, 128, dtype=torch.float16))
     with pytest.raises(ValueError):                                          # CPU tensors
         kda.fwd(q, q, v, q, b, 0.1, v.clone(), A, dt, -5.0)
+
+
+def call_ex(parts, events, n_events, **over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, scale=0.088, out=FAKE, A_log=FAKE, dt_bias=FAKE,
+             lb=-5.0, s0=None, s0_dt=0, s1=None, s1_dt=0, cu=None, N=0, B=1, T=64, H=2, K=128, V=128,
+             ws=WS, ws_bytes=1 << 40, stream=None)
+    a.update(over)
+    return kda.lib().kda_fwd_ex(a["q"], a["k"], a["v"], a["g"], a["beta"], a["scale"], a["out"], a["A_log"],
+                                a["dt_bias"], a["lb"], a["s0"], a["s0_dt"], a["s1"], a["s1_dt"], a["cu"],
+                                a["N"], a["B"], a["T"], a["H"], a["K"], a["V"], a["ws"], a["ws_bytes"],
+                                a["stream"], parts, events, n_events)
+
+
+def test_parts_choice():
+    assert kda.parts(1, 0) == 1 and kda.parts(1, 0, 5) == 1      # nothing to overlap
+    assert kda.parts(1, 8192) == 1 and kda.parts(4, 8192) == 1    # the library's own choice
+    assert kda.parts(1, 64, 3) == 3 and kda.parts(1, 64, 100) == 8
+    assert kda.lib().kda_fwd_parts(1, 64, -1) == 0 and kda.lib().kda_fwd_parts(-1, 64, 0) == 0
+
+
+def test_fwd_ex_rejects_bad_parts_and_event_counts():
+    assert call_ex(-1, None, 0) == kda.KDA_EINVAL
+    ev = (ctypes.c_void_p * 10)(*([FAKE.value] * 10))
+    # parts = 2 needs 2 + 4 * 2 = 10 events; 9 or 14 are rejected before any HIP call
+    assert call_ex(2, ev, 9) == kda.KDA_EINVAL and "events" in kda.last_error()
+    assert call_ex(3, ev, 10) == kda.KDA_EINVAL
+    null_ev = (ctypes.c_void_p * 10)()
+    assert call_ex(2, null_ev, 10) == kda.KDA_EINVAL and "NULL" in kda.last_error()
+    assert call_ex(2, None, 0, q=None) == kda.KDA_EINVAL

@@ -176,3 +176,63 @@ def test_bad_cu_seqlens_sets_status_and_touches_nothing():
     ws = kda.alloc_workspace(1, 64, 2, 2, True, "cuda")
     run_gpu(inp, d=d, workspace=ws)
     assert kda.check_status(ws) == kda.KDA_STATUS_OK
+
+
+PART_CASES = [
+    dict(B=2, T=300, H=3, state_dtype="fp32", lower_bound=-5.0, seed=300),
+    dict(B=1, T=513, H=2, state_dtype="bf16", lower_bound=-5.0, seed=301, seq_lens=ragged_lengths(513, 9)),
+    dict(B=1, T=200, H=2, state_dtype="fp32", lower_bound=-1.0, seed=302, seq_lens=[0, 3, 0, 150, 1, 46, 0]),
+    dict(B=1, T=40, H=4, state_dtype=None, lower_bound=-5.0, seed=303),
+]
+
+
+@pytest.mark.parametrize("i", range(len(PART_CASES)))
+def test_parts_bitwise_equal_one_part(i):
+    """Cutting the rows into parts (prep of part p + 1 overlapped with the
+    recurrence of part p, the state handed over in fp32) changes no bit of
+    the result; part boundaries fall inside chunks, between sequences and
+    inside empty sequences."""
+    inp = make_inputs(**PART_CASES[i])
+    d = device_inputs(inp)
+    say("case parts%d B=%d T=%d H=%d N=%d" % (i, inp.B, inp.T, inp.H, inp.N))
+    o1, f1 = run_gpu(inp, d=d, parts=1)
+    torch.cuda.synchronize()
+    ref_o, ref_f = oracle_run(inp)
+    assert_close(to_f64(o1), ref_o, "out")
+    if inp.output_final_state:
+        assert_close(to_f64(f1), ref_f, "final_state", inp.state_dtype)
+    for P in (2, 3, 5, 8):
+        say("  parts=%d" % P)
+        o, f = run_gpu(inp, d=d, parts=P)
+        torch.cuda.synchronize()
+        assert torch.equal(o.view(torch.int16), o1.view(torch.int16)), P
+        if inp.output_final_state:
+            assert torch.equal(f.view(torch.int16) if f.dtype == torch.bfloat16 else f,
+                               f1.view(torch.int16) if f1.dtype == torch.bfloat16 else f1), P
+
+
+def test_parts_inplace_state_and_events():
+    """In-place state (initial_state is final_state) with parts, and the
+    per-kernel events of kda_fwd_ex (2 + 4 P of them) all complete in order."""
+    from gated_delta_rule_prep_amd import kda
+    inp = make_inputs(1, 700, 2, seed=304, state_dtype="fp32")
+    d = device_inputs(inp)
+    say("case parts in-place + events")
+    o_ref, f_ref = run_gpu(inp, d=d, parts=1)
+    st = d["initial_state"].clone()
+    out = torch.empty_like(o_ref)
+    P = kda.parts(1, 700, 4)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 + 4 * P)]
+    for e in ev:
+        e.record()
+    torch.cuda.synchronize()
+    kda.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], inp.scale, out, d["A_log"], d["dt_bias"],
+            inp.lower_bound, initial_state=st, final_state=st, workspace=None, events=ev, parts=4)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), o_ref.view(torch.int16))
+    assert torch.equal(st, f_ref)
+    for p in range(P):
+        assert ev[2 + 2 * p].elapsed_time(ev[3 + 2 * p]) >= 0
+        assert ev[2 + 2 * P + 2 * p].elapsed_time(ev[3 + 2 * P + 2 * p]) >= 0
+        # the recurrence of part p starts after the prep of part p ended
+        assert ev[3 + 2 * p].elapsed_time(ev[2 + 2 * P + 2 * p]) >= 0
