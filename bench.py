@@ -48,7 +48,7 @@ def param_bytes(inp):
     return inp.H * 4 + inp.H * inp.K * 4
 
 
-def run_workload(cfg, steps, warmup, torch, kda, device_inputs):
+def run_workload(cfg, steps, warmup, torch, kda, device_inputs, chunk=None):
     inp = cfg.make()
     d = device_inputs(inp, "cuda")
     out = torch.empty((inp.B, inp.T, inp.H, inp.V), dtype=torch.bfloat16, device="cuda")
@@ -59,7 +59,7 @@ def run_workload(cfg, steps, warmup, torch, kda, device_inputs):
     def step(events=None):
         kda.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], inp.scale, out, d["A_log"], d["dt_bias"],
                 inp.lower_bound, initial_state=d["initial_state"], final_state=fin,
-                cu_seqlens=d["cu_seqlens"], workspace=ws, events=events)
+                cu_seqlens=d["cu_seqlens"], workspace=ws, events=events, chunk=chunk)
 
     for _ in range(warmup):
         step()
@@ -162,6 +162,8 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=96, help="heads of the headline workload the oracle runs")
     ap.add_argument("--only", choices=["both", "fixed", "varlen"], default="both",
                     help="time only one workload (for profiler runs); the JSON line needs both")
+    ap.add_argument("--chunk", type=int, default=0, choices=[0, 16, 32],
+                    help="tokens per chunk (0: the library's choice)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="with --only: afterwards run 3 device-to-device copies of this many MiB, a plain copy "
                          "kernel of known size that scales the HBM byte counters")
@@ -179,7 +181,7 @@ def main():
     cfgs = configs()
     if args.only != "both":
         res = run_workload(cfgs[2] if args.only == "fixed" else cfgs[3], args.steps, args.warmup, torch, kda,
-                           device_inputs)
+                           device_inputs, args.chunk or None)
         print(json.dumps({"workload": res["inp"].name, "ms_per_step": round(res["ms"], 4),
                           "kernels_ms": {k: round(res[k + "_ms"], 4) for k in ("sched", "prep", "recur")}}))
         if args.copy_mib > 0:
@@ -191,8 +193,8 @@ def main():
             torch.cuda.synchronize()
             print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copies": 3}))
         return
-    fixed = run_workload(cfgs[2], args.steps, args.warmup, torch, kda, device_inputs)
-    varlen = run_workload(cfgs[3], args.steps, args.warmup, torch, kda, device_inputs)
+    fixed = run_workload(cfgs[2], args.steps, args.warmup, torch, kda, device_inputs, args.chunk or None)
+    varlen = run_workload(cfgs[3], args.steps, args.warmup, torch, kda, device_inputs, args.chunk or None)
     traffic = load_traffic()
     rl, path = roofline(fixed, traffic.get("fixed"))
     rl_v, path_v = roofline(varlen, traffic.get("varlen"))

@@ -118,9 +118,10 @@ int check_sizes(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V, const int
 
 namespace kda {
 
-bool layout_for(int64_t B, int64_t T, int64_t H, int64_t N, Layout* L) {
-  if (B < 1 || T < 0 || H < 1 || N < 0) return false;
-  const int64_t max_chunks = (B * T) / C + N;   // sum_n ceil(len_n / C) <= B*T/C + N
+bool layout_for(int64_t B, int64_t T, int64_t H, int64_t N, int chunk, Layout* L) {
+  if (B < 1 || T < 0 || H < 1 || N < 0 || (chunk != C && chunk != C32)) return false;
+  const int64_t rec_bytes = chunk == C ? REC_BYTES : REC32_BYTES;
+  const int64_t max_chunks = (B * T) / chunk + N;   // sum_n ceil(len_n / chunk) <= B*T/chunk + N
   int64_t off = sizeof(WsHeader);
   L->chunk_table = off;
   off = align_up(off + max_chunks * (int64_t)sizeof(ChunkEntry), 256);
@@ -128,10 +129,11 @@ bool layout_for(int64_t B, int64_t T, int64_t H, int64_t N, Layout* L) {
   off = align_up(off + N * (int64_t)sizeof(SeqEntry), 256);
   L->order = off;
   off = align_up(off + N * 4, 256);
+  L->chunk = chunk;
   L->records = off;
-  L->rec_bytes = REC_BYTES;
+  L->rec_bytes = rec_bytes;
   L->max_chunks = max_chunks;
-  off = align_up(off + H * max_chunks * REC_BYTES, 256);
+  off = align_up(off + H * max_chunks * rec_bytes, 256);
   L->state = off;
   off += N * H * V * K * (int64_t)sizeof(float);
   L->total = align_up(off, 256);
@@ -145,6 +147,9 @@ bool layout_for(int64_t B, int64_t T, int64_t H, int64_t N, Layout* L) {
 // left to callers that measure a gain at their own shapes.
 int parts_for(int64_t) { return 1; }
 
+// Chunk size used when the caller leaves the choice to the library.
+int default_chunk() { return C; }
+
 }  // namespace kda
 
 extern "C" {
@@ -156,19 +161,20 @@ const char* kda_get_last_error(void) { return g_last_error.c_str(); }
 size_t kda_fwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t num_seqs, int has_cu_seqlens) {
   int64_t N = 0;
   if (check_sizes(B, T, H, kda::K, kda::V, nullptr, num_seqs, has_cu_seqlens, &N) != KDA_OK) return 0;
-  kda::Layout L;
-  if (!kda::layout_for(B, T, H, N, &L)) return 0;
-  return (size_t)L.total;
+  kda::Layout L16, L32;   // enough for either chunk size
+  if (!kda::layout_for(B, T, H, N, kda::C, &L16) || !kda::layout_for(B, T, H, N, kda::C32, &L32)) return 0;
+  return (size_t)std::max(L16.total, L32.total);
 }
 
-int kda_workspace_layout(int64_t B, int64_t T, int64_t H, int64_t num_seqs, int has_cu_seqlens,
+int kda_workspace_layout(int64_t B, int64_t T, int64_t H, int64_t num_seqs, int has_cu_seqlens, int chunk,
                          int64_t offsets[7]) {
   int64_t N = 0;
   if (offsets == nullptr) return fail(KDA_EINVAL, "kda: offsets is NULL");
+  if (chunk != kda::C && chunk != kda::C32) return fail(KDA_EINVAL, "kda: chunk must be 16 or 32 (got %d)", chunk);
   int rc = check_sizes(B, T, H, kda::K, kda::V, nullptr, num_seqs, has_cu_seqlens, &N);
   if (rc != KDA_OK) return rc;
   kda::Layout L;
-  if (!kda::layout_for(B, T, H, N, &L)) return fail(KDA_EINVAL, "kda: bad sizes");
+  if (!kda::layout_for(B, T, H, N, chunk, &L)) return fail(KDA_EINVAL, "kda: bad sizes");
   offsets[0] = L.chunk_table;
   offsets[1] = L.seq_table;
   offsets[2] = L.order;
@@ -182,7 +188,7 @@ int kda_workspace_layout(int64_t B, int64_t T, int64_t H, int64_t num_seqs, int 
 static int validate_common(const void* q, const void* k, const void* g, const void* beta, float scale,
                            const float* A_log, const float* dt_bias, float lower_bound,
                            const int64_t* cu, int64_t num_seqs, int64_t B, int64_t T, int64_t H,
-                           int64_t K, int64_t V, void* workspace, size_t workspace_bytes,
+                           int64_t K, int64_t V, void* workspace, size_t workspace_bytes, int chunk,
                            kda::Layout* L, int64_t* N) {
   int rc = check_sizes(B, T, H, K, V, cu, num_seqs, cu != nullptr, N);
   if (rc != KDA_OK) return rc;
@@ -195,7 +201,8 @@ static int validate_common(const void* q, const void* k, const void* g, const vo
   if (!std::isfinite(scale)) return fail(KDA_EINVAL, "kda: scale is not finite");
   if (!std::isfinite(lower_bound) || lower_bound < -5.0f || lower_bound > 0.0f)
     return fail(KDA_EINVAL, "kda: lower_bound must lie in [-5, 0] (got %g)", (double)lower_bound);
-  if (!kda::layout_for(B, T, H, *N, L)) return fail(KDA_EINVAL, "kda: bad sizes");
+  if (chunk != kda::C && chunk != kda::C32) return fail(KDA_EINVAL, "kda: chunk must be 16 or 32 (got %d)", chunk);
+  if (!kda::layout_for(B, T, H, *N, chunk, L)) return fail(KDA_EINVAL, "kda: bad sizes");
   if (!workspace) return fail(KDA_EINVAL, "kda: workspace is NULL");
   if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
     return fail(KDA_EINVAL, "kda: workspace must be 256-byte aligned");
@@ -218,7 +225,8 @@ static int fwd_impl(const void* q, const void* k, const void* v, const void* g, 
                     const void* initial_state, int initial_state_dtype, void* final_state,
                     int final_state_dtype, const int64_t* cu_seqlens, int64_t num_seqs, int64_t B,
                     int64_t T, int64_t H, int64_t K, int64_t V, void* workspace, size_t workspace_bytes,
-                    hipStream_t stream, int parts_req, hipEvent_t* ev, int n_ev, hipEvent_t* ev4) {
+                    hipStream_t stream, int chunk_req, int parts_req, hipEvent_t* ev, int n_ev,
+                    hipEvent_t* ev4) {
   try {
     if ((!v || !out) && B * T > 0) return fail(KDA_EINVAL, "kda: v or out is NULL");
     auto dtype_ok = [](int d) { return d == KDA_DTYPE_NONE || d == KDA_DTYPE_BF16 || d == KDA_DTYPE_FP32; };
@@ -231,10 +239,13 @@ static int fwd_impl(const void* q, const void* k, const void* v, const void* g, 
     if (initial_state && final_state && initial_state_dtype != final_state_dtype)
       return fail(KDA_EDTYPE, "kda: initial_state and final_state dtypes differ");
     if (parts_req < 0) return fail(KDA_EINVAL, "kda: parts must be >= 0 (got %d)", parts_req);
+    if (chunk_req != 0 && chunk_req != kda::C && chunk_req != kda::C32)
+      return fail(KDA_EINVAL, "kda: chunk must be 0, 16 or 32 (got %d)", chunk_req);
+    const int chunk = chunk_req == 0 ? kda::default_chunk() : chunk_req;
     kda::Layout L;
     int64_t N = 0;
     int rc = validate_common(q, k, g, beta, scale, A_log, dt_bias, lower_bound, cu_seqlens, num_seqs, B, T,
-                             H, K, V, workspace, workspace_bytes, &L, &N);
+                             H, K, V, workspace, workspace_bytes, chunk, &L, &N);
     if (rc != KDA_OK) return rc;
     if (misaligned(v) || misaligned(out) || misaligned(initial_state) || misaligned(final_state))
       return fail(KDA_EINVAL, "kda: v, out and the states must be 16-byte aligned");
@@ -275,7 +286,7 @@ static int fwd_impl(const void* q, const void* k, const void* v, const void* g, 
     for (int p = 0; p < P && e == hipSuccess; ++p) {
       // chunks whose first row lies in the part's rows: at most one per 16 rows
       // plus one per sequence start
-      const int64_t bound = P == 1 ? L.max_chunks : std::min(L.max_chunks, part_rows / kda::C + N + 1);
+      const int64_t bound = P == 1 ? L.max_chunks : std::min(L.max_chunks, part_rows / chunk + N + 1);
       kda::PrepArgs pa{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                        static_cast<const uint16_t*>(g), static_cast<const uint16_t*>(beta), A_log, dt_bias,
                        scale, lower_bound, H, p, bound, ws, L};
@@ -314,7 +325,7 @@ int kda_fwd(const void* q, const void* k, const void* v, const void* g, const vo
             hipStream_t stream) {
   return fwd_impl(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
                   initial_state_dtype, final_state, final_state_dtype, cu_seqlens, num_seqs, B, T, H, K, V,
-                  workspace, workspace_bytes, stream, 0, nullptr, 0, nullptr);
+                  workspace, workspace_bytes, stream, 0, 0, nullptr, 0, nullptr);
 }
 
 int kda_fwd_profiled(const void* q, const void* k, const void* v, const void* g, const void* beta,
@@ -327,7 +338,7 @@ int kda_fwd_profiled(const void* q, const void* k, const void* v, const void* g,
     return fail(KDA_EINVAL, "kda: kda_fwd_profiled needs four events");
   return fwd_impl(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
                   initial_state_dtype, final_state, final_state_dtype, cu_seqlens, num_seqs, B, T, H, K, V,
-                  workspace, workspace_bytes, stream, 0, nullptr, 0, events);
+                  workspace, workspace_bytes, stream, 0, 0, nullptr, 0, events);
 }
 
 int kda_fwd_parts(int64_t B, int64_t T, int parts) {
@@ -339,25 +350,25 @@ int kda_fwd_ex(const void* q, const void* k, const void* v, const void* g, const
                void* out, const float* A_log, const float* dt_bias, float lower_bound,
                const void* initial_state, int initial_state_dtype, void* final_state, int final_state_dtype,
                const int64_t* cu_seqlens, int64_t num_seqs, int64_t B, int64_t T, int64_t H, int64_t K,
-               int64_t V, void* workspace, size_t workspace_bytes, hipStream_t stream, int parts,
-               hipEvent_t* events, int num_events) {
+               int64_t V, void* workspace, size_t workspace_bytes, hipStream_t stream, int chunk,
+               int parts, hipEvent_t* events, int num_events) {
   if (events != nullptr)
     for (int i = 0; i < num_events; ++i)
       if (!events[i]) return fail(KDA_EINVAL, "kda: event %d is NULL", i);
   return fwd_impl(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
                   initial_state_dtype, final_state, final_state_dtype, cu_seqlens, num_seqs, B, T, H, K, V,
-                  workspace, workspace_bytes, stream, parts, events, num_events, nullptr);
+                  workspace, workspace_bytes, stream, chunk, parts, events, num_events, nullptr);
 }
 
 int kda_debug_prep(const void* q, const void* k, const void* g, const void* beta, float scale,
                    const float* A_log, const float* dt_bias, float lower_bound, const int64_t* cu_seqlens,
                    int64_t num_seqs, int64_t B, int64_t T, int64_t H, int64_t K, void* workspace,
-                   size_t workspace_bytes, hipStream_t stream) {
+                   size_t workspace_bytes, hipStream_t stream, int chunk) {
   try {
     kda::Layout L;
     int64_t N = 0;
     int rc = validate_common(q, k, g, beta, scale, A_log, dt_bias, lower_bound, cu_seqlens, num_seqs, B, T,
-                             H, K, kda::V, workspace, workspace_bytes, &L, &N);
+                             H, K, kda::V, workspace, workspace_bytes, chunk, &L, &N);
     if (rc != KDA_OK) return rc;
     rc = check_device();
     if (rc != KDA_OK) return rc;

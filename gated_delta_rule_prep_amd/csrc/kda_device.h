@@ -70,6 +70,21 @@ __device__ __forceinline__ f16x4 lds_read_tr(const _Float16* m, int stride, int 
   return __builtin_bit_cast(f16x4, v);
 }
 
+// x from the lane n places lower in the same 16-lane row (row_shr:n); the
+// first n lanes of a row read 0.
+__device__ __forceinline__ float dpp_shr(float x, int n) {
+  switch (n) {
+    case 1: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xF, 0xF, true));
+    case 2: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xF, 0xF, true));
+    case 4: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xF, 0xF, true));
+    default: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xF, 0xF, true));
+  }
+}
+// Lane 15 of each 16-lane row, broadcast to the row (row_newbcast:15).
+__device__ __forceinline__ float dpp_bcast15(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x15F, 0xF, 0xF, false));
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 

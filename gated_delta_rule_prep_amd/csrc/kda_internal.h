@@ -7,7 +7,8 @@
 
 namespace kda {
 
-constexpr int C = 16;     // chunk size (tokens per chunk)
+constexpr int C = 16;     // chunk size of the 16-token kernels (tokens per chunk)
+constexpr int C32 = 32;   // chunk size of the 32-token kernels
 constexpr int K = 128;    // key channels
 constexpr int V = 128;    // value channels
 
@@ -19,6 +20,20 @@ constexpr int REC_T = 12288;     // T^T   fp16 [16][16]
 constexpr int REC_MQK = 12800;   // Mqk^T fp16 [16][16]
 constexpr int REC_GAM = 13312;   // gamma fp32 [128], channel c at slot kGamSlot(c)
 constexpr int REC_BYTES = 13824;
+
+// Chunk record of the 32-token kernels, one per (head, chunk), head-major.
+// T and Mqk are row-major with the columns (tokens) of each row stored in the
+// permuted order kPermCh, the same order as the channels of Qhat / -W: a lane
+// of the recurrence then reads the 8 k-values of its 16x16x32 MFMA operand as
+// one 16-byte piece, and the tokens it gets are exactly the accumulator rows
+// (4g .. 4g+3 of both 16-token tiles) that it holds for E.
+constexpr int REC32_QH = 0;        // Qhat  fp16 [32][128], channels in kPermCh order per 32-block
+constexpr int REC32_NW = 8192;     // -W    fp16 [32][128], same channel order
+constexpr int REC32_KB = 16384;    // Kbar  fp16 [32][128], token-major, natural channel order
+constexpr int REC32_T = 24576;     // T     fp16 [32][32], row-major, columns in kPermCh order
+constexpr int REC32_MQK = 26624;   // Mqk   fp16 [32][32], row-major, columns in kPermCh order
+constexpr int REC32_GAM = 28672;   // gamma fp32 [128], channel c at slot kGamSlot(c)
+constexpr int REC32_BYTES = 29184;
 
 // Slot of channel c = 64 r + 16 a + 4 b + i in the stored gamma: lane
 // L = 16 b + 4 a + i of a recurrence wave reads slots 2L and 2L + 1 (r = 0, 1),
@@ -44,7 +59,7 @@ static_assert(sizeof(WsHeader) == 256, "header size");
 struct ChunkEntry {     // chunk table entry
   int32_t seq;          // sequence index n
   int32_t row0;         // first flattened token row (b * T + t) of the chunk
-  int32_t len;          // tokens in the chunk (1..16)
+  int32_t len;          // tokens in the chunk (1 .. chunk size)
 };
 
 struct SeqEntry {
@@ -58,6 +73,7 @@ struct Layout {
   int64_t chunk_table;  // byte offsets into the workspace
   int64_t seq_table;
   int64_t order;
+  int64_t chunk;        // tokens per chunk: C or C32
   int64_t records;
   int64_t rec_bytes;
   int64_t max_chunks;
@@ -65,9 +81,10 @@ struct Layout {
   int64_t total;
 };
 
-// Returns false if the sizes are invalid.
-bool layout_for(int64_t B, int64_t T, int64_t H, int64_t N, Layout* out);
+// Returns false if the sizes or the chunk size (C or C32) are invalid.
+bool layout_for(int64_t B, int64_t T, int64_t H, int64_t N, int chunk, Layout* out);
 int parts_for(int64_t rows);   // parts used for B*T token rows when the caller does not choose
+int default_chunk();           // chunk size used when the caller does not choose
 
 struct SchedArgs {
   const int64_t* cu;    // device, N + 1 entries, or nullptr
@@ -108,8 +125,10 @@ struct RecurArgs {
 };
 
 hipError_t launch_sched(const SchedArgs& a, hipStream_t s);
+// The launchers pick the 16- or 32-token kernels by a.lay.chunk.
 hipError_t launch_prep(const PrepArgs& a, hipStream_t s);
 hipError_t launch_recur(const RecurArgs& a, hipStream_t s);
-int recur_tile_cols(int64_t pairs);   // value columns per recurrence workgroup (32, 64 or 128)
+hipError_t launch_prep32(const PrepArgs& a, hipStream_t s);
+hipError_t launch_recur32(const RecurArgs& a, hipStream_t s);
 
 }  // namespace kda

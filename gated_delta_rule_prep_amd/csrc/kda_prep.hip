@@ -46,20 +46,6 @@ struct __align__(16) WaveSmem {
   float beta[C];
 };
 
-__device__ __forceinline__ float dpp_shr(float x, int n) {
-  // row_shr:n within 16-lane rows, lanes without a source read 0
-  switch (n) {
-    case 1: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xF, 0xF, true));
-    case 2: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xF, 0xF, true));
-    case 4: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xF, 0xF, true));
-    default: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xF, 0xF, true));
-  }
-}
-// Lane 15 of each 16-lane row, broadcast to the row (row_newbcast:15).
-__device__ __forceinline__ float dpp_bcast15(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x15F, 0xF, 0xF, false));
-}
-
 __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
   __shared__ WaveSmem wsm[kWaves];
   const int tid = threadIdx.x;
@@ -232,6 +218,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
 }  // namespace
 
 hipError_t launch_prep(const PrepArgs& a, hipStream_t s) {
+  if (a.lay.chunk == C32) return launch_prep32(a, s);
   if (a.grid_chunks == 0) return hipSuccess;
   const unsigned hx = (unsigned)((a.H + kWaves - 1) / kWaves);
   hipLaunchKernelGGL(prep_kernel, dim3((unsigned)a.grid_chunks, hx), dim3(kThreads), 0, s, a);

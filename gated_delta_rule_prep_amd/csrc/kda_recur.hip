@@ -4,13 +4,11 @@
 // delta-rule recurrence, output projection, rolling state).  The state's value
 // columns never interact (every step acts on each value column of the state
 // separately), so a (sequence, head) pair is cut into V-tiles, one workgroup
-// of four waves per tile, and each wave owns 16 or 32 of the tile's columns.
-// Nothing is exchanged between workgroups.  The 128 x 16 (or 32) fp32 state
-// slice of a wave lives in registers as 8 x 1 (or 8 x 2) MFMA accumulator
-// tiles for the whole sequence.  With enough pairs to fill the chip a
-// workgroup takes all 128 columns of a pair (32 per wave); with few pairs (one
-// long sequence, 64-96 heads) it takes 64 (16 per wave), so two workgroups
-// share a pair and each wave's serial per-chunk work is halved.
+// of four waves per tile, and each wave owns 16 (or, when built for it, 32) of
+// the tile's columns.  Nothing is exchanged between workgroups.  The 128 x 16
+// fp32 state slice of a wave lives in registers as 8 MFMA accumulator tiles
+// for the whole sequence; two workgroups share a pair, so each wave's serial
+// per-chunk work is half of what a whole pair would need (see launch_recur).
 //
 // P1 = blog post "FlashKDA：月之暗面开源的 Kimi Delta Attention 高性能内核".
 //
@@ -448,35 +446,23 @@ hipError_t launch_tiles(const RecurArgs& a, hipStream_t s) {
 
 }  // namespace
 
-// Value columns per recurrence workgroup from the number of (sequence, head)
-// pairs.  With enough pairs to fill the 256 CUs, one workgroup of four waves
-// takes a whole pair, 32 columns per wave, with a 3-chunk ring (60 KB of LDS,
-// two workgroups per CU).  With fewer, each wave takes 16 columns and a pair
-// is split over two workgroups: the per-step VALU work (state conversion and
-// decay) and MFMA work of a wave are halved, twice as many SIMDs carry the
-// serial chains, and a 4-chunk ring (64 KB) hides the HBM latency (deeper
-// rings measured no faster).
-int recur_tile_cols(int64_t pairs) {
-#ifdef KDA_RECUR_FORCE_COLS
-  (void)pairs;
-  return KDA_RECUR_FORCE_COLS;
-#else
-  return pairs >= 256 ? 128 : 64;
-#endif
-}
-
-#ifndef KDA_RECUR_DEPTH64
-#define KDA_RECUR_DEPTH64 4
-#endif
-#ifndef KDA_RECUR_DEPTH128
-#define KDA_RECUR_DEPTH128 3
+// Value columns per recurrence workgroup: 64.  Each wave takes 16 columns and
+// a pair is split over two workgroups, so the per-step VALU work (state
+// conversion and decay) and MFMA work of a wave are half of a whole pair's
+// and the longest chain of the batch (the critical path) runs twice as fast
+// per chunk.  Whole pairs per workgroup (32 columns per wave, NT = 2) read
+// each record once instead of twice but measured faster only with many short
+// sequences of equal length (3 % at 8 x 1024 tokens, H = 96) and 25 % slower
+// with one long sequence among short ones.  A 4-chunk ring (64 KB) covers the
+// HBM latency (deeper rings measured no faster).
+#ifndef KDA_RECUR_DEPTH
+#define KDA_RECUR_DEPTH 4
 #endif
 
 hipError_t launch_recur(const RecurArgs& a, hipStream_t s) {
-  const int64_t pairs = a.N * a.H;
-  if (pairs == 0) return hipSuccess;
-  if (recur_tile_cols(pairs) == 64) return launch_tiles<1, KDA_RECUR_DEPTH64>(a, s);
-  return launch_tiles<2, KDA_RECUR_DEPTH128>(a, s);
+  if (a.lay.chunk == C32) return launch_recur32(a, s);
+  if (a.N * a.H == 0) return hipSuccess;
+  return launch_tiles<1, KDA_RECUR_DEPTH>(a, s);
 }
 
 }  // namespace kda

@@ -2,7 +2,7 @@
 //
 // Turns the sequence boundaries into
 //   * a chunk table: chunk i -> {sequence n, first flattened token row, length},
-//     chunks of at most 16 tokens that restart at every sequence start (so a
+//     chunks of at most lay.chunk (16 or 32) tokens that restart at every sequence start (so a
 //     chunk never straddles two sequences; the pages batch variable-length
 //     sequences through cu_seqlens: README mirror "内核 API", cu_seqlens row);
 //   * a per-sequence table {first chunk, chunk count, first token row, length};
@@ -30,6 +30,7 @@ __global__ __launch_bounds__(kThreads) void sched_kernel(SchedArgs a) {
   int32_t* order = reinterpret_cast<int32_t*>(a.ws + a.lay.order);
   const int tid = threadIdx.x;
   const int64_t N = a.N;
+  const int64_t C = a.lay.chunk;
 
   __shared__ int s_bad;
   __shared__ int32_t s_scan[kThreads];

@@ -41,7 +41,8 @@ _lib.kda_fwd.argtypes = [_p, _p, _p, _p, _p, ctypes.c_float, _p, _p, _p, ctypes.
 _lib.kda_fwd.restype = ctypes.c_int
 _lib.kda_fwd_profiled.argtypes = _lib.kda_fwd.argtypes + [ctypes.POINTER(ctypes.c_void_p)]
 _lib.kda_fwd_profiled.restype = ctypes.c_int
-_lib.kda_fwd_ex.argtypes = _lib.kda_fwd.argtypes + [ctypes.c_int, ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
+_lib.kda_fwd_ex.argtypes = _lib.kda_fwd.argtypes + [ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_void_p),
+                                                     ctypes.c_int]
 _lib.kda_fwd_ex.restype = ctypes.c_int
 _lib.kda_fwd_parts.argtypes = [_i64, _i64, ctypes.c_int]
 _lib.kda_fwd_parts.restype = ctypes.c_int
@@ -51,10 +52,11 @@ _lib.kda_get_last_error.restype = ctypes.c_char_p
 _lib.kda_version.restype = ctypes.c_int
 _lib.kda_fwd_check_status.argtypes = [_p, _p, ctypes.POINTER(ctypes.c_int)]
 _lib.kda_fwd_check_status.restype = ctypes.c_int
-_lib.kda_workspace_layout.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.POINTER(ctypes.c_int64)]
+_lib.kda_workspace_layout.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int,
+                                      ctypes.POINTER(ctypes.c_int64)]
 _lib.kda_workspace_layout.restype = ctypes.c_int
 _lib.kda_debug_prep.argtypes = [_p, _p, _p, _p, ctypes.c_float, _p, _p, ctypes.c_float, _p, _i64, _i64,
-                                _i64, _i64, _i64, _p, ctypes.c_size_t, _p]
+                                _i64, _i64, _i64, _p, ctypes.c_size_t, _p, ctypes.c_int]
 _lib.kda_debug_prep.restype = ctypes.c_int
 
 
@@ -91,9 +93,10 @@ def workspace_bytes(B: int, T: int, H: int, num_seqs: int = 0, has_cu_seqlens: b
     return int(_lib.kda_fwd_workspace_bytes(B, T, H, num_seqs, int(has_cu_seqlens)))
 
 
-def workspace_layout(B: int, T: int, H: int, num_seqs: int = 0, has_cu_seqlens: bool = False) -> dict:
+def workspace_layout(B: int, T: int, H: int, num_seqs: int = 0, has_cu_seqlens: bool = False,
+                     chunk: int = CHUNK) -> dict:
     off = (ctypes.c_int64 * 7)()
-    rc = _lib.kda_workspace_layout(B, T, H, num_seqs, int(has_cu_seqlens), off)
+    rc = _lib.kda_workspace_layout(B, T, H, num_seqs, int(has_cu_seqlens), chunk, off)
     if rc != KDA_OK:
         _raise(rc)
     keys = ("chunk_table", "seq_table", "order", "records", "rec_bytes", "max_chunks", "total")
@@ -140,12 +143,14 @@ def parts(B: int, T: int, requested: int = 0) -> int:
 
 
 def fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state=None, final_state=None,
-        cu_seqlens=None, workspace: Optional[torch.Tensor] = None, events=None, parts: Optional[int] = None):
+        cu_seqlens=None, workspace: Optional[torch.Tensor] = None, events=None, parts: Optional[int] = None,
+        chunk: Optional[int] = None):
     """Chunked KDA forward into the caller's ``out`` (and ``final_state``).
 
     Shapes and dtypes as in include/kda.h.  Runs on the current stream of the
-    tensors' device.  Returns ``out``.  ``parts``: None for kda_fwd's own
-    choice, or the number of overlapped ranges (kda_fwd_ex).  ``events``:
+    tensors' device.  Returns ``out``.  ``chunk``: None for the library's
+    choice, or 16 / 32 tokens per chunk (kda_fwd_ex).  ``parts``: None for
+    kda_fwd's own choice, or the number of overlapped ranges.  ``events``:
     optional torch.cuda.Event list (enable_timing=True): four go through
     kda_fwd_profiled; 2 + 4 P (P = ``parts(B, T, parts or 0)``) go through
     kda_fwd_ex, which records them around every kernel.
@@ -187,15 +192,15 @@ def fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state
             _state_code(initial_state), _ptr(final_state), _state_code(final_state),
             _ptr(cu_seqlens), N, B, T, H, K, V, _ptr(workspace), workspace.numel())
     with torch.cuda.device(dev):
-        if events is None and parts is None:
+        if events is None and parts is None and chunk is None:
             rc = _lib.kda_fwd(*args, _stream(dev))
-        elif parts is None and len(events) == 4:
+        elif parts is None and chunk is None and len(events) == 4:
             ev = (ctypes.c_void_p * 4)(*[e.cuda_event for e in events])
             rc = _lib.kda_fwd_profiled(*args, _stream(dev), ev)
         else:
             n = 0 if events is None else len(events)
             ev = None if events is None else (ctypes.c_void_p * n)(*[e.cuda_event for e in events])
-            rc = _lib.kda_fwd_ex(*args, _stream(dev), int(parts or 0), ev, n)
+            rc = _lib.kda_fwd_ex(*args, _stream(dev), int(chunk or 0), int(parts or 0), ev, n)
     if rc != KDA_OK:
         _raise(rc)
     return out
@@ -210,7 +215,8 @@ def check_status(workspace: torch.Tensor) -> int:
     return st.value
 
 
-def debug_prep(q, k, g, beta, scale, A_log, dt_bias, lower_bound, cu_seqlens=None, workspace=None):
+def debug_prep(q, k, g, beta, scale, A_log, dt_bias, lower_bound, cu_seqlens=None, workspace=None,
+               chunk: int = CHUNK):
     """Test-only: run the scheduler and prep kernels; returns the workspace tensor."""
     B, T, H, K = q.shape
     N = B if cu_seqlens is None else cu_seqlens.numel() - 1
@@ -219,7 +225,7 @@ def debug_prep(q, k, g, beta, scale, A_log, dt_bias, lower_bound, cu_seqlens=Non
     with torch.cuda.device(q.device):
         rc = _lib.kda_debug_prep(_ptr(q), _ptr(k), _ptr(g), _ptr(beta), float(scale), _ptr(A_log),
                                  _ptr(dt_bias), float(lower_bound), _ptr(cu_seqlens), N, B, T, H, K,
-                                 _ptr(workspace), workspace.numel(), _stream(q.device))
+                                 _ptr(workspace), workspace.numel(), _stream(q.device), chunk)
     if rc != KDA_OK:
         _raise(rc)
     return workspace

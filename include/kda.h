@@ -133,8 +133,16 @@ int kda_fwd_profiled(const void* q, const void* k, const void* v, const void* g,
                      size_t workspace_bytes, hipStream_t stream, hipEvent_t events[4]);
 
 /*
- * kda_fwd_ex -- kda_fwd with the overlap of its two stages under the caller's
- * control, and optional per-kernel events.
+ * kda_fwd_ex -- kda_fwd with the chunk size and the overlap of its two stages
+ * under the caller's control, and optional per-kernel events.
+ *
+ * chunk: 0 (the library's choice, as kda_fwd), 16 or 32 tokens per chunk.
+ * The pages use 16 (P1 §二 2.1) so that the in-chunk decay factors stay in
+ * range; the 32-token kernels build each chunk from two 16-token halves whose
+ * coupling block needs only bounded factors, and step the state half as
+ * often.  Both compute the same chunked form (any chunk size gives the exact
+ * recurrence up to rounding); their results differ only in rounding.  Any
+ * other value returns KDA_EINVAL.
  *
  * The token rows (B * T, flattened) are cut into `parts` consecutive ranges of
  * equal size.  The chunk-prep kernel of range p + 1 runs on `stream` while the
@@ -161,8 +169,8 @@ int kda_fwd_ex(const void* q, const void* k, const void* v, const void* g, const
                void* out, const float* A_log, const float* dt_bias, float lower_bound,
                const void* initial_state, int initial_state_dtype, void* final_state, int final_state_dtype,
                const int64_t* cu_seqlens, int64_t num_seqs, int64_t B, int64_t T, int64_t H, int64_t K,
-               int64_t V, void* workspace, size_t workspace_bytes, hipStream_t stream, int parts,
-               hipEvent_t* events, int num_events);
+               int64_t V, void* workspace, size_t workspace_bytes, hipStream_t stream, int chunk,
+               int parts, hipEvent_t* events, int num_events);
 
 /* Number of parts kda_fwd_ex uses for these sizes and `parts` request (0 on bad input). */
 int kda_fwd_parts(int64_t B, int64_t T, int parts);
@@ -188,34 +196,41 @@ int kda_version(void);
 int kda_fwd_check_status(const void* workspace, hipStream_t stream, int* status);
 
 /*
- * Workspace layout, for tests that decode the chunk records:
+ * Workspace layout for chunk = 16 or 32, for tests that decode the chunk records:
  * offsets[0] = chunk table (int32 triples {sequence, first token row, length}),
  * offsets[1] = per-sequence table (int32 quadruples {first chunk, chunk count,
  *              first token row, length}),
  * offsets[2] = work order (int32 [N], sequences longest first),
  * offsets[3] = chunk records, head-major: record (h, c) at
  *              offsets[3] + (h * offsets[5] + c) * offsets[4],
- * offsets[4] = bytes per record, offsets[5] = chunk capacity (floor(B*T/16) + N),
+ * offsets[4] = bytes per record, offsets[5] = chunk capacity (floor(B*T/chunk) + N),
  * offsets[6] = total bytes.  Returns KDA_OK or KDA_EINVAL.
- * Record layout (bytes): [0, 4096) Qhat fp16 [16][128]; [4096, 8192) -W fp16
+ * Record layout for chunk 16 (bytes): [0, 4096) Qhat fp16 [16][128]; [4096, 8192) -W fp16
  * [16][128]; both with the channels of each 32-block stored in the order
  * {0-3, 16-19, 4-7, 20-23, 8-11, 24-27, 12-15, 28-31}; [8192, 12288) Kbar fp16
  * [16][128] (token-major, natural channel order); [12288, 12800) T^T fp16
  * [16][16]; [12800, 13312) Mqk^T fp16 [16][16]; [13312, 13824) gamma fp32 [128],
  * channel c = 64 r + 16 a + 4 b + i stored at slot 2 (16 b + 4 a + i) + r.
+ * Record layout for chunk 32 (bytes): [0, 8192) Qhat fp16 [32][128] and
+ * [8192, 16384) -W fp16 [32][128], channels as above; [16384, 24576) Kbar fp16
+ * [32][128] (token-major, natural order); [24576, 26624) T fp16 [32][32] and
+ * [26624, 28672) Mqk fp16 [32][32], both row-major with the columns of each row
+ * in the order {0-3, 16-19, 4-7, 20-23, 8-11, 24-27, 12-15, 28-31};
+ * [28672, 29184) gamma fp32 [128] as above.
  */
-int kda_workspace_layout(int64_t B, int64_t T, int64_t H, int64_t num_seqs, int has_cu_seqlens,
+int kda_workspace_layout(int64_t B, int64_t T, int64_t H, int64_t num_seqs, int has_cu_seqlens, int chunk,
                          int64_t offsets[7]);
 
 /*
  * kda_debug_prep -- test-only: enqueue the scheduler and chunk-prep kernels
- * alone (same arguments as kda_fwd minus v, out and the states), leaving the
- * chunk table and records in `workspace` for inspection.
+ * alone (same arguments as kda_fwd minus v, out and the states, plus the
+ * chunk size, 16 or 32), leaving the chunk table and records in `workspace`
+ * for inspection.
  */
 int kda_debug_prep(const void* q, const void* k, const void* g, const void* beta, float scale,
                    const float* A_log, const float* dt_bias, float lower_bound,
                    const int64_t* cu_seqlens, int64_t num_seqs, int64_t B, int64_t T, int64_t H,
-                   int64_t K, void* workspace, size_t workspace_bytes, hipStream_t stream);
+                   int64_t K, void* workspace, size_t workspace_bytes, hipStream_t stream, int chunk);
 
 #ifdef __cplusplus
 }

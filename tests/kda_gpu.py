@@ -50,7 +50,7 @@ def state_torch_dtype(inp):
     return torch.bfloat16 if inp.state_dtype == "bf16" else torch.float32
 
 
-def run_gpu(inp, device="cuda", d=None, workspace=None, out=None, final=None, parts=None):
+def run_gpu(inp, device="cuda", d=None, workspace=None, out=None, final=None, parts=None, chunk=None):
     from gated_delta_rule_prep_amd import kda
     if d is None:
         d = device_inputs(inp, device)
@@ -61,7 +61,7 @@ def run_gpu(inp, device="cuda", d=None, workspace=None, out=None, final=None, pa
         final = torch.full((inp.N, H, V, inp.K), float("nan"), dtype=state_torch_dtype(inp), device=device)
     kda.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], inp.scale, out, d["A_log"], d["dt_bias"],
             inp.lower_bound, initial_state=d["initial_state"], final_state=final,
-            cu_seqlens=d["cu_seqlens"], workspace=workspace, parts=parts)
+            cu_seqlens=d["cu_seqlens"], workspace=workspace, parts=parts, chunk=chunk)
     return out, final
 
 

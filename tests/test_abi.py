@@ -48,7 +48,7 @@ def test_workspace_sizes_and_layout():
     assert lay["rec_bytes"] == 13824
     assert lay["records"] % 256 == 0 and lay["total"] % 256 == 0
     assert lay["total"] >= lay["records"] + 96 * lay["max_chunks"] * lay["rec_bytes"]
-    assert kda.workspace_bytes(1, 8192, 96) == lay["total"]
+    assert kda.workspace_bytes(1, 8192, 96) >= lay["total"]
     # varlen capacity: floor(T/16) + N chunks covers every split into N sequences
     lay2 = kda.workspace_layout(1, 8192, 96, 12, True)
     assert lay2["max_chunks"] == 512 + 12
@@ -122,8 +122,11 @@ def test_host_validation_rejects(over, code):
 
 def test_debug_prep_validation():
     rc = kda.lib().kda_debug_prep(FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, FAKE, -6.0, None, 0, 1, 64, 2, 128, WS,
-                                  1 << 40, None)
+                                  1 << 40, None, 16)
     assert rc == kda.KDA_EINVAL
+    rc = kda.lib().kda_debug_prep(FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, FAKE, -5.0, None, 0, 1, 64, 2, 128, WS,
+                                  1 << 40, None, 24)
+    assert rc == kda.KDA_EINVAL and "chunk" in kda.last_error()
 
 
 def test_python_binding_rejects_bad_tensors():
@@ -144,7 +147,7 @@ def test_python_binding_rejects_bad_tensors():
         kda.fwd(q, q, v, q, b, 0.1, v.clone(), A, dt, -5.0)
 
 
-def call_ex(parts, events, n_events, **over):
+def call_ex(parts, events, n_events, chunk=0, **over):
     a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, scale=0.088, out=FAKE, A_log=FAKE, dt_bias=FAKE,
              lb=-5.0, s0=None, s0_dt=0, s1=None, s1_dt=0, cu=None, N=0, B=1, T=64, H=2, K=128, V=128,
              ws=WS, ws_bytes=1 << 40, stream=None)
@@ -152,7 +155,7 @@ def call_ex(parts, events, n_events, **over):
     return kda.lib().kda_fwd_ex(a["q"], a["k"], a["v"], a["g"], a["beta"], a["scale"], a["out"], a["A_log"],
                                 a["dt_bias"], a["lb"], a["s0"], a["s0_dt"], a["s1"], a["s1_dt"], a["cu"],
                                 a["N"], a["B"], a["T"], a["H"], a["K"], a["V"], a["ws"], a["ws_bytes"],
-                                a["stream"], parts, events, n_events)
+                                a["stream"], chunk, parts, events, n_events)
 
 
 def test_parts_choice():
@@ -171,3 +174,16 @@ def test_fwd_ex_rejects_bad_parts_and_event_counts():
     null_ev = (ctypes.c_void_p * 10)()
     assert call_ex(2, null_ev, 10) == kda.KDA_EINVAL and "NULL" in kda.last_error()
     assert call_ex(2, None, 0, q=None) == kda.KDA_EINVAL
+    for bad in (8, 17, 64, -16):
+        assert call_ex(1, None, 0, chunk=bad) == kda.KDA_EINVAL and "chunk" in kda.last_error()
+
+
+def test_layout_for_both_chunk_sizes():
+    l16 = kda.workspace_layout(1, 8192, 96, chunk=16)
+    l32 = kda.workspace_layout(1, 8192, 96, chunk=32)
+    assert l32["max_chunks"] == 8192 // 32 + 1 and l32["rec_bytes"] == 29184
+    assert l32["records"] % 256 == 0 and l32["total"] >= l32["records"] + 96 * l32["max_chunks"] * 29184
+    # the workspace query covers either chunk size
+    assert kda.workspace_bytes(1, 8192, 96) == max(l16["total"], l32["total"])
+    with pytest.raises(ValueError):
+        kda.workspace_layout(1, 64, 2, chunk=24)

@@ -30,10 +30,10 @@ def oracle_run(inp, heads=None):
                           output_final_state=True, cu_seqlens=inp.cu_seqlens)
 
 
-def check(inp, heads=None, tag=""):
-    say("case %s B=%d T=%d H=%d N=%d state=%s lb=%g" % (tag or inp.name, inp.B, inp.T, inp.H, inp.N,
-                                                      inp.state_dtype, inp.lower_bound))
-    out, fin = run_gpu(inp)
+def check(inp, heads=None, tag="", chunk=None):
+    say("case %s B=%d T=%d H=%d N=%d state=%s lb=%g chunk=%s" % (tag or inp.name, inp.B, inp.T, inp.H, inp.N,
+                                                               inp.state_dtype, inp.lower_bound, chunk))
+    out, fin = run_gpu(inp, chunk=chunk)
     torch.cuda.synchronize()
     ref_o, ref_f = oracle_run(inp, heads)
     hs = list(range(inp.H)) if heads is None else heads
@@ -57,36 +57,40 @@ SMALL = [
 ]
 
 
+@pytest.mark.parametrize("chunk", [16, 32])
 @pytest.mark.parametrize("i", range(len(SMALL)))
-def test_small_parity(i):
+def test_small_parity(i, chunk):
     kw = dict(SMALL[i])
     inp = make_inputs(**kw)
-    check(inp, tag="small%d" % i)
+    check(inp, tag="small%d" % i, chunk=chunk)
 
 
+@pytest.mark.parametrize("chunk", [16, 32])
 @pytest.mark.parametrize("ci", range(5))
-def test_config_parity(ci):
+def test_config_parity(ci, chunk):
     cfg = configs()[ci]
     inp = cfg.make()
     heads = None if inp.H <= 4 else sorted({0, 1, inp.H // 2, inp.H - 1})
-    check(inp, heads, tag="config%d %s" % (ci, cfg.name))
+    check(inp, heads, tag="config%d %s" % (ci, cfg.name), chunk=chunk)
 
 
-def test_deterministic_bitwise():
+@pytest.mark.parametrize("chunk", [16, 32])
+def test_deterministic_bitwise(chunk):
     inp = make_inputs(1, 500, 4, seed=200, state_dtype="fp32")
-    say("case determinism T=500 H=4")
-    o1, f1 = run_gpu(inp)
-    o2, f2 = run_gpu(inp)
+    say("case determinism T=500 H=4 chunk=%d" % chunk)
+    o1, f1 = run_gpu(inp, chunk=chunk)
+    o2, f2 = run_gpu(inp, chunk=chunk)
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
     assert torch.equal(f1, f2)
 
 
-def test_varlen_equals_separate_calls_bitwise():
+@pytest.mark.parametrize("chunk", [16, 32])
+def test_varlen_equals_separate_calls_bitwise(chunk):
     lens = [1, 15, 17, 33, 130, 60]
     inp = make_inputs(1, sum(lens), 3, seed=201, state_dtype="bf16", seq_lens=lens)
-    say("case varlen-vs-separate lens=%s" % lens)
-    out, fin = run_gpu(inp)
+    say("case varlen-vs-separate lens=%s chunk=%d" % (lens, chunk))
+    out, fin = run_gpu(inp, chunk=chunk)
     cu = inp.cu_seqlens
     for n in range(len(lens)):
         a, b = int(cu[n]), int(cu[n + 1])
@@ -95,7 +99,7 @@ def test_varlen_equals_separate_calls_bitwise():
             setattr(sub, f, np.ascontiguousarray(getattr(inp, f)[:, a:b]))
         sub.A_log, sub.dt_bias = inp.A_log, inp.dt_bias
         sub.initial_state = np.ascontiguousarray(inp.initial_state[n:n + 1])
-        o, f = run_gpu(sub)
+        o, f = run_gpu(sub, chunk=chunk)
         torch.cuda.synchronize()
         assert torch.equal(o.view(torch.int16), out[:, a:b].view(torch.int16)), n
         assert torch.equal(f[0].view(torch.int16), fin[n].view(torch.int16)), n
@@ -186,16 +190,17 @@ PART_CASES = [
 ]
 
 
+@pytest.mark.parametrize("chunk", [16, 32])
 @pytest.mark.parametrize("i", range(len(PART_CASES)))
-def test_parts_bitwise_equal_one_part(i):
+def test_parts_bitwise_equal_one_part(i, chunk):
     """Cutting the rows into parts (prep of part p + 1 overlapped with the
     recurrence of part p, the state handed over in fp32) changes no bit of
     the result; part boundaries fall inside chunks, between sequences and
     inside empty sequences."""
     inp = make_inputs(**PART_CASES[i])
     d = device_inputs(inp)
-    say("case parts%d B=%d T=%d H=%d N=%d" % (i, inp.B, inp.T, inp.H, inp.N))
-    o1, f1 = run_gpu(inp, d=d, parts=1)
+    say("case parts%d B=%d T=%d H=%d N=%d chunk=%d" % (i, inp.B, inp.T, inp.H, inp.N, chunk))
+    o1, f1 = run_gpu(inp, d=d, parts=1, chunk=chunk)
     torch.cuda.synchronize()
     ref_o, ref_f = oracle_run(inp)
     assert_close(to_f64(o1), ref_o, "out")
@@ -203,7 +208,7 @@ def test_parts_bitwise_equal_one_part(i):
         assert_close(to_f64(f1), ref_f, "final_state", inp.state_dtype)
     for P in (2, 3, 5, 8):
         say("  parts=%d" % P)
-        o, f = run_gpu(inp, d=d, parts=P)
+        o, f = run_gpu(inp, d=d, parts=P, chunk=chunk)
         torch.cuda.synchronize()
         assert torch.equal(o.view(torch.int16), o1.view(torch.int16)), P
         if inp.output_final_state:

@@ -1,6 +1,7 @@
-"""GPU unit test of the scheduler and chunk-prep kernels alone: the chunk table
-and every chunk record are decoded from the workspace and compared with the
-fp64 chunked-form intermediates of tests/chunked_ref.py."""
+"""GPU unit test of the scheduler and chunk-prep kernels alone, for 16- and
+32-token chunks: the chunk table and every chunk record are decoded from the
+workspace and compared with the fp64 chunked-form intermediates of
+tests/chunked_ref.py."""
 import numpy as np
 import pytest
 import torch
@@ -25,43 +26,58 @@ def perm_ch(p):
 
 
 PERM = np.array([(p // 32) * 32 + perm_ch(p % 32) for p in range(128)])
+PERM32 = np.array([perm_ch(p) for p in range(32)])
 
 
-def unpermute(x):
+def unpermute(x, perm=PERM):
     y = np.empty_like(x)
-    y[..., PERM] = x
+    y[..., perm] = x
     return y
 
 
-def test_chunk_table_and_records_match_chunked_form():
+def decode_record(rec, C):
+    """Record fields as natural-order float64 arrays (layouts in include/kda.h)."""
+    f16 = lambda o, shape: rec[o:o + 2 * int(np.prod(shape))].view(np.float16).astype(np.float64).reshape(shape)
+    gam = lambda o: rec[o:o + 512].view(np.float32).astype(np.float64)[GAM_SLOT]
+    if C == 16:
+        return dict(Qh=unpermute(f16(0, (16, 128))), W=-unpermute(f16(4096, (16, 128))), Kb=f16(8192, (16, 128)),
+                    T=f16(12288, (16, 16)).T, M=f16(12800, (16, 16)).T, gamma=gam(13312))
+    return dict(Qh=unpermute(f16(0, (32, 128))), W=-unpermute(f16(8192, (32, 128))), Kb=f16(16384, (32, 128)),
+                T=unpermute(f16(24576, (32, 32)), PERM32), M=unpermute(f16(26624, (32, 32)), PERM32),
+                gamma=gam(28672))
+
+
+@pytest.mark.parametrize("C", [16, 32])
+def test_chunk_table_and_records_match_chunked_form(C):
     from gated_delta_rule_prep_amd import kda
-    lens = [1, 15, 17, 40, 0, 33]
+    lens = [1, 15, 17, 40, 0, 33, 64]
     T = sum(lens)
     H = 3
     inp = make_inputs(1, T, H, seed=300, lower_bound=-5.0, seq_lens=lens)
-    say("case prep records lens=%s H=%d" % (lens, H))
+    say("case prep records C=%d lens=%s H=%d" % (C, lens, H))
     d = device_inputs(inp)
     ws = kda.debug_prep(d["q"], d["k"], d["g"], d["beta"], inp.scale, d["A_log"], d["dt_bias"], inp.lower_bound,
-                        cu_seqlens=d["cu_seqlens"])
+                        cu_seqlens=d["cu_seqlens"], chunk=C)
     torch.cuda.synchronize()
-    lay = kda.workspace_layout(1, T, H, len(lens), True)
+    lay = kda.workspace_layout(1, T, H, len(lens), True, chunk=C)
+    assert lay["rec_bytes"] == (13824 if C == 16 else 29184)
     buf = ws.cpu().numpy()
     hdr = buf[:8].view(np.int32)
     assert hdr[0] == kda.KDA_STATUS_OK
-    nch = sum((l + 15) // 16 for l in lens)
+    nch = sum((l + C - 1) // C for l in lens)
     cu = inp.cu_seqlens
     assert hdr[1] == nch
     table = buf[lay["chunk_table"]:lay["chunk_table"] + 12 * nch].view(np.int32).reshape(nch, 3)
     want = []
     for n, l in enumerate(lens):
-        for c in range(0, l, 16):
-            want.append((n, int(cu[n]) + c, min(16, l - c)))
+        for c in range(0, l, C):
+            want.append((n, int(cu[n]) + c, min(C, l - c)))
     assert [tuple(r) for r in table] == want
     seqs = buf[lay["seq_table"]:lay["seq_table"] + 16 * len(lens)].view(np.int32).reshape(-1, 4)
     order = buf[lay["order"]:lay["order"] + 4 * len(lens)].view(np.int32)
-    assert list(seqs[:, 1]) == [(l + 15) // 16 for l in lens]
+    assert list(seqs[:, 1]) == [(l + C - 1) // C for l in lens]
     assert list(seqs[:, 2]) == [int(x) for x in cu[:-1]] and list(seqs[:, 3]) == lens
-    assert list(seqs[:, 0]) == [sum((l + 15) // 16 for l in lens[:n]) for n in range(len(lens))]
+    assert list(seqs[:, 0]) == [sum((l + C - 1) // C for l in lens[:n]) for n in range(len(lens))]
     assert sorted(order) == list(range(len(lens)))
     counts = [seqs[n, 1] for n in order]
     assert counts == sorted(counts, reverse=True)               # longest first
@@ -80,16 +96,13 @@ def test_chunk_table_and_records_match_chunked_form():
             qn = inp.scale * qq / np.sqrt((qq * qq).sum(-1, keepdims=True) + EPS)
             P = chunked_ref.chunk_pieces(qn, kn, a, 1 / (1 + np.exp(-bf[sl, h])))
             off = lay["records"] + (h * lay["max_chunks"] + ci) * R
-            rec = buf[off:off + R]
-            f16 = lambda o, shape: rec[o:o + 2 * int(np.prod(shape))].view(np.float16).astype(np.float64).reshape(shape)
-            got = dict(Qh=unpermute(f16(0, (16, 128)))[:ln], W=-unpermute(f16(4096, (16, 128)))[:ln],
-                       Kb=f16(8192, (16, 128))[:ln], T=f16(12288, (16, 16)).T[:ln, :ln],
-                       M=f16(12800, (16, 16)).T[:ln, :ln], gamma=rec[13312:13824].view(np.float32).astype(np.float64)[GAM_SLOT])
+            full = decode_record(buf[off:off + R], C)
+            got = {k: (v if k == "gamma" else v[:ln, :ln] if k in ("T", "M") else v[:ln]) for k, v in full.items()}
             ref = dict(Qh=P["Qh"], W=P["T"] @ P["Kh"], Kb=P["Kb"], T=P["T"], M=P["M"], gamma=P["gamma"])
             # padded rows / columns of a partial chunk are exactly zero
-            assert np.all(f16(0, (16, 128))[ln:] == 0) and np.all(f16(4096, (16, 128))[ln:] == 0)
-            assert np.all(f16(8192, (16, 128))[ln:] == 0)
-            assert np.all(f16(12288, (16, 16)).T[ln:] == 0) and np.all(f16(12800, (16, 16)).T[ln:] == 0)
+            for key in ("Qh", "W", "Kb", "T", "M"):
+                assert np.all(full[key][ln:] == 0), key
+            assert np.all(full["T"][:, ln:] == 0) and np.all(full["M"][:, ln:] == 0)
             # structure: T lower triangular, Mqk lower triangular incl. diagonal
             assert np.all(np.triu(got["T"], 1) == 0) and np.all(np.triu(got["M"], 1) == 0)
             for key in ref:
