@@ -6,4 +6,4 @@ is the thin ctypes binding that marshals torch tensors into it.  Importing
 this package loads nothing: ``from gated_delta_rule_prep_amd import kda``
 loads the library and fails loudly if it has not been built.
 """
-__all__ = ["kda", "inputs"]
+__all__ = ["kda", "inputs", "chunk_kda"]

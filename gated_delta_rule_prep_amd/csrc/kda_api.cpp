@@ -387,6 +387,49 @@ int kda_debug_prep(const void* q, const void* k, const void* g, const void* beta
   }
 }
 
+int kda_decode(const void* q, const void* k, const void* v, const void* g, const void* beta, float scale,
+               void* out, const float* A_log, const float* dt_bias, float lower_bound,
+               const void* initial_state, int initial_state_dtype, void* final_state, int final_state_dtype,
+               int64_t N, int64_t H, int64_t K, int64_t V, hipStream_t stream) {
+  try {
+    if (N < 0 || H < 1)
+      return fail(KDA_EINVAL, "kda: need N >= 0, H >= 1 (got N=%lld H=%lld)", (long long)N, (long long)H);
+    if (K != kda::K || V != kda::V)
+      return fail(KDA_EINVAL, "kda: K and V must both be 128 (got K=%lld V=%lld)", (long long)K, (long long)V);
+    if (N * H >= (int64_t(1) << 31)) return fail(KDA_EINVAL, "kda: N*H too large");
+    if (N > 0 && (!q || !k || !v || !g || !beta || !out))
+      return fail(KDA_EINVAL, "kda: a required token pointer is NULL");
+    if (!A_log || !dt_bias) return fail(KDA_EINVAL, "kda: A_log or dt_bias is NULL");
+    auto dtype_ok = [](int d) { return d == KDA_DTYPE_NONE || d == KDA_DTYPE_BF16 || d == KDA_DTYPE_FP32; };
+    if (!dtype_ok(initial_state_dtype) || !dtype_ok(final_state_dtype))
+      return fail(KDA_EDTYPE, "kda: state dtype codes must be KDA_DTYPE_NONE/BF16/FP32");
+    if ((initial_state == nullptr) != (initial_state_dtype == KDA_DTYPE_NONE))
+      return fail(KDA_EDTYPE, "kda: initial_state pointer and dtype disagree");
+    if ((final_state == nullptr) != (final_state_dtype == KDA_DTYPE_NONE))
+      return fail(KDA_EDTYPE, "kda: final_state pointer and dtype disagree");
+    if (initial_state && final_state && initial_state_dtype != final_state_dtype)
+      return fail(KDA_EDTYPE, "kda: initial_state and final_state dtypes differ");
+    if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(g) || misaligned(out) ||
+        misaligned(dt_bias) || misaligned(initial_state) || misaligned(final_state))
+      return fail(KDA_EINVAL, "kda: q, k, v, g, out, dt_bias and the states must be 16-byte aligned");
+    if (!std::isfinite(scale)) return fail(KDA_EINVAL, "kda: scale is not finite");
+    if (!std::isfinite(lower_bound) || lower_bound < -5.0f || lower_bound > 0.0f)
+      return fail(KDA_EINVAL, "kda: lower_bound must lie in [-5, 0] (got %g)", (double)lower_bound);
+    int rc = check_device(nullptr);
+    if (rc != KDA_OK) return rc;
+    kda::DecodeArgs da{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                       static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(g),
+                       static_cast<const uint16_t*>(beta), A_log, dt_bias, scale, lower_bound, initial_state,
+                       final_state, initial_state ? initial_state_dtype : final_state_dtype,
+                       static_cast<uint16_t*>(out), N, H};
+    hipError_t e = kda::launch_decode(da, stream);
+    if (e != hipSuccess) return fail(KDA_EHIP, "kda: decode launch: %s", hipGetErrorString(e));
+    return KDA_OK;
+  } catch (...) {
+    return fail(KDA_EHIP, "kda: unexpected C++ exception");
+  }
+}
+
 int kda_fwd_check_status(const void* workspace, hipStream_t stream, int* status) {
   if (!workspace || !status) return fail(KDA_EINVAL, "kda: workspace or status is NULL");
   hipError_t e = hipStreamSynchronize(stream);

@@ -124,7 +124,27 @@ struct RecurArgs {
   Layout lay;
 };
 
+// Single-token step: token n of every sequence is row n of q, k, v, g, beta
+// ([N][H][128], [N][H]) and of out.
+struct DecodeArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* g;
+  const uint16_t* beta;
+  const float* A_log;
+  const float* dt_bias;
+  float scale;
+  float lower_bound;
+  const void* s_in;
+  void* s_out;
+  int state_dtype;      // KDA_DTYPE_* of whichever state is given
+  uint16_t* out;
+  int64_t N, H;
+};
+
 hipError_t launch_sched(const SchedArgs& a, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 // The launchers pick the 16- or 32-token kernels by a.lay.chunk.
 hipError_t launch_prep(const PrepArgs& a, hipStream_t s);
 hipError_t launch_recur(const RecurArgs& a, hipStream_t s);

@@ -228,19 +228,19 @@ __device__ __forceinline__ void compute(f32x4 (&Z)[8][NT], const Ops<NT>& o, u32
 template <int NT, int D>
 struct LoadPlan {
   int32_t off[Cfg<NT, D>::kLoads];   // record byte offset, or value byte offset within the token row
-  int32_t row[Cfg<NT, D>::kLoads];   // value token row (value blocks)
+  int32_t row[Cfg<NT, D>::kLoads];   // value blocks: byte offset of the piece within the chunk's rows
 };
 
 template <int NT, int D>
-__device__ __forceinline__ void make_plan(LoadPlan<NT, D>& pl, int wave, int lane) {
+__device__ __forceinline__ void make_plan(LoadPlan<NT, D>& pl, int wave, int lane, int row_bytes) {
   using Cf = Cfg<NT, D>;
 #pragma unroll
   for (int j = 0; j < Cf::kLoads; ++j) {
     const int b = kWaves * j + wave;
     if (b < Cf::kValBlocks) {
       const int s = 64 * b + lane, r = s / Cf::kRowPieces, p = s % Cf::kRowPieces;
-      pl.row[j] = r;
       pl.off[j] = 16 * (p ^ (2 * (r & 3)));
+      pl.row[j] = r * row_bytes + pl.off[j];
     } else {
       pl.row[j] = 0;
       pl.off[j] = rec_source(64 * (b - Cf::kValBlocks) + lane);
@@ -264,44 +264,44 @@ __device__ __forceinline__ i32x4 buf_rsrc(const void* base, int bytes) {
 // that the compiler does not treat it as an LDS store of unknown extent (it
 // would then wait for every outstanding load before each LDS read); the waits
 // are explicit in the kernel.  M0 carries the LDS address (one wait state
-// between setting it and the load) and is restored afterwards.
+// between setting it and the load); it is declared clobbered, so the compiler
+// sets it again wherever it needs it itself.
 __device__ __forceinline__ void load_lds16(const i32x4& rsrc, uint32_t lds, int voff) {
-  int saved;
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
+      "s_mov_b32 m0, %1\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %1, %3, 0 offen lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
+      "buffer_load_dwordx4 %0, %2, 0 offen lds"
+      :
       : "v"(voff), "s"(__builtin_amdgcn_readfirstlane((int)lds)), "s"(rsrc)
-      : "memory");
+      : "memory", "m0");
 }
 
-// Issue the loads of chunk min(c, clast) into ring slot `slot` (all lanes, no
-// waits); clast is the last chunk of the part, so loads never run ahead into
-// records that the next part's prep may still be writing.
+// Issue the loads of chunk min(c, clast) into the ring slot at LDS address
+// `slot_lds` (all lanes, no waits); clast is the last chunk of the part, so
+// loads never run ahead into records that the next part's prep may still be
+// writing.  `vseq` is the sequence's first value row at this tile's first
+// column; everything but the per-lane offsets of the load plan is
+// wave-uniform, so the per-chunk bookkeeping stays in scalar registers.
 // Value rows past the end of a partial chunk repeat the last row: the
 // record gives them zero weight (their T rows and columns and their -W, Qhat
 // and Kbar rows are exactly zero), so any finite values are harmless.
 template <int NT, int D>
-__device__ __forceinline__ void issue_chunk(char* slot, const LoadPlan<NT, D>& pl, const char* recs,
-                                            const uint16_t* v, const SeqEntry& se, int c, int clast, int64_t H,
-                                            int h, int v0, int wave) {
+__device__ __forceinline__ void issue_chunk(uint32_t slot_lds, const LoadPlan<NT, D>& pl, const char* recs,
+                                            const char* vseq, const SeqEntry& se, int c, int clast, int row_bytes,
+                                            int wave) {
   using Cf = Cfg<NT, D>;
   c = min(c, clast);
-  const Rows cr = chunk_rows(se, c);
+  const int len = min(se.len - C * c, C);
   const i32x4 rrec = buf_rsrc(recs + (int64_t)c * REC_BYTES, REC_BYTES);
-  const int row_bytes = (int)(H * V * 2);
-  const i32x4 rval = buf_rsrc(v + (cr.row0 * H + h) * V + v0, (cr.len - 1) * row_bytes + 2 * Cf::kCols);
-  const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>((lds_void*)slot);
+  const i32x4 rval = buf_rsrc(vseq + (int64_t)c * C * row_bytes, C * row_bytes);
+  const int last = (len - 1) * row_bytes;   // byte offset of the chunk's last value row
 #pragma unroll
   for (int j = 0; j < Cf::kLoads; ++j) {
     const int b = kWaves * j + wave;   // wave-uniform
     if (b < Cf::kValBlocks) {
-      load_lds16(rval, lds0 + 1024 * b, min(pl.row[j], cr.len - 1) * row_bytes + pl.off[j]);
+      load_lds16(rval, slot_lds + 1024 * b, min(pl.row[j], last + pl.off[j]));
     } else {
-      load_lds16(rrec, lds0 + 1024 * b, pl.off[j]);
+      load_lds16(rrec, slot_lds + 1024 * b, pl.off[j]);
     }
   }
 }
@@ -348,7 +348,7 @@ __global__ __launch_bounds__(kThreads) void recur_kernel(RecurArgs a) {
   float* const ws_state = reinterpret_cast<float*>(a.ws + a.lay.state);
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, lg = lane >> 4, lc = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, lg = lane >> 4, lc = lane & 15;
   const int64_t sbase = ((int64_t)n * H + h) * V * K;   // state [n][h][v][k]
   const int wc = Cf::kWaveCols * wave;                   // first tile column of this wave
   const int col0 = v0 + wc;                              // first state column of this wave
@@ -373,14 +373,22 @@ __global__ __launch_bounds__(kThreads) void recur_kernel(RecurArgs a) {
     }
 
   if (ci_lo < ci_hi) {
+    const int row_bytes = (int)(H * V * 2);
     LoadPlan<NT, D> pl;
-    make_plan<NT, D>(pl, wave, lane);
+    make_plan<NT, D>(pl, wave, lane, row_bytes);
     const int clast = ci_hi - 1;
+    const char* vseq = reinterpret_cast<const char*>(a.v + ((int64_t)se.row0 * H + h) * V + v0);
+    const uint32_t ring0 = (uint32_t)reinterpret_cast<uintptr_t>((lds_void*)ring[0]);
+    // Output rows of a full chunk: a wave-uniform base per chunk plus this
+    // lane's fixed offset (token lc, columns 16 nt + 4 lg .. +3).
+    uint16_t* const out_seq = a.out + ((int64_t)se.row0 * H + h) * V + col0;
+    const int64_t out_chunk = (int64_t)C * H * V;
+    const int out_lane = (int)((lc * H) * V) + 4 * lg;
     // Chunks ci_lo .. ci_lo + D-2 in flight before the first step.  Loads past
     // the part's last chunk repeat it into slots that are never read.
 #pragma unroll
     for (int c = 0; c < D - 1; ++c)
-      issue_chunk<NT, D>(ring[c], pl, recs, a.v, se, ci_lo + c, clast, H, h, v0, wave);
+      issue_chunk<NT, D>(ring0 + c * Cf::kSlotBytes, pl, recs, vseq, se, ci_lo + c, clast, row_bytes, wave);
     u32x2 o_prev[NT];
     int slot = 0;   // ring slot of chunk ci
     for (int ci = ci_lo; ci < ci_hi; ++ci) {
@@ -393,20 +401,18 @@ __global__ __launch_bounds__(kThreads) void recur_kernel(RecurArgs a) {
       // Every wave is done with chunk ci - 1, whose slot is refilled now, and
       // every wave's loads of chunk ci have landed.
       const int refill = slot == 0 ? D - 1 : slot - 1;
-      issue_chunk<NT, D>(ring[refill], pl, recs, a.v, se, ci + D - 1, clast, H, h, v0, wave);
-      if (ci > ci_lo) {   // output of chunk ci - 1
-        const Rows pr = chunk_rows(se, ci - 1);
-        if (lc < pr.len) {
+      issue_chunk<NT, D>(ring0 + refill * Cf::kSlotBytes, pl, recs, vseq, se, ci + D - 1, clast, row_bytes, wave);
+      if (ci > ci_lo) {   // output of chunk ci - 1, a full chunk (only a sequence's last chunk is partial)
+        uint16_t* const ob = out_seq + (int64_t)(ci - 1) * out_chunk;
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt)
-            *reinterpret_cast<u32x2*>(a.out + ((pr.row0 + lc) * H + h) * V + col0 + 16 * nt + 4 * lg) = o_prev[nt];
-        }
+        for (int nt = 0; nt < NT; ++nt) *reinterpret_cast<u32x2*>(ob + out_lane + 16 * nt) = o_prev[nt];
       }
       Ops<NT> ops;
       read_ops<NT, D>(ops, ring[slot], wc, lane);
       compute<NT>(Z, ops, o_prev);
       slot = slot == D - 1 ? 0 : slot + 1;
     }
+    wait_vmcnt<0>();   // no load into the ring outlives the workgroup
     const Rows pr = chunk_rows(se, clast);
     if (lc < pr.len) {
 #pragma unroll

@@ -25,7 +25,7 @@ KDA_DTYPE_NONE, KDA_DTYPE_BF16, KDA_DTYPE_FP32 = 0, 1, 2
 KDA_STATUS_OK, KDA_STATUS_BAD_CU_SEQLENS = 0, 1
 CHUNK = 16
 
-EXPORTS = ("kda_fwd", "kda_fwd_profiled", "kda_fwd_ex", "kda_fwd_parts", "kda_fwd_workspace_bytes",
+EXPORTS = ("kda_fwd", "kda_fwd_profiled", "kda_fwd_ex", "kda_fwd_parts", "kda_decode", "kda_fwd_workspace_bytes",
            "kda_get_last_error", "kda_version", "kda_fwd_check_status", "kda_workspace_layout", "kda_debug_prep")
 
 if not os.path.exists(LIB_PATH):
@@ -46,6 +46,9 @@ _lib.kda_fwd_ex.argtypes = _lib.kda_fwd.argtypes + [ctypes.c_int, ctypes.c_int, 
 _lib.kda_fwd_ex.restype = ctypes.c_int
 _lib.kda_fwd_parts.argtypes = [_i64, _i64, ctypes.c_int]
 _lib.kda_fwd_parts.restype = ctypes.c_int
+_lib.kda_decode.argtypes = [_p, _p, _p, _p, _p, ctypes.c_float, _p, _p, _p, ctypes.c_float,
+                            _p, ctypes.c_int, _p, ctypes.c_int, _i64, _i64, _i64, _i64, _p]
+_lib.kda_decode.restype = ctypes.c_int
 _lib.kda_fwd_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int]
 _lib.kda_fwd_workspace_bytes.restype = ctypes.c_size_t
 _lib.kda_get_last_error.restype = ctypes.c_char_p
@@ -201,6 +204,49 @@ def fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state
             n = 0 if events is None else len(events)
             ev = None if events is None else (ctypes.c_void_p * n)(*[e.cuda_event for e in events])
             rc = _lib.kda_fwd_ex(*args, _stream(dev), int(chunk or 0), int(parts or 0), ev, n)
+    if rc != KDA_OK:
+        _raise(rc)
+    return out
+
+
+def decode(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state=None, final_state=None):
+    """One recurrent step, one token per sequence (kda_decode), into ``out``.
+
+    q, k, g, v: bf16 [N, H, 128] or [N, 1, H, 128]; beta: bf16 [N, H] or
+    [N, 1, H]; out like v; states [N, H, V, K] (bf16 / fp32, may be the same
+    tensor).  Runs on the current stream of the tensors' device.  Returns out.
+    """
+    if q.dim() == 4:
+        if q.shape[1] != 1:
+            raise KDAValueError(KDA_EINVAL, "decode takes one token per sequence: q must be [N, 1, H, K]")
+        N, _, H, K = q.shape
+    elif q.dim() == 3:
+        N, H, K = q.shape
+    else:
+        raise KDAValueError(KDA_EINVAL, "q must be [N, H, K] or [N, 1, H, K]")
+    V = v.shape[-1]
+    dev = q.device
+    for name, t, last in (("q", q, K), ("k", k, K), ("g", g, K), ("v", v, V), ("out", out, V), ("beta", beta, 1)):
+        _check(name, t, torch.bfloat16)
+        if t.numel() != N * H * last:
+            raise KDAValueError(KDA_EINVAL, "%s has %d elements, expected %d (N=%d, H=%d)"
+                                % (name, t.numel(), N * H * last, N, H))
+    _check("A_log", A_log, torch.float32, (H,))
+    _check("dt_bias", dt_bias, torch.float32, (H, K))
+    for name, t in (("initial_state", initial_state), ("final_state", final_state)):
+        if t is not None:
+            _state_code(t)
+            _check(name, t, t.dtype, (N, H, V, K))
+    for t in (q, k, v, g, beta, out, A_log, dt_bias, initial_state, final_state):
+        if t is not None and t.device != dev:
+            raise KDAValueError(KDA_EINVAL, "all tensors must be on %s" % dev)
+    if dev.type != "cuda":
+        raise KDAValueError(KDA_EINVAL, "tensors must be on a HIP device, got %s" % dev)
+    with torch.cuda.device(dev):
+        rc = _lib.kda_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(out),
+                             _ptr(A_log), _ptr(dt_bias), float(lower_bound), _ptr(initial_state),
+                             _state_code(initial_state), _ptr(final_state), _state_code(final_state),
+                             N, H, K, V, _stream(dev))
     if rc != KDA_OK:
         _raise(rc)
     return out

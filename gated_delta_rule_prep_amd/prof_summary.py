@@ -28,7 +28,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = ["csrc/kda_device.h", "csrc/kda_internal.h", "csrc/kda_sched.hip", "csrc/kda_prep.hip",
-                  "csrc/kda_recur.hip", "csrc/kda_prep32.hip", "csrc/kda_recur32.hip"]
+                  "csrc/kda_recur.hip", "csrc/kda_prep32.hip", "csrc/kda_recur32.hip", "csrc/kda_decode.hip"]
 
 
 def source_hash() -> str:
@@ -40,7 +40,8 @@ def source_hash() -> str:
 
 
 def short_name(name: str) -> str:
-    m = re.search(r"(sched_kernel|prep32_kernel|prep_kernel|recur32_kernel|recur_kernel|copyBuffer|elementwise_kernel)",
+    m = re.search(r"(sched_kernel|prep32_kernel|prep_kernel|recur32_kernel|recur_kernel|decode_kernel|copyBuffer|"
+                  r"elementwise_kernel)",
                   name)
     return m.group(1) if m else name[:40]
 

@@ -176,6 +176,24 @@ int kda_fwd_ex(const void* q, const void* k, const void* v, const void* g, const
 int kda_fwd_parts(int64_t B, int64_t T, int parts);
 
 /*
+ * kda_decode -- enqueue one recurrent step (one new token per sequence) on
+ * `stream`: the token-by-token recurrence of P1 §一 with the activations of
+ * kda_fwd, no chunking and no workspace.
+ *
+ * q, k, g, v: bf16 [N][H][128] (token n of sequence n, i.e. kda_fwd's
+ * [B, T, H, 128] with B = N, T = 1); beta: bf16 [N][H]; out: bf16 [N][H][128];
+ * A_log, dt_bias, lower_bound, scale and the states ([N][H][V][K], bf16 or
+ * fp32, NULL = zero state / not written, the same buffer allowed for both) as
+ * for kda_fwd.  Each (sequence, head) state is read and written once, so the
+ * call is bound by the state bytes.  Argument errors are caught on the host
+ * before any HIP call, with the codes of kda_fwd.
+ */
+int kda_decode(const void* q, const void* k, const void* v, const void* g, const void* beta, float scale,
+               void* out, const float* A_log, const float* dt_bias, float lower_bound,
+               const void* initial_state, int initial_state_dtype, void* final_state, int final_state_dtype,
+               int64_t N, int64_t H, int64_t K, int64_t V, hipStream_t stream);
+
+/*
  * Workspace bytes kda_fwd needs for these sizes (0 if the sizes are invalid).
  * num_seqs is ignored when has_cu_seqlens is 0 (then N = B).
  */

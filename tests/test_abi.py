@@ -187,3 +187,38 @@ def test_layout_for_both_chunk_sizes():
     assert kda.workspace_bytes(1, 8192, 96) == max(l16["total"], l32["total"])
     with pytest.raises(ValueError):
         kda.workspace_layout(1, 64, 2, chunk=24)
+
+
+def call_decode(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, scale=0.088, out=FAKE, A_log=FAKE, dt_bias=FAKE,
+             lb=-5.0, s0=None, s0_dt=0, s1=None, s1_dt=0, N=4, H=2, K=128, V=128, stream=None)
+    a.update(over)
+    return kda.lib().kda_decode(a["q"], a["k"], a["v"], a["g"], a["beta"], a["scale"], a["out"], a["A_log"],
+                                a["dt_bias"], a["lb"], a["s0"], a["s0_dt"], a["s1"], a["s1_dt"], a["N"], a["H"],
+                                a["K"], a["V"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), kda.KDA_EINVAL),
+    (dict(v=None), kda.KDA_EINVAL),
+    (dict(out=None), kda.KDA_EINVAL),
+    (dict(beta=None), kda.KDA_EINVAL),
+    (dict(A_log=None), kda.KDA_EINVAL),
+    (dict(dt_bias=ctypes.c_void_p(0x1004)), kda.KDA_EINVAL),   # misaligned
+    (dict(k=ctypes.c_void_p(0x1008)), kda.KDA_EINVAL),
+    (dict(K=64), kda.KDA_EINVAL),
+    (dict(V=64), kda.KDA_EINVAL),
+    (dict(N=-1), kda.KDA_EINVAL),
+    (dict(H=0), kda.KDA_EINVAL),
+    (dict(N=1 << 30, H=4), kda.KDA_EINVAL),
+    (dict(lb=-6.0), kda.KDA_EINVAL),
+    (dict(scale=float("nan")), kda.KDA_EINVAL),
+    (dict(s0=FAKE, s0_dt=0), kda.KDA_EDTYPE),
+    (dict(s1=None, s1_dt=2), kda.KDA_EDTYPE),
+    (dict(s0=FAKE, s0_dt=2, s1=FAKE, s1_dt=1), kda.KDA_EDTYPE),
+    (dict(s0=FAKE, s0_dt=7), kda.KDA_EDTYPE),
+])
+def test_decode_host_validation_rejects(over, code):
+    rc = call_decode(**over)
+    assert rc == code, (rc, kda.last_error())
+    assert kda.last_error()
