@@ -12,7 +12,11 @@ outputs of the method that kernel is responsible for), and for the whole path.
 The fp64 oracle is timed on a bounded sample of the headline workload on the
 host cores (cpu_baseline).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+Also timed (not the headline): one decode step (kda_decode) of 256
+one-token sequences x 96 heads with a bf16 state updated in place.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--chunk 16|32]
+                       [--only fixed|varlen|decode]
 """
 from __future__ import annotations
 
@@ -133,6 +137,44 @@ def roofline(res, traffic=None):
              mfma_frac=round(th * FLOPS_PER_TH / (path_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4))
 
 
+DECODE_N, DECODE_H = 256, 96   # one decode step of a serving batch: 256 sequences, 96 heads
+
+
+def run_decode(steps, warmup, torch, kda, device_inputs):
+    """kda_decode on a batch of DECODE_N one-token sequences, bf16 state updated
+    in place (the state is 805 MB, past the 256 MB Infinity Cache, so every
+    step streams it from and to HBM).  Roofline: the state bytes (in + out) and
+    the token bytes per launch over the mean kernel time."""
+    from gated_delta_rule_prep_amd.inputs import make_inputs
+    inp = make_inputs(DECODE_N, 1, DECODE_H, seed=9, state_dtype="bf16", name="decode_N256_H96_bf16state")
+    d = device_inputs(inp, "cuda")
+    st = d["initial_state"]
+    out = torch.empty((DECODE_N, 1, DECODE_H, 128), dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        kda.decode(d["q"], d["k"], d["v"], d["g"], d["beta"], inp.scale, out, d["A_log"], d["dt_bias"],
+                   inp.lower_bound, initial_state=st, final_state=st)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    pairs = DECODE_N * DECODE_H
+    nbytes = pairs * (2 * 128 * 128 * 2 + PATH_BYTES_PER_TH) + param_bytes(inp)
+    ach = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": inp.name, "ms_per_step": round(ms, 4), "token_heads_per_s": round(pairs / (ms * 1e-3), 1),
+            "roofline": {"kernel": "kda::decode_kernel", "bound": "hbm", "achieved": round(ach, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                         "algorithmic_bytes_per_launch": int(nbytes)}}
+
+
 def cpu_baseline(cfg, heads: int):
     """The fp64 oracle on the first `heads` heads of the workload (all tokens)."""
     import oracle
@@ -153,6 +195,18 @@ def cpu_baseline(cfg, heads: int):
                 % (cfg.name, heads - 1, inp.H, inp.T, th, dt))
 
 
+def copy_for_counters(torch, mib):
+    """Three device-to-device copies of `mib` MiB: a plain copy kernel of known
+    size whose byte counters scale the workload's (prof_summary traffic)."""
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copies": 3}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -160,7 +214,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle cpu_baseline leg")
     ap.add_argument("--cpu-heads", type=int, default=96, help="heads of the headline workload the oracle runs")
-    ap.add_argument("--only", choices=["both", "fixed", "varlen"], default="both",
+    ap.add_argument("--only", choices=["both", "fixed", "varlen", "decode"], default="both",
                     help="time only one workload (for profiler runs); the JSON line needs both")
     ap.add_argument("--chunk", type=int, default=0, choices=[0, 16, 32],
                     help="tokens per chunk (0: the library's choice)")
@@ -179,23 +233,25 @@ def main():
     from tests.kda_gpu import device_inputs
 
     cfgs = configs()
+    if args.only == "decode":
+        print(json.dumps(run_decode(args.steps, args.warmup, torch, kda, device_inputs)))
+        if args.copy_mib > 0:
+            copy_for_counters(torch, args.copy_mib)
+        return
     if args.only != "both":
         res = run_workload(cfgs[2] if args.only == "fixed" else cfgs[3], args.steps, args.warmup, torch, kda,
                            device_inputs, args.chunk or None)
         print(json.dumps({"workload": res["inp"].name, "ms_per_step": round(res["ms"], 4),
                           "kernels_ms": {k: round(res[k + "_ms"], 4) for k in ("sched", "prep", "recur")}}))
         if args.copy_mib > 0:
-            n = args.copy_mib << 20
-            src = torch.ones(n, dtype=torch.uint8, device="cuda")
-            dst = torch.empty_like(src)
-            for _ in range(3):
-                dst.copy_(src)
-            torch.cuda.synchronize()
-            print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copies": 3}))
+            copy_for_counters(torch, args.copy_mib)
         return
     fixed = run_workload(cfgs[2], args.steps, args.warmup, torch, kda, device_inputs, args.chunk or None)
     varlen = run_workload(cfgs[3], args.steps, args.warmup, torch, kda, device_inputs, args.chunk or None)
+    decode = run_decode(args.steps, args.warmup, torch, kda, device_inputs)
     traffic = load_traffic()
+    t = traffic.get("decode", {}).get("decode_kernel")
+    decode["roofline"]["traffic"] = None if t is None else int(t["fetch_bytes"] + t["write_bytes"])
     rl, path = roofline(fixed, traffic.get("fixed"))
     rl_v, path_v = roofline(varlen, traffic.get("varlen"))
     cpu = None if args.no_cpu else cpu_baseline(cfgs[2], args.cpu_heads)
@@ -224,6 +280,7 @@ def main():
                           "kernels_ms": {"sched": round(varlen["sched_ms"], 4), "prep": round(varlen["prep_ms"], 4),
                                          "recur": round(varlen["recur_ms"], 4)},
                           "roofline": rl_v, "path_roofline": path_v},
+        "decode_256x96": decode,
         "status_ok": fixed["status"] == 0 and varlen["status"] == 0,
         "cpu_baseline": cpu,
     }
