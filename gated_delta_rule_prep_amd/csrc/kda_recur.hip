@@ -45,6 +45,8 @@
 // pair's records come from HBM once per XCD L2 rather than once per tile.
 #include "kda_device.h"
 #include "kda_internal.h"
+#include "kda_lds_pipe.h"
+#include "kda_step16.h"
 #include "../../include/kda.h"
 
 namespace kda {
@@ -53,7 +55,6 @@ namespace {
 constexpr int kRecPieces = REC_BYTES / 16;   // 864 16-byte pieces per record
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kBufWord3 = 0x00020000;        // raw buffer descriptor, dword 3 (gfx9 family)
 
 template <int NT, int D>
 struct Cfg {
@@ -68,8 +69,6 @@ struct Cfg {
   // byte offsets of the fields inside a slot
   static constexpr int kVal = 0;
   static constexpr int kRec = kValBlocks * 1024;
-  static constexpr int kQh = kRec + REC_QH, kNw = kRec + REC_NW, kKb = kRec + REC_KB;
-  static constexpr int kTt = kRec + REC_T, kMt = kRec + REC_MQK, kGam = kRec + REC_GAM;
   static_assert(C * kRowPieces % 64 == 0, "value rows fill whole blocks");
   static_assert(D >= 3 && (D - 2) * kLoads <= 63, "ring depth within the vmcnt range");
   static_assert(V % kCols == 0, "tile shape");
@@ -85,15 +84,6 @@ __device__ __forceinline__ Rows chunk_rows(const SeqEntry& se, int j) {
   return Rows{(int64_t)se.row0 + C * j, rem < C ? rem : C};
 }
 
-__device__ __forceinline__ f16x4 f16x4_of(f32x4 x) {
-  f16x4 r;
-  r[0] = (_Float16)x[0]; r[1] = (_Float16)x[1]; r[2] = (_Float16)x[2]; r[3] = (_Float16)x[3];
-  return r;
-}
-
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
-
 // ---- swizzled slot layout -------------------------------------------------
 // Qhat and -W: token row r, 16-byte piece p (8 channels in record order) at
 // piece position p ^ r of the row.  Kbar and the value tile: piece p of row r
@@ -107,119 +97,6 @@ __device__ __forceinline__ int rec_source(int s) {
   if (s < 512) return 16 * ((s & ~15) | (p ^ r));
   if (s < 768) return 16 * ((s & ~15) | (p ^ (2 * (r & 3))));
   return 16 * s;
-}
-
-// Transposing read of the 16 x 16 block of a swizzled token-major 16-bit tile
-// (row stride `rowb` bytes) whose first column is `col` (a multiple of 16):
-// lane (lc, lg) receives M[4lg..4lg+3][col + lc] (see lds_read_tr).
-__device__ __forceinline__ s16x4 tr_swz(const char* tile, int rowb, int col, int lane) {
-  const int g = lane >> 4, j = lane & 15;
-  const int r = 4 * g + (j >> 2);
-  const int c = col + 4 * (j & 3);                 // first of the 4 elements this lane fetches
-  const int p = (c >> 3) ^ (2 * (r & 3));
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tile + r * rowb + 16 * p + 2 * (c & 7)));
-}
-
-// The MFMA operands of one chunk step.
-template <int NT>
-struct Ops {
-  f16x4 aT, am;          // T[lc][4lg..4lg+3], Mqk[lc][4lg..4lg+3]
-  f16x4 bv[NT];          // V[4lg..4lg+3][wc + 16nt + lc] (converted from bf16)
-  f16x8 aw[4], aq[4];    // -W, Qhat row lc, channels of 32-block s at the lane's 8 positions
-  f16x4 ak[8];           // Kbar[4lg..4lg+3][16m + lc]
-  f32x2 g2;              // gamma of the rows that this lane hands to its 16-lane row
-};
-
-template <int NT, int D>
-__device__ __forceinline__ void read_ops(Ops<NT>& o, const char* slot, int wc, int lane) {
-  using Cf = Cfg<NT, D>;
-  const int lg = lane >> 4, lc = lane & 15;
-  o.aT = lds_read_tr(reinterpret_cast<const _Float16*>(slot + Cf::kTt), C, lane);
-  o.am = lds_read_tr(reinterpret_cast<const _Float16*>(slot + Cf::kMt), C, lane);
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const s16x4 raw = tr_swz(slot + Cf::kVal, 2 * Cf::kCols, wc + 16 * nt, lane);
-    f16x4 b;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) b[i] = (_Float16)bf16_to_f32((uint16_t)raw[i]);
-    o.bv[nt] = b;
-  }
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const int p = (4 * s + lg) ^ lc;
-    o.aw[s] = *reinterpret_cast<const f16x8*>(slot + Cf::kNw + 256 * lc + 16 * p);
-    o.aq[s] = *reinterpret_cast<const f16x8*>(slot + Cf::kQh + 256 * lc + 16 * p);
-  }
-#pragma unroll
-  for (int m = 0; m < 8; ++m) o.ak[m] = __builtin_bit_cast(f16x4, tr_swz(slot + Cf::kKb, 2 * K, 16 * m, lane));
-  o.g2 = *reinterpret_cast<const f32x2*>(slot + Cf::kGam + 8 * lane);
-}
-
-// x from lane L of this lane's 16-lane row.
-template <int L>
-__device__ __forceinline__ float row_bcast(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + L, 0xF, 0xF, false));
-}
-
-// Row 16M + 4lg + i decays by gamma[16M + 4lg + i], held by lane 4 (M % 4) + i
-// of the 16-lane row in register M / 4 (see kGamSlot).
-template <int M>
-__device__ __forceinline__ f32x4 decay(f32x4 z, f32x2 g2) {
-  const float g = g2[M >> 2];
-  return f32x4{z[0] * row_bcast<4 * (M & 3) + 0>(g), z[1] * row_bcast<4 * (M & 3) + 1>(g),
-               z[2] * row_bcast<4 * (M & 3) + 2>(g), z[3] * row_bcast<4 * (M & 3) + 3>(g)};
-}
-
-// One chunk step from operands in registers: updates Z and returns the output
-// tile as O^T (lane (lc, lg): token lc, value columns 16nt + 4lg .. +3 of the
-// wave), rounded to bf16 and packed.
-template <int NT>
-__device__ __forceinline__ void compute(f32x4 (&Z)[8][NT], const Ops<NT>& o, u32x2 (&out)[NT]) {
-  // ---- U = T V ; E = U + (-W) Z ; O^T = Z^T Qhat^T
-  f32x4 E[NT], O[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    E[nt] = mfma_f16_k16(o.aT, o.bv[nt], f32x4{0.f, 0.f, 0.f, 0.f});
-    O[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      f16x8 zb;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        zb[i] = (_Float16)Z[2 * s][nt][i];
-        zb[4 + i] = (_Float16)Z[2 * s + 1][nt][i];
-      }
-      E[nt] = mfma_f16_k32(o.aw[s], zb, E[nt]);
-      O[nt] = mfma_f16_k32(zb, o.aq[s], O[nt]);
-    }
-  }
-
-  // ---- O^T += E^T Mqk^T
-  f16x4 eb[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    eb[nt] = f16x4_of(E[nt]);
-    O[nt] = mfma_f16_k16(eb[nt], o.am, O[nt]);
-  }
-
-  // ---- Z = diag(gam) Z + Kbar^T E
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    Z[0][nt] = mfma_f16_k16(o.ak[0], eb[nt], decay<0>(Z[0][nt], o.g2));
-    Z[1][nt] = mfma_f16_k16(o.ak[1], eb[nt], decay<1>(Z[1][nt], o.g2));
-    Z[2][nt] = mfma_f16_k16(o.ak[2], eb[nt], decay<2>(Z[2][nt], o.g2));
-    Z[3][nt] = mfma_f16_k16(o.ak[3], eb[nt], decay<3>(Z[3][nt], o.g2));
-    Z[4][nt] = mfma_f16_k16(o.ak[4], eb[nt], decay<4>(Z[4][nt], o.g2));
-    Z[5][nt] = mfma_f16_k16(o.ak[5], eb[nt], decay<5>(Z[5][nt], o.g2));
-    Z[6][nt] = mfma_f16_k16(o.ak[6], eb[nt], decay<6>(Z[6][nt], o.g2));
-    Z[7][nt] = mfma_f16_k16(o.ak[7], eb[nt], decay<7>(Z[7][nt], o.g2));
-  }
-
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) out[nt] = u32x2{pack_bf16(O[nt][0], O[nt][1]), pack_bf16(O[nt][2], O[nt][3])};
 }
 
 // Where this lane's load instruction j of a chunk reads from.  Slot block
@@ -246,34 +123,6 @@ __device__ __forceinline__ void make_plan(LoadPlan<NT, D>& pl, int wave, int lan
       pl.off[j] = rec_source(64 * (b - Cf::kValBlocks) + lane);
     }
   }
-}
-
-typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
-
-// Raw buffer descriptor over `bytes` bytes at `base` (stride 0, no swizzle),
-// made wave-uniform so that it can live in scalar registers.
-__device__ __forceinline__ i32x4 buf_rsrc(const void* base, int bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  return i32x4{__builtin_amdgcn_readfirstlane((int32_t)(uint32_t)a),
-               __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)(a >> 32) & 0xffff),
-               __builtin_amdgcn_readfirstlane(bytes), kBufWord3};
-}
-
-// buffer_load_dwordx4 ... lds: lane i's 16 bytes at rsrc + voff land at LDS
-// byte address lds + 16 i (lds wave-uniform).  Written as inline assembly so
-// that the compiler does not treat it as an LDS store of unknown extent (it
-// would then wait for every outstanding load before each LDS read); the waits
-// are explicit in the kernel.  M0 carries the LDS address (one wait state
-// between setting it and the load); it is declared clobbered, so the compiler
-// sets it again wherever it needs it itself.
-__device__ __forceinline__ void load_lds16(const i32x4& rsrc, uint32_t lds, int voff) {
-  asm volatile(
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %0, %2, 0 offen lds"
-      :
-      : "v"(voff), "s"(__builtin_amdgcn_readfirstlane((int)lds)), "s"(rsrc)
-      : "memory", "m0");
 }
 
 // Issue the loads of chunk min(c, clast) into the ring slot at LDS address
@@ -305,13 +154,6 @@ __device__ __forceinline__ void issue_chunk(uint32_t slot_lds, const LoadPlan<NT
     }
   }
 }
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 template <int NT, int D>
 __global__ __launch_bounds__(kThreads) void recur_kernel(RecurArgs a) {
@@ -408,7 +250,7 @@ __global__ __launch_bounds__(kThreads) void recur_kernel(RecurArgs a) {
         for (int nt = 0; nt < NT; ++nt) *reinterpret_cast<u32x2*>(ob + out_lane + 16 * nt) = o_prev[nt];
       }
       Ops<NT> ops;
-      read_ops<NT, D>(ops, ring[slot], wc, lane);
+      read_ops<NT>(ops, ring[slot] + Cf::kRec, ring[slot] + Cf::kVal, 2 * Cf::kCols, wc, lane);
       compute<NT>(Z, ops, o_prev);
       slot = slot == D - 1 ? 0 : slot + 1;
     }

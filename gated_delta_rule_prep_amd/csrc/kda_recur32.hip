@@ -24,6 +24,7 @@
 // their columns in the same order.
 #include "kda_device.h"
 #include "kda_internal.h"
+#include "kda_lds_pipe.h"
 #include "../../include/kda.h"
 
 namespace kda {
@@ -33,7 +34,6 @@ constexpr int CC = C32;
 constexpr int kRecPieces = REC32_BYTES / 16;   // 1824 16-byte pieces per record
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kBufWord3 = 0x00020000;          // raw buffer descriptor, dword 3 (gfx9 family)
 
 template <int NT, int D>
 struct Cfg {
@@ -65,7 +65,6 @@ __device__ __forceinline__ Rows chunk_rows(const SeqEntry& se, int j) {
   return Rows{(int64_t)se.row0 + CC * j, rem < CC ? rem : CC};
 }
 
-typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 
 // ---- swizzled slot layout -------------------------------------------------
@@ -251,32 +250,6 @@ __device__ __forceinline__ void make_plan(LoadPlan<NT, D>& pl, int wave, int lan
   }
 }
 
-typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
-
-// Raw buffer descriptor over `bytes` bytes at `base` (stride 0, no swizzle),
-// made wave-uniform so that it can live in scalar registers.
-__device__ __forceinline__ i32x4 buf_rsrc(const void* base, int bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  return i32x4{__builtin_amdgcn_readfirstlane((int32_t)(uint32_t)a),
-               __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)(a >> 32) & 0xffff),
-               __builtin_amdgcn_readfirstlane(bytes), kBufWord3};
-}
-
-// buffer_load_dwordx4 ... lds: lane i's 16 bytes at rsrc + voff land at LDS
-// byte address lds + 16 i (lds wave-uniform).  Inline assembly, so that the
-// compiler does not wait for every outstanding load before each LDS read; the
-// waits are explicit in the kernel.  M0 carries the LDS address (one wait
-// state between setting it and the load) and is declared clobbered.
-__device__ __forceinline__ void load_lds16(const i32x4& rsrc, uint32_t lds, int voff) {
-  asm volatile(
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %0, %2, 0 offen lds"
-      :
-      : "v"(voff), "s"(__builtin_amdgcn_readfirstlane((int)lds)), "s"(rsrc)
-      : "memory", "m0");
-}
-
 // Issue the loads of chunk min(c, clast) into the ring slot at LDS address
 // `slot_lds` (all lanes, no waits; wave-uniform bookkeeping).  Value rows past
 // the end of a partial chunk repeat the last row: the record gives them zero
@@ -302,12 +275,6 @@ __device__ __forceinline__ void issue_chunk(uint32_t slot_lds, const LoadPlan<NT
   }
 }
 
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 template <int NT>
 __device__ __forceinline__ void store_out(uint16_t* out, const Rows& pr, int64_t H, int h, int col0, int lc, int lg,
