@@ -1,7 +1,8 @@
 """Benchmark of the chunked KDA forward on one MI355X.
 
-One step = one kda_fwd call (scheduler + chunk-prep + chunk-recurrence kernels)
-over one batch of seeded synthetic input already resident in HBM.  Workloads:
+One step = one kda_fwd call (the scheduler, then chunk prep and chunk
+recurrence: one fused kernel by default, two kernels on the split path) over
+one batch of seeded synthetic input already resident in HBM.  Workloads:
   * headline: T = 8192, H = 96, K = V = 128, one fixed-length sequence, bf16
     initial and final state, lower_bound = -5;
   * also timed: the same shape as 8 varlen sequences of 1024 tokens.
@@ -16,7 +17,7 @@ Also timed (not the headline): one decode step (kda_decode) of 256
 one-token sequences x 96 heads with a bf16 state updated in place.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--chunk 16|32]
-                       [--only fixed|varlen|decode]
+                       [--path auto|fused|split] [--only fixed|varlen|decode]
 """
 from __future__ import annotations
 
@@ -52,18 +53,20 @@ def param_bytes(inp):
     return inp.H * 4 + inp.H * inp.K * 4
 
 
-def run_workload(cfg, steps, warmup, torch, kda, device_inputs, chunk=None):
+def run_workload(cfg, steps, warmup, torch, kda, device_inputs, chunk=None, path=None):
     inp = cfg.make()
     d = device_inputs(inp, "cuda")
     out = torch.empty((inp.B, inp.T, inp.H, inp.V), dtype=torch.bfloat16, device="cuda")
     fin = torch.empty((inp.N, inp.H, inp.V, inp.K),
                       dtype=torch.bfloat16 if inp.state_dtype == "bf16" else torch.float32, device="cuda")
-    ws = kda.alloc_workspace(inp.B, inp.T, inp.H, inp.N, inp.cu_seqlens is not None, "cuda")
+    path = path or "auto"
+    used = kda.path_used(chunk, None, path)
+    ws = kda.alloc_workspace(inp.B, inp.T, inp.H, inp.N, inp.cu_seqlens is not None, "cuda", chunk, None, path)
 
     def step(events=None):
         kda.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], inp.scale, out, d["A_log"], d["dt_bias"],
                 inp.lower_bound, initial_state=d["initial_state"], final_state=fin,
-                cu_seqlens=d["cu_seqlens"], workspace=ws, events=events, chunk=chunk)
+                cu_seqlens=d["cu_seqlens"], workspace=ws, events=events, chunk=chunk, path=path)
 
     for _ in range(warmup):
         step()
@@ -80,8 +83,8 @@ def run_workload(cfg, steps, warmup, torch, kda, device_inputs, chunk=None):
     # per-kernel durations: kda_fwd_ex records HIP events before and after
     # every kernel on the stream it launches that kernel on
     n_prof = max(steps, 5)
-    P = kda.parts(inp.B, inp.T)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2 + 4 * P)] for _ in range(n_prof)]
+    n_ev = kda.num_events(inp.B, inp.T, chunk, None, path)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(n_prof)]
     for row in ev:
         for e in row:
             e.record()          # creates the underlying HIP event
@@ -90,12 +93,17 @@ def run_workload(cfg, steps, warmup, torch, kda, device_inputs, chunk=None):
         step(events=row)
     torch.cuda.synchronize()
     span = lambda row, i: row[i].elapsed_time(row[i + 1])
-    k_ms = np.array([[span(row, 0), sum(span(row, 2 + 2 * p) for p in range(P)),
-                      sum(span(row, 2 + 2 * P + 2 * p) for p in range(P))] for row in ev]).mean(axis=0)
+    if used == "fused":         # [0, 1] scheduler, [2, 3] the fused kernel
+        k_ms = np.array([[span(row, 0), span(row, 2)] for row in ev]).mean(axis=0)
+        kernels = {"sched": float(k_ms[0]), "fused": float(k_ms[1])}
+    else:                       # [0, 1] scheduler, then prep and recurrence of each part
+        P = (n_ev - 2) // 4
+        k_ms = np.array([[span(row, 0), sum(span(row, 2 + 2 * p) for p in range(P)),
+                          sum(span(row, 2 + 2 * P + 2 * p) for p in range(P))] for row in ev]).mean(axis=0)
+        kernels = {"sched": float(k_ms[0]), "prep": float(k_ms[1]), "recur": float(k_ms[2])}
     status = kda.check_status(ws)
     th = inp.B * inp.T * inp.H
-    return dict(inp=inp, ms=ms, sched_ms=float(k_ms[0]), prep_ms=float(k_ms[1]), recur_ms=float(k_ms[2]),
-                token_heads=th, status=status)
+    return dict(inp=inp, ms=ms, kernels=kernels, path=used, token_heads=th, status=status)
 
 
 TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "hbm_traffic_T8192_H96.md")
@@ -116,14 +124,16 @@ def load_traffic():
 
 
 def roofline(res, traffic=None):
-    inp, th = res["inp"], res["token_heads"]
+    inp, th, km = res["inp"], res["token_heads"], res["kernels"]
     prep_bytes = th * PREP_BYTES_PER_TH + param_bytes(inp)
     recur_bytes = th * RECUR_BYTES_PER_TH + state_bytes(inp)
     path_bytes = prep_bytes + recur_bytes
-    if res["recur_ms"] >= res["prep_ms"]:
-        name, kbytes, kms = "kda::recur_kernel", recur_bytes, res["recur_ms"]
+    if "fused" in km:           # one kernel moves every algorithmic byte of the path
+        name, kbytes, kms = "kda::fused_kernel", path_bytes, km["fused"]
+    elif km["recur"] >= km["prep"]:
+        name, kbytes, kms = "kda::recur_kernel", recur_bytes, km["recur"]
     else:
-        name, kbytes, kms = "kda::prep_kernel", prep_bytes, res["prep_ms"]
+        name, kbytes, kms = "kda::prep_kernel", prep_bytes, km["prep"]
     ach = kbytes / (kms * 1e-3) / 1e9
     t = (traffic or {}).get(name.split("::")[1])
     tbytes = None if t is None else int(t["fetch_bytes"] + t["write_bytes"])
@@ -218,6 +228,8 @@ def main():
                     help="time only one workload (for profiler runs); the JSON line needs both")
     ap.add_argument("--chunk", type=int, default=0, choices=[0, 16, 32],
                     help="tokens per chunk (0: the library's choice)")
+    ap.add_argument("--path", choices=["auto", "fused", "split"], default="auto",
+                    help="execution path of kda_fwd_ex (auto: the library's choice)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="with --only: afterwards run 3 device-to-device copies of this many MiB, a plain copy "
                          "kernel of known size that scales the HBM byte counters")
@@ -238,16 +250,26 @@ def main():
         if args.copy_mib > 0:
             copy_for_counters(torch, args.copy_mib)
         return
+    chunk = args.chunk or None
     if args.only != "both":
         res = run_workload(cfgs[2] if args.only == "fixed" else cfgs[3], args.steps, args.warmup, torch, kda,
-                           device_inputs, args.chunk or None)
-        print(json.dumps({"workload": res["inp"].name, "ms_per_step": round(res["ms"], 4),
-                          "kernels_ms": {k: round(res[k + "_ms"], 4) for k in ("sched", "prep", "recur")}}))
+                           device_inputs, chunk, args.path)
+        print(json.dumps({"workload": res["inp"].name, "path": res["path"], "ms_per_step": round(res["ms"], 4),
+                          "kernels_ms": {k: round(v, 4) for k, v in res["kernels"].items()}}))
         if args.copy_mib > 0:
             copy_for_counters(torch, args.copy_mib)
         return
-    fixed = run_workload(cfgs[2], args.steps, args.warmup, torch, kda, device_inputs, args.chunk or None)
-    varlen = run_workload(cfgs[3], args.steps, args.warmup, torch, kda, device_inputs, args.chunk or None)
+    # Both execution paths are timed on both headline workloads; each headline
+    # number is the faster path (kda_fwd_ex selects it; the split path is the
+    # library's default) and the line names the path and gives both times.
+    paths = ["split", "fused"] if args.path == "auto" and chunk in (None, 16) else [args.path]
+    runs = {}
+    for wl, cfg in (("fixed", cfgs[2]), ("varlen", cfgs[3])):
+        for pth in paths:
+            runs[wl, pth] = run_workload(cfg, args.steps, args.warmup, torch, kda, device_inputs, chunk, pth)
+    best = lambda wl: min((runs[wl, p] for p in paths), key=lambda r: r["ms"])
+    fixed, varlen = best("fixed"), best("varlen")
+    paths_ms = lambda wl: {p: round(runs[wl, p]["ms"], 4) for p in paths}
     decode = run_decode(args.steps, args.warmup, torch, kda, device_inputs)
     traffic = load_traffic()
     t = traffic.get("decode", {}).get("decode_kernel")
@@ -267,19 +289,18 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 in/out, fp16/fp32 MFMA, fp32 state on chip",
+        "dtype": "bf16 in/out, fp16 and fp32 MFMA with fp32 accumulation, fp32 state on chip",
         "data": "synthetic (seeded normal q/k/v/g/beta, A_log=log U[1,16], dt_bias~N(0,0.1), state~N(0,0.05))",
         "config": {"workload": cfgs[2].name, "B": 1, "T": 8192, "H": 96, "K": 128, "V": 128,
-                   "state": "bf16", "lower_bound": -5.0, "chunk": 16},
+                   "state": "bf16", "lower_bound": -5.0, "chunk": args.chunk or 16, "path": fixed["path"]},
         "roofline": rl,
         "path_roofline": path,
-        "kernels_ms": {"sched": round(fixed["sched_ms"], 4), "prep": round(fixed["prep_ms"], 4),
-                       "recur": round(fixed["recur_ms"], 4)},
-        "varlen_8x1024": {"workload": cfgs[3].name, "ms_per_step": round(varlen["ms"], 4),
+        "kernels_ms": {k: round(v, 4) for k, v in fixed["kernels"].items()},
+        "paths_ms": paths_ms("fixed"),
+        "varlen_8x1024": {"workload": cfgs[3].name, "path": varlen["path"], "ms_per_step": round(varlen["ms"], 4),
                           "value": round(varlen["token_heads"] / (varlen["ms"] * 1e-3), 1),
-                          "kernels_ms": {"sched": round(varlen["sched_ms"], 4), "prep": round(varlen["prep_ms"], 4),
-                                         "recur": round(varlen["recur_ms"], 4)},
-                          "roofline": rl_v, "path_roofline": path_v},
+                          "kernels_ms": {k: round(v, 4) for k, v in varlen["kernels"].items()},
+                          "paths_ms": paths_ms("varlen"), "roofline": rl_v, "path_roofline": path_v},
         "decode_256x96": decode,
         "status_ok": fixed["status"] == 0 and varlen["status"] == 0,
         "cpu_baseline": cpu,

@@ -140,6 +140,25 @@ bool layout_for(int64_t B, int64_t T, int64_t H, int64_t N, int chunk, Layout* L
   return true;
 }
 
+// The fused path keeps only the header and the per-sequence tables: no chunk
+// table, no records, no hand-over states.
+bool layout_fused(int64_t B, int64_t T, int64_t H, int64_t N, Layout* L) {
+  if (B < 1 || T < 0 || H < 1 || N < 0) return false;
+  int64_t off = sizeof(WsHeader);
+  L->chunk_table = off;
+  L->seq_table = off;
+  off = align_up(off + N * (int64_t)sizeof(SeqEntry), 256);
+  L->order = off;
+  off = align_up(off + N * 4, 256);
+  L->chunk = C;
+  L->records = off;
+  L->rec_bytes = 0;
+  L->max_chunks = 0;
+  L->state = off;
+  L->total = off;
+  return true;
+}
+
 // Parts used when the caller leaves the choice to the library: one.  On
 // MI355X the two kernels slow each other down by about as much as running
 // them side by side saves (measured at T = 8192, H = 64 / 96, fixed and
@@ -152,9 +171,30 @@ int default_chunk() { return C; }
 
 }  // namespace kda
 
+namespace {
+
+// Path a kda_fwd_ex call takes (KDA_PATH_SPLIT / KDA_PATH_FUSED), or -1.
+// The library's own choice is the split path.  Measured on MI355X (T = 8192,
+// K = V = 128): the fused kernel is faster for batches of many short
+// sequences (8 x 1024 tokens, H = 96: 0.45 ms against 0.66) but slower
+// whenever one sequence is long (one 8192-token sequence: 0.93 ms against
+// 0.68; 12 ragged sequences with one of ~6000 tokens: 0.97 against 0.71),
+// and the longest sequence is only known on the device.
+int resolve_path(int chunk, int parts, int path) {
+  if (chunk != 0 && chunk != kda::C && chunk != kda::C32) return -1;
+  if (parts < 0) return -1;
+  const bool fusable = (chunk == 0 || chunk == kda::C) && parts <= 1;
+  if (path == KDA_PATH_AUTO) return KDA_PATH_SPLIT;
+  if (path == KDA_PATH_SPLIT) return KDA_PATH_SPLIT;
+  if (path == KDA_PATH_FUSED) return fusable ? KDA_PATH_FUSED : -1;
+  return -1;
+}
+
+}  // namespace
+
 extern "C" {
 
-int kda_version(void) { return 100; }  // 0.1.0
+int kda_version(void) { return 200; }  // 0.2.0
 
 const char* kda_get_last_error(void) { return g_last_error.c_str(); }
 
@@ -165,6 +205,20 @@ size_t kda_fwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t num_seqs
   if (!kda::layout_for(B, T, H, N, kda::C, &L16) || !kda::layout_for(B, T, H, N, kda::C32, &L32)) return 0;
   return (size_t)std::max(L16.total, L32.total);
 }
+
+size_t kda_fwd_workspace_bytes_ex(int64_t B, int64_t T, int64_t H, int64_t num_seqs, int has_cu_seqlens,
+                                  int chunk, int parts, int path) {
+  int64_t N = 0;
+  const int p = resolve_path(chunk, parts, path);
+  if (p < 0) return 0;
+  if (check_sizes(B, T, H, kda::K, kda::V, nullptr, num_seqs, has_cu_seqlens, &N) != KDA_OK) return 0;
+  kda::Layout L;
+  const bool ok = p == KDA_PATH_FUSED ? kda::layout_fused(B, T, H, N, &L)
+                                      : kda::layout_for(B, T, H, N, chunk == 0 ? kda::default_chunk() : chunk, &L);
+  return ok ? (size_t)L.total : 0;
+}
+
+int kda_fwd_path(int chunk, int parts, int path) { return resolve_path(chunk, parts, path); }
 
 int kda_workspace_layout(int64_t B, int64_t T, int64_t H, int64_t num_seqs, int has_cu_seqlens, int chunk,
                          int64_t offsets[7]) {
@@ -189,7 +243,7 @@ static int validate_common(const void* q, const void* k, const void* g, const vo
                            const float* A_log, const float* dt_bias, float lower_bound,
                            const int64_t* cu, int64_t num_seqs, int64_t B, int64_t T, int64_t H,
                            int64_t K, int64_t V, void* workspace, size_t workspace_bytes, int chunk,
-                           kda::Layout* L, int64_t* N) {
+                           bool fused, kda::Layout* L, int64_t* N) {
   int rc = check_sizes(B, T, H, K, V, cu, num_seqs, cu != nullptr, N);
   if (rc != KDA_OK) return rc;
   // With no tokens (B * T == 0) the token tensors are empty and may be NULL.
@@ -198,11 +252,13 @@ static int validate_common(const void* q, const void* k, const void* g, const vo
   if (!A_log || !dt_bias) return fail(KDA_EINVAL, "kda: A_log or dt_bias is NULL");
   if (misaligned(q) || misaligned(k) || misaligned(g))
     return fail(KDA_EINVAL, "kda: q, k and g must be 16-byte aligned");
+  if (fused && misaligned(dt_bias)) return fail(KDA_EINVAL, "kda: dt_bias must be 16-byte aligned");
   if (!std::isfinite(scale)) return fail(KDA_EINVAL, "kda: scale is not finite");
   if (!std::isfinite(lower_bound) || lower_bound < -5.0f || lower_bound > 0.0f)
     return fail(KDA_EINVAL, "kda: lower_bound must lie in [-5, 0] (got %g)", (double)lower_bound);
   if (chunk != kda::C && chunk != kda::C32) return fail(KDA_EINVAL, "kda: chunk must be 16 or 32 (got %d)", chunk);
-  if (!kda::layout_for(B, T, H, *N, chunk, L)) return fail(KDA_EINVAL, "kda: bad sizes");
+  if (!(fused ? kda::layout_fused(B, T, H, *N, L) : kda::layout_for(B, T, H, *N, chunk, L)))
+    return fail(KDA_EINVAL, "kda: bad sizes");
   if (!workspace) return fail(KDA_EINVAL, "kda: workspace is NULL");
   if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
     return fail(KDA_EINVAL, "kda: workspace must be 256-byte aligned");
@@ -225,7 +281,7 @@ static int fwd_impl(const void* q, const void* k, const void* v, const void* g, 
                     const void* initial_state, int initial_state_dtype, void* final_state,
                     int final_state_dtype, const int64_t* cu_seqlens, int64_t num_seqs, int64_t B,
                     int64_t T, int64_t H, int64_t K, int64_t V, void* workspace, size_t workspace_bytes,
-                    hipStream_t stream, int chunk_req, int parts_req, hipEvent_t* ev, int n_ev,
+                    hipStream_t stream, int chunk_req, int parts_req, int path_req, hipEvent_t* ev, int n_ev,
                     hipEvent_t* ev4) {
   try {
     if ((!v || !out) && B * T > 0) return fail(KDA_EINVAL, "kda: v or out is NULL");
@@ -241,20 +297,54 @@ static int fwd_impl(const void* q, const void* k, const void* v, const void* g, 
     if (parts_req < 0) return fail(KDA_EINVAL, "kda: parts must be >= 0 (got %d)", parts_req);
     if (chunk_req != 0 && chunk_req != kda::C && chunk_req != kda::C32)
       return fail(KDA_EINVAL, "kda: chunk must be 0, 16 or 32 (got %d)", chunk_req);
+    const int path = resolve_path(chunk_req, parts_req, path_req);
+    if (path < 0)
+      return fail(KDA_EINVAL, "kda: path %d cannot run chunk=%d with parts=%d (the fused path takes 16-token "
+                  "chunks and one part)", path_req, chunk_req, parts_req);
+    const bool fused = path == KDA_PATH_FUSED;
     const int chunk = chunk_req == 0 ? kda::default_chunk() : chunk_req;
     kda::Layout L;
     int64_t N = 0;
     int rc = validate_common(q, k, g, beta, scale, A_log, dt_bias, lower_bound, cu_seqlens, num_seqs, B, T,
-                             H, K, V, workspace, workspace_bytes, chunk, &L, &N);
+                             H, K, V, workspace, workspace_bytes, chunk, fused, &L, &N);
     if (rc != KDA_OK) return rc;
     if (misaligned(v) || misaligned(out) || misaligned(initial_state) || misaligned(final_state))
       return fail(KDA_EINVAL, "kda: v, out and the states must be 16-byte aligned");
-    const int P = parts_used(B, T, parts_req);
-    if (ev && n_ev != 2 + 4 * P)
-      return fail(KDA_EINVAL, "kda: %d events given, this call needs %d (2 + 4 x %d parts)", n_ev, 2 + 4 * P, P);
+    const int P = fused ? 1 : parts_used(B, T, parts_req);
+    const int n_need = fused ? 4 : 2 + 4 * P;
+    if (ev && n_ev != n_need)
+      return fail(KDA_EINVAL, "kda: %d events given, this call needs %d", n_ev, n_need);
     int dev = 0;
     rc = check_device(&dev);
     if (rc != KDA_OK) return rc;
+    if (fused) {
+      hipError_t e = hipSuccess;
+      auto rec = [&](int i) {
+        if (e == hipSuccess && ev) e = hipEventRecord(ev[i], stream);
+        if (e == hipSuccess && ev4) e = hipEventRecord(ev4[i], stream);
+      };
+      char* ws = static_cast<char*>(workspace);
+      rec(0);
+      if (e == hipSuccess) {
+        kda::SchedArgs sa{cu_seqlens, N, B, T, 1, B * T > 0 ? B * T : 1, ws, L};
+        e = kda::launch_sched(sa, stream);
+      }
+      rec(1);
+      if (e == hipSuccess && ev4) e = hipEventRecord(ev4[2], stream);
+      if (e == hipSuccess && ev) e = hipEventRecord(ev[2], stream);
+      if (e == hipSuccess) {
+        kda::FusedArgs fa{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                          static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(g),
+                          static_cast<const uint16_t*>(beta), static_cast<uint16_t*>(out), A_log, dt_bias, scale,
+                          lower_bound, initial_state, final_state,
+                          initial_state ? initial_state_dtype : final_state_dtype, N, H, ws, L};
+        e = kda::launch_fused(fa, stream);
+      }
+      if (e == hipSuccess && ev) e = hipEventRecord(ev[3], stream);
+      if (e == hipSuccess && ev4) e = hipEventRecord(ev4[3], stream);
+      if (e != hipSuccess) return fail(KDA_EHIP, "kda: launch or event call: %s", hipGetErrorString(e));
+      return KDA_OK;
+    }
     SideRes* side = nullptr;
     std::unique_lock<std::mutex> lock;
     if (P > 1) {
@@ -293,6 +383,7 @@ static int fwd_impl(const void* q, const void* k, const void* v, const void* g, 
       rec(2 + 2 * p, stream);
       if (e == hipSuccess) e = kda::launch_prep(pa, stream);
       rec(3 + 2 * p, stream);
+      if (p == P - 1) rec4(2);   // after the last chunk prep
       if (P > 1 && e == hipSuccess) {
         e = hipEventRecord(side->prep_done[p], stream);
         if (e == hipSuccess) e = hipStreamWaitEvent(rstream, side->prep_done[p], 0);
@@ -304,7 +395,6 @@ static int fwd_impl(const void* q, const void* k, const void* v, const void* g, 
       if (e == hipSuccess) e = kda::launch_recur(ra, rstream);
       rec(3 + 2 * P + 2 * p, rstream);
     }
-    rec4(2);
     if (P > 1 && e == hipSuccess) {
       e = hipEventRecord(side->join, rstream);
       if (e == hipSuccess) e = hipStreamWaitEvent(stream, side->join, 0);
@@ -325,7 +415,7 @@ int kda_fwd(const void* q, const void* k, const void* v, const void* g, const vo
             hipStream_t stream) {
   return fwd_impl(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
                   initial_state_dtype, final_state, final_state_dtype, cu_seqlens, num_seqs, B, T, H, K, V,
-                  workspace, workspace_bytes, stream, 0, 0, nullptr, 0, nullptr);
+                  workspace, workspace_bytes, stream, 0, 0, KDA_PATH_AUTO, nullptr, 0, nullptr);
 }
 
 int kda_fwd_profiled(const void* q, const void* k, const void* v, const void* g, const void* beta,
@@ -338,7 +428,7 @@ int kda_fwd_profiled(const void* q, const void* k, const void* v, const void* g,
     return fail(KDA_EINVAL, "kda: kda_fwd_profiled needs four events");
   return fwd_impl(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
                   initial_state_dtype, final_state, final_state_dtype, cu_seqlens, num_seqs, B, T, H, K, V,
-                  workspace, workspace_bytes, stream, 0, 0, nullptr, 0, events);
+                  workspace, workspace_bytes, stream, 0, 0, KDA_PATH_AUTO, nullptr, 0, events);
 }
 
 int kda_fwd_parts(int64_t B, int64_t T, int parts) {
@@ -351,13 +441,19 @@ int kda_fwd_ex(const void* q, const void* k, const void* v, const void* g, const
                const void* initial_state, int initial_state_dtype, void* final_state, int final_state_dtype,
                const int64_t* cu_seqlens, int64_t num_seqs, int64_t B, int64_t T, int64_t H, int64_t K,
                int64_t V, void* workspace, size_t workspace_bytes, hipStream_t stream, int chunk,
-               int parts, hipEvent_t* events, int num_events) {
+               int parts, int path, hipEvent_t* events, int num_events) {
   if (events != nullptr)
     for (int i = 0; i < num_events; ++i)
       if (!events[i]) return fail(KDA_EINVAL, "kda: event %d is NULL", i);
   return fwd_impl(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
                   initial_state_dtype, final_state, final_state_dtype, cu_seqlens, num_seqs, B, T, H, K, V,
-                  workspace, workspace_bytes, stream, chunk, parts, events, num_events, nullptr);
+                  workspace, workspace_bytes, stream, chunk, parts, path, events, num_events, nullptr);
+}
+
+int kda_fwd_num_events(int64_t B, int64_t T, int chunk, int parts, int path) {
+  const int p = resolve_path(chunk, parts, path);
+  if (p < 0 || B < 0 || T < 0) return 0;
+  return p == KDA_PATH_FUSED ? 4 : 2 + 4 * parts_used(B, T, parts);
 }
 
 int kda_debug_prep(const void* q, const void* k, const void* g, const void* beta, float scale,
@@ -368,7 +464,7 @@ int kda_debug_prep(const void* q, const void* k, const void* g, const void* beta
     kda::Layout L;
     int64_t N = 0;
     int rc = validate_common(q, k, g, beta, scale, A_log, dt_bias, lower_bound, cu_seqlens, num_seqs, B, T,
-                             H, K, kda::V, workspace, workspace_bytes, chunk, &L, &N);
+                             H, K, kda::V, workspace, workspace_bytes, chunk, false, &L, &N);
     if (rc != KDA_OK) return rc;
     rc = check_device();
     if (rc != KDA_OK) return rc;

@@ -1,0 +1,557 @@
+// kda_fused.hip -- chunk prep and chunk recurrence of the KDA forward in one
+// kernel for gfx950, with the chunk records kept in LDS.
+//
+// The FlashKDA blog post ("FlashKDA：月之暗面开源的 Kimi Delta Attention 高性能内核",
+// §二 2.2) splits the forward pass into a token-parallel prep stage and a
+// chunk-recurrent stage, joined by per-chunk records in global memory.  On
+// MI355X the recurrence is bound by how fast each CU can stream its operands
+// (records and values, about 16 KB per 16-token step per workgroup), not by
+// its arithmetic; the raw inputs a chunk's record is made from (q, k, g, beta:
+// 12.3 KB) are smaller than the record (13.8 KB), so building the record next
+// to the recurrence costs no extra bytes per CU and removes the record's
+// round trip through HBM (about 1.6 GB per call at T = 8192, H = 96) and the
+// separate prep launch.
+//
+// One workgroup per (sequence, head, V-tile), eight waves:
+//   * waves 0-3 run the recurrence (kda_step16.h) on 16 NT value columns each,
+//     with the fp32 state slice in registers for the whole sequence;
+//   * waves 4-7 build the records: prep wave p owns the chunks c = p mod 4 and
+//     builds the record of chunk c during the four steps before step c, one
+//     phase per step (0: inputs, norms, channels 0-31; 1: channels 32-63;
+//     2: channels 64-95; 3: channels 96-127, L, Mqk and the 16 x 16 inverse).
+//     At every step each prep wave runs one phase, of four different chunks,
+//     so the per-step work is close to even, and each SIMD holds one wave of
+//     each kind: the prep wave's ALU work fills the recurrence wave's stalls.
+// Step s (s = -4 .. nchunks - 1) has one barrier.  Before it, every wave waits
+// for its own loads of group s; a group is the raw q, k, g, beta of chunk s + 4
+// (read by the phase-0 wave of step s) and the value rows of chunk s (read by
+// the recurrence at step s), streamed HBM -> LDS with buffer_load ... lds
+// D - 1 groups ahead into a ring of D group slots.  Records live in a ring of
+// five slots (chunks s .. s + 4).  The record layout in LDS is the swizzled
+// one kda_step16.h reads.
+//
+// Per chunk, as in the split prep kernel (kda_prep.hip), with a2 the gate in
+// log2 units, G its in-chunk inclusive cumulative sum, P = 2^G, Pinv = 2^-G,
+// gam = P at the last token:
+//   L   = strict_lower(diag(beta) (kn P)(kn Pinv)^T)
+//   Mqk = lower_incl((qn P)(kn Pinv)^T)
+//   T   = (I + L)^-1 diag(beta)   (forward substitution, exact for a unit
+//                                 lower-triangular matrix)
+//   record: Qhat = qn P, -Khat = -kn P, Kbar = kn Pinv gam, T^T, Mqk^T, gam
+// L and Mqk multiply factors spanning up to e^(+-80) (the range argument of
+// §二 2.1 of the same post at lower_bound = -5), so they are fp32 16x16x4
+// products; the matrix cores run them beside the prep wave's vector work,
+// which is what bounds the prep (each 64-lane vector instruction holds a
+// SIMD for four cycles, a transcendental for sixteen).
+#include "kda_device.h"
+#include "kda_internal.h"
+#include "kda_lds_pipe.h"
+#include "kda_step16.h"
+#include "../../include/kda.h"
+
+namespace kda {
+namespace {
+
+constexpr int kRecWaves = 4;                 // recurrence waves
+constexpr int kPrepWaves = 4;                // record-building waves
+constexpr int kAllWaves = kRecWaves + kPrepWaves;
+constexpr int kThreads = 64 * kAllWaves;
+constexpr int kLead = 5;                     // raw inputs of chunk s + 5 arrive with group s
+constexpr int kRecSlots = kLead + 1;         // records of chunks s .. s + 5
+constexpr int kSlotBytes = REC_BYTES + 64;   // record + the chunk's beta (fp32 [16]) in LDS
+constexpr float kEps = 1e-6f;
+
+template <int NT, int D>
+struct FCfg {
+  static constexpr int kWaveCols = 16 * NT;               // value columns per recurrence wave
+  static constexpr int kCols = kWaveCols * kRecWaves;     // value columns per workgroup
+  static constexpr int kTiles = V / kCols;                // workgroups per (sequence, head)
+  static constexpr int kRowPieces = kCols / 8;            // 16-byte pieces per value row of the tile
+  static constexpr int kVBlocks = C * kRowPieces / 64;    // 1 KB blocks of value rows
+  // 1 KB blocks of a group slot: q, k, g (4 each: 16 rows x 256 B), beta, values
+  static constexpr int kQ = 0, kK = 4, kG = 8, kB = 12, kV = 13;
+  static constexpr int kBlocks = kV + kVBlocks;
+  static constexpr int kMaxLoads = (kBlocks + kAllWaves - 1) / kAllWaves;   // per wave per group
+  static constexpr int kGroupBytes = kBlocks * 1024;
+  static_assert(C * kRowPieces % 64 == 0, "value rows fill whole blocks");
+  static_assert(D >= 3 && (D - 2) * kMaxLoads <= 63, "ring depth within the vmcnt range");
+  static_assert(V % kCols == 0, "tile shape");
+};
+
+// Values a prep wave carries from one phase of a chunk to the next.
+struct Carry {
+  u32x4 qw[3], kw[3], gw[3];   // raw bf16 q, k, g of channel blocks 1..3 (block j at j - 1)
+  float rq, rk;                // scale / |q|, 1 / |k| (0 for padded tokens)
+  int valid;                   // token row < chunk length
+  f32x4 accL, accM;            // L and Mqk partial sums over the blocks done so far
+};
+
+// Chunk j of a sequence: first flattened token row and length (1..16).
+struct Rows {
+  int64_t row0;
+  int len;
+};
+__device__ __forceinline__ Rows chunk_rows(const SeqEntry& se, int j) {
+  const int rem = se.len - C * j;
+  return Rows{(int64_t)se.row0 + C * j, rem < C ? rem : C};
+}
+
+// Where this lane's load j of a group reads from.  Group block b = 8 j + wave
+// (64 pieces, one per lane).  q / k / g blocks: slot piece s of the tensor's
+// 16 x 16-piece tile is row s / 16, position s % 16, and holds source piece
+// position ^ row (XOR swizzle: the phase-0 reads of 16 rows at one piece
+// index hit distinct banks).  Value blocks: as in kda_step16.h.  The beta
+// block: lane l fetches the 16-byte piece holding beta of token row l % 16.
+template <int NT, int D>
+struct GroupPlan {
+  int32_t row[FCfg<NT, D>::kMaxLoads];   // token row 0..15 in the chunk
+  int32_t off[FCfg<NT, D>::kMaxLoads];   // byte offset of the piece within the row (not beta)
+};
+
+template <int NT, int D>
+__device__ __forceinline__ void make_plan(GroupPlan<NT, D>& pl, int wave, int lane) {
+  using F = FCfg<NT, D>;
+#pragma unroll
+  for (int j = 0; j < F::kMaxLoads; ++j) {
+    const int b = kAllWaves * j + wave;
+    if (b < F::kB) {
+      const int s = 64 * (b & 3) + lane, r = s >> 4, pos = s & 15;
+      pl.row[j] = r;
+      pl.off[j] = 16 * (pos ^ r);
+    } else if (b == F::kB) {
+      pl.row[j] = lane & 15;
+      pl.off[j] = 0;
+    } else {
+      const int s = 64 * (b - F::kV) + lane, r = s / F::kRowPieces, pos = s % F::kRowPieces;
+      pl.row[j] = r;
+      pl.off[j] = 16 * (pos ^ (2 * (r & 3)));
+    }
+  }
+}
+
+struct Seq {
+  const uint16_t* q;       // q, k, g at (sequence row 0, head h)
+  const uint16_t* k;
+  const uint16_t* g;
+  const char* beta;        // &beta[sequence row 0][h] (bytes)
+  const uint16_t* v;       // v at (sequence row 0, head h, tile column 0)
+  int64_t H;
+  SeqEntry se;
+};
+
+// Issue the loads of group s into the group slot at LDS address `slot_lds`:
+// q, k, g, beta of chunk s + kLead and the value rows of chunk s, each chunk
+// index clamped into the sequence (clamped loads land in parts of slots that
+// are never read).  Rows past the end of a partial chunk repeat its last row;
+// the prep gives them zero weight.  All lanes, no waits.
+template <int NT, int D>
+__device__ __forceinline__ void issue_group(uint32_t slot_lds, const GroupPlan<NT, D>& pl, const Seq& x, int s,
+                                            int wave) {
+  using F = FCfg<NT, D>;
+  const int nch = x.se.nchunks;
+  const int cq = min(max(s + kLead, 0), nch - 1), cv = min(max(s, 0), nch - 1);
+  const Rows rq = chunk_rows(x.se, cq), rv = chunk_rows(x.se, cv);
+  const int64_t H = x.H;
+  const int rs = (int)(H * K * 2);   // bytes between token rows (q, k, g, v alike: K = V)
+  const int64_t eq = (rq.row0 - x.se.row0) * H * K, ev = (rv.row0 - x.se.row0) * H * V;
+  const int qbytes = (rq.len - 1) * rs + K * 2;
+#pragma unroll
+  for (int j = 0; j < F::kMaxLoads; ++j) {
+    const int b = kAllWaves * j + wave;   // wave-uniform
+    if (b >= F::kBlocks) break;
+    const uint32_t dst = slot_lds + 1024 * b;
+    if (b < F::kB) {
+      // integer select (wave-uniform b): a pointer select here became an
+      // indexed private array with a full memory wait
+      const uintptr_t base = (b < F::kK ? reinterpret_cast<uintptr_t>(x.q)
+                              : b < F::kG ? reinterpret_cast<uintptr_t>(x.k)
+                                          : reinterpret_cast<uintptr_t>(x.g)) + 2 * eq;
+      load_lds16(buf_rsrc(reinterpret_cast<const void*>(base), qbytes), dst,
+                 min(pl.row[j], rq.len - 1) * rs + pl.off[j]);
+    } else if (b == F::kB) {
+      // 16-byte piece holding beta[row][h]; the descriptor starts at the piece
+      // holding the chunk's first beta, so every offset is a multiple of 16
+      const uintptr_t first = reinterpret_cast<uintptr_t>(x.beta + 2 * (rq.row0 - x.se.row0) * H);
+      const uintptr_t mine = first + (uintptr_t)(2 * (int64_t)min(pl.row[j], rq.len - 1) * H);
+      const uintptr_t base16 = first & ~(uintptr_t)15;
+      load_lds16(buf_rsrc(reinterpret_cast<const void*>(base16), (rq.len - 1) * 2 * (int)H + 32), dst,
+                 (int)((mine & ~(uintptr_t)15) - base16));
+    } else {
+      load_lds16(buf_rsrc(x.v + ev, (rv.len - 1) * rs + F::kCols * 2), dst,
+                 min(pl.row[j], rv.len - 1) * rs + pl.off[j]);
+    }
+  }
+}
+
+// Record field writers (swizzled layout of kda_step16.h).
+__device__ __forceinline__ void put_qh(char* rec, int field, int row, int pos, u32x2 w) {
+  // 4 fp16 values at channel position pos (a multiple of 4) of a Qhat / -W row
+  *reinterpret_cast<u32x2*>(rec + field + 256 * row + 16 * ((pos >> 3) ^ row) + 2 * (pos & 7)) = w;
+}
+
+// Channel block J (channels 32 J + 8 cq .. + 7, lane (r, cq)) of a chunk:
+// gates, their in-chunk cumulative sum, the decay factors and the decayed
+// operands; Qhat, -Khat, Kbar and gamma go to the record, and the block's
+// part of L and Mqk is added to accL / accM.  s_adt holds A2 * dt_bias, so
+// the gate argument A2 (g + dt_bias) is one fma.
+template <int J>
+__device__ __forceinline__ void chan_block(u32x4 qw, u32x4 kw, u32x4 gw, float rq, float rk, bool valid, float A2,
+                                           float lb2, const float* s_adt, int r, int cq, char* rec, f32x4& accL,
+                                           f32x4& accM) {
+  const int c0 = 32 * J + 8 * cq;
+  const f32x4 dtA = *reinterpret_cast<const f32x4*>(s_adt + c0);
+  const f32x4 dtB = *reinterpret_cast<const f32x4*>(s_adt + c0 + 4);
+  float kh[8], kb[8], qh[8], gm[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t wg = gw[e >> 1], wq = qw[e >> 1], wk = kw[e >> 1];
+    const float gv = (e & 1) ? bf16_hi(wg) : bf16_lo(wg);
+    const float qv = (e & 1) ? bf16_hi(wq) : bf16_lo(wq);
+    const float kv = (e & 1) ? bf16_hi(wk) : bf16_lo(wk);
+    const float adt = e < 4 ? dtA[e] : dtB[e - 4];
+    const float sg = valid ? fast_rcp(1.f + fast_exp2(fmaf(A2, gv, adt))) : 0.f;
+    float cs = sg + dpp_shr(sg, 1);   // inclusive prefix sum over the 16 token lanes
+    cs += dpp_shr(cs, 2);
+    cs += dpp_shr(cs, 4);
+    cs += dpp_shr(cs, 8);
+    const float G = lb2 * cs;
+    const float P = fast_exp2(G), Pinv = fast_exp2(-G);
+    const float gam = dpp_bcast15(P);
+    const float kn = kv * rk, qn = qv * rq;
+    const float kP = kn * P, kI = kn * Pinv, qP = qn * P;
+    // fp32 16x16x4: lane (r, cq) holds A[r][k = cq] and B[k = cq][r] for
+    // channel c0 + e, so L and Mqk take the factors straight from registers
+    accL = mfma_f32_k4(kP, kI, accL);
+    accM = mfma_f32_k4(qP, kI, accM);
+    kh[e] = -kP;
+    qh[e] = qP;
+    kb[e] = kI * gam;
+    gm[e] = P;
+  }
+  u32x4 wkb;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) wkb[w] = pack_f16(kb[2 * w], kb[2 * w + 1]);
+  *reinterpret_cast<u32x4*>(rec + REC_KB + 256 * r + 16 * ((c0 >> 3) ^ (2 * (r & 3)))) = wkb;
+  // Qhat and -Khat: channels 8cq .. 8cq+7 of block J sit at two runs of 4 positions
+  const int p0 = 32 * J + kPermPos(8 * cq), p1 = 32 * J + kPermPos(8 * cq + 4);
+  put_qh(rec, REC_QH, r, p0, u32x2{pack_f16(qh[0], qh[1]), pack_f16(qh[2], qh[3])});
+  put_qh(rec, REC_QH, r, p1, u32x2{pack_f16(qh[4], qh[5]), pack_f16(qh[6], qh[7])});
+  put_qh(rec, REC_NK, r, p0, u32x2{pack_f16(kh[0], kh[1]), pack_f16(kh[2], kh[3])});
+  put_qh(rec, REC_NK, r, p1, u32x2{pack_f16(kh[4], kh[5]), pack_f16(kh[6], kh[7])});
+  if (r == 15) {   // gam = P of the last token (padded tokens keep G constant)
+    float* gam_out = reinterpret_cast<float*>(rec + REC_GAM);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) gam_out[kGamSlot(c0 + e)] = gm[e];
+  }
+}
+
+struct PrepCtx {
+  float A2, lb2, scale;
+  const float* s_adt;  // A2 * dt_bias of the head, in LDS
+  int r, cq, lane;
+};
+
+// Phase 0 of a chunk: raw inputs from the group slot, norms, beta, channel
+// block 0.
+__device__ __forceinline__ void phase0(const PrepCtx& p, const char* grp, const Rows& rw, const Seq& x, char* rec,
+                                       Carry& cr, int kQ, int kK, int kG, int kB) {
+  const int r = p.r, cq = p.cq;
+  u32x4 qw[4], kw[4], gw[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int o = 256 * r + 16 * ((4 * j + cq) ^ r);
+    qw[j] = *reinterpret_cast<const u32x4*>(grp + 1024 * kQ + o);
+    kw[j] = *reinterpret_cast<const u32x4*>(grp + 1024 * kK + o);
+    gw[j] = *reinterpret_cast<const u32x4*>(grp + 1024 * kG + o);
+  }
+  const int rr = min(r, rw.len - 1);
+  const uintptr_t addr = reinterpret_cast<uintptr_t>(x.beta + 2 * (rw.row0 - x.se.row0 + rr) * x.H);
+  const uint16_t braw16 = *reinterpret_cast<const uint16_t*>(grp + 1024 * kB + 16 * r + (int)(addr & 15));
+  const bool valid = r < rw.len;
+  const float beta = valid ? fast_rcp(1.f + fast_exp2(-kLog2e * bf16_to_f32(braw16))) : 0.f;
+
+  float sq = 0.f, sk = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float q0 = bf16_lo(qw[j][w]), q1 = bf16_hi(qw[j][w]);
+      const float k0 = bf16_lo(kw[j][w]), k1 = bf16_hi(kw[j][w]);
+      sq = fmaf(q0, q0, fmaf(q1, q1, sq));
+      sk = fmaf(k0, k0, fmaf(k1, k1, sk));
+    }
+  sq += __shfl_xor(sq, 16);
+  sq += __shfl_xor(sq, 32);
+  sk += __shfl_xor(sk, 16);
+  sk += __shfl_xor(sk, 32);
+  cr.rq = valid ? p.scale * __builtin_amdgcn_rsqf(sq + kEps) : 0.f;
+  cr.rk = valid ? __builtin_amdgcn_rsqf(sk + kEps) : 0.f;
+  cr.valid = valid;
+  if (cq == 0) reinterpret_cast<float*>(rec + REC_BYTES)[r] = beta;
+
+  cr.accL = f32x4{0.f, 0.f, 0.f, 0.f};
+  cr.accM = f32x4{0.f, 0.f, 0.f, 0.f};
+  chan_block<0>(qw[0], kw[0], gw[0], cr.rq, cr.rk, valid, p.A2, p.lb2, p.s_adt, r, cq, rec, cr.accL, cr.accM);
+#pragma unroll
+  for (int j = 1; j < 4; ++j) {
+    cr.qw[j - 1] = qw[j];
+    cr.kw[j - 1] = kw[j];
+    cr.gw[j - 1] = gw[j];
+  }
+}
+
+// Phases 1 and 2: channel block J (1 or 2).
+template <int J>
+__device__ __forceinline__ void phase_mid(const PrepCtx& p, char* rec, Carry& cr) {
+  chan_block<J>(cr.qw[J - 1], cr.kw[J - 1], cr.gw[J - 1], cr.rq, cr.rk, cr.valid != 0, p.A2, p.lb2, p.s_adt, p.r,
+                p.cq, rec, cr.accL, cr.accM);
+}
+
+// Phase 3: channel block 3, then L^T (to `lt`, for the inverse that the
+// recurrence waves take one step later) and Mqk^T (record).
+__device__ __forceinline__ void phase3(const PrepCtx& p, char* rec, float (*lt)[C + 4], Carry& cr) {
+  chan_block<3>(cr.qw[2], cr.kw[2], cr.gw[2], cr.rq, cr.rk, cr.valid != 0, p.A2, p.lb2, p.s_adt, p.r, p.cq, rec,
+                cr.accL, cr.accM);
+  // lane (c, g) holds rows 4g..4g+3 of column c of L and Mqk
+  const int lane = p.lane, lc = lane & 15, lg = lane >> 4;
+  const float* beta = reinterpret_cast<const float*>(rec + REC_BYTES);
+  float mv[4];
+  f32x4 lv;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int rr = 4 * lg + i;
+    lv[i] = lc < rr ? beta[rr] * cr.accL[i] : 0.f;
+    mv[i] = lc <= rr ? cr.accM[i] : 0.f;
+  }
+  *reinterpret_cast<f32x4*>(&lt[lc][4 * lg]) = lv;   // lt[m][r] = L[r][m]
+  *reinterpret_cast<u32x2*>(rec + REC_MQK + (lc * C + 4 * lg) * 2) = u32x2{pack_f16(mv[0], mv[1]),
+                                                                          pack_f16(mv[2], mv[3])};
+}
+
+// T = (I + L)^-1 diag(beta) of one chunk, columns 4w .. 4w + 3 by recurrence
+// wave w, into the record as T^T.  Forward substitution, exact for a unit
+// lower-triangular matrix: x_r = e_j[r] - sum_{m<r} L[r][m] x_m.  Lane
+// (row j' of 16 lanes, m) owns x_m of column j = 4w + j'; each row's sum over
+// m is a 16-lane DPP reduction, so the 16 sequential rows cost a few vector
+// instructions each and no memory traffic.  L[r][m] for the lane's m comes
+// from lt[m][0..15]; beta from the record's beta area.
+__device__ __forceinline__ void chunk_inverse(const float (*lt)[C + 4], char* rec, int w, int lane) {
+  const int m = lane & 15, j = 4 * w + (lane >> 4);
+  f32x4 l4[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) l4[q] = *reinterpret_cast<const f32x4*>(&lt[m][4 * q]);
+  float x = 0.f;
+#pragma unroll
+  for (int r = 0; r < C; ++r) {
+    float t = l4[r >> 2][r & 3] * x;   // L[r][m] x_m (zero unless m < r)
+    t += dpp_shr(t, 1);                // inclusive sum over the 16 lanes of the row
+    t += dpp_shr(t, 2);
+    t += dpp_shr(t, 4);
+    t += dpp_shr(t, 8);
+    const float xr = (r == j ? 1.f : 0.f) - dpp_bcast15(t);
+    x = m == r ? xr : x;
+  }
+  const float bj = reinterpret_cast<const float*>(rec + REC_BYTES)[j];
+  *reinterpret_cast<_Float16*>(rec + REC_T + (j * C + m) * 2) = (_Float16)(x * bj);   // T^T[j][m] = T[m][j]
+}
+
+// Top of a step: wait until this wave's loads of the current group have
+// landed (at most the loads of the D - 2 later groups may still be in flight;
+// loads complete in issue order, and the output stores, also counted, only
+// make the wait stricter), then the barrier that makes every wave's loads and
+// record writes visible.
+template <int kMax, int D>
+__device__ __forceinline__ void step_sync(int nload) {
+  if (nload == kMax) wait_vmcnt<(D - 2) * kMax>();
+  else wait_vmcnt<(D - 2) * (kMax - 1)>();
+  wait_lgkm0();
+  barrier();
+}
+
+template <int NT, int D>
+__global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
+  using F = FCfg<NT, D>;
+  __shared__ __align__(1024) char groups[D][F::kGroupBytes];
+  __shared__ __align__(16) char recs[kRecSlots][kSlotBytes];
+  __shared__ __align__(16) float lts[2][C][C + 4];   // L^T of chunks c (even / odd), from prep to the inverse
+  __shared__ __align__(16) float s_adt[K];
+
+  const int64_t H = a.H;
+  // XCD-aware placement: id b runs on XCD b % 8; the kTiles tiles of pair
+  // 8 * g + x get ids 8 * (kTiles * g + tile) + x, so they share an L2.
+  const int64_t bid = blockIdx.x, xcd = bid & 7, qb = bid >> 3;
+  const int64_t pair = 8 * (qb / F::kTiles) + xcd;
+  const int tile = (int)(qb % F::kTiles);
+  if (pair >= a.N * H) return;
+  const int64_t slot_id = pair / H;
+  const int h = (int)(pair - slot_id * H);
+  const int v0 = tile * F::kCols;
+  const int n = reinterpret_cast<const int32_t*>(a.ws + a.lay.order)[slot_id];
+  const SeqEntry se = reinterpret_cast<const SeqEntry*>(a.ws + a.lay.seq_table)[n];
+  const int nch = se.nchunks;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, lg = lane >> 4, lc = lane & 15;
+  const bool rec_wave = wave < kRecWaves;
+  // The gate rate and bias, read before any buffer-to-LDS load is issued: the
+  // compiler does not count those loads and would otherwise wait for all of
+  // them at the first use of these values.
+  float A2 = -expf(a.A_log[h]) * kLog2e;   // sigmoid(x) = 1 / (1 + 2^(-x log2 e))
+  asm volatile("" : "+v"(A2));
+  if (tid < K) s_adt[tid] = A2 * a.dt_bias[(int64_t)h * K + tid];   // visible after the first barrier
+
+  const int64_t sbase = ((int64_t)n * H + h) * V * K;   // state [n][h][v][k]
+  const int wc = F::kWaveCols * (rec_wave ? wave : 0);  // first tile column of a recurrence wave
+  const int col0 = v0 + wc;
+  f32x4 Z[8][NT];
+  if (rec_wave) {
+    load_state<NT>(Z, a.s_in, a.state_dtype, sbase, col0, lc, lg);
+    // the state must have arrived before the first buffer-to-LDS load is
+    // issued (otherwise the compiler's wait for it also waits for those)
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) asm volatile("" : "+v"(Z[m][nt]));
+  }
+
+  if (nch > 0) {
+    Seq x;
+    x.q = a.q + ((int64_t)se.row0 * H + h) * K;
+    x.k = a.k + ((int64_t)se.row0 * H + h) * K;
+    x.g = a.g + ((int64_t)se.row0 * H + h) * K;
+    x.beta = reinterpret_cast<const char*>(a.beta + (int64_t)se.row0 * H + h);
+    x.v = a.v + ((int64_t)se.row0 * H + h) * V + v0;
+    x.H = H;
+    x.se = se;
+    GroupPlan<NT, D> pl;
+    make_plan<NT, D>(pl, wave, lane);
+    const int nload = (F::kBlocks - wave + kAllWaves - 1) / kAllWaves;   // this wave's loads per group
+    const uint32_t g0 = lds_addr(groups[0]);
+
+    // The two kinds of wave run separate loops over the same steps (one
+    // barrier each per step), so that neither carries the other's registers.
+    if (rec_wave) {
+      uint16_t* const out_seq = a.out + ((int64_t)se.row0 * H + h) * V + col0;
+      const int64_t out_chunk = (int64_t)C * H * V;
+      const int out_lane = (int)((lc * H) * V) + 4 * lg;
+      u32x2 o_prev[NT];
+#pragma unroll
+      for (int s = -kLead; s < -kLead + D - 1; ++s)   // groups -5 .. D - 7 in flight
+        issue_group<NT, D>(g0 + (s + kLead) * F::kGroupBytes, pl, x, s, wave);
+      int gslot = 0;   // group slot of group s
+      // steps -5 .. -1: the prep waves start the first records; at step -1 the
+      // inverse of chunk 0
+      for (int s = -kLead; s < 0; ++s) {
+        step_sync<F::kMaxLoads, D>(nload);
+        issue_group<NT, D>(g0 + (gslot == 0 ? D - 1 : gslot - 1) * F::kGroupBytes, pl, x, s + D - 1, wave);
+        if (s == -1) chunk_inverse(lts[0], recs[0], wave, lane);
+        gslot = gslot == D - 1 ? 0 : gslot + 1;
+      }
+      int rs = 0;   // record slot of chunk s
+      for (int s = 0; s < nch; ++s) {
+        step_sync<F::kMaxLoads, D>(nload);
+        // every wave is done with group s - 1 and with the record of chunk
+        // s - 1; group s has landed; the record of chunk s is complete
+        issue_group<NT, D>(g0 + (gslot == 0 ? D - 1 : gslot - 1) * F::kGroupBytes, pl, x, s + D - 1, wave);
+        if (s > 0) {   // output of chunk s - 1, a full chunk (only the last chunk is partial)
+          uint16_t* const ob = out_seq + (int64_t)(s - 1) * out_chunk;
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) *reinterpret_cast<u32x2*>(ob + out_lane + 16 * nt) = o_prev[nt];
+        }
+        // T of chunk s + 1 (L^T completed at step s - 1), independent of this
+        // step's chain; past the last chunk it lands in a record slot that no
+        // chunk uses any more
+        const int rs1 = rs == kRecSlots - 1 ? 0 : rs + 1;
+        chunk_inverse(lts[(s + 1) & 1], recs[rs1], wave, lane);
+        Ops<NT> ops;
+        read_ops<NT>(ops, recs[rs], groups[gslot] + 1024 * F::kV, 2 * F::kCols, wc, lane);
+        compute<NT>(Z, ops, o_prev);
+        gslot = gslot == D - 1 ? 0 : gslot + 1;
+        rs = rs1;
+      }
+      wait_vmcnt<0>();   // no load into the ring outlives the workgroup
+      const Rows pr = chunk_rows(se, nch - 1);
+      if (lc < pr.len) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          *reinterpret_cast<u32x2*>(a.out + ((pr.row0 + lc) * H + h) * V + col0 + 16 * nt + 4 * lg) = o_prev[nt];
+      }
+    } else {
+      PrepCtx pc;
+      pc.A2 = A2;
+      pc.lb2 = a.lower_bound * kLog2e;
+      pc.scale = a.scale;
+      pc.s_adt = s_adt;
+      pc.r = lc;
+      pc.cq = lg;
+      pc.lane = lane;
+      Carry cr;
+      const int pw = wave - kRecWaves;   // this prep wave builds the chunks c = pw mod 4
+
+#pragma unroll
+      for (int s = -kLead; s < -kLead + D - 1; ++s)
+        issue_group<NT, D>(g0 + (s + kLead) * F::kGroupBytes, pl, x, s, wave);
+      int gslot = 0;
+      for (int s = -kLead; s < nch; ++s) {
+        step_sync<F::kMaxLoads, D>(nload);
+        issue_group<NT, D>(g0 + (gslot == 0 ? D - 1 : gslot - 1) * F::kGroupBytes, pl, x, s + D - 1, wave);
+        // chunk c (c = pw mod 4) is built in phases 0..3 at steps c - 5 .. c - 2
+        const int ph = (s + kLead - pw) & 3;
+        const int c = s + kLead - ph;
+        if (c >= 0 && c < nch) {
+          // The lane id passes through an empty asm each step, so that the
+          // lane-dependent addresses and constants of the four phases are
+          // computed where they are used instead of being hoisted out of the
+          // loop and held (or spilled) across it.
+          int ln = lane;
+          asm volatile("" : "+v"(ln));
+          pc.r = ln & 15;
+          pc.cq = ln >> 4;
+          pc.lane = ln;
+          char* rec = recs[c % kRecSlots];
+          if (ph == 0) {
+            phase0(pc, groups[gslot], chunk_rows(se, c), x, rec, cr, F::kQ, F::kK, F::kG, F::kB);
+          } else if (ph == 1) {
+            phase_mid<1>(pc, rec, cr);
+          } else if (ph == 2) {
+            phase_mid<2>(pc, rec, cr);
+          } else {
+            phase3(pc, rec, lts[c & 1], cr);
+          }
+        }
+        gslot = gslot == D - 1 ? 0 : gslot + 1;
+      }
+      wait_vmcnt<0>();
+    }
+  }
+
+  if (rec_wave && a.s_out != nullptr) store_state<NT>(Z, a.s_out, a.state_dtype, sbase, col0, lc, lg);
+}
+
+template <int NT, int D>
+hipError_t launch_tiles(const FusedArgs& a, hipStream_t s) {
+  const int64_t pairs = a.N * a.H;
+  const int64_t grid = 8 * FCfg<NT, D>::kTiles * ((pairs + 7) / 8);
+  hipLaunchKernelGGL((fused_kernel<NT, D>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// Value columns per workgroup: 64 (two workgroups per (sequence, head), each
+// building the pair's records itself) while the pairs are few, so that the
+// longest chain of the batch runs at half the per-step work; 128 (one
+// workgroup per pair, each record built once) once two tiles per pair would
+// not all fit on the 256 CUs at once.
+hipError_t launch_fused(const FusedArgs& a, hipStream_t s) {
+  if (a.N * a.H == 0) return hipSuccess;
+#if defined(KDA_FUSED_NT)
+  if (KDA_FUSED_NT == 2) return launch_tiles<2, 3>(a, s);
+  return launch_tiles<1, 4>(a, s);
+#else
+  if (2 * a.N * a.H <= 512) return launch_tiles<1, 4>(a, s);
+  return launch_tiles<2, 3>(a, s);
+#endif
+}
+
+}  // namespace kda

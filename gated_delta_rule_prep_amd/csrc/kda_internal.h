@@ -14,7 +14,7 @@ constexpr int V = 128;    // value channels
 
 // Chunk record, one per (head, chunk), head-major.  Offsets in bytes.
 constexpr int REC_QH = 0;        // Qhat  fp16 [16][128], 32-block channel order (see kPermCh)
-constexpr int REC_NW = 4096;     // -W    fp16 [16][128], same channel order
+constexpr int REC_NK = 4096;     // -Khat fp16 [16][128], same channel order
 constexpr int REC_KB = 8192;     // Kbar  fp16 [16][128], token-major, natural channel order
 constexpr int REC_T = 12288;     // T^T   fp16 [16][16]
 constexpr int REC_MQK = 12800;   // Mqk^T fp16 [16][16]
@@ -124,6 +124,27 @@ struct RecurArgs {
   Layout lay;
 };
 
+// Fused chunk prep + recurrence (one kernel, records kept in LDS): the
+// inputs and outputs of kda_fwd, the scheduler's tables in `ws`.
+struct FusedArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* g;
+  const uint16_t* beta;
+  uint16_t* out;
+  const float* A_log;
+  const float* dt_bias;
+  float scale;
+  float lower_bound;
+  const void* s_in;
+  void* s_out;
+  int state_dtype;      // KDA_DTYPE_* of whichever state is given
+  int64_t N, H;
+  char* ws;
+  Layout lay;
+};
+
 // Single-token step: token n of every sequence is row n of q, k, v, g, beta
 // ([N][H][128], [N][H]) and of out.
 struct DecodeArgs {
@@ -145,6 +166,7 @@ struct DecodeArgs {
 
 hipError_t launch_sched(const SchedArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_fused(const FusedArgs& a, hipStream_t s);
 // The launchers pick the 16- or 32-token kernels by a.lay.chunk.
 hipError_t launch_prep(const PrepArgs& a, hipStream_t s);
 hipError_t launch_recur(const RecurArgs& a, hipStream_t s);

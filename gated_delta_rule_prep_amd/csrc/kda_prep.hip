@@ -22,8 +22,8 @@
 //   Mqk = lower_incl((qn P)(kn Pinv)^T)                 fp32 MFMA 16x16x4
 //   T   = (I + L)^-1 diag(beta)   forward substitution in fp32 (L is strictly
 //                                 lower, so the inverse is exact)
-//   W^T = (kn P)^T T^T            fp16 MFMA 16x16x16, operands by LDS transpose reads
-// The record holds Qhat = qn P, -W, Kbar = kn Pinv gam, T^T, Mqk^T and gam.
+// The record holds Qhat = qn P, -Khat = -kn P, Kbar = kn Pinv gam, T^T, Mqk^T
+// and gam (the recurrence forms T (V - Khat Z), so W = T Khat is never needed).
 // The factor pair (kn P, kn Pinv) spans up to e^(+-80) at lower_bound = -5 (the
 // range argument of P1 §二 2.1): it fits fp32, so L and Mqk are multiplied in
 // fp32 (rounding these factors to a 16-bit type costs about 2^-9 of every
@@ -40,9 +40,7 @@ constexpr int kThreads = 64 * kWaves;
 constexpr float kEps = 1e-6f;
 
 struct __align__(16) WaveSmem {
-  __align__(16) _Float16 kh[C][K + 8];   // Khat = kn P (fp16), token-major, 272-byte rows
   __align__(16) float L[C][C + 4];       // L (fp32), 80-byte rows
-  __align__(16) _Float16 tt[C][C + 8];   // T^T (fp16), 48-byte rows
   float beta[C];
 };
 
@@ -95,6 +93,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
   const float lb2 = a.lower_bound * kLog2e;
   char* rec = a.ws + a.lay.records + ((int64_t)h * a.lay.max_chunks + chunk) * REC_BYTES;
   _Float16* rec_qh = reinterpret_cast<_Float16*>(rec + REC_QH) + r * K;
+  _Float16* rec_nk = reinterpret_cast<_Float16*>(rec + REC_NK) + r * K;
   _Float16* rec_kb = reinterpret_cast<_Float16*>(rec + REC_KB) + r * K;
   float* rec_gam = reinterpret_cast<float*>(rec + REC_GAM);
 
@@ -131,24 +130,17 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
       kb[e] = kI * gam;
       gm[e] = P;
     }
-    // Khat -> LDS (token-major), Kbar -> record (token-major), Qhat -> record
-    // (channels 8cq .. 8cq+7 of 32-block j sit at two runs of 4 positions)
-    u32x4 wkh, wkb;
+    // Kbar -> record (token-major); Qhat and -Khat -> record (channels
+    // 8cq .. 8cq+7 of 32-block j sit at two runs of 4 positions)
+    u32x4 wkb;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      wkh[w] = pack_f16(kh[2 * w], kh[2 * w + 1]);
-      wkb[w] = pack_f16(kb[2 * w], kb[2 * w + 1]);
-    }
-    *reinterpret_cast<u32x4*>(&sm.kh[r][c0]) = wkh;
+    for (int w = 0; w < 4; ++w) wkb[w] = pack_f16(kb[2 * w], kb[2 * w + 1]);
     *reinterpret_cast<u32x4*>(rec_kb + c0) = wkb;
     const int p0 = 32 * j + kPermPos(8 * cq), p1 = 32 * j + kPermPos(8 * cq + 4);
-    u32x2 wq0, wq1;
-    wq0[0] = pack_f16(qh[0], qh[1]);
-    wq0[1] = pack_f16(qh[2], qh[3]);
-    wq1[0] = pack_f16(qh[4], qh[5]);
-    wq1[1] = pack_f16(qh[6], qh[7]);
-    *reinterpret_cast<u32x2*>(rec_qh + p0) = wq0;
-    *reinterpret_cast<u32x2*>(rec_qh + p1) = wq1;
+    *reinterpret_cast<u32x2*>(rec_qh + p0) = u32x2{pack_f16(qh[0], qh[1]), pack_f16(qh[2], qh[3])};
+    *reinterpret_cast<u32x2*>(rec_qh + p1) = u32x2{pack_f16(qh[4], qh[5]), pack_f16(qh[6], qh[7])};
+    *reinterpret_cast<u32x2*>(rec_nk + p0) = u32x2{pack_f16(-kh[0], -kh[1]), pack_f16(-kh[2], -kh[3])};
+    *reinterpret_cast<u32x2*>(rec_nk + p1) = u32x2{pack_f16(-kh[4], -kh[5]), pack_f16(-kh[6], -kh[7])};
     if (r == 15) {   // gam = P of the last token (padded tokens keep G constant)
 #pragma unroll
       for (int e = 0; e < 8; ++e) rec_gam[kGamSlot(c0 + e)] = gm[e];
@@ -192,26 +184,8 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
       t0[w] = pack_f16(x[2 * w] * bj, x[2 * w + 1] * bj);
       t1[w] = pack_f16(x[8 + 2 * w] * bj, x[8 + 2 * w + 1] * bj);
     }
-    *reinterpret_cast<u32x4*>(&sm.tt[jc][0]) = t0;
-    *reinterpret_cast<u32x4*>(&sm.tt[jc][8]) = t1;
     *reinterpret_cast<u32x4*>(rec + REC_T + jc * C * 2) = t0;
     *reinterpret_cast<u32x4*>(rec + REC_T + jc * C * 2 + 16) = t1;
-  }
-  __builtin_amdgcn_wave_barrier();
-
-  // ---- W^T = Khat^T T^T, tile n = channels 16n..16n+15; lane (token c, g) gets
-  // W[c][16n + 4g + i]; -W goes to the record in its permuted channel order
-  const f16x4 bT = lds_read_tr(&sm.tt[0][0], C + 8, lane);
-  _Float16* rec_nw = reinterpret_cast<_Float16*>(rec + REC_NW) + lc * K;
-#pragma unroll
-  for (int n = 0; n < 8; ++n) {
-    const f16x4 aK = lds_read_tr(&sm.kh[0][16 * n], K + 8, lane);
-    const f32x4 w4 = mfma_f16_k16(aK, bT, f32x4{0.f, 0.f, 0.f, 0.f});
-    const int c = 16 * n + 4 * lg;
-    u32x2 ww;
-    ww[0] = pack_f16(-w4[0], -w4[1]);
-    ww[1] = pack_f16(-w4[2], -w4[3]);
-    *reinterpret_cast<u32x2*>(rec_nw + (c & ~31) + kPermPos(c & 31)) = ww;
   }
 }
 

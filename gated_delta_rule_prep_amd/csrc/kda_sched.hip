@@ -79,11 +79,14 @@ __global__ __launch_bounds__(kThreads) void sched_kernel(SchedArgs a) {
   }
   const int32_t total = s_carry;
 
-  // 3. chunk table.  Up to kThreads sequences (one scan tile, still in LDS)
+  // 3. chunk table (the fused path, whose layout has no chunk table, skips
+  // this step and the next).  Up to kThreads sequences (one scan tile, still in LDS)
   // the threads fill each sequence's chunks together, so that one long
   // sequence does not leave a single thread writing all of its entries;
   // beyond that each thread fills the chunks of its own sequences.
-  if (N <= kThreads) {
+  const bool table = a.lay.max_chunks > 0;
+  if (!table) {
+  } else if (N <= kThreads) {
     for (int64_t n = 0; n < N; ++n) {
       const int32_t nch = bad ? 0 : s_scan[n] - (n > 0 ? s_scan[n - 1] : 0);
       const int32_t first = s_scan[n] - nch;
@@ -110,12 +113,12 @@ __global__ __launch_bounds__(kThreads) void sched_kernel(SchedArgs a) {
   // 4. parts: part_first[p] = index of the first chunk whose first token row is
   // at or past p * part_rows (the chunk table is in token order)
   auto part_of = [&](int32_t row0) { return (int)min((int64_t)row0 / a.part_rows, (int64_t)a.parts - 1); };
-  for (int32_t i = tid; i < total; i += kThreads) {
+  for (int32_t i = tid; table && i < total; i += kThreads) {
     const int pi = part_of(chunks[i].row0);
     const int pprev = i > 0 ? part_of(chunks[i - 1].row0) : -1;
     for (int p = pprev + 1; p <= pi; ++p) hdr->part_first[p] = i;
   }
-  if (tid == 0) {
+  if (tid == 0 && table) {
     const int plast = total > 0 ? part_of(chunks[total - 1].row0) : -1;
     for (int p = plast + 1; p <= a.parts; ++p) hdr->part_first[p] = total;
   }

@@ -5,22 +5,25 @@
 // The chunkwise form of the delta-rule recurrence (the second of the two
 // stages in the FlashKDA blog post "FlashKDA：月之暗面开源的 Kimi Delta Attention
 // 高性能内核", §二 2.2), with Z the chunk-start state slice (K x 16 NT), the
-// chunk record (Qhat, -W, Kbar, T, Mqk, gamma) and the chunk's value rows V:
-//   U = T V                      fp16 MFMA 16x16x16
-//   E = U + (-W) Z               fp16 MFMA 16x16x32 chain over the 128 channels
+// chunk record (Qhat, -Khat, Kbar, T, Mqk, gamma) and the chunk's value rows V.
+// The residual E = T V - (T Khat) Z is taken as T (V - Khat Z), so the record
+// needs Khat itself rather than W = T Khat:
+//   R = V + (-Khat) Z            fp16 MFMA 16x16x32 chain over the 128 channels,
+//                                accumulating onto V (fp32)
+//   E = T R                      fp16 MFMA 16x16x16
 //   O^T = Z^T Qhat^T + E^T Mqk^T fp16 MFMA; the same register operands as
 //                                O = Qhat Z + Mqk E with A and B swapped, so
 //                                each lane ends up with four consecutive value
 //                                columns of one token and stores them directly
 //   Z = diag(gam) Z + Kbar^T E   fp16 MFMA 16x16x16, accumulating onto gam * Z
 // Z is converted to fp16 per step for the two products that read it; the state
-// itself stays fp32.  The channel order of Qhat / -W in the record matches the
+// itself stays fp32.  The channel order of Qhat / -Khat in the record matches the
 // rows a lane holds in its two accumulator tiles (kPermCh), so the conversion
 // needs no lane exchange.  The decay factors reach the lanes by DPP row
 // broadcast from a permuted copy of gamma (kGamSlot).
 //
 // Record layout in LDS (byte offsets REC_* of kda_internal.h), swizzled so
-// that the operand reads hit distinct banks: Qhat and -W token row r keeps
+// that the operand reads hit distinct banks: Qhat and -Khat token row r keeps
 // its 16-byte piece p at piece position p ^ r; Kbar row r keeps piece p at
 // p ^ 2 (r % 4); T^T, Mqk^T and gamma are stored as in the HBM record.  The
 // value tile (raw bf16, `val_row_bytes` bytes per token row) keeps piece p of
@@ -56,8 +59,8 @@ __device__ __forceinline__ s16x4 tr_swz(const char* tile, int rowb, int col, int
 template <int NT>
 struct Ops {
   f16x4 aT, am;          // T[lc][4lg..4lg+3], Mqk[lc][4lg..4lg+3]
-  f16x4 bv[NT];          // V[4lg..4lg+3][wc + 16nt + lc] (converted from bf16)
-  f16x8 aw[4], aq[4];    // -W, Qhat row lc, channels of 32-block s at the lane's 8 positions
+  f32x4 v[NT];           // V[4lg..4lg+3][wc + 16nt + lc] (exact from bf16)
+  f16x8 aw[4], aq[4];    // -Khat, Qhat row lc, channels of 32-block s at the lane's 8 positions
   f16x4 ak[8];           // Kbar[4lg..4lg+3][16m + lc]
   f32x2 g2;              // gamma of the rows that this lane hands to its 16-lane row
 };
@@ -74,15 +77,13 @@ __device__ __forceinline__ void read_ops(Ops<NT>& o, const char* rec, const char
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const s16x4 raw = tr_swz(val, val_row_bytes, wc + 16 * nt, lane);
-    f16x4 b;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) b[i] = (_Float16)bf16_to_f32((uint16_t)raw[i]);
-    o.bv[nt] = b;
+    for (int i = 0; i < 4; ++i) o.v[nt][i] = bf16_to_f32((uint16_t)raw[i]);
   }
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const int p = (4 * s + lg) ^ lc;
-    o.aw[s] = *reinterpret_cast<const f16x8*>(rec + REC_NW + 256 * lc + 16 * p);
+    o.aw[s] = *reinterpret_cast<const f16x8*>(rec + REC_NK + 256 * lc + 16 * p);
     o.aq[s] = *reinterpret_cast<const f16x8*>(rec + REC_QH + 256 * lc + 16 * p);
   }
 #pragma unroll
@@ -110,11 +111,11 @@ __device__ __forceinline__ f32x4 decay(f32x4 z, f32x2 g2) {
 // wave), rounded to bf16 and packed.
 template <int NT>
 __device__ __forceinline__ void compute(f32x4 (&Z)[8][NT], const Ops<NT>& o, u32x2 (&out)[NT]) {
-  // ---- U = T V ; E = U + (-W) Z ; O^T = Z^T Qhat^T
-  f32x4 E[NT], O[NT];
+  // ---- R = V + (-Khat) Z ; O^T = Z^T Qhat^T
+  f32x4 R[NT], O[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    E[nt] = mfma_f16_k16(o.aT, o.bv[nt], f32x4{0.f, 0.f, 0.f, 0.f});
+    R[nt] = o.v[nt];
     O[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 #pragma unroll
@@ -127,16 +128,17 @@ __device__ __forceinline__ void compute(f32x4 (&Z)[8][NT], const Ops<NT>& o, u32
         zb[i] = (_Float16)Z[2 * s][nt][i];
         zb[4 + i] = (_Float16)Z[2 * s + 1][nt][i];
       }
-      E[nt] = mfma_f16_k32(o.aw[s], zb, E[nt]);
+      R[nt] = mfma_f16_k32(o.aw[s], zb, R[nt]);
       O[nt] = mfma_f16_k32(zb, o.aq[s], O[nt]);
     }
   }
 
-  // ---- O^T += E^T Mqk^T
+  // ---- E = T R ; O^T += E^T Mqk^T (R's accumulator layout is the B operand
+  // layout of the 16x16x16 product: rows 4lg..4lg+3 of column lc)
   f16x4 eb[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    eb[nt] = f16x4_of(E[nt]);
+    eb[nt] = f16x4_of(mfma_f16_k16(o.aT, f16x4_of(R[nt]), f32x4{0.f, 0.f, 0.f, 0.f}));
     O[nt] = mfma_f16_k16(eb[nt], o.am, O[nt]);
   }
 

@@ -23,10 +23,14 @@ LIB_PATH = os.path.join(_HERE, "libkda.so")
 KDA_OK, KDA_EINVAL, KDA_EDTYPE, KDA_EWORKSPACE, KDA_EUNSUPPORTED, KDA_EHIP = range(6)
 KDA_DTYPE_NONE, KDA_DTYPE_BF16, KDA_DTYPE_FP32 = 0, 1, 2
 KDA_STATUS_OK, KDA_STATUS_BAD_CU_SEQLENS = 0, 1
+KDA_PATH_AUTO, KDA_PATH_SPLIT, KDA_PATH_FUSED = 0, 1, 2
+PATHS = {None: KDA_PATH_AUTO, "auto": KDA_PATH_AUTO, "split": KDA_PATH_SPLIT, "fused": KDA_PATH_FUSED,
+         KDA_PATH_AUTO: KDA_PATH_AUTO, KDA_PATH_SPLIT: KDA_PATH_SPLIT, KDA_PATH_FUSED: KDA_PATH_FUSED}
 CHUNK = 16
 
-EXPORTS = ("kda_fwd", "kda_fwd_profiled", "kda_fwd_ex", "kda_fwd_parts", "kda_decode", "kda_fwd_workspace_bytes",
-           "kda_get_last_error", "kda_version", "kda_fwd_check_status", "kda_workspace_layout", "kda_debug_prep")
+EXPORTS = ("kda_fwd", "kda_fwd_profiled", "kda_fwd_ex", "kda_fwd_parts", "kda_fwd_path", "kda_fwd_num_events",
+           "kda_decode", "kda_fwd_workspace_bytes", "kda_fwd_workspace_bytes_ex", "kda_get_last_error",
+           "kda_version", "kda_fwd_check_status", "kda_workspace_layout", "kda_debug_prep")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError("libkda.so is not built (run gated_delta_rule_prep_amd/build.py or "
@@ -41,11 +45,18 @@ _lib.kda_fwd.argtypes = [_p, _p, _p, _p, _p, ctypes.c_float, _p, _p, _p, ctypes.
 _lib.kda_fwd.restype = ctypes.c_int
 _lib.kda_fwd_profiled.argtypes = _lib.kda_fwd.argtypes + [ctypes.POINTER(ctypes.c_void_p)]
 _lib.kda_fwd_profiled.restype = ctypes.c_int
-_lib.kda_fwd_ex.argtypes = _lib.kda_fwd.argtypes + [ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_void_p),
-                                                     ctypes.c_int]
+_lib.kda_fwd_ex.argtypes = _lib.kda_fwd.argtypes + [ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                     ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
 _lib.kda_fwd_ex.restype = ctypes.c_int
 _lib.kda_fwd_parts.argtypes = [_i64, _i64, ctypes.c_int]
 _lib.kda_fwd_parts.restype = ctypes.c_int
+_lib.kda_fwd_path.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+_lib.kda_fwd_path.restype = ctypes.c_int
+_lib.kda_fwd_num_events.argtypes = [_i64, _i64, ctypes.c_int, ctypes.c_int, ctypes.c_int]
+_lib.kda_fwd_num_events.restype = ctypes.c_int
+_lib.kda_fwd_workspace_bytes_ex.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                            ctypes.c_int]
+_lib.kda_fwd_workspace_bytes_ex.restype = ctypes.c_size_t
 _lib.kda_decode.argtypes = [_p, _p, _p, _p, _p, ctypes.c_float, _p, _p, _p, ctypes.c_float,
                             _p, ctypes.c_int, _p, ctypes.c_int, _i64, _i64, _i64, _i64, _p]
 _lib.kda_decode.restype = ctypes.c_int
@@ -92,8 +103,34 @@ def _raise(code: int):
     raise KDAError(code, msg)
 
 
-def workspace_bytes(B: int, T: int, H: int, num_seqs: int = 0, has_cu_seqlens: bool = False) -> int:
-    return int(_lib.kda_fwd_workspace_bytes(B, T, H, num_seqs, int(has_cu_seqlens)))
+def _path_code(path) -> int:
+    if path not in PATHS:
+        raise KDAValueError(KDA_EINVAL, "path must be None, 'auto', 'split' or 'fused', got %r" % (path,))
+    return PATHS[path]
+
+
+def workspace_bytes(B: int, T: int, H: int, num_seqs: int = 0, has_cu_seqlens: bool = False, chunk=None,
+                    parts=None, path=None) -> int:
+    """Workspace bytes: with no chunk / parts / path, a size that suits every
+    path (kda_fwd_workspace_bytes); otherwise what that configuration needs
+    (kda_fwd_workspace_bytes_ex)."""
+    if chunk is None and parts is None and path is None:
+        return int(_lib.kda_fwd_workspace_bytes(B, T, H, num_seqs, int(has_cu_seqlens)))
+    return int(_lib.kda_fwd_workspace_bytes_ex(B, T, H, num_seqs, int(has_cu_seqlens), int(chunk or 0),
+                                               int(parts or 0), _path_code(path)))
+
+
+def path_used(chunk=None, parts=None, path=None) -> str:
+    """'split' or 'fused': the path kda_fwd_ex takes for these requests."""
+    p = _lib.kda_fwd_path(int(chunk or 0), int(parts or 0), _path_code(path))
+    if p < 0:
+        raise KDAValueError(KDA_EINVAL, "invalid chunk / parts / path combination")
+    return "fused" if p == KDA_PATH_FUSED else "split"
+
+
+def num_events(B: int, T: int, chunk=None, parts=None, path=None) -> int:
+    """Events kda_fwd_ex records for these sizes and requests."""
+    return int(_lib.kda_fwd_num_events(B, T, int(chunk or 0), int(parts or 0), _path_code(path)))
 
 
 def workspace_layout(B: int, T: int, H: int, num_seqs: int = 0, has_cu_seqlens: bool = False,
@@ -133,8 +170,9 @@ def _stream(device: torch.device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def alloc_workspace(B: int, T: int, H: int, num_seqs: int, has_cu: bool, device) -> torch.Tensor:
-    n = workspace_bytes(B, T, H, num_seqs, has_cu)
+def alloc_workspace(B: int, T: int, H: int, num_seqs: int, has_cu: bool, device, chunk=None, parts=None,
+                    path=None) -> torch.Tensor:
+    n = workspace_bytes(B, T, H, num_seqs, has_cu, chunk, parts, path)
     if n == 0:
         raise KDAValueError(KDA_EINVAL, "bad sizes for the workspace: B=%d T=%d H=%d" % (B, T, H))
     return torch.empty(n, dtype=torch.uint8, device=device)
@@ -147,16 +185,18 @@ def parts(B: int, T: int, requested: int = 0) -> int:
 
 def fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state=None, final_state=None,
         cu_seqlens=None, workspace: Optional[torch.Tensor] = None, events=None, parts: Optional[int] = None,
-        chunk: Optional[int] = None):
+        chunk: Optional[int] = None, path=None):
     """Chunked KDA forward into the caller's ``out`` (and ``final_state``).
 
     Shapes and dtypes as in include/kda.h.  Runs on the current stream of the
-    tensors' device.  Returns ``out``.  ``chunk``: None for the library's
-    choice, or 16 / 32 tokens per chunk (kda_fwd_ex).  ``parts``: None for
-    kda_fwd's own choice, or the number of overlapped ranges.  ``events``:
-    optional torch.cuda.Event list (enable_timing=True): four go through
-    kda_fwd_profiled; 2 + 4 P (P = ``parts(B, T, parts or 0)``) go through
-    kda_fwd_ex, which records them around every kernel.
+    tensors' device.  Returns ``out``.  ``path``: None / 'auto' for the
+    library's choice, 'split' or 'fused' (kda_fwd_ex).  ``chunk``: None for
+    the library's choice, or 16 / 32 tokens per chunk (32: split path only).
+    ``parts``: None for one, or the number of overlapped ranges (split path).
+    ``events``: optional torch.cuda.Event list (enable_timing=True): with no
+    chunk / parts / path, four go through kda_fwd_profiled; otherwise
+    ``num_events(B, T, chunk, parts, path)`` go through kda_fwd_ex, which
+    records them around every kernel.
     """
     if q.dim() != 4:
         raise KDAValueError(KDA_EINVAL, "q must be [B, T, H, K]")
@@ -188,22 +228,25 @@ def fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state
             raise KDAValueError(KDA_EINVAL, "all tensors must be on %s" % dev)
     if dev.type != "cuda":
         raise KDAValueError(KDA_EINVAL, "tensors must be on a HIP device, got %s" % dev)
-    if workspace is None:
-        workspace = alloc_workspace(B, T, H, N, cu_seqlens is not None, dev)
+    path_c = _path_code(path)
+    if workspace is None:   # just what this call's path needs
+        workspace = alloc_workspace(B, T, H, N, cu_seqlens is not None, dev, chunk, parts,
+                                    "auto" if path is None else path)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(out),
             _ptr(A_log), _ptr(dt_bias), float(lower_bound), _ptr(initial_state),
             _state_code(initial_state), _ptr(final_state), _state_code(final_state),
             _ptr(cu_seqlens), N, B, T, H, K, V, _ptr(workspace), workspace.numel())
     with torch.cuda.device(dev):
-        if events is None and parts is None and chunk is None:
+        plain = parts is None and chunk is None and path is None
+        if events is None and plain:
             rc = _lib.kda_fwd(*args, _stream(dev))
-        elif parts is None and chunk is None and len(events) == 4:
+        elif plain and len(events) == 4:
             ev = (ctypes.c_void_p * 4)(*[e.cuda_event for e in events])
             rc = _lib.kda_fwd_profiled(*args, _stream(dev), ev)
         else:
             n = 0 if events is None else len(events)
             ev = None if events is None else (ctypes.c_void_p * n)(*[e.cuda_event for e in events])
-            rc = _lib.kda_fwd_ex(*args, _stream(dev), int(chunk or 0), int(parts or 0), ev, n)
+            rc = _lib.kda_fwd_ex(*args, _stream(dev), int(chunk or 0), int(parts or 0), path_c, ev, n)
     if rc != KDA_OK:
         _raise(rc)
     return out

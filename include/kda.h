@@ -80,15 +80,31 @@ extern "C" {
 /* Chunk size of the chunked form (P1 §二 2.1 uses 16). */
 #define KDA_CHUNK 16
 
+/* Execution paths (kda_fwd_ex).  Both compute the same chunked form; their
+   results differ only in rounding.
+   KDA_PATH_SPLIT: the two stages of P1 §二 2.2 as two kernels, the chunk
+     records handed over through the workspace in HBM (16- or 32-token chunks,
+     optional overlap of the stages by parts);
+   KDA_PATH_FUSED: one kernel per (sequence, head, value tile) that builds each
+     chunk's record in LDS a few chunks ahead of the recurrence that consumes
+     it, so the records never reach HBM (16-token chunks, one part);
+   KDA_PATH_AUTO: the library's choice (the split path: on MI355X the fused
+     kernel is faster only for batches of many short sequences, and the
+     longest sequence of a cu_seqlens batch is not known on the host). */
+#define KDA_PATH_AUTO 0
+#define KDA_PATH_SPLIT 1
+#define KDA_PATH_FUSED 2
+
 /*
  * kda_fwd -- enqueue the chunked KDA forward pass on `stream`.
  *
- * Work is done by three kernels on `stream`: a scheduler that turns
- * cu_seqlens into a chunk table and a longest-first work order, a
- * token-parallel chunk-prep kernel (gate activation, L2 norm, in-chunk decay,
- * the L / Mqk matrices and the 16 x 16 unit-lower-triangular inverse; P1 §二
- * 2.2 first stage) and a chunk-recurrence kernel (the chunk-by-chunk delta-rule
- * state update and the output; P1 §二 2.2 second stage).
+ * The work is a scheduler kernel that turns cu_seqlens into per-sequence
+ * tables and a longest-first work order, then the two stages of P1 §二 2.2:
+ * chunk prep (gate activation, L2 norm, in-chunk decay, the L / Mqk matrices
+ * and the 16 x 16 unit-lower-triangular inverse) and the chunk recurrence (the
+ * chunk-by-chunk delta-rule state update and the output).  kda_fwd runs them
+ * on the split path (two kernels, chunk records in the workspace);
+ * kda_fwd_ex selects the path.
  *
  * initial_state / final_state: NULL with dtype KDA_DTYPE_NONE, or a pointer
  * with KDA_DTYPE_BF16 / KDA_DTYPE_FP32.  When both are given their dtypes must
@@ -97,10 +113,11 @@ extern "C" {
  * other overlap between inputs and outputs is undefined.
  * cu_seqlens: NULL, or num_seqs + 1 int64 prefix sums on the device (B == 1).
  * Its contents are checked on the device (see kda_fwd_check_status).
- * workspace: at least kda_fwd_workspace_bytes(B, T, H, num_seqs, cu != NULL)
- * bytes of device memory, 256-byte aligned (chunk tables, chunk records and an
- * fp32 state per (sequence, head) for the hand-over between parts).  Its
- * contents are scratch between calls except for the status word.
+ * workspace: device memory, 256-byte aligned, of at least
+ * kda_fwd_workspace_bytes_ex(B, T, H, num_seqs, cu != NULL, 0, 0, KDA_PATH_AUTO)
+ * bytes (tables and the chunk records, about 864 B per token-head) --
+ * kda_fwd_workspace_bytes gives a size that suits every path.  Its contents
+ * are scratch between calls except for the status word.
  * stream: a hipStream_t (NULL = the default stream).
  *
  * With no tokens (B * T == 0) the token tensors q, k, v, g, beta and out are
@@ -118,12 +135,12 @@ int kda_fwd(const void* q, const void* k, const void* v, const void* g, const vo
 
 /*
  * kda_fwd_profiled -- kda_fwd that also records events[0..3] on `stream`:
- * before the scheduler, before the first prep kernel, after the last prep
- * kernel is enqueued (when the recurrence runs on the second stream, parts
- * still being computed there are not covered), and after the whole call, so a
- * caller can time the stages with hipEventElapsedTime.  Same arguments,
- * checks and results as kda_fwd; the four events are created and owned by
- * the caller.  kda_fwd_ex gives per-kernel events.
+ * before the scheduler, after it, after the chunk prep (on the fused path,
+ * where prep and recurrence are one kernel, this is event [1] again) and
+ * after the whole call, so a caller can time the stages with
+ * hipEventElapsedTime.  Same arguments, checks and results as kda_fwd; the
+ * four events are created and owned by the caller.  kda_fwd_ex gives
+ * per-kernel events.
  */
 int kda_fwd_profiled(const void* q, const void* k, const void* v, const void* g, const void* beta,
                      float scale, void* out, const float* A_log, const float* dt_bias, float lower_bound,
@@ -133,8 +150,15 @@ int kda_fwd_profiled(const void* q, const void* k, const void* v, const void* g,
                      size_t workspace_bytes, hipStream_t stream, hipEvent_t events[4]);
 
 /*
- * kda_fwd_ex -- kda_fwd with the chunk size and the overlap of its two stages
- * under the caller's control, and optional per-kernel events.
+ * kda_fwd_ex -- kda_fwd with the execution path, the chunk size and the
+ * overlap of the two stages under the caller's control, and optional
+ * per-kernel events.
+ *
+ * path: KDA_PATH_AUTO (the split path), KDA_PATH_SPLIT or KDA_PATH_FUSED
+ * (chunk 0 or 16 and parts 0 or 1 only; otherwise KDA_EINVAL).  The workspace
+ * must hold kda_fwd_workspace_bytes_ex(..., chunk, parts, path) bytes: the
+ * split path keeps its chunk records there (about 864 B per token-head at
+ * chunk 16), the fused path only the per-sequence tables.
  *
  * chunk: 0 (the library's choice, as kda_fwd), 16 or 32 tokens per chunk.
  * The pages use 16 (P1 §二 2.1) so that the in-chunk decay factors stay in
@@ -157,11 +181,13 @@ int kda_fwd_profiled(const void* q, const void* k, const void* v, const void* g,
  * to 8.  The split into two stages and their roles follow P1 §二
  * 2.2; overlapping them is this library's addition.
  *
- * events: NULL (num_events ignored) or num_events = 2 + 4 P caller-owned
- * events, P = kda_fwd_parts(B, T, parts): [0] before the scheduler, [1] after
- * it, [2 + 2p] / [3 + 2p] before / after the prep kernel of part p (on
- * `stream`), [2 + 2P + 2p] / [3 + 2P + 2p] before / after the recurrence of
- * part p (on the stream it runs on).  A wrong count returns KDA_EINVAL.
+ * events: NULL (num_events ignored) or kda_fwd_num_events(B, T, chunk, parts,
+ * path) caller-owned events.  Split path (P = kda_fwd_parts(B, T, parts)):
+ * 2 + 4 P events, [0] before the scheduler, [1] after it, [2 + 2p] / [3 + 2p]
+ * before / after the prep kernel of part p (on `stream`), [2 + 2P + 2p] /
+ * [3 + 2P + 2p] before / after the recurrence of part p (on the stream it runs
+ * on).  Fused path: 4 events, [0] / [1] around the scheduler, [2] / [3] around
+ * the fused kernel.  A wrong count returns KDA_EINVAL.
  * Calls on one device that use the second stream are serialised on the host
  * by a per-device lock while they enqueue.
  */
@@ -170,10 +196,17 @@ int kda_fwd_ex(const void* q, const void* k, const void* v, const void* g, const
                const void* initial_state, int initial_state_dtype, void* final_state, int final_state_dtype,
                const int64_t* cu_seqlens, int64_t num_seqs, int64_t B, int64_t T, int64_t H, int64_t K,
                int64_t V, void* workspace, size_t workspace_bytes, hipStream_t stream, int chunk,
-               int parts, hipEvent_t* events, int num_events);
+               int parts, int path, hipEvent_t* events, int num_events);
 
 /* Number of parts kda_fwd_ex uses for these sizes and `parts` request (0 on bad input). */
 int kda_fwd_parts(int64_t B, int64_t T, int parts);
+
+/* Path (KDA_PATH_SPLIT or KDA_PATH_FUSED) that kda_fwd_ex takes for these
+   requests, or -1 if they are invalid together. */
+int kda_fwd_path(int chunk, int parts, int path);
+
+/* Events kda_fwd_ex takes for these sizes and requests (0 on bad input). */
+int kda_fwd_num_events(int64_t B, int64_t T, int chunk, int parts, int path);
 
 /*
  * kda_decode -- enqueue one recurrent step (one new token per sequence) on
@@ -194,11 +227,17 @@ int kda_decode(const void* q, const void* k, const void* v, const void* g, const
                int64_t N, int64_t H, int64_t K, int64_t V, hipStream_t stream);
 
 /*
- * Workspace bytes kda_fwd needs for these sizes (0 if the sizes are invalid).
- * num_seqs is ignored when has_cu_seqlens is 0 (then N = B).
+ * Workspace bytes that suit kda_fwd and every kda_fwd_ex path and chunk size
+ * for these sizes (0 if the sizes are invalid).  num_seqs is ignored when
+ * has_cu_seqlens is 0 (then N = B).
  */
 size_t kda_fwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t num_seqs,
                                int has_cu_seqlens);
+
+/* Workspace bytes for one kda_fwd_ex configuration (chunk, parts, path as
+   there; 0 if invalid).  The fused path needs only the per-sequence tables. */
+size_t kda_fwd_workspace_bytes_ex(int64_t B, int64_t T, int64_t H, int64_t num_seqs, int has_cu_seqlens,
+                                  int chunk, int parts, int path);
 
 /* Thread-local description of the last nonzero return on this thread. */
 const char* kda_get_last_error(void);
@@ -223,7 +262,7 @@ int kda_fwd_check_status(const void* workspace, hipStream_t stream, int* status)
  *              offsets[3] + (h * offsets[5] + c) * offsets[4],
  * offsets[4] = bytes per record, offsets[5] = chunk capacity (floor(B*T/chunk) + N),
  * offsets[6] = total bytes.  Returns KDA_OK or KDA_EINVAL.
- * Record layout for chunk 16 (bytes): [0, 4096) Qhat fp16 [16][128]; [4096, 8192) -W fp16
+ * Record layout for chunk 16 (bytes): [0, 4096) Qhat fp16 [16][128]; [4096, 8192) -Khat fp16
  * [16][128]; both with the channels of each 32-block stored in the order
  * {0-3, 16-19, 4-7, 20-23, 8-11, 24-27, 12-15, 28-31}; [8192, 12288) Kbar fp16
  * [16][128] (token-major, natural channel order); [12288, 12800) T^T fp16
@@ -240,7 +279,7 @@ int kda_workspace_layout(int64_t B, int64_t T, int64_t H, int64_t num_seqs, int 
                          int64_t offsets[7]);
 
 /*
- * kda_debug_prep -- test-only: enqueue the scheduler and chunk-prep kernels
+ * kda_debug_prep -- test-only: enqueue the scheduler and the split path's chunk-prep kernels
  * alone (same arguments as kda_fwd minus v, out and the states, plus the
  * chunk size, 16 or 32), leaving the chunk table and records in `workspace`
  * for inspection.

@@ -50,7 +50,12 @@ def state_torch_dtype(inp):
     return torch.bfloat16 if inp.state_dtype == "bf16" else torch.float32
 
 
-def run_gpu(inp, device="cuda", d=None, workspace=None, out=None, final=None, parts=None, chunk=None):
+# (path, chunk) variants of kda_fwd_ex that the parity tests cover
+VARIANTS = [("fused", 16), ("split", 16), ("split", 32)]
+VARIANT_IDS = ["%s%d" % v for v in VARIANTS]
+
+
+def run_gpu(inp, device="cuda", d=None, workspace=None, out=None, final=None, parts=None, chunk=None, path=None):
     from gated_delta_rule_prep_amd import kda
     if d is None:
         d = device_inputs(inp, device)
@@ -61,7 +66,7 @@ def run_gpu(inp, device="cuda", d=None, workspace=None, out=None, final=None, pa
         final = torch.full((inp.N, H, V, inp.K), float("nan"), dtype=state_torch_dtype(inp), device=device)
     kda.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], inp.scale, out, d["A_log"], d["dt_bias"],
             inp.lower_bound, initial_state=d["initial_state"], final_state=final,
-            cu_seqlens=d["cu_seqlens"], workspace=workspace, parts=parts, chunk=chunk)
+            cu_seqlens=d["cu_seqlens"], workspace=workspace, parts=parts, chunk=chunk, path=path)
     return out, final
 
 

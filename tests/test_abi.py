@@ -31,7 +31,8 @@ def test_header_codes_match_binding():
     src = open(HEADER).read()
     for name, val in [("KDA_OK", 0), ("KDA_EINVAL", 1), ("KDA_EDTYPE", 2), ("KDA_EWORKSPACE", 3),
                       ("KDA_EUNSUPPORTED", 4), ("KDA_EHIP", 5), ("KDA_DTYPE_NONE", 0), ("KDA_DTYPE_BF16", 1),
-                      ("KDA_DTYPE_FP32", 2), ("KDA_STATUS_BAD_CU_SEQLENS", 1), ("KDA_CHUNK", 16)]:
+                      ("KDA_DTYPE_FP32", 2), ("KDA_STATUS_BAD_CU_SEQLENS", 1), ("KDA_CHUNK", 16),
+                      ("KDA_PATH_AUTO", 0), ("KDA_PATH_SPLIT", 1), ("KDA_PATH_FUSED", 2)]:
         m = re.search(r"#define\s+%s\s+(\d+)" % name, src)
         assert m and int(m.group(1)) == val, name
         if hasattr(kda, name):
@@ -112,7 +113,7 @@ def call(**over):
     (dict(s0=FAKE, s0_dt=0), kda.KDA_EDTYPE),                 # pointer without dtype
     (dict(s0=None, s0_dt=1), kda.KDA_EDTYPE),                 # dtype without pointer
     (dict(s0=FAKE, s0_dt=1, s1=FAKE, s1_dt=2), kda.KDA_EDTYPE),  # dtypes differ
-    (dict(ws_bytes=1024), kda.KDA_EWORKSPACE),
+    (dict(ws_bytes=700), kda.KDA_EWORKSPACE),
 ])
 def test_host_validation_rejects(over, code):
     rc = call(**over)
@@ -147,7 +148,7 @@ def test_python_binding_rejects_bad_tensors():
         kda.fwd(q, q, v, q, b, 0.1, v.clone(), A, dt, -5.0)
 
 
-def call_ex(parts, events, n_events, chunk=0, **over):
+def call_ex(parts, events, n_events, chunk=0, path=0, **over):
     a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, scale=0.088, out=FAKE, A_log=FAKE, dt_bias=FAKE,
              lb=-5.0, s0=None, s0_dt=0, s1=None, s1_dt=0, cu=None, N=0, B=1, T=64, H=2, K=128, V=128,
              ws=WS, ws_bytes=1 << 40, stream=None)
@@ -155,7 +156,7 @@ def call_ex(parts, events, n_events, chunk=0, **over):
     return kda.lib().kda_fwd_ex(a["q"], a["k"], a["v"], a["g"], a["beta"], a["scale"], a["out"], a["A_log"],
                                 a["dt_bias"], a["lb"], a["s0"], a["s0_dt"], a["s1"], a["s1_dt"], a["cu"],
                                 a["N"], a["B"], a["T"], a["H"], a["K"], a["V"], a["ws"], a["ws_bytes"],
-                                a["stream"], chunk, parts, events, n_events)
+                                a["stream"], chunk, parts, path, events, n_events)
 
 
 def test_parts_choice():
@@ -176,6 +177,40 @@ def test_fwd_ex_rejects_bad_parts_and_event_counts():
     assert call_ex(2, None, 0, q=None) == kda.KDA_EINVAL
     for bad in (8, 17, 64, -16):
         assert call_ex(1, None, 0, chunk=bad) == kda.KDA_EINVAL and "chunk" in kda.last_error()
+
+
+def test_path_choice_events_and_workspace():
+    """Which path a kda_fwd_ex request takes, how many events it records and
+    how much workspace it needs, and the requests it rejects on the host."""
+    assert kda.path_used() == "split"                                   # the library's own choice
+    assert kda.path_used(chunk=16) == "split" and kda.path_used(parts=1) == "split"
+    assert kda.path_used(chunk=32) == "split" and kda.path_used(parts=2) == "split"
+    assert kda.path_used(path="split") == "split" and kda.path_used(path="fused", chunk=16) == "fused"
+    assert kda.path_used(path="fused", parts=1) == "fused"
+    for bad in (dict(path="fused", chunk=32), dict(path="fused", parts=3), dict(path=7), dict(chunk=24)):
+        with pytest.raises(ValueError):
+            kda.path_used(**bad)
+    assert kda.num_events(1, 8192, path="fused") == 4 and kda.num_events(1, 8192) == 6
+    assert kda.num_events(1, 8192, parts=3) == 2 + 4 * 3
+    assert kda.lib().kda_fwd_num_events(1, 64, 32, 0, 2) == 0         # fused cannot take 32-token chunks
+    # the fused path keeps only the per-sequence tables; the split path its records
+    fused = kda.workspace_bytes(1, 8192, 96, path="fused")
+    split = kda.workspace_bytes(1, 8192, 96, path="split")
+    assert 0 < fused <= 4096 and fused % 256 == 0
+    assert split == kda.workspace_layout(1, 8192, 96, chunk=16)["total"]
+    assert kda.workspace_bytes(1, 8192, 96, chunk=32) == kda.workspace_layout(1, 8192, 96, chunk=32)["total"]
+    assert kda.workspace_bytes(1, 8192, 96) >= max(fused, split)
+    assert kda.workspace_bytes(1, 8192, 96, 100000, True, path="fused") >= 100000 * 20
+    assert kda.lib().kda_fwd_workspace_bytes_ex(1, 64, 2, 0, 0, 32, 0, 2) == 0
+    # a fused call is rejected when its workspace is smaller than that, and the
+    # fused path refuses what it cannot run; all on the host
+    assert call_ex(0, None, 0, path=2, ws_bytes=fused - 1, T=8192, H=96) == kda.KDA_EWORKSPACE
+    assert call_ex(0, None, 0, chunk=32, path=2) == kda.KDA_EINVAL and "fused" in kda.last_error()
+    assert call_ex(2, None, 0, path=2) == kda.KDA_EINVAL
+    assert call_ex(0, None, 0, path=3) == kda.KDA_EINVAL
+    ev = (ctypes.c_void_p * 6)(*([FAKE.value] * 6))
+    assert call_ex(0, ev, 6, path=2) == kda.KDA_EINVAL and "events" in kda.last_error()   # fused takes 4
+    assert call_ex(0, None, 0, path=2, dt_bias=ctypes.c_void_p(0x1004)) == kda.KDA_EINVAL
 
 
 def test_layout_for_both_chunk_sizes():

@@ -11,7 +11,7 @@ import torch
 
 import oracle
 from gated_delta_rule_prep_amd.inputs import configs, make_inputs, ragged_lengths, f32_to_bf16_bits
-from tests.kda_gpu import assert_close, device_inputs, run_gpu, say, to_f64
+from tests.kda_gpu import VARIANT_IDS, VARIANTS, assert_close, device_inputs, run_gpu, say, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -30,10 +30,10 @@ def oracle_run(inp, heads=None):
                           output_final_state=True, cu_seqlens=inp.cu_seqlens)
 
 
-def check(inp, heads=None, tag="", chunk=None):
-    say("case %s B=%d T=%d H=%d N=%d state=%s lb=%g chunk=%s" % (tag or inp.name, inp.B, inp.T, inp.H, inp.N,
-                                                               inp.state_dtype, inp.lower_bound, chunk))
-    out, fin = run_gpu(inp, chunk=chunk)
+def check(inp, heads=None, tag="", chunk=None, path=None):
+    say("case %s B=%d T=%d H=%d N=%d state=%s lb=%g path=%s chunk=%s" % (
+        tag or inp.name, inp.B, inp.T, inp.H, inp.N, inp.state_dtype, inp.lower_bound, path, chunk))
+    out, fin = run_gpu(inp, chunk=chunk, path=path)
     torch.cuda.synchronize()
     ref_o, ref_f = oracle_run(inp, heads)
     hs = list(range(inp.H)) if heads is None else heads
@@ -57,40 +57,50 @@ SMALL = [
 ]
 
 
-@pytest.mark.parametrize("chunk", [16, 32])
+@pytest.mark.parametrize("path,chunk", VARIANTS, ids=VARIANT_IDS)
 @pytest.mark.parametrize("i", range(len(SMALL)))
-def test_small_parity(i, chunk):
+def test_small_parity(i, path, chunk):
     kw = dict(SMALL[i])
     inp = make_inputs(**kw)
-    check(inp, tag="small%d" % i, chunk=chunk)
+    check(inp, tag="small%d" % i, chunk=chunk, path=path)
 
 
-@pytest.mark.parametrize("chunk", [16, 32])
+@pytest.mark.parametrize("path,chunk", VARIANTS, ids=VARIANT_IDS)
 @pytest.mark.parametrize("ci", range(5))
-def test_config_parity(ci, chunk):
+def test_config_parity(ci, path, chunk):
     cfg = configs()[ci]
     inp = cfg.make()
     heads = None if inp.H <= 4 else sorted({0, 1, inp.H // 2, inp.H - 1})
-    check(inp, heads, tag="config%d %s" % (ci, cfg.name), chunk=chunk)
+    check(inp, heads, tag="config%d %s" % (ci, cfg.name), chunk=chunk, path=path)
 
 
-@pytest.mark.parametrize("chunk", [16, 32])
-def test_deterministic_bitwise(chunk):
+def test_fused_many_pairs_parity():
+    """More (sequence, head) pairs than two 64-column tiles each can place on
+    the 256 CUs at once: the fused path then runs one workgroup per pair
+    with 128 columns; checked on sampled heads of a varlen batch."""
+    lens = [5, 300, 16, 77, 1, 130, 64, 33]
+    inp = make_inputs(1, sum(lens), 40, seed=110, state_dtype="bf16", seq_lens=lens)
+    assert 2 * inp.N * inp.H > 512
+    check(inp, [0, 7, 21, 39], tag="many-pairs", path="fused")
+
+
+@pytest.mark.parametrize("path,chunk", VARIANTS, ids=VARIANT_IDS)
+def test_deterministic_bitwise(path, chunk):
     inp = make_inputs(1, 500, 4, seed=200, state_dtype="fp32")
-    say("case determinism T=500 H=4 chunk=%d" % chunk)
-    o1, f1 = run_gpu(inp, chunk=chunk)
-    o2, f2 = run_gpu(inp, chunk=chunk)
+    say("case determinism T=500 H=4 path=%s chunk=%d" % (path, chunk))
+    o1, f1 = run_gpu(inp, chunk=chunk, path=path)
+    o2, f2 = run_gpu(inp, chunk=chunk, path=path)
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
     assert torch.equal(f1, f2)
 
 
-@pytest.mark.parametrize("chunk", [16, 32])
-def test_varlen_equals_separate_calls_bitwise(chunk):
+@pytest.mark.parametrize("path,chunk", VARIANTS, ids=VARIANT_IDS)
+def test_varlen_equals_separate_calls_bitwise(path, chunk):
     lens = [1, 15, 17, 33, 130, 60]
     inp = make_inputs(1, sum(lens), 3, seed=201, state_dtype="bf16", seq_lens=lens)
-    say("case varlen-vs-separate lens=%s chunk=%d" % (lens, chunk))
-    out, fin = run_gpu(inp, chunk=chunk)
+    say("case varlen-vs-separate lens=%s path=%s chunk=%d" % (lens, path, chunk))
+    out, fin = run_gpu(inp, chunk=chunk, path=path)
     cu = inp.cu_seqlens
     for n in range(len(lens)):
         a, b = int(cu[n]), int(cu[n + 1])
@@ -99,7 +109,7 @@ def test_varlen_equals_separate_calls_bitwise(chunk):
             setattr(sub, f, np.ascontiguousarray(getattr(inp, f)[:, a:b]))
         sub.A_log, sub.dt_bias = inp.A_log, inp.dt_bias
         sub.initial_state = np.ascontiguousarray(inp.initial_state[n:n + 1])
-        o, f = run_gpu(sub, chunk=chunk)
+        o, f = run_gpu(sub, chunk=chunk, path=path)
         torch.cuda.synchronize()
         assert torch.equal(o.view(torch.int16), out[:, a:b].view(torch.int16)), n
         assert torch.equal(f[0].view(torch.int16), fin[n].view(torch.int16)), n
@@ -200,7 +210,7 @@ def test_parts_bitwise_equal_one_part(i, chunk):
     inp = make_inputs(**PART_CASES[i])
     d = device_inputs(inp)
     say("case parts%d B=%d T=%d H=%d N=%d chunk=%d" % (i, inp.B, inp.T, inp.H, inp.N, chunk))
-    o1, f1 = run_gpu(inp, d=d, parts=1, chunk=chunk)
+    o1, f1 = run_gpu(inp, d=d, parts=1, chunk=chunk, path="split")
     torch.cuda.synchronize()
     ref_o, ref_f = oracle_run(inp)
     assert_close(to_f64(o1), ref_o, "out")
@@ -208,7 +218,7 @@ def test_parts_bitwise_equal_one_part(i, chunk):
         assert_close(to_f64(f1), ref_f, "final_state", inp.state_dtype)
     for P in (2, 3, 5, 8):
         say("  parts=%d" % P)
-        o, f = run_gpu(inp, d=d, parts=P, chunk=chunk)
+        o, f = run_gpu(inp, d=d, parts=P, chunk=chunk, path="split")
         torch.cuda.synchronize()
         assert torch.equal(o.view(torch.int16), o1.view(torch.int16)), P
         if inp.output_final_state:
@@ -223,7 +233,7 @@ def test_parts_inplace_state_and_events():
     inp = make_inputs(1, 700, 2, seed=304, state_dtype="fp32")
     d = device_inputs(inp)
     say("case parts in-place + events")
-    o_ref, f_ref = run_gpu(inp, d=d, parts=1)
+    o_ref, f_ref = run_gpu(inp, d=d, parts=1, path="split")
     st = d["initial_state"].clone()
     out = torch.empty_like(o_ref)
     P = kda.parts(1, 700, 4)

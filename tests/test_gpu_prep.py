@@ -39,8 +39,8 @@ def decode_record(rec, C):
     """Record fields as natural-order float64 arrays (layouts in include/kda.h)."""
     f16 = lambda o, shape: rec[o:o + 2 * int(np.prod(shape))].view(np.float16).astype(np.float64).reshape(shape)
     gam = lambda o: rec[o:o + 512].view(np.float32).astype(np.float64)[GAM_SLOT]
-    if C == 16:
-        return dict(Qh=unpermute(f16(0, (16, 128))), W=-unpermute(f16(4096, (16, 128))), Kb=f16(8192, (16, 128)),
+    if C == 16:   # the 16-token record holds -Khat (the recurrence forms T (V - Khat Z))
+        return dict(Qh=unpermute(f16(0, (16, 128))), Kh=-unpermute(f16(4096, (16, 128))), Kb=f16(8192, (16, 128)),
                     T=f16(12288, (16, 16)).T, M=f16(12800, (16, 16)).T, gamma=gam(13312))
     return dict(Qh=unpermute(f16(0, (32, 128))), W=-unpermute(f16(8192, (32, 128))), Kb=f16(16384, (32, 128)),
                 T=unpermute(f16(24576, (32, 32)), PERM32), M=unpermute(f16(26624, (32, 32)), PERM32),
@@ -98,9 +98,13 @@ def test_chunk_table_and_records_match_chunked_form(C):
             off = lay["records"] + (h * lay["max_chunks"] + ci) * R
             full = decode_record(buf[off:off + R], C)
             got = {k: (v if k == "gamma" else v[:ln, :ln] if k in ("T", "M") else v[:ln]) for k, v in full.items()}
-            ref = dict(Qh=P["Qh"], W=P["T"] @ P["Kh"], Kb=P["Kb"], T=P["T"], M=P["M"], gamma=P["gamma"])
+            ref = dict(Qh=P["Qh"], Kb=P["Kb"], T=P["T"], M=P["M"], gamma=P["gamma"])
+            if C == 16:
+                ref["Kh"] = P["Kh"]
+            else:
+                ref["W"] = P["T"] @ P["Kh"]
             # padded rows / columns of a partial chunk are exactly zero
-            for key in ("Qh", "W", "Kb", "T", "M"):
+            for key in ("Qh", "Kh" if C == 16 else "W", "Kb", "T", "M"):
                 assert np.all(full[key][ln:] == 0), key
             assert np.all(full["T"][:, ln:] == 0) and np.all(full["M"][:, ln:] == 0)
             # structure: T lower triangular, Mqk lower triangular incl. diagonal
@@ -110,4 +114,5 @@ def test_chunk_table_and_records_match_chunked_form(C):
                 worst[key] = max(worst.get(key, 0.0), e)
     say("  worst relative max error per record field: %s" % {k: "%.2e" % v for k, v in worst.items()})
     assert worst["Qh"] < 2e-3 and worst["Kb"] < 2e-3 and worst["gamma"] < 1e-5
-    assert worst["T"] < 1e-2 and worst["M"] < 1e-2 and worst["W"] < 1e-2
+    assert worst["T"] < 1e-2 and worst["M"] < 1e-2
+    assert worst["Kh"] < 2e-3 if C == 16 else worst["W"] < 1e-2
