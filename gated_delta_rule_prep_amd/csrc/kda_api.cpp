@@ -7,6 +7,7 @@
 // [N, H, V, K]; without it each batch row is a sequence.  lower_bound lies in
 // [-5, 0] (the same table).  Every check runs on the host before any HIP call.
 #include <cmath>
+#include <cstddef>
 #include <cstdarg>
 #include <cstdio>
 #include <algorithm>
@@ -173,18 +174,20 @@ int default_chunk() { return C; }
 
 namespace {
 
-// Path a kda_fwd_ex call takes (KDA_PATH_SPLIT / KDA_PATH_FUSED), or -1.
-// The library's own choice is the split path.  Measured on MI355X (T = 8192,
-// K = V = 128): the fused kernel is faster for batches of many short
-// sequences (8 x 1024 tokens, H = 96: 0.45 ms against 0.66) but slower
-// whenever one sequence is long (one 8192-token sequence: 0.93 ms against
-// 0.68; 12 ragged sequences with one of ~6000 tokens: 0.97 against 0.71),
-// and the longest sequence is only known on the device.
+// Path a kda_fwd_ex call takes: KDA_PATH_SPLIT, KDA_PATH_FUSED, KDA_PATH_AUTO
+// (both paths enqueued, the scheduler kernel picks one from the sequence
+// lengths), or -1.  Measured on MI355X (T = 8192, K = V = 128): the fused
+// kernel is faster for batches of many short sequences (8 x 1024 tokens,
+// H = 96: 0.45 ms against 0.66) but slower whenever one sequence is long (one
+// 8192-token sequence: 0.93 ms against 0.68; 12 ragged sequences with one of
+// ~6000 tokens: 0.97 against 0.71), and the lengths are only known on the
+// device.  The library chooses only where both paths can run (16-token
+// chunks, one part).
 int resolve_path(int chunk, int parts, int path) {
   if (chunk != 0 && chunk != kda::C && chunk != kda::C32) return -1;
   if (parts < 0) return -1;
   const bool fusable = (chunk == 0 || chunk == kda::C) && parts <= 1;
-  if (path == KDA_PATH_AUTO) return KDA_PATH_SPLIT;
+  if (path == KDA_PATH_AUTO) return fusable ? KDA_PATH_AUTO : KDA_PATH_SPLIT;
   if (path == KDA_PATH_SPLIT) return KDA_PATH_SPLIT;
   if (path == KDA_PATH_FUSED) return fusable ? KDA_PATH_FUSED : -1;
   return -1;
@@ -213,7 +216,7 @@ size_t kda_fwd_workspace_bytes_ex(int64_t B, int64_t T, int64_t H, int64_t num_s
   if (p < 0) return 0;
   if (check_sizes(B, T, H, kda::K, kda::V, nullptr, num_seqs, has_cu_seqlens, &N) != KDA_OK) return 0;
   kda::Layout L;
-  const bool ok = p == KDA_PATH_FUSED ? kda::layout_fused(B, T, H, N, &L)
+  const bool ok = p == KDA_PATH_FUSED ? kda::layout_fused(B, T, H, N, &L)   // the split path's otherwise
                                       : kda::layout_for(B, T, H, N, chunk == 0 ? kda::default_chunk() : chunk, &L);
   return ok ? (size_t)L.total : 0;
 }
@@ -252,7 +255,6 @@ static int validate_common(const void* q, const void* k, const void* g, const vo
   if (!A_log || !dt_bias) return fail(KDA_EINVAL, "kda: A_log or dt_bias is NULL");
   if (misaligned(q) || misaligned(k) || misaligned(g))
     return fail(KDA_EINVAL, "kda: q, k and g must be 16-byte aligned");
-  if (fused && misaligned(dt_bias)) return fail(KDA_EINVAL, "kda: dt_bias must be 16-byte aligned");
   if (!std::isfinite(scale)) return fail(KDA_EINVAL, "kda: scale is not finite");
   if (!std::isfinite(lower_bound) || lower_bound < -5.0f || lower_bound > 0.0f)
     return fail(KDA_EINVAL, "kda: lower_bound must lie in [-5, 0] (got %g)", (double)lower_bound);
@@ -301,7 +303,8 @@ static int fwd_impl(const void* q, const void* k, const void* v, const void* g, 
     if (path < 0)
       return fail(KDA_EINVAL, "kda: path %d cannot run chunk=%d with parts=%d (the fused path takes 16-token "
                   "chunks and one part)", path_req, chunk_req, parts_req);
-    const bool fused = path == KDA_PATH_FUSED;
+    const bool fused = path == KDA_PATH_FUSED;   // fused kernel only
+    const bool both = path == KDA_PATH_AUTO;     // both paths enqueued, the scheduler picks
     const int chunk = chunk_req == 0 ? kda::default_chunk() : chunk_req;
     kda::Layout L;
     int64_t N = 0;
@@ -310,8 +313,8 @@ static int fwd_impl(const void* q, const void* k, const void* v, const void* g, 
     if (rc != KDA_OK) return rc;
     if (misaligned(v) || misaligned(out) || misaligned(initial_state) || misaligned(final_state))
       return fail(KDA_EINVAL, "kda: v, out and the states must be 16-byte aligned");
-    const int P = fused ? 1 : parts_used(B, T, parts_req);
-    const int n_need = fused ? 4 : 2 + 4 * P;
+    const int P = fused || both ? 1 : parts_used(B, T, parts_req);
+    const int n_need = fused ? 4 : 2 + 4 * P + (both ? 2 : 0);
     if (ev && n_ev != n_need)
       return fail(KDA_EINVAL, "kda: %d events given, this call needs %d", n_ev, n_need);
     int dev = 0;
@@ -326,7 +329,7 @@ static int fwd_impl(const void* q, const void* k, const void* v, const void* g, 
       char* ws = static_cast<char*>(workspace);
       rec(0);
       if (e == hipSuccess) {
-        kda::SchedArgs sa{cu_seqlens, N, B, T, 1, B * T > 0 ? B * T : 1, ws, L};
+        kda::SchedArgs sa{cu_seqlens, N, B, T, H, 1, B * T > 0 ? B * T : 1, KDA_PATH_FUSED, ws, L};
         e = kda::launch_sched(sa, stream);
       }
       rec(1);
@@ -367,7 +370,7 @@ static int fwd_impl(const void* q, const void* k, const void* v, const void* g, 
     rec(0, stream);
     rec4(0);
     if (e == hipSuccess) {
-      kda::SchedArgs sa{cu_seqlens, N, B, T, P, part_rows, ws, L};
+      kda::SchedArgs sa{cu_seqlens, N, B, T, H, P, part_rows, both ? KDA_PATH_AUTO : KDA_PATH_SPLIT, ws, L};
       e = kda::launch_sched(sa, stream);
     }
     rec(1, stream);
@@ -398,6 +401,17 @@ static int fwd_impl(const void* q, const void* k, const void* v, const void* g, 
     if (P > 1 && e == hipSuccess) {
       e = hipEventRecord(side->join, rstream);
       if (e == hipSuccess) e = hipStreamWaitEvent(stream, side->join, 0);
+    }
+    if (both) {   // exits at once unless the scheduler chose it (then prep and recurrence exited)
+      rec(6, stream);
+      if (e == hipSuccess) {
+        kda::FusedArgs fa{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                          static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(g),
+                          static_cast<const uint16_t*>(beta), static_cast<uint16_t*>(out), A_log, dt_bias, scale,
+                          lower_bound, initial_state, final_state, sdt, N, H, ws, L};
+        e = kda::launch_fused(fa, stream);
+      }
+      rec(7, stream);
     }
     rec4(3);
     if (e != hipSuccess) return fail(KDA_EHIP, "kda: launch or event call: %s", hipGetErrorString(e));
@@ -453,7 +467,21 @@ int kda_fwd_ex(const void* q, const void* k, const void* v, const void* g, const
 int kda_fwd_num_events(int64_t B, int64_t T, int chunk, int parts, int path) {
   const int p = resolve_path(chunk, parts, path);
   if (p < 0 || B < 0 || T < 0) return 0;
-  return p == KDA_PATH_FUSED ? 4 : 2 + 4 * parts_used(B, T, parts);
+  if (p == KDA_PATH_FUSED) return 4;
+  if (p == KDA_PATH_AUTO) return 8;
+  return 2 + 4 * parts_used(B, T, parts);
+}
+
+int kda_fwd_path_taken(const void* workspace, hipStream_t stream, int* path) {
+  if (!workspace || !path) return fail(KDA_EINVAL, "kda: workspace or path is NULL");
+  hipError_t e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return fail(KDA_EHIP, "kda: hipStreamSynchronize: %s", hipGetErrorString(e));
+  int32_t p = 0;
+  e = hipMemcpy(&p, static_cast<const char*>(workspace) + offsetof(kda::WsHeader, path), sizeof p,
+                hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return fail(KDA_EHIP, "kda: hipMemcpy: %s", hipGetErrorString(e));
+  *path = p;
+  return KDA_OK;
 }
 
 int kda_debug_prep(const void* q, const void* k, const void* g, const void* beta, float scale,
@@ -469,7 +497,7 @@ int kda_debug_prep(const void* q, const void* k, const void* g, const void* beta
     rc = check_device();
     if (rc != KDA_OK) return rc;
     char* ws = static_cast<char*>(workspace);
-    kda::SchedArgs sa{cu_seqlens, N, B, T, 1, B * T > 0 ? B * T : 1, ws, L};
+    kda::SchedArgs sa{cu_seqlens, N, B, T, H, 1, B * T > 0 ? B * T : 1, KDA_PATH_SPLIT, ws, L};
     hipError_t e = kda::launch_sched(sa, stream);
     if (e != hipSuccess) return fail(KDA_EHIP, "kda: scheduler launch: %s", hipGetErrorString(e));
     kda::PrepArgs pa{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),

@@ -383,6 +383,7 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
   const int64_t pair = 8 * (qb / F::kTiles) + xcd;
   const int tile = (int)(qb % F::kTiles);
   if (pair >= a.N * H) return;
+  if (reinterpret_cast<const WsHeader*>(a.ws)->path == KDA_PATH_SPLIT) return;   // the split kernels run instead
   const int64_t slot_id = pair / H;
   const int h = (int)(pair - slot_id * H);
   const int v0 = tile * F::kCols;
@@ -538,20 +539,15 @@ hipError_t launch_tiles(const FusedArgs& a, hipStream_t s) {
 
 }  // namespace
 
-// Value columns per workgroup: 64 (two workgroups per (sequence, head), each
-// building the pair's records itself) while the pairs are few, so that the
-// longest chain of the batch runs at half the per-step work; 128 (one
-// workgroup per pair, each record built once) once two tiles per pair would
-// not all fit on the 256 CUs at once.
+// Value columns per workgroup (fused_two_tiles): 64 (two workgroups per
+// (sequence, head), each building the pair's records itself) while the pairs
+// are few, so that the longest chain of the batch runs at half the per-step
+// work; 128 (one workgroup per pair, each record built once) once two tiles
+// per pair would not all fit on the 256 CUs at once.
 hipError_t launch_fused(const FusedArgs& a, hipStream_t s) {
   if (a.N * a.H == 0) return hipSuccess;
-#if defined(KDA_FUSED_NT)
-  if (KDA_FUSED_NT == 2) return launch_tiles<2, 3>(a, s);
-  return launch_tiles<1, 4>(a, s);
-#else
-  if (2 * a.N * a.H <= 512) return launch_tiles<1, 4>(a, s);
+  if (fused_two_tiles(a.N * a.H)) return launch_tiles<1, 4>(a, s);
   return launch_tiles<2, 3>(a, s);
-#endif
 }
 
 }  // namespace kda

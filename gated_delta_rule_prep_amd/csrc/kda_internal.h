@@ -52,7 +52,8 @@ struct WsHeader {
   int32_t status;                   // KDA_STATUS_*
   int32_t chunk_count;              // number of valid chunk-table entries
   int32_t part_first[kMaxParts + 1];  // chunk-table index of the first chunk of each part; [parts] = count
-  int32_t pad[53];
+  int32_t path;                     // KDA_PATH_SPLIT or KDA_PATH_FUSED: the kernels of the other path exit
+  int32_t pad[52];
 };
 static_assert(sizeof(WsHeader) == 256, "header size");
 
@@ -88,12 +89,17 @@ int default_chunk();           // chunk size used when the caller does not choos
 
 struct SchedArgs {
   const int64_t* cu;    // device, N + 1 entries, or nullptr
-  int64_t N, B, T;
+  int64_t N, B, T, H;
   int parts;            // 1 .. kMaxParts
   int64_t part_rows;    // token rows per part (the last part takes the rest)
+  int path;             // KDA_PATH_SPLIT / KDA_PATH_FUSED, or KDA_PATH_AUTO: choose from the lengths
   char* ws;
   Layout lay;
 };
+
+// Fused-kernel value-column tiling: 64 columns per workgroup (two per
+// (sequence, head)) while two tiles per pair fit on the CUs at once, else 128.
+inline __host__ __device__ bool fused_two_tiles(int64_t pairs) { return 2 * pairs <= 512; }
 
 struct PrepArgs {
   const uint16_t* q;

@@ -31,6 +31,7 @@
 // recurrence reads is bounded by 1 (or by scale) and is stored in fp16.
 #include "kda_device.h"
 #include "kda_internal.h"
+#include "../../include/kda.h"
 
 namespace kda {
 namespace {
@@ -53,6 +54,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
   const WsHeader* hdr = reinterpret_cast<const WsHeader*>(a.ws);
   const int chunk = hdr->part_first[a.part] + (int)blockIdx.x;   // this launch covers one part
   if (chunk >= hdr->part_first[a.part + 1] || h >= H) return;   // whole waves only; no barriers below
+  if (hdr->path == KDA_PATH_FUSED) return;                      // the scheduler chose the fused kernel
   WaveSmem& sm = wsm[wave];
   const ChunkEntry ce = reinterpret_cast<const ChunkEntry*>(a.ws + a.lay.chunk_table)[chunk];
   const int r = lane & 15, cq = lane >> 4;

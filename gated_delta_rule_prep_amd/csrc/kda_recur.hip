@@ -166,6 +166,7 @@ __global__ __launch_bounds__(kThreads) void recur_kernel(RecurArgs a) {
   const int64_t pair = 8 * (q / Cf::kTiles) + x;
   const int tile = (int)(q % Cf::kTiles);
   if (pair >= a.N * H) return;
+  if (reinterpret_cast<const WsHeader*>(a.ws)->path == KDA_PATH_FUSED) return;   // the fused kernel runs instead
   const int64_t slot_id = pair / H;
   const int h = (int)(pair - slot_id * H);
   const int v0 = tile * Cf::kCols;

@@ -12,7 +12,11 @@
 //     ranges of part_rows rows, so that prep and recurrence can overlap);
 //   * a status word: KDA_STATUS_BAD_CU_SEQLENS when cu_seqlens[0] != 0, the
 //     boundaries decrease, or cu_seqlens[N] != T.  Then every sequence gets zero
-//     chunks, so no later kernel touches a token.
+//     chunks, so no later kernel touches a token;
+//   * the execution path, when the caller leaves it to the library: both
+//     paths' kernels are enqueued and the ones not chosen exit at once.  The
+//     choice compares estimates of the two paths built from the total and the
+//     longest chunk count (see choose_path).
 // Without cu_seqlens sequence n is batch row n: rows [n*T, (n+1)*T).
 #include "kda_internal.h"
 #include "../../include/kda.h"
@@ -22,6 +26,28 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kRankSortMax = 2048;   // longest-first order by rank sort up to this N
+
+// Estimated time (us) of each path on MI355X for H heads, `total` chunks over
+// all sequences, the longest sequence's `maxc` chunks and N sequences.  The
+// constants are measured on the box at K = V = 128 (T = 8192, H = 64 and 96,
+// fixed length, 8 x 1024 and 12 ragged sequences):
+//   split: the prep kernel streams inputs and records at about 6.4 ns per
+//     (chunk, head); the recurrence is either the longest chain (0.63 us per
+//     chunk step) or, with many pairs, throughput (0.70 us per 64-column tile
+//     step per CU, 256 CUs);
+//   fused: one 16-token step of a workgroup takes about 1.8 us (two 64-column
+//     tiles per pair) or 2.15 us (one 128-column tile), each sequence takes
+//     five pipeline steps more than its chunk count, and the work spreads
+//     over 256 CUs, one workgroup per CU.
+__device__ int choose_path(int64_t H, int64_t N, int64_t total, int64_t maxc) {
+  const double chunk_heads = (double)total * (double)H;
+  const double split = 6.4e-3 * chunk_heads + fmax(0.63 * (double)maxc, 0.70 * 2.0 * chunk_heads / 256.0);
+  const bool two = fused_two_tiles(N * H);
+  const double step = two ? 1.8 : 2.15;
+  const double wg_steps = ((double)total + 5.0 * (double)N) * (double)H * (two ? 2.0 : 1.0);
+  const double fused = fmax(step * (double)(maxc + 5), step * wg_steps / 256.0);
+  return fused < split ? KDA_PATH_FUSED : KDA_PATH_SPLIT;
+}
 
 __global__ __launch_bounds__(kThreads) void sched_kernel(SchedArgs a) {
   WsHeader* hdr = reinterpret_cast<WsHeader*>(a.ws);
@@ -36,9 +62,11 @@ __global__ __launch_bounds__(kThreads) void sched_kernel(SchedArgs a) {
   __shared__ int32_t s_scan[kThreads];
   __shared__ int32_t s_carry;
   __shared__ int32_t s_nch[kRankSortMax];
+  __shared__ int32_t s_maxc;
   if (tid == 0) {
     s_bad = 0;
     s_carry = 0;
+    s_maxc = 0;
   }
   __syncthreads();
 
@@ -60,6 +88,7 @@ __global__ __launch_bounds__(kThreads) void sched_kernel(SchedArgs a) {
       nch = (int32_t)((len + C - 1) / C);
     }
     s_scan[tid] = nch;
+    if (nch > 0) atomicMax(&s_maxc, nch);
     __syncthreads();
     for (int off = 1; off < kThreads; off <<= 1) {  // Hillis-Steele inclusive scan
       const int32_t x = tid >= off ? s_scan[tid - off] : 0;
@@ -143,6 +172,7 @@ __global__ __launch_bounds__(kThreads) void sched_kernel(SchedArgs a) {
   if (tid == 0) {
     hdr->status = bad ? KDA_STATUS_BAD_CU_SEQLENS : KDA_STATUS_OK;
     hdr->chunk_count = total;
+    hdr->path = a.path == KDA_PATH_AUTO ? choose_path(a.H, N, total, s_maxc) : a.path;
   }
 }
 

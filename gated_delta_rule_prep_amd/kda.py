@@ -28,7 +28,8 @@ PATHS = {None: KDA_PATH_AUTO, "auto": KDA_PATH_AUTO, "split": KDA_PATH_SPLIT, "f
          KDA_PATH_AUTO: KDA_PATH_AUTO, KDA_PATH_SPLIT: KDA_PATH_SPLIT, KDA_PATH_FUSED: KDA_PATH_FUSED}
 CHUNK = 16
 
-EXPORTS = ("kda_fwd", "kda_fwd_profiled", "kda_fwd_ex", "kda_fwd_parts", "kda_fwd_path", "kda_fwd_num_events",
+EXPORTS = ("kda_fwd", "kda_fwd_profiled", "kda_fwd_ex", "kda_fwd_parts", "kda_fwd_path", "kda_fwd_path_taken",
+           "kda_fwd_num_events",
            "kda_decode", "kda_fwd_workspace_bytes", "kda_fwd_workspace_bytes_ex", "kda_get_last_error",
            "kda_version", "kda_fwd_check_status", "kda_workspace_layout", "kda_debug_prep")
 
@@ -52,6 +53,8 @@ _lib.kda_fwd_parts.argtypes = [_i64, _i64, ctypes.c_int]
 _lib.kda_fwd_parts.restype = ctypes.c_int
 _lib.kda_fwd_path.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
 _lib.kda_fwd_path.restype = ctypes.c_int
+_lib.kda_fwd_path_taken.argtypes = [_p, _p, ctypes.POINTER(ctypes.c_int)]
+_lib.kda_fwd_path_taken.restype = ctypes.c_int
 _lib.kda_fwd_num_events.argtypes = [_i64, _i64, ctypes.c_int, ctypes.c_int, ctypes.c_int]
 _lib.kda_fwd_num_events.restype = ctypes.c_int
 _lib.kda_fwd_workspace_bytes_ex.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
@@ -120,12 +123,27 @@ def workspace_bytes(B: int, T: int, H: int, num_seqs: int = 0, has_cu_seqlens: b
                                                int(parts or 0), _path_code(path)))
 
 
+_PATH_NAMES = {KDA_PATH_AUTO: "auto", KDA_PATH_SPLIT: "split", KDA_PATH_FUSED: "fused"}
+
+
 def path_used(chunk=None, parts=None, path=None) -> str:
-    """'split' or 'fused': the path kda_fwd_ex takes for these requests."""
+    """'split', 'fused' or 'auto' (chosen on the device by the scheduler
+    kernel): the path kda_fwd_ex takes for these requests."""
     p = _lib.kda_fwd_path(int(chunk or 0), int(parts or 0), _path_code(path))
     if p < 0:
         raise KDAValueError(KDA_EINVAL, "invalid chunk / parts / path combination")
-    return "fused" if p == KDA_PATH_FUSED else "split"
+    return _PATH_NAMES[p]
+
+
+def path_taken(workspace: torch.Tensor) -> str:
+    """'split' or 'fused': the path the last call using this workspace ran
+    (synchronises the current stream)."""
+    p = ctypes.c_int(-1)
+    with torch.cuda.device(workspace.device):
+        rc = _lib.kda_fwd_path_taken(_ptr(workspace), _stream(workspace.device), ctypes.byref(p))
+    if rc != KDA_OK:
+        _raise(rc)
+    return _PATH_NAMES.get(p.value, "unknown")
 
 
 def num_events(B: int, T: int, chunk=None, parts=None, path=None) -> int:

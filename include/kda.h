@@ -88,9 +88,12 @@ extern "C" {
    KDA_PATH_FUSED: one kernel per (sequence, head, value tile) that builds each
      chunk's record in LDS a few chunks ahead of the recurrence that consumes
      it, so the records never reach HBM (16-token chunks, one part);
-   KDA_PATH_AUTO: the library's choice (the split path: on MI355X the fused
-     kernel is faster only for batches of many short sequences, and the
-     longest sequence of a cu_seqlens batch is not known on the host). */
+   KDA_PATH_AUTO: the library's choice.  On MI355X the fused kernel is
+     faster for batches of many short sequences and the split path whenever
+     a sequence is long; the lengths are known only on the device, so both
+     paths are enqueued and the scheduler kernel picks one from the chunk
+     counts (the other path's kernels exit at once).  The workspace is the
+     split path's. */
 #define KDA_PATH_AUTO 0
 #define KDA_PATH_SPLIT 1
 #define KDA_PATH_FUSED 2
@@ -102,9 +105,8 @@ extern "C" {
  * tables and a longest-first work order, then the two stages of P1 §二 2.2:
  * chunk prep (gate activation, L2 norm, in-chunk decay, the L / Mqk matrices
  * and the 16 x 16 unit-lower-triangular inverse) and the chunk recurrence (the
- * chunk-by-chunk delta-rule state update and the output).  kda_fwd runs them
- * on the split path (two kernels, chunk records in the workspace);
- * kda_fwd_ex selects the path.
+ * chunk-by-chunk delta-rule state update and the output).  kda_fwd leaves
+ * the execution path to the library (KDA_PATH_AUTO); kda_fwd_ex selects it.
  *
  * initial_state / final_state: NULL with dtype KDA_DTYPE_NONE, or a pointer
  * with KDA_DTYPE_BF16 / KDA_DTYPE_FP32.  When both are given their dtypes must
@@ -154,8 +156,9 @@ int kda_fwd_profiled(const void* q, const void* k, const void* v, const void* g,
  * overlap of the two stages under the caller's control, and optional
  * per-kernel events.
  *
- * path: KDA_PATH_AUTO (the split path), KDA_PATH_SPLIT or KDA_PATH_FUSED
- * (chunk 0 or 16 and parts 0 or 1 only; otherwise KDA_EINVAL).  The workspace
+ * path: KDA_PATH_AUTO (the library's choice; with a 32-token chunk or more
+ * than one part, the split path), KDA_PATH_SPLIT or KDA_PATH_FUSED (chunk 0 or
+ * 16 and parts 0 or 1 only; otherwise KDA_EINVAL).  The workspace
  * must hold kda_fwd_workspace_bytes_ex(..., chunk, parts, path) bytes: the
  * split path keeps its chunk records there (about 864 B per token-head at
  * chunk 16), the fused path only the per-sequence tables.
@@ -187,7 +190,9 @@ int kda_fwd_profiled(const void* q, const void* k, const void* v, const void* g,
  * before / after the prep kernel of part p (on `stream`), [2 + 2P + 2p] /
  * [3 + 2P + 2p] before / after the recurrence of part p (on the stream it runs
  * on).  Fused path: 4 events, [0] / [1] around the scheduler, [2] / [3] around
- * the fused kernel.  A wrong count returns KDA_EINVAL.
+ * the fused kernel.  Library's choice (KDA_PATH_AUTO with 16-token chunks and
+ * one part): 8 events, the split path's 6 and [6] / [7] around the fused
+ * kernel.  A wrong count returns KDA_EINVAL.
  * Calls on one device that use the second stream are serialised on the host
  * by a per-device lock while they enqueue.
  */
@@ -201,9 +206,14 @@ int kda_fwd_ex(const void* q, const void* k, const void* v, const void* g, const
 /* Number of parts kda_fwd_ex uses for these sizes and `parts` request (0 on bad input). */
 int kda_fwd_parts(int64_t B, int64_t T, int parts);
 
-/* Path (KDA_PATH_SPLIT or KDA_PATH_FUSED) that kda_fwd_ex takes for these
-   requests, or -1 if they are invalid together. */
+/* Path that kda_fwd_ex takes for these requests: KDA_PATH_SPLIT,
+   KDA_PATH_FUSED, KDA_PATH_AUTO (chosen on the device, see
+   kda_fwd_path_taken), or -1 if they are invalid together. */
 int kda_fwd_path(int chunk, int parts, int path);
+
+/* Path (KDA_PATH_SPLIT or KDA_PATH_FUSED) that the last call using
+   `workspace` ran.  Synchronises `stream` first; for tests and tools. */
+int kda_fwd_path_taken(const void* workspace, hipStream_t stream, int* path);
 
 /* Events kda_fwd_ex takes for these sizes and requests (0 on bad input). */
 int kda_fwd_num_events(int64_t B, int64_t T, int chunk, int parts, int path);

@@ -182,15 +182,16 @@ def test_fwd_ex_rejects_bad_parts_and_event_counts():
 def test_path_choice_events_and_workspace():
     """Which path a kda_fwd_ex request takes, how many events it records and
     how much workspace it needs, and the requests it rejects on the host."""
-    assert kda.path_used() == "split"                                   # the library's own choice
-    assert kda.path_used(chunk=16) == "split" and kda.path_used(parts=1) == "split"
+    assert kda.path_used() == "auto"                # both enqueued, the scheduler kernel picks
+    assert kda.path_used(chunk=16) == "auto" and kda.path_used(parts=1) == "auto"
     assert kda.path_used(chunk=32) == "split" and kda.path_used(parts=2) == "split"
     assert kda.path_used(path="split") == "split" and kda.path_used(path="fused", chunk=16) == "fused"
     assert kda.path_used(path="fused", parts=1) == "fused"
     for bad in (dict(path="fused", chunk=32), dict(path="fused", parts=3), dict(path=7), dict(chunk=24)):
         with pytest.raises(ValueError):
             kda.path_used(**bad)
-    assert kda.num_events(1, 8192, path="fused") == 4 and kda.num_events(1, 8192) == 6
+    assert kda.num_events(1, 8192, path="fused") == 4 and kda.num_events(1, 8192, path="split") == 6
+    assert kda.num_events(1, 8192) == 8                  # scheduler, prep, recurrence, fused
     assert kda.num_events(1, 8192, parts=3) == 2 + 4 * 3
     assert kda.lib().kda_fwd_num_events(1, 64, 32, 0, 2) == 0         # fused cannot take 32-token chunks
     # the fused path keeps only the per-sequence tables; the split path its records
@@ -200,6 +201,7 @@ def test_path_choice_events_and_workspace():
     assert split == kda.workspace_layout(1, 8192, 96, chunk=16)["total"]
     assert kda.workspace_bytes(1, 8192, 96, chunk=32) == kda.workspace_layout(1, 8192, 96, chunk=32)["total"]
     assert kda.workspace_bytes(1, 8192, 96) >= max(fused, split)
+    assert kda.workspace_bytes(1, 8192, 96, path="auto") == split      # both paths enqueued
     assert kda.workspace_bytes(1, 8192, 96, 100000, True, path="fused") >= 100000 * 20
     assert kda.lib().kda_fwd_workspace_bytes_ex(1, 64, 2, 0, 0, 32, 0, 2) == 0
     # a fused call is rejected when its workspace is smaller than that, and the
@@ -210,7 +212,6 @@ def test_path_choice_events_and_workspace():
     assert call_ex(0, None, 0, path=3) == kda.KDA_EINVAL
     ev = (ctypes.c_void_p * 6)(*([FAKE.value] * 6))
     assert call_ex(0, ev, 6, path=2) == kda.KDA_EINVAL and "events" in kda.last_error()   # fused takes 4
-    assert call_ex(0, None, 0, path=2, dt_bias=ctypes.c_void_p(0x1004)) == kda.KDA_EINVAL
 
 
 def test_layout_for_both_chunk_sizes():

@@ -84,6 +84,29 @@ def test_fused_many_pairs_parity():
     check(inp, [0, 7, 21, 39], tag="many-pairs", path="fused")
 
 
+@pytest.mark.parametrize("lens,H,expect", [([2048], 8, "split"), ([512] * 8, 64, "fused")],
+                         ids=["one-long", "many-short"])
+def test_library_choice_picks_a_path_and_matches_it_bitwise(lens, H, expect):
+    """kda_fwd enqueues both paths and the scheduler kernel picks one from the
+    chunk counts: a single long sequence runs the split path, many short ones
+    the fused kernel; the result is bit for bit the chosen path's."""
+    from gated_delta_rule_prep_amd import kda
+    inp = make_inputs(1, sum(lens), H, seed=111, state_dtype="bf16", seq_lens=lens if len(lens) > 1 else None)
+    d = device_inputs(inp)
+    say("case library choice lens=%s H=%d (expect %s)" % (lens[:2], H, expect))
+    ws = kda.alloc_workspace(1, inp.T, H, inp.N, inp.cu_seqlens is not None, "cuda", None, None, "auto")
+    out, fin = run_gpu(inp, d=d, workspace=ws)
+    assert kda.path_taken(ws) == expect
+    o2, f2 = run_gpu(inp, d=d, path=expect)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(fin.view(torch.int16), f2.view(torch.int16))
+    hs = [0, H // 2, H - 1]
+    ref_o, ref_f = oracle_run(inp, hs)
+    assert_close(to_f64(out)[:, :, hs], ref_o, "out")
+    assert_close(to_f64(fin)[:, hs], ref_f, "final_state", "bf16")
+
+
 @pytest.mark.parametrize("path,chunk", VARIANTS, ids=VARIANT_IDS)
 def test_deterministic_bitwise(path, chunk):
     inp = make_inputs(1, 500, 4, seed=200, state_dtype="fp32")
