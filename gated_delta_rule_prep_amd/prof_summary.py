@@ -27,8 +27,9 @@ import statistics
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCES = ["csrc/kda_device.h", "csrc/kda_internal.h", "csrc/kda_sched.hip", "csrc/kda_prep.hip",
-                  "csrc/kda_recur.hip", "csrc/kda_prep32.hip", "csrc/kda_recur32.hip", "csrc/kda_decode.hip"]
+KERNEL_SOURCES = ["csrc/kda_device.h", "csrc/kda_internal.h", "csrc/kda_lds_pipe.h", "csrc/kda_step16.h",
+                  "csrc/kda_sched.hip", "csrc/kda_prep.hip", "csrc/kda_recur.hip", "csrc/kda_prep32.hip",
+                  "csrc/kda_recur32.hip", "csrc/kda_fused.hip", "csrc/kda_decode.hip"]
 
 
 def source_hash() -> str:
@@ -40,8 +41,8 @@ def source_hash() -> str:
 
 
 def short_name(name: str) -> str:
-    m = re.search(r"(sched_kernel|prep32_kernel|prep_kernel|recur32_kernel|recur_kernel|decode_kernel|copyBuffer|"
-                  r"elementwise_kernel)",
+    m = re.search(r"(sched_kernel|prep32_kernel|prep_kernel|recur32_kernel|recur_kernel|fused_kernel|decode_kernel|"
+                  r"copyBuffer|elementwise_kernel)",
                   name)
     return m.group(1) if m else name[:40]
 
@@ -82,7 +83,8 @@ def traffic(workload, fetch_dir, write_dir, copy_bytes):
     fs = copy_bytes / copy_value(f, kib)   # bytes per counter unit
     ws = copy_bytes / copy_value(w, kib)
     kernels = {}
-    for k in ("sched_kernel", "prep_kernel", "recur_kernel", "prep32_kernel", "recur32_kernel", "decode_kernel"):
+    for k in ("sched_kernel", "prep_kernel", "recur_kernel", "prep32_kernel", "recur32_kernel", "fused_kernel",
+              "decode_kernel"):
         if k in f and k in w:
             kernels[k] = {"fetch_bytes": int(statistics.median(f[k]) * fs),
                           "write_bytes": int(statistics.median(w[k]) * ws), "dispatches": len(f[k])}
