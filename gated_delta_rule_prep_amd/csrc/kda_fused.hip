@@ -83,7 +83,8 @@ struct Carry {
   u32x4 qw[3], kw[3], gw[3];   // raw bf16 q, k, g of channel blocks 1..3 (block j at j - 1)
   float rq, rk;                // scale / |q|, 1 / |k| (0 for padded tokens)
   int valid;                   // token row < chunk length
-  f32x4 accL, accM;            // L and Mqk partial sums over the blocks done so far
+  f32x4 accL[2], accM[2];      // L and Mqk partial sums over the blocks done so far (even / odd
+                               // channels, two independent MFMA chains)
 };
 
 // Chunk j of a sequence: first flattened token row and length (1..16).
@@ -196,8 +197,8 @@ __device__ __forceinline__ void put_qh(char* rec, int field, int row, int pos, u
 // the gate argument A2 (g + dt_bias) is one fma.
 template <int J>
 __device__ __forceinline__ void chan_block(u32x4 qw, u32x4 kw, u32x4 gw, float rq, float rk, bool valid, float A2,
-                                           float lb2, const float* s_adt, int r, int cq, char* rec, f32x4& accL,
-                                           f32x4& accM) {
+                                           float lb2, const float* s_adt, int r, int cq, char* rec, f32x4 (&accL)[2],
+                                           f32x4 (&accM)[2]) {
   const int c0 = 32 * J + 8 * cq;
   const f32x4 dtA = *reinterpret_cast<const f32x4*>(s_adt + c0);
   const f32x4 dtB = *reinterpret_cast<const f32x4*>(s_adt + c0 + 4);
@@ -221,8 +222,8 @@ __device__ __forceinline__ void chan_block(u32x4 qw, u32x4 kw, u32x4 gw, float r
     const float kP = kn * P, kI = kn * Pinv, qP = qn * P;
     // fp32 16x16x4: lane (r, cq) holds A[r][k = cq] and B[k = cq][r] for
     // channel c0 + e, so L and Mqk take the factors straight from registers
-    accL = mfma_f32_k4(kP, kI, accL);
-    accM = mfma_f32_k4(qP, kI, accM);
+    accL[e & 1] = mfma_f32_k4(kP, kI, accL[e & 1]);
+    accM[e & 1] = mfma_f32_k4(qP, kI, accM[e & 1]);
     kh[e] = -kP;
     qh[e] = qP;
     kb[e] = kI * gam;
@@ -270,16 +271,21 @@ __device__ __forceinline__ void phase0(const PrepCtx& p, const char* grp, const 
   const bool valid = r < rw.len;
   const float beta = valid ? fast_rcp(1.f + fast_exp2(-kLog2e * bf16_to_f32(braw16))) : 0.f;
 
-  float sq = 0.f, sk = 0.f;
+  // sums of squares straight from the packed bf16 words (v_dot2: exact
+  // products, fp32 accumulation), four independent chains per tensor.  The
+  // words go through scalars before the bit cast: hipcc reads element 0 of
+  // the vector for a bit cast applied to a vector element directly.
+  float sqv[4] = {0.f, 0.f, 0.f, 0.f}, skv[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const float q0 = bf16_lo(qw[j][w]), q1 = bf16_hi(qw[j][w]);
-      const float k0 = bf16_lo(kw[j][w]), k1 = bf16_hi(kw[j][w]);
-      sq = fmaf(q0, q0, fmaf(q1, q1, sq));
-      sk = fmaf(k0, k0, fmaf(k1, k1, sk));
+      const uint32_t qword = qw[j][w], kword = kw[j][w];
+      const bf16x2 qv = __builtin_bit_cast(bf16x2, qword), kv = __builtin_bit_cast(bf16x2, kword);
+      sqv[w] = __builtin_amdgcn_fdot2_f32_bf16(qv, qv, sqv[w], false);
+      skv[w] = __builtin_amdgcn_fdot2_f32_bf16(kv, kv, skv[w], false);
     }
+  float sq = (sqv[0] + sqv[1]) + (sqv[2] + sqv[3]), sk = (skv[0] + skv[1]) + (skv[2] + skv[3]);
   sq += __shfl_xor(sq, 16);
   sq += __shfl_xor(sq, 32);
   sk += __shfl_xor(sk, 16);
@@ -289,8 +295,11 @@ __device__ __forceinline__ void phase0(const PrepCtx& p, const char* grp, const 
   cr.valid = valid;
   if (cq == 0) reinterpret_cast<float*>(rec + REC_BYTES)[r] = beta;
 
-  cr.accL = f32x4{0.f, 0.f, 0.f, 0.f};
-  cr.accM = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    cr.accL[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    cr.accM[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   chan_block<0>(qw[0], kw[0], gw[0], cr.rq, cr.rk, valid, p.A2, p.lb2, p.s_adt, r, cq, rec, cr.accL, cr.accM);
 #pragma unroll
   for (int j = 1; j < 4; ++j) {
@@ -315,13 +324,14 @@ __device__ __forceinline__ void phase3(const PrepCtx& p, char* rec, float (*lt)[
   // lane (c, g) holds rows 4g..4g+3 of column c of L and Mqk
   const int lane = p.lane, lc = lane & 15, lg = lane >> 4;
   const float* beta = reinterpret_cast<const float*>(rec + REC_BYTES);
+  const f32x4 accL = cr.accL[0] + cr.accL[1], accM = cr.accM[0] + cr.accM[1];
   float mv[4];
   f32x4 lv;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int rr = 4 * lg + i;
-    lv[i] = lc < rr ? beta[rr] * cr.accL[i] : 0.f;
-    mv[i] = lc <= rr ? cr.accM[i] : 0.f;
+    lv[i] = lc < rr ? beta[rr] * accL[i] : 0.f;
+    mv[i] = lc <= rr ? accM[i] : 0.f;
   }
   *reinterpret_cast<f32x4*>(&lt[lc][4 * lg]) = lv;   // lt[m][r] = L[r][m]
   *reinterpret_cast<u32x2*>(rec + REC_MQK + (lc * C + 4 * lg) * 2) = u32x2{pack_f16(mv[0], mv[1]),

@@ -53,24 +53,26 @@ namespace kda {
 namespace {
 
 constexpr int kRecPieces = REC_BYTES / 16;   // 864 16-byte pieces per record
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
 
-template <int NT, int D>
+// NT: 16-column MFMA tiles per wave; D: ring depth; W: waves per workgroup.
+template <int NT, int D, int W>
 struct Cfg {
+  static constexpr int kWaves = W;
+  static constexpr int kThreads = 64 * W;
   static constexpr int kWaveCols = 16 * NT;             // value columns per wave
-  static constexpr int kCols = kWaveCols * kWaves;      // value columns per workgroup
+  static constexpr int kCols = kWaveCols * W;           // value columns per workgroup
   static constexpr int kTiles = V / kCols;              // workgroups per (sequence, head)
   static constexpr int kRowPieces = kCols / 8;          // 16-byte pieces per value row of the tile
   static constexpr int kValBlocks = C * kRowPieces / 64;             // 64-piece blocks of values
-  static constexpr int kBlocks = (kValBlocks + (kRecPieces + 63) / 64 + kWaves - 1) / kWaves * kWaves;
-  static constexpr int kLoads = kBlocks / kWaves;       // load instructions per wave per chunk
+  static constexpr int kBlocks = kValBlocks + (kRecPieces + 63) / 64;   // 1 KB blocks of a slot
+  static constexpr int kMaxLoads = (kBlocks + W - 1) / W;   // load instructions per wave per chunk (at most)
+  static constexpr bool kEven = kBlocks % W == 0;           // every wave issues kMaxLoads
   static constexpr int kSlotBytes = kBlocks * 1024;     // one ring slot
   // byte offsets of the fields inside a slot
   static constexpr int kVal = 0;
   static constexpr int kRec = kValBlocks * 1024;
   static_assert(C * kRowPieces % 64 == 0, "value rows fill whole blocks");
-  static_assert(D >= 3 && (D - 2) * kLoads <= 63, "ring depth within the vmcnt range");
+  static_assert(D >= 3 && (D - 2) * kMaxLoads <= 63, "ring depth within the vmcnt range");
   static_assert(V % kCols == 0, "tile shape");
 };
 
@@ -100,20 +102,20 @@ __device__ __forceinline__ int rec_source(int s) {
 }
 
 // Where this lane's load instruction j of a chunk reads from.  Slot block
-// b = kWaves j + wave (64 pieces, one per lane); blocks below kValBlocks hold
-// the value tile, the rest the record.
-template <int NT, int D>
+// b = W j + wave (64 pieces, one per lane); blocks below kValBlocks hold the
+// value tile, the rest the record.
+template <int NT, int D, int W>
 struct LoadPlan {
-  int32_t off[Cfg<NT, D>::kLoads];   // record byte offset, or value byte offset within the token row
-  int32_t row[Cfg<NT, D>::kLoads];   // value blocks: byte offset of the piece within the chunk's rows
+  int32_t off[Cfg<NT, D, W>::kMaxLoads];   // record byte offset, or value byte offset within the token row
+  int32_t row[Cfg<NT, D, W>::kMaxLoads];   // value blocks: byte offset of the piece within the chunk's rows
 };
 
-template <int NT, int D>
-__device__ __forceinline__ void make_plan(LoadPlan<NT, D>& pl, int wave, int lane, int row_bytes) {
-  using Cf = Cfg<NT, D>;
+template <int NT, int D, int W>
+__device__ __forceinline__ void make_plan(LoadPlan<NT, D, W>& pl, int wave, int lane, int row_bytes) {
+  using Cf = Cfg<NT, D, W>;
 #pragma unroll
-  for (int j = 0; j < Cf::kLoads; ++j) {
-    const int b = kWaves * j + wave;
+  for (int j = 0; j < Cf::kMaxLoads; ++j) {
+    const int b = W * j + wave;
     if (b < Cf::kValBlocks) {
       const int s = 64 * b + lane, r = s / Cf::kRowPieces, p = s % Cf::kRowPieces;
       pl.off[j] = 16 * (p ^ (2 * (r & 3)));
@@ -134,19 +136,20 @@ __device__ __forceinline__ void make_plan(LoadPlan<NT, D>& pl, int wave, int lan
 // Value rows past the end of a partial chunk repeat the last row: the
 // record gives them zero weight (their T rows and columns and their -W, Qhat
 // and Kbar rows are exactly zero), so any finite values are harmless.
-template <int NT, int D>
-__device__ __forceinline__ void issue_chunk(uint32_t slot_lds, const LoadPlan<NT, D>& pl, const char* recs,
+template <int NT, int D, int W>
+__device__ __forceinline__ void issue_chunk(uint32_t slot_lds, const LoadPlan<NT, D, W>& pl, const char* recs,
                                             const char* vseq, const SeqEntry& se, int c, int clast, int row_bytes,
                                             int wave) {
-  using Cf = Cfg<NT, D>;
+  using Cf = Cfg<NT, D, W>;
   c = min(c, clast);
   const int len = min(se.len - C * c, C);
   const i32x4 rrec = buf_rsrc(recs + (int64_t)c * REC_BYTES, REC_BYTES);
   const i32x4 rval = buf_rsrc(vseq + (int64_t)c * C * row_bytes, C * row_bytes);
   const int last = (len - 1) * row_bytes;   // byte offset of the chunk's last value row
 #pragma unroll
-  for (int j = 0; j < Cf::kLoads; ++j) {
-    const int b = kWaves * j + wave;   // wave-uniform
+  for (int j = 0; j < Cf::kMaxLoads; ++j) {
+    const int b = W * j + wave;   // wave-uniform
+    if (b >= Cf::kBlocks) break;
     if (b < Cf::kValBlocks) {
       load_lds16(rval, slot_lds + 1024 * b, min(pl.row[j], last + pl.off[j]));
     } else {
@@ -155,9 +158,23 @@ __device__ __forceinline__ void issue_chunk(uint32_t slot_lds, const LoadPlan<NT
   }
 }
 
-template <int NT, int D>
-__global__ __launch_bounds__(kThreads) void recur_kernel(RecurArgs a) {
-  using Cf = Cfg<NT, D>;
+// Wait until this wave's loads of chunk ci have landed: at most the loads of
+// the D - 2 later chunks may still be in flight (loads complete in issue
+// order; the output stores, also counted, only make the wait stricter).
+template <int NT, int D, int W>
+__device__ __forceinline__ void wait_chunk(int wave) {
+  using Cf = Cfg<NT, D, W>;
+  if constexpr (Cf::kEven) {
+    wait_vmcnt<(D - 2) * Cf::kMaxLoads>();
+  } else {
+    if (wave < Cf::kBlocks % W) wait_vmcnt<(D - 2) * Cf::kMaxLoads>();
+    else wait_vmcnt<(D - 2) * (Cf::kMaxLoads - 1)>();
+  }
+}
+
+template <int NT, int D, int W>
+__global__ __launch_bounds__(64 * W) void recur_kernel(RecurArgs a) {
+  using Cf = Cfg<NT, D, W>;
   __shared__ __align__(1024) char ring[D][Cf::kSlotBytes];
   const int64_t H = a.H;
   // XCD-aware placement: id b runs on XCD b % 8; the kTiles tiles of pair
@@ -217,8 +234,8 @@ __global__ __launch_bounds__(kThreads) void recur_kernel(RecurArgs a) {
 
   if (ci_lo < ci_hi) {
     const int row_bytes = (int)(H * V * 2);
-    LoadPlan<NT, D> pl;
-    make_plan<NT, D>(pl, wave, lane, row_bytes);
+    LoadPlan<NT, D, W> pl;
+    make_plan<NT, D, W>(pl, wave, lane, row_bytes);
     const int clast = ci_hi - 1;
     const char* vseq = reinterpret_cast<const char*>(a.v + ((int64_t)se.row0 * H + h) * V + v0);
     const uint32_t ring0 = (uint32_t)reinterpret_cast<uintptr_t>((lds_void*)ring[0]);
@@ -231,20 +248,20 @@ __global__ __launch_bounds__(kThreads) void recur_kernel(RecurArgs a) {
     // the part's last chunk repeat it into slots that are never read.
 #pragma unroll
     for (int c = 0; c < D - 1; ++c)
-      issue_chunk<NT, D>(ring0 + c * Cf::kSlotBytes, pl, recs, vseq, se, ci_lo + c, clast, row_bytes, wave);
+      issue_chunk<NT, D, W>(ring0 + c * Cf::kSlotBytes, pl, recs, vseq, se, ci_lo + c, clast, row_bytes, wave);
     u32x2 o_prev[NT];
     int slot = 0;   // ring slot of chunk ci
     for (int ci = ci_lo; ci < ci_hi; ++ci) {
       // At most the D - 2 chunks issued after chunk ci may still be in flight
       // (loads complete in issue order); the output stores of the step
       // before, also counted, have had a whole step to complete.
-      wait_vmcnt<(D - 2) * Cf::kLoads>();
+      wait_chunk<NT, D, W>(wave);
       wait_lgkm0();
       barrier();
       // Every wave is done with chunk ci - 1, whose slot is refilled now, and
       // every wave's loads of chunk ci have landed.
       const int refill = slot == 0 ? D - 1 : slot - 1;
-      issue_chunk<NT, D>(ring0 + refill * Cf::kSlotBytes, pl, recs, vseq, se, ci + D - 1, clast, row_bytes, wave);
+      issue_chunk<NT, D, W>(ring0 + refill * Cf::kSlotBytes, pl, recs, vseq, se, ci + D - 1, clast, row_bytes, wave);
       if (ci > ci_lo) {   // output of chunk ci - 1, a full chunk (only a sequence's last chunk is partial)
         uint16_t* const ob = out_seq + (int64_t)(ci - 1) * out_chunk;
 #pragma unroll
@@ -285,11 +302,11 @@ __global__ __launch_bounds__(kThreads) void recur_kernel(RecurArgs a) {
   }
 }
 
-template <int NT, int D>
+template <int NT, int D, int W>
 hipError_t launch_tiles(const RecurArgs& a, hipStream_t s) {
   const int64_t pairs = a.N * a.H;
-  const int64_t grid = 8 * Cfg<NT, D>::kTiles * ((pairs + 7) / 8);
-  hipLaunchKernelGGL((recur_kernel<NT, D>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  const int64_t grid = 8 * Cfg<NT, D, W>::kTiles * ((pairs + 7) / 8);
+  hipLaunchKernelGGL((recur_kernel<NT, D, W>), dim3((unsigned)grid), dim3(64 * W), 0, s, a);
   return hipGetLastError();
 }
 
@@ -299,7 +316,10 @@ hipError_t launch_tiles(const RecurArgs& a, hipStream_t s) {
 // a pair is split over two workgroups, so the per-step VALU work (state
 // conversion and decay) and MFMA work of a wave are half of a whole pair's
 // and the longest chain of the batch (the critical path) runs twice as fast
-// per chunk.  Whole pairs per workgroup (32 columns per wave, NT = 2) read
+// per chunk.  One workgroup of eight 16-column waves per pair (W = 8: each
+// record streamed once per pair, two recurrence waves per SIMD) measured
+// slower: 0.43 ms against 0.33 at T = 8192, H = 96 fixed, 0.44 against 0.34 on
+// the ragged batch, 0.26 against 0.27 at 8 x 1024.  Whole pairs per workgroup (32 columns per wave, NT = 2) read
 // each record once instead of twice but measured faster only with many short
 // sequences of equal length (3 % at 8 x 1024 tokens, H = 96) and 25 % slower
 // with one long sequence among short ones.  A 4-chunk ring (64 KB) covers the
@@ -311,7 +331,7 @@ hipError_t launch_tiles(const RecurArgs& a, hipStream_t s) {
 hipError_t launch_recur(const RecurArgs& a, hipStream_t s) {
   if (a.lay.chunk == C32) return launch_recur32(a, s);
   if (a.N * a.H == 0) return hipSuccess;
-  return launch_tiles<1, KDA_RECUR_DEPTH>(a, s);
+  return launch_tiles<1, KDA_RECUR_DEPTH, 4>(a, s);
 }
 
 }  // namespace kda
