@@ -189,6 +189,42 @@ def run_decode(steps, warmup, torch, kda, device_inputs):
                          "algorithmic_bytes_per_launch": int(nbytes)}}
 
 
+def run_segmented(steps, warmup, torch, kda, device_inputs, T=8192, H=4):
+    """One long sequence with few heads, the case kda_fwd_segmented is for:
+    kda_fwd and kda_fwd_segmented with the library's segment count, on the
+    same synthetic inputs (fp32 state)."""
+    from gated_delta_rule_prep_amd.inputs import make_inputs
+    inp = make_inputs(1, T, H, seed=7, state_dtype="fp32")
+    d = device_inputs(inp, "cuda")
+    out = torch.empty((1, T, H, 128), dtype=torch.bfloat16, device="cuda")
+    fin = torch.empty((1, H, 128, 128), dtype=torch.float32, device="cuda")
+    S = kda.segments_for(1, T, H)
+    ws = kda.alloc_workspace(1, T, H, 1, False, "cuda")
+    wss = torch.empty(kda.segmented_workspace_bytes(1, T, H, 1, False, S), dtype=torch.uint8, device="cuda")
+
+    def timed(segments, workspace):
+        f = lambda: kda.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], inp.scale, out, d["A_log"], d["dt_bias"],
+                            inp.lower_bound, initial_state=d["initial_state"], final_state=fin,
+                            workspace=workspace, segments=segments)
+        for _ in range(warmup):
+            f()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(steps):
+            f()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / steps
+
+    plain = timed(None, ws)
+    seg = timed(S, wss)
+    return {"workload": "T%d_H%d_fixed_fp32state" % (T, H), "segments": S, "ms_per_step": round(seg, 4),
+            "kda_fwd_ms": round(plain, 4), "value": round(T * H / (seg * 1e-3), 1),
+            "speedup_vs_kda_fwd": round(plain / seg, 3), "status_ok": kda.check_status(wss) == 0}
+
+
 def cpu_baseline(cfg, heads: int):
     """The fp64 oracle on the first `heads` heads of the workload (all tokens)."""
     import oracle
@@ -228,7 +264,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle cpu_baseline leg")
     ap.add_argument("--cpu-heads", type=int, default=96, help="heads of the headline workload the oracle runs")
-    ap.add_argument("--only", choices=["both", "fixed", "varlen", "decode"], default="both",
+    ap.add_argument("--only", choices=["both", "fixed", "varlen", "decode", "segmented"], default="both",
                     help="time only one workload (for profiler runs); the JSON line needs both")
     ap.add_argument("--chunk", type=int, default=0, choices=[0, 16, 32],
                     help="tokens per chunk (0: the library's choice)")
@@ -254,6 +290,9 @@ def main():
         if args.copy_mib > 0:
             copy_for_counters(torch, args.copy_mib)
         return
+    if args.only == "segmented":
+        print(json.dumps(run_segmented(args.steps, args.warmup, torch, kda, device_inputs)))
+        return
     chunk = args.chunk or None
     if args.only != "both":
         res = run_workload(cfgs[2] if args.only == "fixed" else cfgs[3], args.steps, args.warmup, torch, kda,
@@ -275,6 +314,7 @@ def main():
     fixed, varlen = runs["fixed", paths[0]], runs["varlen", paths[0]]
     paths_ms = lambda wl: {p: round(runs[wl, p]["ms"], 4) for p in paths}
     decode = run_decode(args.steps, args.warmup, torch, kda, device_inputs)
+    segmented = run_segmented(args.steps, args.warmup, torch, kda, device_inputs)
     traffic = load_traffic()
     t = traffic.get("decode", {}).get("decode_kernel")
     decode["roofline"]["traffic"] = None if t is None else int(t["fetch_bytes"] + t["write_bytes"])
@@ -308,7 +348,8 @@ def main():
                           "kernels_ms": {k: round(v, 4) for k, v in varlen["kernels"].items()},
                           "paths_ms": paths_ms("varlen"), "roofline": rl_v, "path_roofline": path_v},
         "decode_256x96": decode,
-        "status_ok": fixed["status"] == 0 and varlen["status"] == 0,
+        "segmented_8192x4": segmented,
+        "status_ok": fixed["status"] == 0 and varlen["status"] == 0 and segmented["status_ok"],
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -484,6 +484,170 @@ int kda_fwd_path_taken(const void* workspace, hipStream_t stream, int* path) {
   return KDA_OK;
 }
 
+// ---- segmented forward -----------------------------------------------------
+
+namespace {
+
+// Workspace regions of kda_fwd_segmented (byte offsets), or false on bad sizes.
+// The plain forward's workspace comes first, so its header (status, path
+// taken) sits at the start as for kda_fwd.
+struct SegLayout {
+  int64_t inner, inner_bytes, seg_cu, A, B, starts, total;
+};
+
+bool seg_layout(int64_t B, int64_t T, int64_t H, int64_t N, int S, SegLayout* L) {
+  const int64_t NS = N * S, mat = NS * H * kda::V * kda::K * (int64_t)sizeof(float);   // fp32 states
+  kda::Layout inner;
+  if (!kda::layout_for(1, B * T, H, NS, kda::C, &inner)) return false;
+  int64_t off = 0;
+  L->inner = off;
+  L->inner_bytes = inner.total;
+  off = align_up(off + inner.total, 256);
+  L->seg_cu = off;
+  off = align_up(off + (NS + 1) * 8, 256);
+  L->A = off;   // the transitions, fp16
+  off = align_up(off + mat / 2, 256);
+  L->B = off;
+  off = align_up(off + mat, 256);
+  L->starts = off;
+  off = align_up(off + mat, 256);
+  L->total = off;
+  return true;
+}
+
+// The library's segment count.  Cutting pays while the recurrence leaves
+// CUs idle: one workgroup per 64 value columns of a (segment, head) chain, and
+// the two-set launch doubles that.  Measured on MI355X (one sequence, H = 2 ..
+// 96, T = 8192 .. 65536), the best count is the largest power of two with at
+// most 128 (segment, head) chains and segments of at least 512 tokens; below
+// four segments the three recurrence passes cost more than they save.  With
+// cu_seqlens the mean length stands in for the lengths, which only the device
+// knows.
+int choose_segments(int64_t B, int64_t T, int64_t H, int64_t N, bool has_cu) {
+  const int64_t len = has_cu ? (B * T) / (N > 0 ? N : 1) : T;
+  int64_t S = 1;
+  while (2 * S * N * H <= 128 && len / (2 * S) >= 512 && 2 * S <= 4096) S *= 2;
+  return S >= 4 ? (int)S : 1;
+}
+
+}  // namespace
+
+int kda_fwd_segments(int64_t B, int64_t T, int64_t H, int64_t num_seqs, int has_cu_seqlens) {
+  int64_t N = 0;
+  if (check_sizes(B, T, H, kda::K, kda::V, nullptr, num_seqs, has_cu_seqlens, &N) != KDA_OK) return 0;
+  return choose_segments(B, T, H, N, has_cu_seqlens != 0);
+}
+
+size_t kda_fwd_segmented_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t num_seqs, int has_cu_seqlens,
+                                         int segments) {
+  int64_t N = 0;
+  if (segments < 0 || segments > 4096) return 0;
+  if (check_sizes(B, T, H, kda::K, kda::V, nullptr, num_seqs, has_cu_seqlens, &N) != KDA_OK) return 0;
+  if (segments == 0) segments = choose_segments(B, T, H, N, has_cu_seqlens != 0);
+  if (segments == 1) return kda_fwd_workspace_bytes_ex(B, T, H, num_seqs, has_cu_seqlens, 0, 0, KDA_PATH_AUTO);
+  if (N * segments >= (int64_t(1) << 30) || N * segments * H >= (int64_t(1) << 31)) return 0;
+  SegLayout L;
+  return seg_layout(B, T, H, N, segments, &L) ? (size_t)L.total : 0;
+}
+
+int kda_fwd_segmented(const void* q, const void* k, const void* v, const void* g, const void* beta, float scale,
+                      void* out, const float* A_log, const float* dt_bias, float lower_bound,
+                      const void* initial_state, int initial_state_dtype, void* final_state, int final_state_dtype,
+                      const int64_t* cu_seqlens, int64_t num_seqs, int64_t B, int64_t T, int64_t H, int64_t K,
+                      int64_t V, int segments, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  try {
+    if (segments < 0 || segments > 4096)
+      return fail(KDA_EINVAL, "kda: segments must lie in 0 .. 4096 (got %d)", segments);
+    if (segments == 0) {   // the library's choice
+      int64_t N0 = 0;
+      const int rc0 = check_sizes(B, T, H, K, V, cu_seqlens, num_seqs, cu_seqlens != nullptr, &N0);
+      if (rc0 != KDA_OK) return rc0;
+      segments = choose_segments(B, T, H, N0, cu_seqlens != nullptr);
+    }
+    if (segments == 1)
+      return fwd_impl(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
+                      initial_state_dtype, final_state, final_state_dtype, cu_seqlens, num_seqs, B, T, H, K, V,
+                      workspace, workspace_bytes, stream, 0, 0, KDA_PATH_AUTO, nullptr, 0, nullptr);
+    // Every check of kda_fwd, on the caller's arguments, before any HIP call.
+    if ((!v || !out) && B * T > 0) return fail(KDA_EINVAL, "kda: v or out is NULL");
+    auto dtype_ok = [](int d) { return d == KDA_DTYPE_NONE || d == KDA_DTYPE_BF16 || d == KDA_DTYPE_FP32; };
+    if (!dtype_ok(initial_state_dtype) || !dtype_ok(final_state_dtype))
+      return fail(KDA_EDTYPE, "kda: state dtype codes must be KDA_DTYPE_NONE/BF16/FP32");
+    if ((initial_state == nullptr) != (initial_state_dtype == KDA_DTYPE_NONE))
+      return fail(KDA_EDTYPE, "kda: initial_state pointer and dtype disagree");
+    if ((final_state == nullptr) != (final_state_dtype == KDA_DTYPE_NONE))
+      return fail(KDA_EDTYPE, "kda: final_state pointer and dtype disagree");
+    if (initial_state && final_state && initial_state_dtype != final_state_dtype)
+      return fail(KDA_EDTYPE, "kda: initial_state and final_state dtypes differ");
+    int64_t N = 0;
+    int rc = check_sizes(B, T, H, K, V, cu_seqlens, num_seqs, cu_seqlens != nullptr, &N);
+    if (rc != KDA_OK) return rc;
+    if (N * segments >= (int64_t(1) << 30) || N * segments * H >= (int64_t(1) << 31))
+      return fail(KDA_EINVAL, "kda: N * segments too large");
+    SegLayout SL;
+    if (!seg_layout(B, T, H, N, segments, &SL)) return fail(KDA_EINVAL, "kda: bad sizes");
+    if (!workspace) return fail(KDA_EINVAL, "kda: workspace is NULL");
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+      return fail(KDA_EINVAL, "kda: workspace must be 256-byte aligned");
+    if ((int64_t)workspace_bytes < SL.total)
+      return fail(KDA_EWORKSPACE, "kda: workspace has %zu bytes, needs %lld", workspace_bytes,
+                  (long long)SL.total);
+    if (misaligned(v) || misaligned(out) || misaligned(initial_state) || misaligned(final_state))
+      return fail(KDA_EINVAL, "kda: v, out and the states must be 16-byte aligned");
+    char* ws = static_cast<char*>(workspace);
+    int64_t* seg_cu = reinterpret_cast<int64_t*>(ws + SL.seg_cu);
+    kda::Layout probe;
+    int64_t NS = 0;
+    rc = validate_common(q, k, g, beta, scale, A_log, dt_bias, lower_bound, seg_cu, N * segments, 1, B * T, H, K,
+                         V, ws + SL.inner, (size_t)SL.inner_bytes, kda::C, false, &probe, &NS);
+    if (rc != KDA_OK) return rc;
+    rc = check_device(nullptr);
+    if (rc != KDA_OK) return rc;
+
+    uint16_t* Am = reinterpret_cast<uint16_t*>(ws + SL.A);
+    float* Bm = reinterpret_cast<float*>(ws + SL.B);
+    float* starts = reinterpret_cast<float*>(ws + SL.starts);
+    const int64_t NS_ = N * segments, rows = B * T;
+    const int sdt = initial_state ? initial_state_dtype : final_state_dtype;
+
+    kda::Layout L;   // the plain forward's workspace for the segments
+    if (!kda::layout_for(1, rows, H, NS_, kda::C, &L)) return fail(KDA_EINVAL, "kda: bad sizes");
+    hipError_t e = kda::launch_seg_cu(kda::SegArgs{cu_seqlens, N, T, segments, seg_cu}, stream);
+    if (e != hipSuccess) return fail(KDA_EHIP, "kda: segment launch: %s", hipGetErrorString(e));
+    // The segments' chunk records: scheduler and chunk prep of the split path.
+    char* const iws = ws + SL.inner;
+    e = kda::launch_sched(kda::SchedArgs{seg_cu, NS_, 1, rows, H, 1, rows > 0 ? rows : 1, KDA_PATH_SPLIT, iws, L},
+                          stream);
+    if (e == hipSuccess)
+      e = kda::launch_prep(kda::PrepArgs{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                         static_cast<const uint16_t*>(g), static_cast<const uint16_t*>(beta), A_log,
+                                         dt_bias, scale, lower_bound, H, 0, L.max_chunks, iws, L},
+                           stream);
+    // One recurrence launch over those records, two argument sets and no
+    // outputs: B_j (the values from a zero start) and A_j (zero values from
+    // the identity).
+    if (e == hipSuccess) {
+      kda::RecurArgs ra{static_cast<const uint16_t*>(v), nullptr, nullptr, Bm, KDA_DTYPE_FP32, NS_, H, 0, 0,
+                        INT64_MAX / 2, iws, L, 2, Am};
+      e = kda::launch_recur(ra, stream);
+    }
+    if (e != hipSuccess) return fail(KDA_EHIP, "kda: launch: %s", hipGetErrorString(e));
+    // the segments' start states and the sequences' final states
+    e = kda::launch_prefix(kda::PrefixArgs{Am, Bm, starts, initial_state, final_state, sdt, N, H, segments,
+                                           reinterpret_cast<const kda::WsHeader*>(ws + SL.inner), seg_cu},
+                           stream);
+    if (e != hipSuccess) return fail(KDA_EHIP, "kda: prefix launch: %s", hipGetErrorString(e));
+    // the outputs, every segment from its true start
+    kda::RecurArgs ro{static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out), starts, nullptr,
+                      KDA_DTYPE_FP32, NS_, H, 0, 0, INT64_MAX / 2, iws, L};
+    e = kda::launch_recur(ro, stream);
+    if (e != hipSuccess) return fail(KDA_EHIP, "kda: recurrence launch: %s", hipGetErrorString(e));
+    return KDA_OK;
+  } catch (...) {
+    return fail(KDA_EHIP, "kda: unexpected C++ exception");
+  }
+}
+
 int kda_debug_prep(const void* q, const void* k, const void* g, const void* beta, float scale,
                    const float* A_log, const float* dt_bias, float lower_bound, const int64_t* cu_seqlens,
                    int64_t num_seqs, int64_t B, int64_t T, int64_t H, int64_t K, void* workspace,

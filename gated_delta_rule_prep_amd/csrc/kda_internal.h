@@ -128,6 +128,14 @@ struct RecurArgs {
   int64_t row_lo, row_hi;
   char* ws;
   Layout lay;
+  // sets == 2 (16-token chunks, one part): a second recurrence over the same
+  // chunk records in the same launch, pairs N H .. 2 N H - 1, that computes
+  // each pair's transition: zero values from the identity state, written as
+  // fp16 to s_out2 in math layout [n][h][k][v] (the values are read from v
+  // and ignored).  A NULL output pointer skips the outputs (always, for the
+  // second set).
+  int sets;
+  uint16_t* s_out2;
 };
 
 // Fused chunk prep + recurrence (one kernel, records kept in LDS): the
@@ -149,6 +157,28 @@ struct FusedArgs {
   int64_t N, H;
   char* ws;
   Layout lay;
+};
+
+// Segmented forward: segment boundaries and the prefix over the segments'
+// affine state maps (kda_segment.hip).
+struct SegArgs {
+  const int64_t* cu;    // the caller's cu_seqlens (device) or nullptr (N rows of T tokens)
+  int64_t N, T;
+  int S;                // segments per sequence
+  int64_t* seg_cu;      // written: N S + 1 boundaries
+};
+
+struct PrefixArgs {
+  const uint16_t* A;    // [N S][H][K][K]: transition of each (segment, head), fp16, math layout A[k][m]
+  const float* B;       // [N S][H][V][K]: end state from a zero start
+  float* starts;        // written: [N S][H][V][K] start state of each segment
+  const void* s_in;     // the caller's initial state [N][H][V][K] or nullptr
+  void* s_out;          // the caller's final state or nullptr
+  int state_dtype;      // KDA_DTYPE_* of the caller's states
+  int64_t N, H;
+  int S;
+  const WsHeader* hdr;  // the forward's header: nothing is written unless its status is OK
+  const int64_t* seg_cu;  // N S + 1 segment boundaries: an empty segment passes its state through
 };
 
 // Single-token step: token n of every sequence is row n of q, k, v, g, beta
@@ -173,6 +203,8 @@ struct DecodeArgs {
 hipError_t launch_sched(const SchedArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_fused(const FusedArgs& a, hipStream_t s);
+hipError_t launch_seg_cu(const SegArgs& a, hipStream_t s);
+hipError_t launch_prefix(const PrefixArgs& a, hipStream_t s);
 // The launchers pick the 16- or 32-token kernels by a.lay.chunk.
 hipError_t launch_prep(const PrepArgs& a, hipStream_t s);
 hipError_t launch_recur(const RecurArgs& a, hipStream_t s);

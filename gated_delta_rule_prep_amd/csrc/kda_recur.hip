@@ -180,9 +180,15 @@ __global__ __launch_bounds__(64 * W) void recur_kernel(RecurArgs a) {
   // XCD-aware placement: id b runs on XCD b % 8; the kTiles tiles of pair
   // 8 * g + x get ids 8 * (kTiles * g + tile) + x.
   const int64_t bid = blockIdx.x, x = bid & 7, q = bid >> 3;
-  const int64_t pair = 8 * (q / Cf::kTiles) + x;
+  const int64_t pairs = a.N * H, pair2 = 8 * (q / Cf::kTiles) + x;
   const int tile = (int)(q % Cf::kTiles);
-  if (pair >= a.N * H) return;
+  if (pair2 >= (a.sets == 2 ? 2 * pairs : pairs)) return;
+  const bool alt = pair2 >= pairs;   // the second set: the transition (zero values, identity start)
+  const int64_t pair = alt ? pair2 - pairs : pair2;
+  uint16_t* const outp = alt ? nullptr : a.out;
+  const void* const s_in = alt ? nullptr : a.s_in;
+  void* const s_out = alt ? static_cast<void*>(a.s_out2) : a.s_out;   // (alt: written below as fp16)
+  const int sdt = alt ? KDA_DTYPE_FP32 : a.state_dtype;
   if (reinterpret_cast<const WsHeader*>(a.ws)->path == KDA_PATH_FUSED) return;   // the fused kernel runs instead
   const int64_t slot_id = pair / H;
   const int h = (int)(pair - slot_id * H);
@@ -222,12 +228,15 @@ __global__ __launch_bounds__(64 * W) void recur_kernel(RecurArgs a) {
       const int64_t idx = sbase + (int64_t)(col0 + 16 * nt + lc) * K + 16 * m + 4 * lg;
       if (!from_caller) {
         Z[m][nt] = *reinterpret_cast<const f32x4*>(ws_state + idx);
-      } else if (a.s_in == nullptr) {
+      } else if (alt) {   // stored [v][k] = (v == k); this lane holds k = 16 m + 4 lg + i, v = col0 + 16 nt + lc
+        const int kv = col0 + 16 * nt + lc - 16 * m - 4 * lg;
+        Z[m][nt] = f32x4{kv == 0 ? 1.f : 0.f, kv == 1 ? 1.f : 0.f, kv == 2 ? 1.f : 0.f, kv == 3 ? 1.f : 0.f};
+      } else if (s_in == nullptr) {
         Z[m][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      } else if (a.state_dtype == KDA_DTYPE_FP32) {
-        Z[m][nt] = *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.s_in) + idx);
+      } else if (sdt == KDA_DTYPE_FP32) {
+        Z[m][nt] = *reinterpret_cast<const f32x4*>(static_cast<const float*>(s_in) + idx);
       } else {
-        const u32x2 w = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(a.s_in) + idx);
+        const u32x2 w = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(s_in) + idx);
         Z[m][nt] = f32x4{bf16_lo(w[0]), bf16_hi(w[0]), bf16_lo(w[1]), bf16_hi(w[1])};
       }
     }
@@ -241,7 +250,7 @@ __global__ __launch_bounds__(64 * W) void recur_kernel(RecurArgs a) {
     const uint32_t ring0 = (uint32_t)reinterpret_cast<uintptr_t>((lds_void*)ring[0]);
     // Output rows of a full chunk: a wave-uniform base per chunk plus this
     // lane's fixed offset (token lc, columns 16 nt + 4 lg .. +3).
-    uint16_t* const out_seq = a.out + ((int64_t)se.row0 * H + h) * V + col0;
+    uint16_t* const out_seq = outp + ((int64_t)se.row0 * H + h) * V + col0;
     const int64_t out_chunk = (int64_t)C * H * V;
     const int out_lane = (int)((lc * H) * V) + 4 * lg;
     // Chunks ci_lo .. ci_lo + D-2 in flight before the first step.  Loads past
@@ -262,27 +271,31 @@ __global__ __launch_bounds__(64 * W) void recur_kernel(RecurArgs a) {
       // every wave's loads of chunk ci have landed.
       const int refill = slot == 0 ? D - 1 : slot - 1;
       issue_chunk<NT, D, W>(ring0 + refill * Cf::kSlotBytes, pl, recs, vseq, se, ci + D - 1, clast, row_bytes, wave);
-      if (ci > ci_lo) {   // output of chunk ci - 1, a full chunk (only a sequence's last chunk is partial)
+      if (ci > ci_lo && outp != nullptr) {   // output of chunk ci - 1, a full chunk (only a sequence's last chunk is partial)
         uint16_t* const ob = out_seq + (int64_t)(ci - 1) * out_chunk;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) *reinterpret_cast<u32x2*>(ob + out_lane + 16 * nt) = o_prev[nt];
       }
       Ops<NT> ops;
       read_ops<NT>(ops, ring[slot] + Cf::kRec, ring[slot] + Cf::kVal, 2 * Cf::kCols, wc, lane);
+      if (alt) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) ops.v[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
       compute<NT>(Z, ops, o_prev);
       slot = slot == D - 1 ? 0 : slot + 1;
     }
     wait_vmcnt<0>();   // no load into the ring outlives the workgroup
     const Rows pr = chunk_rows(se, clast);
-    if (lc < pr.len) {
+    if (lc < pr.len && outp != nullptr) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
-        *reinterpret_cast<u32x2*>(a.out + ((pr.row0 + lc) * H + h) * V + col0 + 16 * nt + 4 * lg) = o_prev[nt];
+        *reinterpret_cast<u32x2*>(outp + ((pr.row0 + lc) * H + h) * V + col0 + 16 * nt + 4 * lg) = o_prev[nt];
     }
   }
 
   // ---- state out
-  if (!to_caller || a.s_out != nullptr) {
+  if (!to_caller || s_out != nullptr) {
 #pragma unroll
     for (int m = 0; m < 8; ++m)
 #pragma unroll
@@ -290,13 +303,17 @@ __global__ __launch_bounds__(64 * W) void recur_kernel(RecurArgs a) {
         const int64_t idx = sbase + (int64_t)(col0 + 16 * nt + lc) * K + 16 * m + 4 * lg;
         if (!to_caller) {
           *reinterpret_cast<f32x4*>(ws_state + idx) = Z[m][nt];
-        } else if (a.state_dtype == KDA_DTYPE_FP32) {
-          *reinterpret_cast<f32x4*>(static_cast<float*>(a.s_out) + idx) = Z[m][nt];
+        } else if (alt) {   // the transition, fp16 in math layout [k][v]
+          uint16_t* const at = a.s_out2 + sbase + (int64_t)(16 * m + 4 * lg) * V + col0 + 16 * nt + lc;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) at[i * V] = __builtin_bit_cast(uint16_t, (_Float16)Z[m][nt][i]);
+        } else if (sdt == KDA_DTYPE_FP32) {
+          *reinterpret_cast<f32x4*>(static_cast<float*>(s_out) + idx) = Z[m][nt];
         } else {
           u32x2 w;
           w[0] = pack_bf16(Z[m][nt][0], Z[m][nt][1]);
           w[1] = pack_bf16(Z[m][nt][2], Z[m][nt][3]);
-          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.s_out) + idx) = w;
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(s_out) + idx) = w;
         }
       }
   }
@@ -304,8 +321,9 @@ __global__ __launch_bounds__(64 * W) void recur_kernel(RecurArgs a) {
 
 template <int NT, int D, int W>
 hipError_t launch_tiles(const RecurArgs& a, hipStream_t s) {
-  const int64_t pairs = a.N * a.H;
+  const int64_t pairs = a.N * a.H * (a.sets == 2 ? 2 : 1);
   const int64_t grid = 8 * Cfg<NT, D, W>::kTiles * ((pairs + 7) / 8);
+  if (grid > INT32_MAX) return hipErrorInvalidValue;
   hipLaunchKernelGGL((recur_kernel<NT, D, W>), dim3((unsigned)grid), dim3(64 * W), 0, s, a);
   return hipGetLastError();
 }
@@ -329,7 +347,7 @@ hipError_t launch_tiles(const RecurArgs& a, hipStream_t s) {
 #endif
 
 hipError_t launch_recur(const RecurArgs& a, hipStream_t s) {
-  if (a.lay.chunk == C32) return launch_recur32(a, s);
+  if (a.lay.chunk == C32) return a.sets == 2 ? hipErrorInvalidValue : launch_recur32(a, s);
   if (a.N * a.H == 0) return hipSuccess;
   return launch_tiles<1, KDA_RECUR_DEPTH, 4>(a, s);
 }

@@ -29,7 +29,8 @@ PATHS = {None: KDA_PATH_AUTO, "auto": KDA_PATH_AUTO, "split": KDA_PATH_SPLIT, "f
 CHUNK = 16
 
 EXPORTS = ("kda_fwd", "kda_fwd_profiled", "kda_fwd_ex", "kda_fwd_parts", "kda_fwd_path", "kda_fwd_path_taken",
-           "kda_fwd_num_events",
+           "kda_fwd_num_events", "kda_fwd_segmented", "kda_fwd_segmented_workspace_bytes",
+           "kda_fwd_segments",
            "kda_decode", "kda_fwd_workspace_bytes", "kda_fwd_workspace_bytes_ex", "kda_get_last_error",
            "kda_version", "kda_fwd_check_status", "kda_workspace_layout", "kda_debug_prep")
 
@@ -60,6 +61,12 @@ _lib.kda_fwd_num_events.restype = ctypes.c_int
 _lib.kda_fwd_workspace_bytes_ex.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                             ctypes.c_int]
 _lib.kda_fwd_workspace_bytes_ex.restype = ctypes.c_size_t
+_lib.kda_fwd_segmented.argtypes = _lib.kda_fwd.argtypes[:21] + [ctypes.c_int, _p, ctypes.c_size_t, _p]
+_lib.kda_fwd_segmented.restype = ctypes.c_int
+_lib.kda_fwd_segmented_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int]
+_lib.kda_fwd_segmented_workspace_bytes.restype = ctypes.c_size_t
+_lib.kda_fwd_segments.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int]
+_lib.kda_fwd_segments.restype = ctypes.c_int
 _lib.kda_decode.argtypes = [_p, _p, _p, _p, _p, ctypes.c_float, _p, _p, _p, ctypes.c_float,
                             _p, ctypes.c_int, _p, ctypes.c_int, _i64, _i64, _i64, _i64, _p]
 _lib.kda_decode.restype = ctypes.c_int
@@ -196,6 +203,16 @@ def alloc_workspace(B: int, T: int, H: int, num_seqs: int, has_cu: bool, device,
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
+def segmented_workspace_bytes(B: int, T: int, H: int, num_seqs: int, has_cu_seqlens: bool, segments: int) -> int:
+    """Bytes of workspace kda_fwd_segmented needs (0 on bad sizes)."""
+    return _lib.kda_fwd_segmented_workspace_bytes(B, T, H, num_seqs, int(bool(has_cu_seqlens)), int(segments))
+
+
+def segments_for(B: int, T: int, H: int, num_seqs: int = 0, has_cu_seqlens: bool = False) -> int:
+    """The segment count kda_fwd_segmented chooses for segments = 0."""
+    return _lib.kda_fwd_segments(B, T, H, num_seqs, int(bool(has_cu_seqlens)))
+
+
 def parts(B: int, T: int, requested: int = 0) -> int:
     """Parts (overlapped prep / recurrence ranges) a call uses; see kda_fwd_ex."""
     return _lib.kda_fwd_parts(B, T, requested)
@@ -203,7 +220,7 @@ def parts(B: int, T: int, requested: int = 0) -> int:
 
 def fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state=None, final_state=None,
         cu_seqlens=None, workspace: Optional[torch.Tensor] = None, events=None, parts: Optional[int] = None,
-        chunk: Optional[int] = None, path=None):
+        chunk: Optional[int] = None, path=None, segments: Optional[int] = None):
     """Chunked KDA forward into the caller's ``out`` (and ``final_state``).
 
     Shapes and dtypes as in include/kda.h.  Runs on the current stream of the
@@ -214,7 +231,9 @@ def fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state
     ``events``: optional torch.cuda.Event list (enable_timing=True): with no
     chunk / parts / path, four go through kda_fwd_profiled; otherwise
     ``num_events(B, T, chunk, parts, path)`` go through kda_fwd_ex, which
-    records them around every kernel.
+    records them around every kernel.  ``segments``: cut every sequence into
+    that many pieces run side by side (kda_fwd_segmented; 0 or 'auto' for the
+    library's choice); it takes none of events / parts / chunk / path.
     """
     if q.dim() != 4:
         raise KDAValueError(KDA_EINVAL, "q must be [B, T, H, K]")
@@ -247,7 +266,18 @@ def fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state
     if dev.type != "cuda":
         raise KDAValueError(KDA_EINVAL, "tensors must be on a HIP device, got %s" % dev)
     path_c = _path_code(path)
-    if workspace is None:   # just what this call's path needs
+    if segments == "auto":
+        segments = 0
+    if segments is not None:
+        if events is not None or parts is not None or chunk is not None or path is not None:
+            raise KDAValueError(KDA_EINVAL, "segments takes none of events, parts, chunk, path")
+        if workspace is None:
+            n = segmented_workspace_bytes(B, T, H, N, cu_seqlens is not None, segments)
+            if n == 0:
+                raise KDAValueError(KDA_EINVAL, "bad sizes for the workspace: B=%d T=%d H=%d segments=%d" % (
+                    B, T, H, segments))
+            workspace = torch.empty(n, dtype=torch.uint8, device=dev)
+    elif workspace is None:   # just what this call's path needs
         workspace = alloc_workspace(B, T, H, N, cu_seqlens is not None, dev, chunk, parts,
                                     "auto" if path is None else path)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(out),
@@ -256,7 +286,9 @@ def fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state
             _ptr(cu_seqlens), N, B, T, H, K, V, _ptr(workspace), workspace.numel())
     with torch.cuda.device(dev):
         plain = parts is None and chunk is None and path is None
-        if events is None and plain:
+        if segments is not None:
+            rc = _lib.kda_fwd_segmented(*args[:21], int(segments), *args[21:], _stream(dev))
+        elif events is None and plain:
             rc = _lib.kda_fwd(*args, _stream(dev))
         elif plain and len(events) == 4:
             ev = (ctypes.c_void_p * 4)(*[e.cuda_event for e in events])

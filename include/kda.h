@@ -219,6 +219,57 @@ int kda_fwd_path_taken(const void* workspace, hipStream_t stream, int* path);
 int kda_fwd_num_events(int64_t B, int64_t T, int chunk, int parts, int path);
 
 /*
+ * kda_fwd_segmented -- kda_fwd with every sequence cut into `segments` pieces
+ * whose chunk chains run side by side, for calls with few long sequences and
+ * few heads, where one (sequence, head) chain per value tile cannot fill the
+ * chip.  P1 §二 2.2 keeps the recurrence stage parallel over heads only and
+ * shows the long unfragmented sequence as the slow case; cutting a sequence
+ * is this library's addition, not on the pages.
+ *
+ * Over a segment the update of P1 §一 maps the starting state affinely,
+ * S_end = A S_start + B, with A the product of (I - beta_t kn_t kn_t^T)
+ * diag(exp(a_t)) over the segment's tokens and B its end state from a zero
+ * start.  The call runs the plain forward (the library's path choice) three
+ * times over all segments of all sequences: with the values from a zero start
+ * (giving B), with zero values from the identity (giving A), and with the
+ * values from each segment's true start, which a small fp32 kernel composes
+ * per (sequence, head) as S_start(0) = initial state,
+ * S_start(j + 1) = A_j S_start(j) + B_j; the last composition is the final
+ * state.  Segments are ceil(len / segments) tokens rounded up to whole
+ * 16-token chunks, the last ones shorter or empty.  The result equals kda_fwd's
+ * up to rounding (the states between segments are kept in fp32).
+ *
+ * The three runs share one set of chunk records (built once by the split
+ * path's scheduler and prep kernels); the first two are one recurrence launch
+ * that writes no outputs.
+ *
+ * Arguments, checks, states (the same buffer allowed for both) and the device
+ * status word are those of kda_fwd.  segments: 1 .. 4096, or 0 for the
+ * library's choice (kda_fwd_segments); 1 is exactly kda_fwd.  workspace:
+ * 256-byte aligned, of at least kda_fwd_segmented_workspace_bytes(...) bytes
+ * with the same `segments` (kda_fwd's workspace for the segments, then per
+ * (segment, head) the 128 x 128 transition A in fp16 and two fp32 128 x 128
+ * states); kda_fwd_check_status reads it as it reads kda_fwd's.
+ * A's entries lie in [-1, 1] (each factor is a contraction), so it is kept in
+ * fp16, and the composition uses fp16 operands with fp32 accumulation.
+ */
+int kda_fwd_segmented(const void* q, const void* k, const void* v, const void* g, const void* beta, float scale,
+                      void* out, const float* A_log, const float* dt_bias, float lower_bound,
+                      const void* initial_state, int initial_state_dtype, void* final_state, int final_state_dtype,
+                      const int64_t* cu_seqlens, int64_t num_seqs, int64_t B, int64_t T, int64_t H, int64_t K,
+                      int64_t V, int segments, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* The segment count kda_fwd_segmented takes for segments = 0: the largest
+   power of two that keeps at most 128 (segment, head) chains and segments of
+   at least 512 tokens (the mean length with cu_seqlens), or 1 (no cut) when
+   that is below 4.  0 on bad sizes. */
+int kda_fwd_segments(int64_t B, int64_t T, int64_t H, int64_t num_seqs, int has_cu_seqlens);
+
+/* Workspace bytes kda_fwd_segmented needs (0 on bad sizes). */
+size_t kda_fwd_segmented_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t num_seqs, int has_cu_seqlens,
+                                         int segments);
+
+/*
  * kda_decode -- enqueue one recurrent step (one new token per sequence) on
  * `stream`: the token-by-token recurrence of P1 §一 with the activations of
  * kda_fwd, no chunking and no workspace.

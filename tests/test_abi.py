@@ -258,3 +258,67 @@ def test_decode_host_validation_rejects(over, code):
     rc = call_decode(**over)
     assert rc == code, (rc, kda.last_error())
     assert kda.last_error()
+
+
+def call_seg(segments, **over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, scale=0.088, out=FAKE, A_log=FAKE, dt_bias=FAKE,
+             lb=-5.0, s0=None, s0_dt=0, s1=None, s1_dt=0, cu=None, N=0, B=1, T=64, H=2, K=128, V=128,
+             ws=WS, ws_bytes=1 << 40, stream=None)
+    a.update(over)
+    return kda.lib().kda_fwd_segmented(a["q"], a["k"], a["v"], a["g"], a["beta"], a["scale"], a["out"],
+                                       a["A_log"], a["dt_bias"], a["lb"], a["s0"], a["s0_dt"], a["s1"], a["s1_dt"],
+                                       a["cu"], a["N"], a["B"], a["T"], a["H"], a["K"], a["V"], segments, a["ws"],
+                                       a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("segments", [1, 4])
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), kda.KDA_EINVAL),
+    (dict(v=None), kda.KDA_EINVAL),
+    (dict(out=None), kda.KDA_EINVAL),
+    (dict(dt_bias=None), kda.KDA_EINVAL),
+    (dict(ws=None), kda.KDA_EINVAL),
+    (dict(ws=ctypes.c_void_p(0x100010)), kda.KDA_EINVAL),
+    (dict(v=ctypes.c_void_p(0x1004)), kda.KDA_EINVAL),
+    (dict(K=64), kda.KDA_EINVAL),
+    (dict(cu=FAKE, N=2, B=2), kda.KDA_EINVAL),
+    (dict(lb=0.5), kda.KDA_EINVAL),
+    (dict(s0=FAKE, s0_dt=1, s1=FAKE, s1_dt=2), kda.KDA_EDTYPE),
+    (dict(s0=None, s0_dt=2), kda.KDA_EDTYPE),
+    (dict(ws_bytes=700), kda.KDA_EWORKSPACE),
+])
+def test_segmented_host_validation_rejects(segments, over, code):
+    rc = call_seg(segments, **over)
+    assert rc == code, (rc, kda.last_error())
+
+
+def test_segmented_segments_and_workspace():
+    """kda_fwd_segmented: the segment count it takes and its workspace, which
+    starts with the plain forward's workspace for the segments (so the status
+    word sits where kda_fwd_check_status reads it)."""
+    for bad in (-1, 4097):
+        assert call_seg(bad) == kda.KDA_EINVAL and "segments" in kda.last_error()
+        assert kda.segmented_workspace_bytes(1, 64, 2, 0, False, bad) == 0
+    # the library's count: the largest power of two with at most 128
+    # (segment, head) chains and segments of at least 512 tokens, 1 below 4
+    for (B, T, H, N, cu), want in (((1, 8192, 4, 0, False), 16), ((1, 8192, 16, 0, False), 8),
+                                   ((1, 8192, 32, 0, False), 4), ((1, 8192, 64, 0, False), 1),
+                                   ((1, 8192, 96, 0, False), 1), ((1, 65536, 4, 0, False), 32),
+                                   ((1, 32768, 8, 0, False), 16), ((1, 1024, 4, 0, False), 1),
+                                   ((2, 8192, 4, 0, False), 16), ((1, 16384, 4, 2, True), 16),
+                                   ((1, 8192, 1, 8, True), 1)):
+        assert kda.segments_for(B, T, H, N, cu) == want, (B, T, H, N, cu)
+        assert (kda.segmented_workspace_bytes(B, T, H, N, cu, 0)
+                == kda.segmented_workspace_bytes(B, T, H, N, cu, want))
+    assert kda.segments_for(1, 64, 0) == 0
+    assert kda.segmented_workspace_bytes(1, 8192, 96, 0, False, 1) == kda.workspace_bytes(1, 8192, 96, path="auto")
+    al = lambda x: (x + 255) // 256 * 256
+    for B, T, H, N, has_cu, S in ((1, 8192, 8, 0, False, 4), (2, 1000, 3, 0, False, 3), (1, 5000, 4, 3, True, 8)):
+        NS = (N if has_cu else B) * S
+        inner = kda.workspace_bytes(1, B * T, H, NS, True, path="auto")
+        mat = NS * H * 128 * 128 * 4
+        want = al(inner) + al((NS + 1) * 8) + al(mat // 2) + 2 * al(mat)   # A in fp16, two fp32 states
+        assert kda.segmented_workspace_bytes(B, T, H, N, has_cu, S) == want
+    # a workspace one byte short is refused on the host
+    need = kda.segmented_workspace_bytes(1, 64, 2, 0, False, 4)
+    assert call_seg(4, ws_bytes=need - 1) == kda.KDA_EWORKSPACE
