@@ -53,17 +53,24 @@ def param_bytes(inp):
     return inp.H * 4 + inp.H * inp.K * 4
 
 
-def run_workload(cfg, steps, warmup, torch, kda, device_inputs, chunk=None, path=None):
+def run_workload(cfg, steps, warmup, torch, kda, device_inputs, chunk=None, path=None, precision=None):
     inp = cfg.make()
     d = device_inputs(inp, "cuda")
     out = torch.empty((inp.B, inp.T, inp.H, inp.V), dtype=torch.bfloat16, device="cuda")
     fin = torch.empty((inp.N, inp.H, inp.V, inp.K),
                       dtype=torch.bfloat16 if inp.state_dtype == "bf16" else torch.float32, device="cuda")
     path = path or "auto"
+    if precision is not None:   # the precision study entry point: split path, 16-token chunks
+        chunk, path = 16, "split"
     used = kda.path_used(chunk, None, path)
     ws = kda.alloc_workspace(inp.B, inp.T, inp.H, inp.N, inp.cu_seqlens is not None, "cuda", chunk, None, path)
 
     def step(events=None):
+        if precision is not None:
+            kda.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], inp.scale, out, d["A_log"], d["dt_bias"],
+                    inp.lower_bound, initial_state=d["initial_state"], final_state=fin,
+                    cu_seqlens=d["cu_seqlens"], workspace=ws, precision=precision)
+            return
         kda.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], inp.scale, out, d["A_log"], d["dt_bias"],
                 inp.lower_bound, initial_state=d["initial_state"], final_state=fin,
                 cu_seqlens=d["cu_seqlens"], workspace=ws, events=events, chunk=chunk, path=path)
@@ -79,6 +86,10 @@ def run_workload(cfg, steps, warmup, torch, kda, device_inputs, chunk=None, path
     t1.record()
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / steps
+    if precision is not None:   # kda_fwd_precision records no events
+        th = inp.B * inp.T * inp.H
+        return dict(inp=inp, ms=ms, kernels={}, path=used, taken="split", token_heads=th,
+                    status=kda.check_status(ws))
 
     # per-kernel durations: kda_fwd_ex records HIP events before and after
     # every kernel on the stream it launches that kernel on
@@ -270,6 +281,8 @@ def main():
                     help="tokens per chunk (0: the library's choice)")
     ap.add_argument("--path", choices=["auto", "fused", "split"], default="auto",
                     help="execution path of kda_fwd_ex (auto: the library's choice)")
+    ap.add_argument("--precision", type=int, default=None, choices=list(range(8)),
+                    help="with --only fixed/varlen: time kda_fwd_precision with this KDA_PREC_* variant")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="with --only: afterwards run 3 device-to-device copies of this many MiB, a plain copy "
                          "kernel of known size that scales the HBM byte counters")
@@ -296,8 +309,9 @@ def main():
     chunk = args.chunk or None
     if args.only != "both":
         res = run_workload(cfgs[2] if args.only == "fixed" else cfgs[3], args.steps, args.warmup, torch, kda,
-                           device_inputs, chunk, args.path)
+                           device_inputs, chunk, args.path, args.precision)
         print(json.dumps({"workload": res["inp"].name, "path": res["path"], "path_taken": res["taken"],
+                          "precision": args.precision,
                           "ms_per_step": round(res["ms"], 4),
                           "kernels_ms": {k: round(v, 4) for k, v in res["kernels"].items()}}))
         if args.copy_mib > 0:

@@ -284,7 +284,7 @@ static int fwd_impl(const void* q, const void* k, const void* v, const void* g, 
                     int final_state_dtype, const int64_t* cu_seqlens, int64_t num_seqs, int64_t B,
                     int64_t T, int64_t H, int64_t K, int64_t V, void* workspace, size_t workspace_bytes,
                     hipStream_t stream, int chunk_req, int parts_req, int path_req, hipEvent_t* ev, int n_ev,
-                    hipEvent_t* ev4) {
+                    hipEvent_t* ev4, int precision = 0) {
   try {
     if ((!v || !out) && B * T > 0) return fail(KDA_EINVAL, "kda: v or out is NULL");
     auto dtype_ok = [](int d) { return d == KDA_DTYPE_NONE || d == KDA_DTYPE_BF16 || d == KDA_DTYPE_FP32; };
@@ -394,6 +394,7 @@ static int fwd_impl(const void* q, const void* k, const void* v, const void* g, 
       const int64_t lo = p * part_rows, hi = p == P - 1 ? (INT64_MAX / 2) : (p + 1) * part_rows;
       kda::RecurArgs ra{static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out), initial_state, final_state,
                         sdt, N, H, p, lo, hi, ws, L};
+      ra.precision = precision;
       rec(2 + 2 * P + 2 * p, rstream);
       if (e == hipSuccess) e = kda::launch_recur(ra, rstream);
       rec(3 + 2 * P + 2 * p, rstream);
@@ -443,6 +444,19 @@ int kda_fwd_profiled(const void* q, const void* k, const void* v, const void* g,
   return fwd_impl(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
                   initial_state_dtype, final_state, final_state_dtype, cu_seqlens, num_seqs, B, T, H, K, V,
                   workspace, workspace_bytes, stream, 0, 0, KDA_PATH_AUTO, nullptr, 0, events);
+}
+
+int kda_fwd_precision(const void* q, const void* k, const void* v, const void* g, const void* beta, float scale,
+                      void* out, const float* A_log, const float* dt_bias, float lower_bound,
+                      const void* initial_state, int initial_state_dtype, void* final_state, int final_state_dtype,
+                      const int64_t* cu_seqlens, int64_t num_seqs, int64_t B, int64_t T, int64_t H, int64_t K,
+                      int64_t V, void* workspace, size_t workspace_bytes, hipStream_t stream, int variant) {
+  const int all = KDA_PREC_BF16_STATE | KDA_PREC_BF16_INVERSE | KDA_PREC_BF16_STATE_PRODUCTS;
+  if (variant < 0 || (variant & ~all) != 0)
+    return fail(KDA_EINVAL, "kda: precision variant must be a combination of KDA_PREC_* bits (got %d)", variant);
+  return fwd_impl(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state, initial_state_dtype,
+                  final_state, final_state_dtype, cu_seqlens, num_seqs, B, T, H, K, V, workspace, workspace_bytes,
+                  stream, kda::C, 1, KDA_PATH_SPLIT, nullptr, 0, nullptr, variant);
 }
 
 int kda_fwd_parts(int64_t B, int64_t T, int parts) {

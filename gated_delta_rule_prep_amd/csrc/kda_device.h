@@ -30,6 +30,12 @@ __device__ __forceinline__ f32x4 mfma_f16_k16(f16x4 a, f16x4 b, f32x4 c) {
 __device__ __forceinline__ f32x4 mfma_bf16_k32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4 mfma_bf16_k16(bf16x4 a, bf16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a), __builtin_bit_cast(s16x4_t, b), c,
+                                                   0, 0, 0);
+}
 // fp32 16x16x4: A lane l holds row l%16, k = l/16; B lane l holds col l%16, k = l/16.
 __device__ __forceinline__ f32x4 mfma_f32_k4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -42,8 +48,7 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_floa
 
 // fp32 -> bf16 bits, round to nearest even (hardware conversion).
 __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
-  __bf16 b = (__bf16)x;
-  return *reinterpret_cast<uint16_t*>(&b);
+  return __builtin_bit_cast(uint16_t, (__bf16)x);   // (not a read through a uint16_t pointer: that aliasing is undefined)
 }
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);

@@ -136,6 +136,9 @@ struct RecurArgs {
   // second set).
   int sets;
   uint16_t* s_out2;
+  // Precision variant of the chunk step (KDA_PREC_*, 16-token chunks only);
+  // 0 is the library's own arithmetic.
+  int precision;
 };
 
 // Fused chunk prep + recurrence (one kernel, records kept in LDS): the

@@ -172,7 +172,7 @@ __device__ __forceinline__ void wait_chunk(int wave) {
   }
 }
 
-template <int NT, int D, int W>
+template <int NT, int D, int W, int PV>
 __global__ __launch_bounds__(64 * W) void recur_kernel(RecurArgs a) {
   using Cf = Cfg<NT, D, W>;
   __shared__ __align__(1024) char ring[D][Cf::kSlotBytes];
@@ -282,7 +282,7 @@ __global__ __launch_bounds__(64 * W) void recur_kernel(RecurArgs a) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) ops.v[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
-      compute<NT>(Z, ops, o_prev);
+      compute<NT, PV>(Z, ops, o_prev);
       slot = slot == D - 1 ? 0 : slot + 1;
     }
     wait_vmcnt<0>();   // no load into the ring outlives the workgroup
@@ -319,12 +319,26 @@ __global__ __launch_bounds__(64 * W) void recur_kernel(RecurArgs a) {
   }
 }
 
+// Launches recur_kernel<..., PV> for PV = a.precision, PV running over 0 .. 7.
+template <int NT, int D, int W, int PV>
+void launch_variant(const RecurArgs& a, int64_t grid, hipStream_t s) {
+  if constexpr (PV < 8) {
+    if (a.precision == PV) {
+      hipLaunchKernelGGL((recur_kernel<NT, D, W, PV>), dim3((unsigned)grid), dim3(64 * W), 0, s, a);
+      return;
+    }
+    launch_variant<NT, D, W, PV + 1>(a, grid, s);
+  }
+}
+
 template <int NT, int D, int W>
 hipError_t launch_tiles(const RecurArgs& a, hipStream_t s) {
   const int64_t pairs = a.N * a.H * (a.sets == 2 ? 2 : 1);
   const int64_t grid = 8 * Cfg<NT, D, W>::kTiles * ((pairs + 7) / 8);
   if (grid > INT32_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((recur_kernel<NT, D, W>), dim3((unsigned)grid), dim3(64 * W), 0, s, a);
+  // the study's variants (kda_fwd_precision): any combination of the three bits
+  if (a.precision < 0 || a.precision > 7) return hipErrorInvalidValue;
+  launch_variant<NT, D, W, 0>(a, grid, s);
   return hipGetLastError();
 }
 
@@ -347,7 +361,7 @@ hipError_t launch_tiles(const RecurArgs& a, hipStream_t s) {
 #endif
 
 hipError_t launch_recur(const RecurArgs& a, hipStream_t s) {
-  if (a.lay.chunk == C32) return a.sets == 2 ? hipErrorInvalidValue : launch_recur32(a, s);
+  if (a.lay.chunk == C32) return a.sets == 2 || a.precision != 0 ? hipErrorInvalidValue : launch_recur32(a, s);
   if (a.N * a.H == 0) return hipSuccess;
   return launch_tiles<1, KDA_RECUR_DEPTH, 4>(a, s);
 }

@@ -106,10 +106,47 @@ __device__ __forceinline__ f32x4 decay(f32x4 z, f32x2 g2) {
                z[2] * row_bcast<4 * (M & 3) + 2>(g), z[3] * row_bcast<4 * (M & 3) + 3>(g)};
 }
 
+// Precision variants of the step (compile-time bits), for the study of the
+// choices in §二 2.3 of the FlashKDA blog post; the library's own arithmetic is
+// kPrecDefault.
+//   kPrecBf16State: the state is rounded to bf16 after every chunk update (the
+//     pages store it in bf16 between updates; the update itself stays fp32).
+//   kPrecBf16Inverse: E = T R with T and R in bf16 (the pages keep the inverse
+//     in fp16); E is rounded to bf16 and, exactly representable in fp16, feeds
+//     the later products unchanged.
+//   kPrecBf16StateProducts: Khat Z and Qhat Z with the state copy and the
+//     record's -Khat and Qhat in bf16 instead of fp16.
+constexpr int kPrecDefault = 0, kPrecBf16State = 1, kPrecBf16Inverse = 2, kPrecBf16StateProducts = 4;
+
+// bf16 rounding for the variants, written out on the fp32 bits (round to
+// nearest even; the values here are finite): the bf16 bits of x, and x rounded
+// to bf16 as an fp32 value.
+__device__ __forceinline__ uint32_t bf16_bits(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ float bf16_round(float x) { return __uint_as_float(bf16_bits(x) << 16); }
+__device__ __forceinline__ bf16x4 bf4_of(f32x4 x) {
+  const u32x2 w = {bf16_bits(x[0]) | (bf16_bits(x[1]) << 16), bf16_bits(x[2]) | (bf16_bits(x[3]) << 16)};
+  return __builtin_bit_cast(bf16x4, w);
+}
+__device__ __forceinline__ bf16x4 bf4_of(f16x4 h) {
+  return bf4_of(f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]});
+}
+__device__ __forceinline__ bf16x8 bf8_of(f32x4 lo, f32x4 hi) {
+  const u32x4 w = {bf16_bits(lo[0]) | (bf16_bits(lo[1]) << 16), bf16_bits(lo[2]) | (bf16_bits(lo[3]) << 16),
+                   bf16_bits(hi[0]) | (bf16_bits(hi[1]) << 16), bf16_bits(hi[2]) | (bf16_bits(hi[3]) << 16)};
+  return __builtin_bit_cast(bf16x8, w);
+}
+__device__ __forceinline__ bf16x8 bf8_of(f16x8 h) {
+  return bf8_of(f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]},
+                f32x4{(float)h[4], (float)h[5], (float)h[6], (float)h[7]});
+}
+
 // One chunk step from operands in registers: updates Z and returns the output
 // tile as O^T (lane (lc, lg): token lc, value columns 16nt + 4lg .. +3 of the
 // wave), rounded to bf16 and packed.
-template <int NT>
+template <int NT, int PV = kPrecDefault>
 __device__ __forceinline__ void compute(f32x4 (&Z)[8][NT], const Ops<NT>& o, u32x2 (&out)[NT]) {
   // ---- R = V + (-Khat) Z ; O^T = Z^T Qhat^T
   f32x4 R[NT], O[NT];
@@ -122,14 +159,20 @@ __device__ __forceinline__ void compute(f32x4 (&Z)[8][NT], const Ops<NT>& o, u32
   for (int s = 0; s < 4; ++s) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      f16x8 zb;
+      if constexpr ((PV & kPrecBf16StateProducts) != 0) {
+        const bf16x8 zb = bf8_of(Z[2 * s][nt], Z[2 * s + 1][nt]);
+        R[nt] = mfma_bf16_k32(bf8_of(o.aw[s]), zb, R[nt]);
+        O[nt] = mfma_bf16_k32(zb, bf8_of(o.aq[s]), O[nt]);
+      } else {
+        f16x8 zb;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        zb[i] = (_Float16)Z[2 * s][nt][i];
-        zb[4 + i] = (_Float16)Z[2 * s + 1][nt][i];
+        for (int i = 0; i < 4; ++i) {
+          zb[i] = (_Float16)Z[2 * s][nt][i];
+          zb[4 + i] = (_Float16)Z[2 * s + 1][nt][i];
+        }
+        R[nt] = mfma_f16_k32(o.aw[s], zb, R[nt]);
+        O[nt] = mfma_f16_k32(zb, o.aq[s], O[nt]);
       }
-      R[nt] = mfma_f16_k32(o.aw[s], zb, R[nt]);
-      O[nt] = mfma_f16_k32(zb, o.aq[s], O[nt]);
     }
   }
 
@@ -138,7 +181,12 @@ __device__ __forceinline__ void compute(f32x4 (&Z)[8][NT], const Ops<NT>& o, u32
   f16x4 eb[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    eb[nt] = f16x4_of(mfma_f16_k16(o.aT, f16x4_of(R[nt]), f32x4{0.f, 0.f, 0.f, 0.f}));
+    if constexpr ((PV & kPrecBf16Inverse) != 0) {
+      const f32x4 e = mfma_bf16_k16(bf4_of(o.aT), bf4_of(R[nt]), f32x4{0.f, 0.f, 0.f, 0.f});
+      eb[nt] = f16x4_of(f32x4{bf16_round(e[0]), bf16_round(e[1]), bf16_round(e[2]), bf16_round(e[3])});
+    } else {
+      eb[nt] = f16x4_of(mfma_f16_k16(o.aT, f16x4_of(R[nt]), f32x4{0.f, 0.f, 0.f, 0.f}));
+    }
     O[nt] = mfma_f16_k16(eb[nt], o.am, O[nt]);
   }
 
@@ -153,6 +201,15 @@ __device__ __forceinline__ void compute(f32x4 (&Z)[8][NT], const Ops<NT>& o, u32
     Z[5][nt] = mfma_f16_k16(o.ak[5], eb[nt], decay<5>(Z[5][nt], o.g2));
     Z[6][nt] = mfma_f16_k16(o.ak[6], eb[nt], decay<6>(Z[6][nt], o.g2));
     Z[7][nt] = mfma_f16_k16(o.ak[7], eb[nt], decay<7>(Z[7][nt], o.g2));
+  }
+
+  if constexpr ((PV & kPrecBf16State) != 0) {   // the state kept in bf16 between updates
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Z[m][nt][i] = bf16_round(Z[m][nt][i]);
   }
 
 #pragma unroll

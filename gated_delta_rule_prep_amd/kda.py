@@ -24,13 +24,14 @@ KDA_OK, KDA_EINVAL, KDA_EDTYPE, KDA_EWORKSPACE, KDA_EUNSUPPORTED, KDA_EHIP = ran
 KDA_DTYPE_NONE, KDA_DTYPE_BF16, KDA_DTYPE_FP32 = 0, 1, 2
 KDA_STATUS_OK, KDA_STATUS_BAD_CU_SEQLENS = 0, 1
 KDA_PATH_AUTO, KDA_PATH_SPLIT, KDA_PATH_FUSED = 0, 1, 2
+KDA_PREC_DEFAULT, KDA_PREC_BF16_STATE, KDA_PREC_BF16_INVERSE, KDA_PREC_BF16_STATE_PRODUCTS = 0, 1, 2, 4
 PATHS = {None: KDA_PATH_AUTO, "auto": KDA_PATH_AUTO, "split": KDA_PATH_SPLIT, "fused": KDA_PATH_FUSED,
          KDA_PATH_AUTO: KDA_PATH_AUTO, KDA_PATH_SPLIT: KDA_PATH_SPLIT, KDA_PATH_FUSED: KDA_PATH_FUSED}
 CHUNK = 16
 
 EXPORTS = ("kda_fwd", "kda_fwd_profiled", "kda_fwd_ex", "kda_fwd_parts", "kda_fwd_path", "kda_fwd_path_taken",
            "kda_fwd_num_events", "kda_fwd_segmented", "kda_fwd_segmented_workspace_bytes",
-           "kda_fwd_segments",
+           "kda_fwd_segments", "kda_fwd_precision",
            "kda_decode", "kda_fwd_workspace_bytes", "kda_fwd_workspace_bytes_ex", "kda_get_last_error",
            "kda_version", "kda_fwd_check_status", "kda_workspace_layout", "kda_debug_prep")
 
@@ -65,6 +66,8 @@ _lib.kda_fwd_segmented.argtypes = _lib.kda_fwd.argtypes[:21] + [ctypes.c_int, _p
 _lib.kda_fwd_segmented.restype = ctypes.c_int
 _lib.kda_fwd_segmented_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int]
 _lib.kda_fwd_segmented_workspace_bytes.restype = ctypes.c_size_t
+_lib.kda_fwd_precision.argtypes = _lib.kda_fwd.argtypes + [ctypes.c_int]
+_lib.kda_fwd_precision.restype = ctypes.c_int
 _lib.kda_fwd_segments.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int]
 _lib.kda_fwd_segments.restype = ctypes.c_int
 _lib.kda_decode.argtypes = [_p, _p, _p, _p, _p, ctypes.c_float, _p, _p, _p, ctypes.c_float,
@@ -220,7 +223,7 @@ def parts(B: int, T: int, requested: int = 0) -> int:
 
 def fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state=None, final_state=None,
         cu_seqlens=None, workspace: Optional[torch.Tensor] = None, events=None, parts: Optional[int] = None,
-        chunk: Optional[int] = None, path=None, segments: Optional[int] = None):
+        chunk: Optional[int] = None, path=None, segments: Optional[int] = None, precision: Optional[int] = None):
     """Chunked KDA forward into the caller's ``out`` (and ``final_state``).
 
     Shapes and dtypes as in include/kda.h.  Runs on the current stream of the
@@ -234,6 +237,9 @@ def fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state
     records them around every kernel.  ``segments``: cut every sequence into
     that many pieces run side by side (kda_fwd_segmented; 0 or 'auto' for the
     library's choice); it takes none of events / parts / chunk / path.
+    ``precision``: a KDA_PREC_* combination for the precision study entry
+    point kda_fwd_precision (split path, 16-token chunks); it takes none of
+    events / parts / chunk / path / segments.
     """
     if q.dim() != 4:
         raise KDAValueError(KDA_EINVAL, "q must be [B, T, H, K]")
@@ -268,6 +274,11 @@ def fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state
     path_c = _path_code(path)
     if segments == "auto":
         segments = 0
+    if precision is not None:
+        if events is not None or parts is not None or chunk is not None or path is not None or segments is not None:
+            raise KDAValueError(KDA_EINVAL, "precision takes none of events, parts, chunk, path, segments")
+        if workspace is None:
+            workspace = alloc_workspace(B, T, H, N, cu_seqlens is not None, dev, 16, 1, "split")
     if segments is not None:
         if events is not None or parts is not None or chunk is not None or path is not None:
             raise KDAValueError(KDA_EINVAL, "segments takes none of events, parts, chunk, path")
@@ -286,7 +297,9 @@ def fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state
             _ptr(cu_seqlens), N, B, T, H, K, V, _ptr(workspace), workspace.numel())
     with torch.cuda.device(dev):
         plain = parts is None and chunk is None and path is None
-        if segments is not None:
+        if precision is not None:
+            rc = _lib.kda_fwd_precision(*args, _stream(dev), int(precision))
+        elif segments is not None:
             rc = _lib.kda_fwd_segmented(*args[:21], int(segments), *args[21:], _stream(dev))
         elif events is None and plain:
             rc = _lib.kda_fwd(*args, _stream(dev))

@@ -203,6 +203,34 @@ int kda_fwd_ex(const void* q, const void* k, const void* v, const void* g, const
                int64_t V, void* workspace, size_t workspace_bytes, hipStream_t stream, int chunk,
                int parts, int path, hipEvent_t* events, int num_events);
 
+/*
+ * kda_fwd_precision -- a study entry point, not the hot path: kda_fwd on the
+ * split path (16-token chunks, one part) with the chunk recurrence's
+ * arithmetic changed to one of the alternatives P1 §二 2.3 weighs, so their
+ * accuracy against an exact reference can be measured.
+ *   KDA_PREC_DEFAULT: the library's arithmetic (state fp32 on chip, fp16
+ *     MFMA operands with fp32 accumulation); equal to kda_fwd_ex(path = split).
+ *   KDA_PREC_BF16_STATE: the state rounded to bf16 after every chunk update,
+ *     as the pages store it between updates (the update itself stays fp32).
+ *   KDA_PREC_BF16_INVERSE: E = T R with T (the record's inverse, rounded
+ *     from fp16) and R in bf16, E rounded to bf16; the pages keep the inverse
+ *     in fp16 for its precision.
+ *   KDA_PREC_BF16_STATE_PRODUCTS: Khat Z and Qhat Z with the state copy and
+ *     the record's -Khat and Qhat in bf16 instead of fp16.
+ * variant: any combination of these bits; anything else returns KDA_EINVAL.
+ * Arguments, workspace (kda_fwd_workspace_bytes_ex(..., 16, 1,
+ * KDA_PATH_SPLIT) bytes or more) and checks otherwise as kda_fwd.
+ */
+#define KDA_PREC_DEFAULT 0
+#define KDA_PREC_BF16_STATE 1
+#define KDA_PREC_BF16_INVERSE 2
+#define KDA_PREC_BF16_STATE_PRODUCTS 4
+int kda_fwd_precision(const void* q, const void* k, const void* v, const void* g, const void* beta, float scale,
+                      void* out, const float* A_log, const float* dt_bias, float lower_bound,
+                      const void* initial_state, int initial_state_dtype, void* final_state, int final_state_dtype,
+                      const int64_t* cu_seqlens, int64_t num_seqs, int64_t B, int64_t T, int64_t H, int64_t K,
+                      int64_t V, void* workspace, size_t workspace_bytes, hipStream_t stream, int variant);
+
 /* Number of parts kda_fwd_ex uses for these sizes and `parts` request (0 on bad input). */
 int kda_fwd_parts(int64_t B, int64_t T, int parts);
 

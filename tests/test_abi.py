@@ -322,3 +322,16 @@ def test_segmented_segments_and_workspace():
     # a workspace one byte short is refused on the host
     need = kda.segmented_workspace_bytes(1, 64, 2, 0, False, 4)
     assert call_seg(4, ws_bytes=need - 1) == kda.KDA_EWORKSPACE
+
+
+def test_precision_study_rejects_bad_variants():
+    a = [FAKE, FAKE, FAKE, FAKE, FAKE, 0.088, FAKE, FAKE, FAKE, -5.0, None, 0, None, 0, None, 0, 1, 64, 2, 128,
+         128, WS, 1 << 40, None]
+    for bad in (-1, 8, 9, 16):
+        assert kda.lib().kda_fwd_precision(*a, bad) == kda.KDA_EINVAL and "precision" in kda.last_error()
+    # the remaining checks are kda_fwd's, made before any HIP call
+    a[0] = None
+    assert kda.lib().kda_fwd_precision(*a, 1) == kda.KDA_EINVAL
+    a[0] = FAKE
+    a[22] = 700
+    assert kda.lib().kda_fwd_precision(*a, 7) == kda.KDA_EWORKSPACE
