@@ -31,18 +31,25 @@
 // recurrence reads is bounded by 1 (or by scale) and is stored in fp16.
 #include "kda_device.h"
 #include "kda_internal.h"
+#include "kda_lds_pipe.h"
 #include "../../include/kda.h"
 
 namespace kda {
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 2;
 constexpr int kThreads = 64 * kWaves;
 constexpr float kEps = 1e-6f;
 
+// A wave builds its record in LDS and writes it out at the end as whole
+// contiguous pieces (16 bytes per lane, 1 KB per store instruction), with
+// streaming (nontemporal) stores: the record's scattered 4- to 16-byte parts
+// never reach the caches as partial lines, and the recurrence reads the
+// records only after the whole prep has run.
 struct __align__(16) WaveSmem {
   __align__(16) float L[C][C + 4];       // L (fp32), 80-byte rows
   float beta[C];
+  __align__(16) char rec[REC_BYTES];
 };
 
 __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
@@ -93,7 +100,8 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
 
   const float A2 = -expf(a.A_log[h]) * kLog2e;   // sigmoid(x) = 1 / (1 + 2^(-x log2 e))
   const float lb2 = a.lower_bound * kLog2e;
-  char* rec = a.ws + a.lay.records + ((int64_t)h * a.lay.max_chunks + chunk) * REC_BYTES;
+  char* const rec_out = a.ws + a.lay.records + ((int64_t)h * a.lay.max_chunks + chunk) * REC_BYTES;
+  char* const rec = sm.rec;
   _Float16* rec_qh = reinterpret_cast<_Float16*>(rec + REC_QH) + r * K;
   _Float16* rec_nk = reinterpret_cast<_Float16*>(rec + REC_NK) + r * K;
   _Float16* rec_kb = reinterpret_cast<_Float16*>(rec + REC_KB) + r * K;
@@ -188,6 +196,17 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
     }
     *reinterpret_cast<u32x4*>(rec + REC_T + jc * C * 2) = t0;
     *reinterpret_cast<u32x4*>(rec + REC_T + jc * C * 2 + 16) = t1;
+  }
+
+  // ---- the record to HBM
+  wait_lgkm0();   // this wave's LDS writes are done
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int i = 0; i < (REC_BYTES / 16 + 63) / 64; ++i) {
+    const int piece = 64 * i + lane;
+    if (piece < REC_BYTES / 16)
+      __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(rec + 16 * piece),
+                                  reinterpret_cast<u32x4*>(rec_out + 16 * piece));
   }
 }
 
