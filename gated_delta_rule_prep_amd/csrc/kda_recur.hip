@@ -72,6 +72,11 @@ struct Cfg {
   static constexpr int kVal = 0;
   static constexpr int kRec = kValBlocks * 1024;
   static_assert(C * kRowPieces % 64 == 0, "value rows fill whole blocks");
+  // The value rows are swizzled as piece p ^ 2 (r % 4) (see make_plan): with
+  // fewer than 8 pieces per row that index leaves the tile, and for the last
+  // tile of the last head it reads past the end of v (a 32-column build did,
+  // and faulted).  So tiles are at least 64 columns wide.
+  static_assert(kRowPieces >= 8, "the value swizzle needs at least 8 pieces (64 columns) per tile row");
   static_assert(D >= 3 && (D - 2) * kMaxLoads <= 63, "ring depth within the vmcnt range");
   static_assert(V % kCols == 0, "tile shape");
 };

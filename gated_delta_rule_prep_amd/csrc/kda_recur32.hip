@@ -50,6 +50,8 @@ struct Cfg {
   static constexpr int kQh = kRec + REC32_QH, kNw = kRec + REC32_NW, kKb = kRec + REC32_KB;
   static constexpr int kTt = kRec + REC32_T, kMt = kRec + REC32_MQK, kGam = kRec + REC32_GAM;
   static_assert(CC * kRowPieces % 64 == 0, "value rows fill whole blocks");
+  // the value swizzle p ^ 2 (r % 4) stays inside a row of at least 8 pieces
+  static_assert(kRowPieces >= 8, "the value swizzle needs at least 8 pieces (64 columns) per tile row");
   static_assert(D >= 3 && (D - 2) * kLoads <= 63, "ring depth within the vmcnt range");
   static_assert(D * kSlotBytes <= 160 * 1024, "ring fits the LDS of a CU");
   static_assert(V % kCols == 0, "tile shape");
