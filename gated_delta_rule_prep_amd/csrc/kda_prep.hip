@@ -57,9 +57,14 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int64_t H = a.H;
-  const int h = blockIdx.y * kWaves + wave;
+  // One linear grid, head groups fastest: the workgroups of one chunk launch
+  // together, so they read the same token rows (and the same beta sectors) of
+  // q, k, g and beta at about the same time.
+  const int hx = (int)((H + kWaves - 1) / kWaves);
+  const int hgrp = (int)(blockIdx.x % (unsigned)hx), cidx = (int)(blockIdx.x / (unsigned)hx);
+  const int h = hgrp * kWaves + wave;
   const WsHeader* hdr = reinterpret_cast<const WsHeader*>(a.ws);
-  const int chunk = hdr->part_first[a.part] + (int)blockIdx.x;   // this launch covers one part
+  const int chunk = hdr->part_first[a.part] + cidx;   // this launch covers one part
   if (chunk >= hdr->part_first[a.part + 1] || h >= H) return;   // whole waves only; no barriers below
   if (hdr->path == KDA_PATH_FUSED) return;                      // the scheduler chose the fused kernel
   WaveSmem& sm = wsm[wave];
@@ -216,7 +221,9 @@ hipError_t launch_prep(const PrepArgs& a, hipStream_t s) {
   if (a.lay.chunk == C32) return launch_prep32(a, s);
   if (a.grid_chunks == 0) return hipSuccess;
   const unsigned hx = (unsigned)((a.H + kWaves - 1) / kWaves);
-  hipLaunchKernelGGL(prep_kernel, dim3((unsigned)a.grid_chunks, hx), dim3(kThreads), 0, s, a);
+  const int64_t grid = (int64_t)hx * a.grid_chunks;
+  if (grid > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(prep_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
