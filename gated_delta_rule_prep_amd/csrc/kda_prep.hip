@@ -41,16 +41,38 @@ constexpr int kWaves = 2;
 constexpr int kThreads = 64 * kWaves;
 constexpr float kEps = 1e-6f;
 
-// A wave builds its record in LDS and writes it out at the end as whole
-// contiguous pieces (16 bytes per lane, 1 KB per store instruction), with
-// streaming (nontemporal) stores: the record's scattered 4- to 16-byte parts
-// never reach the caches as partial lines, and the recurrence reads the
-// records only after the whole prep has run.
+// A wave builds its record in LDS and writes it out as whole contiguous
+// pieces (16 bytes per lane, 1 KB per store instruction) with streaming
+// (nontemporal) stores: the record's scattered 4- to 16-byte parts never reach
+// the caches as partial lines, and the recurrence reads the records only after
+// the whole prep has run.  Qhat, -Khat and Kbar are staged one 64-channel half
+// of their rows at a time (written out after channel blocks 1 and 3, each half
+// row a whole 128-byte line), T, Mqk and gamma at the end, so a wave needs
+// 9 KB of LDS and the registers, not the LDS, bound the waves per CU.
+constexpr int kHalfBytes = 128;                 // one 64-channel half of a 256-byte row
+constexpr int kTailBytes = REC_BYTES - REC_T;   // T, Mqk, gamma
+static_assert(REC_NK == REC_QH + C * 2 * K && REC_KB == REC_NK + C * 2 * K && REC_T == REC_KB + C * 2 * K,
+              "Qhat, -Khat and Kbar are three consecutive [16][128] fp16 arrays");
 struct __align__(16) WaveSmem {
   __align__(16) float L[C][C + 4];       // L (fp32), 80-byte rows
   float beta[C];
-  __align__(16) char rec[REC_BYTES];
+  __align__(16) char half[3][C][kHalfBytes];   // Qhat, -Khat, Kbar: the current half of every row
+  __align__(16) char tail[kTailBytes];         // T^T, Mqk^T, gamma as in the record
 };
+
+// Writes the staged half `hf` of the three row arrays: 3 x 16 rows x 8 pieces.
+__device__ __forceinline__ void flush_half(const WaveSmem& sm, char* rec_out, int hf, int lane) {
+  wait_lgkm0();
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int i = 0; i < 3 * C * (kHalfBytes / 16) / 64; ++i) {
+    const int pi = 64 * i + lane, arr = pi >> 7, row = (pi >> 3) & 15, part = pi & 7;
+    const u32x4 x = *reinterpret_cast<const u32x4*>(&sm.half[arr][row][16 * part]);
+    __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(rec_out + REC_QH + arr * C * 2 * K + row * 2 * K +
+                                                            hf * kHalfBytes + 16 * part));
+  }
+  asm volatile("" ::: "memory");   // the next half's LDS writes stay behind these reads
+}
 
 __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
   __shared__ WaveSmem wsm[kWaves];
@@ -106,11 +128,12 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
   const float A2 = -expf(a.A_log[h]) * kLog2e;   // sigmoid(x) = 1 / (1 + 2^(-x log2 e))
   const float lb2 = a.lower_bound * kLog2e;
   char* const rec_out = a.ws + a.lay.records + ((int64_t)h * a.lay.max_chunks + chunk) * REC_BYTES;
-  char* const rec = sm.rec;
-  _Float16* rec_qh = reinterpret_cast<_Float16*>(rec + REC_QH) + r * K;
-  _Float16* rec_nk = reinterpret_cast<_Float16*>(rec + REC_NK) + r * K;
-  _Float16* rec_kb = reinterpret_cast<_Float16*>(rec + REC_KB) + r * K;
-  float* rec_gam = reinterpret_cast<float*>(rec + REC_GAM);
+  // staged row r of the three arrays (element e of the current half) and the tail
+  _Float16* const st_qh = reinterpret_cast<_Float16*>(sm.half[0][r]);
+  _Float16* const st_nk = reinterpret_cast<_Float16*>(sm.half[1][r]);
+  _Float16* const st_kb = reinterpret_cast<_Float16*>(sm.half[2][r]);
+  char* const tail = sm.tail;
+  float* const rec_gam = reinterpret_cast<float*>(tail + (REC_GAM - REC_T));
 
   // ---- per channel slot: gate, scan, decay factors, products, L / Mqk MFMAs
   f32x4 accL = {0.f, 0.f, 0.f, 0.f}, accM = {0.f, 0.f, 0.f, 0.f};
@@ -150,16 +173,18 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
     u32x4 wkb;
 #pragma unroll
     for (int w = 0; w < 4; ++w) wkb[w] = pack_f16(kb[2 * w], kb[2 * w + 1]);
-    *reinterpret_cast<u32x4*>(rec_kb + c0) = wkb;
-    const int p0 = 32 * j + kPermPos(8 * cq), p1 = 32 * j + kPermPos(8 * cq + 4);
-    *reinterpret_cast<u32x2*>(rec_qh + p0) = u32x2{pack_f16(qh[0], qh[1]), pack_f16(qh[2], qh[3])};
-    *reinterpret_cast<u32x2*>(rec_qh + p1) = u32x2{pack_f16(qh[4], qh[5]), pack_f16(qh[6], qh[7])};
-    *reinterpret_cast<u32x2*>(rec_nk + p0) = u32x2{pack_f16(-kh[0], -kh[1]), pack_f16(-kh[2], -kh[3])};
-    *reinterpret_cast<u32x2*>(rec_nk + p1) = u32x2{pack_f16(-kh[4], -kh[5]), pack_f16(-kh[6], -kh[7])};
+    const int hb = 64 * (j >> 1);   // first channel (element) of the staged half
+    *reinterpret_cast<u32x4*>(st_kb + c0 - hb) = wkb;
+    const int p0 = 32 * j + kPermPos(8 * cq) - hb, p1 = 32 * j + kPermPos(8 * cq + 4) - hb;
+    *reinterpret_cast<u32x2*>(st_qh + p0) = u32x2{pack_f16(qh[0], qh[1]), pack_f16(qh[2], qh[3])};
+    *reinterpret_cast<u32x2*>(st_qh + p1) = u32x2{pack_f16(qh[4], qh[5]), pack_f16(qh[6], qh[7])};
+    *reinterpret_cast<u32x2*>(st_nk + p0) = u32x2{pack_f16(-kh[0], -kh[1]), pack_f16(-kh[2], -kh[3])};
+    *reinterpret_cast<u32x2*>(st_nk + p1) = u32x2{pack_f16(-kh[4], -kh[5]), pack_f16(-kh[6], -kh[7])};
     if (r == 15) {   // gam = P of the last token (padded tokens keep G constant)
 #pragma unroll
       for (int e = 0; e < 8; ++e) rec_gam[kGamSlot(c0 + e)] = gm[e];
     }
+    if (j & 1) flush_half(sm, rec_out, j >> 1, lane);
   }
 
   // ---- L (to LDS) and Mqk^T (to the record); lane (c, g) holds rows 4g..4g+3 of column c
@@ -177,7 +202,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
     }
     wm[0] = pack_f16(mv[0], mv[1]);
     wm[1] = pack_f16(mv[2], mv[3]);
-    *reinterpret_cast<u32x2*>(rec + REC_MQK + (lc * C + 4 * lg) * 2) = wm;   // Mqk^T[c][4g..4g+3]
+    *reinterpret_cast<u32x2*>(tail + (REC_MQK - REC_T) + (lc * C + 4 * lg) * 2) = wm;   // Mqk^T[c][4g..4g+3]
   }
   __builtin_amdgcn_wave_barrier();
 
@@ -199,19 +224,19 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
       t0[w] = pack_f16(x[2 * w] * bj, x[2 * w + 1] * bj);
       t1[w] = pack_f16(x[8 + 2 * w] * bj, x[8 + 2 * w + 1] * bj);
     }
-    *reinterpret_cast<u32x4*>(rec + REC_T + jc * C * 2) = t0;
-    *reinterpret_cast<u32x4*>(rec + REC_T + jc * C * 2 + 16) = t1;
+    *reinterpret_cast<u32x4*>(tail + jc * C * 2) = t0;
+    *reinterpret_cast<u32x4*>(tail + jc * C * 2 + 16) = t1;
   }
 
-  // ---- the record to HBM
+  // ---- the tail of the record to HBM
   wait_lgkm0();   // this wave's LDS writes are done
   __builtin_amdgcn_wave_barrier();
 #pragma unroll
-  for (int i = 0; i < (REC_BYTES / 16 + 63) / 64; ++i) {
+  for (int i = 0; i < (kTailBytes / 16 + 63) / 64; ++i) {
     const int piece = 64 * i + lane;
-    if (piece < REC_BYTES / 16)
-      __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(rec + 16 * piece),
-                                  reinterpret_cast<u32x4*>(rec_out + 16 * piece));
+    if (piece < kTailBytes / 16)
+      __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(tail + 16 * piece),
+                                  reinterpret_cast<u32x4*>(rec_out + REC_T + 16 * piece));
   }
 }
 
