@@ -96,13 +96,12 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
   const int64_t tok = (int64_t)ce.row0 + min(r, ce.len - 1);   // clamped: loads stay in the sequence
   const int64_t base = (tok * H + h) * K + 8 * cq;
 
-  // ---- loads: q, k, g (4 x 16 B each) and beta
-  u32x4 qw[4], kw[4], gw[4];
+  // ---- loads: q, k (4 x 16 B each) and beta; g per channel block below
+  u32x4 qw[4], kw[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     qw[j] = *reinterpret_cast<const u32x4*>(a.q + base + 32 * j);
     kw[j] = *reinterpret_cast<const u32x4*>(a.k + base + 32 * j);
-    gw[j] = *reinterpret_cast<const u32x4*>(a.g + base + 32 * j);
   }
   const float braw = bf16_to_f32(a.beta[tok * H + h]);
   const float beta = valid ? 1.f / (1.f + expf(-braw)) : 0.f;
@@ -137,15 +136,20 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
 
   // ---- per channel slot: gate, scan, decay factors, products, L / Mqk MFMAs
   f32x4 accL = {0.f, 0.f, 0.f, 0.f}, accM = {0.f, 0.f, 0.f, 0.f};
+  // g is needed one channel block at a time: block j + 1 loads while block j
+  // computes, so only two of its four 16-byte pieces are ever held
+  u32x4 gnext = *reinterpret_cast<const u32x4*>(a.g + base);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
+    const u32x4 gcur = gnext;
+    if (j < 3) gnext = *reinterpret_cast<const u32x4*>(a.g + base + 32 * (j + 1));
     const int c0 = 32 * j + 8 * cq;
     const f32x4 dtA = *reinterpret_cast<const f32x4*>(a.dt_bias + (int64_t)h * K + c0);
     const f32x4 dtB = *reinterpret_cast<const f32x4*>(a.dt_bias + (int64_t)h * K + c0 + 4);
     float kh[8], qh[8], kb[8], gm[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const uint32_t wg = gw[j][e >> 1], wq = qw[j][e >> 1], wk = kw[j][e >> 1];
+      const uint32_t wg = gcur[e >> 1], wq = qw[j][e >> 1], wk = kw[j][e >> 1];
       const float gv = (e & 1) ? bf16_hi(wg) : bf16_lo(wg);
       const float qv = (e & 1) ? bf16_hi(wq) : bf16_lo(wq);
       const float kv = (e & 1) ? bf16_hi(wk) : bf16_lo(wk);
