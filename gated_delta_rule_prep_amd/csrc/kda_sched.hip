@@ -31,7 +31,7 @@ constexpr int kRankSortMax = 2048;   // longest-first order by rank sort up to t
 // all sequences, the longest sequence's `maxc` chunks and N sequences.  The
 // constants are measured on the box at K = V = 128 (T = 8192, H = 64 and 96,
 // fixed length, 8 x 1024 and 12 ragged sequences):
-//   split: the prep kernel streams inputs and records at about 6.0 ns per
+//   split: the prep kernel streams inputs and records at about 5.2 ns per
 //     (chunk, head); the recurrence is either the longest chain (0.59 us per
 //     chunk step) or, with many pairs, throughput (0.65 us per 64-column tile
 //     step per CU, 256 CUs);
@@ -41,7 +41,7 @@ constexpr int kRankSortMax = 2048;   // longest-first order by rank sort up to t
 //     over 256 CUs, one workgroup per CU.
 __device__ int choose_path(int64_t H, int64_t N, int64_t total, int64_t maxc) {
   const double chunk_heads = (double)total * (double)H;
-  const double split = 6.0e-3 * chunk_heads + fmax(0.59 * (double)maxc, 0.65 * 2.0 * chunk_heads / 256.0);
+  const double split = 5.2e-3 * chunk_heads + fmax(0.59 * (double)maxc, 0.65 * 2.0 * chunk_heads / 256.0);
   const bool two = fused_two_tiles(N * H);
   const double step = two ? 1.8 : 2.15;
   const double wg_steps = ((double)total + 5.0 * (double)N) * (double)H * (two ? 2.0 : 1.0);
