@@ -257,19 +257,19 @@ int kda_fwd_num_events(int64_t B, int64_t T, int chunk, int parts, int path);
  * Over a segment the update of P1 §一 maps the starting state affinely,
  * S_end = A S_start + B, with A the product of (I - beta_t kn_t kn_t^T)
  * diag(exp(a_t)) over the segment's tokens and B its end state from a zero
- * start.  The call runs the plain forward (the library's path choice) three
- * times over all segments of all sequences: with the values from a zero start
- * (giving B), with zero values from the identity (giving A), and with the
- * values from each segment's true start, which a small fp32 kernel composes
- * per (sequence, head) as S_start(0) = initial state,
- * S_start(j + 1) = A_j S_start(j) + B_j; the last composition is the final
- * state.  Segments are ceil(len / segments) tokens rounded up to whole
- * 16-token chunks, the last ones shorter or empty.  The result equals kda_fwd's
- * up to rounding (the states between segments are kept in fp32).
- *
- * The three runs share one set of chunk records (built once by the split
- * path's scheduler and prep kernels); the first two are one recurrence launch
- * that writes no outputs.
+ * start.  The call builds the chunk records of all segments of all sequences
+ * once (the split path's scheduler and prep kernels) and runs the chunk
+ * recurrence three times over them: with the values from a zero start
+ * (giving B) and with zero values from the identity (giving A), both in one
+ * launch that writes no outputs, and, after a small kernel has composed per
+ * (sequence, head) S_start(0) = initial state,
+ * S_start(j + 1) = A_j S_start(j) + B_j (the last composition is the final
+ * state), with the values from each segment's true start.  Segments are
+ * ceil(len / segments) tokens rounded up to whole 16-token chunks, the last
+ * ones shorter or empty; an empty segment passes its state through exactly.
+ * The result equals kda_fwd's up to rounding: the states between segments are
+ * kept in fp32, and each composition rounds its operands to fp16 as the
+ * recurrence does every chunk.
  *
  * Arguments, checks, states (the same buffer allowed for both) and the device
  * status word are those of kda_fwd.  segments: 1 .. 4096, or 0 for the
