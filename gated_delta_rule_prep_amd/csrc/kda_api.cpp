@@ -201,12 +201,66 @@ int kda_version(void) { return 200; }  // 0.2.0
 
 const char* kda_get_last_error(void) { return g_last_error.c_str(); }
 
+// ---- segmented forward -----------------------------------------------------
+
+namespace {
+
+// Workspace regions of kda_fwd_segmented (byte offsets), or false on bad sizes.
+// The plain forward's workspace comes first, so its header (status, path
+// taken) sits at the start as for kda_fwd.
+struct SegLayout {
+  int64_t inner, inner_bytes, seg_cu, A, B, starts, total;
+};
+
+bool seg_layout(int64_t B, int64_t T, int64_t H, int64_t N, int S, SegLayout* L) {
+  const int64_t NS = N * S, mat = NS * H * kda::V * kda::K * (int64_t)sizeof(float);   // fp32 states
+  kda::Layout inner;
+  if (!kda::layout_for(1, B * T, H, NS, kda::C, &inner)) return false;
+  int64_t off = 0;
+  L->inner = off;
+  L->inner_bytes = inner.total;
+  off = align_up(off + inner.total, 256);
+  L->seg_cu = off;
+  off = align_up(off + (NS + 1) * 8, 256);
+  L->A = off;   // the transitions, fp16
+  off = align_up(off + mat / 2, 256);
+  L->B = off;
+  off = align_up(off + mat, 256);
+  L->starts = off;
+  off = align_up(off + mat, 256);
+  L->total = off;
+  return true;
+}
+
+// The library's segment count.  Cutting pays while the recurrence leaves
+// CUs idle: one workgroup per 64 value columns of a (segment, head) chain, and
+// the two-set launch doubles that.  Measured on MI355X (one sequence, H = 2 ..
+// 96, T = 8192 .. 65536), the best count is the largest power of two with at
+// most 128 (segment, head) chains and segments of at least 512 tokens; below
+// four segments the three recurrence passes cost more than they save.  With
+// cu_seqlens the mean length stands in for the lengths, which only the device
+// knows.
+int choose_segments(int64_t B, int64_t T, int64_t H, int64_t N, bool has_cu) {
+  const int64_t len = has_cu ? (B * T) / (N > 0 ? N : 1) : T;
+  int64_t S = 1;
+  while (2 * S * N * H <= 128 && len / (2 * S) >= 512 && 2 * S <= 4096) S *= 2;
+  return S >= 4 ? (int)S : 1;
+}
+
+}  // namespace
+
 size_t kda_fwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t num_seqs, int has_cu_seqlens) {
   int64_t N = 0;
   if (check_sizes(B, T, H, kda::K, kda::V, nullptr, num_seqs, has_cu_seqlens, &N) != KDA_OK) return 0;
   kda::Layout L16, L32;   // enough for either chunk size
   if (!kda::layout_for(B, T, H, N, kda::C, &L16) || !kda::layout_for(B, T, H, N, kda::C32, &L32)) return 0;
-  return (size_t)std::max(L16.total, L32.total);
+  int64_t bytes = std::max(L16.total, L32.total);
+  // and for the segmented form that kda_fwd takes for B sequences of T tokens
+  // when the library's segment count is above 1
+  const int S = has_cu_seqlens ? 1 : choose_segments(B, T, H, N, false);
+  SegLayout SL;
+  if (S > 1 && seg_layout(B, T, H, N, S, &SL)) bytes = std::max(bytes, SL.total);
+  return (size_t)bytes;
 }
 
 size_t kda_fwd_workspace_bytes_ex(int64_t B, int64_t T, int64_t H, int64_t num_seqs, int has_cu_seqlens,
@@ -428,6 +482,20 @@ int kda_fwd(const void* q, const void* k, const void* v, const void* g, const vo
             int final_state_dtype, const int64_t* cu_seqlens, int64_t num_seqs, int64_t B,
             int64_t T, int64_t H, int64_t K, int64_t V, void* workspace, size_t workspace_bytes,
             hipStream_t stream) {
+  // B sequences of T tokens: the library's segment count is known on the
+  // host; above 1 (few heads, long sequences) the call cuts the sequences
+  // when the workspace holds the segmented layout.
+  if (cu_seqlens == nullptr && workspace != nullptr) {
+    int64_t N = 0;
+    if (check_sizes(B, T, H, K, V, nullptr, num_seqs, 0, &N) == KDA_OK) {
+      const int S = choose_segments(B, T, H, N, false);
+      SegLayout SL;
+      if (S > 1 && seg_layout(B, T, H, N, S, &SL) && (int64_t)workspace_bytes >= SL.total)
+        return kda_fwd_segmented(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
+                                 initial_state_dtype, final_state, final_state_dtype, nullptr, num_seqs, B, T, H,
+                                 K, V, S, workspace, workspace_bytes, stream);
+    }
+  }
   return fwd_impl(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state,
                   initial_state_dtype, final_state, final_state_dtype, cu_seqlens, num_seqs, B, T, H, K, V,
                   workspace, workspace_bytes, stream, 0, 0, KDA_PATH_AUTO, nullptr, 0, nullptr);
@@ -498,53 +566,6 @@ int kda_fwd_path_taken(const void* workspace, hipStream_t stream, int* path) {
   return KDA_OK;
 }
 
-// ---- segmented forward -----------------------------------------------------
-
-namespace {
-
-// Workspace regions of kda_fwd_segmented (byte offsets), or false on bad sizes.
-// The plain forward's workspace comes first, so its header (status, path
-// taken) sits at the start as for kda_fwd.
-struct SegLayout {
-  int64_t inner, inner_bytes, seg_cu, A, B, starts, total;
-};
-
-bool seg_layout(int64_t B, int64_t T, int64_t H, int64_t N, int S, SegLayout* L) {
-  const int64_t NS = N * S, mat = NS * H * kda::V * kda::K * (int64_t)sizeof(float);   // fp32 states
-  kda::Layout inner;
-  if (!kda::layout_for(1, B * T, H, NS, kda::C, &inner)) return false;
-  int64_t off = 0;
-  L->inner = off;
-  L->inner_bytes = inner.total;
-  off = align_up(off + inner.total, 256);
-  L->seg_cu = off;
-  off = align_up(off + (NS + 1) * 8, 256);
-  L->A = off;   // the transitions, fp16
-  off = align_up(off + mat / 2, 256);
-  L->B = off;
-  off = align_up(off + mat, 256);
-  L->starts = off;
-  off = align_up(off + mat, 256);
-  L->total = off;
-  return true;
-}
-
-// The library's segment count.  Cutting pays while the recurrence leaves
-// CUs idle: one workgroup per 64 value columns of a (segment, head) chain, and
-// the two-set launch doubles that.  Measured on MI355X (one sequence, H = 2 ..
-// 96, T = 8192 .. 65536), the best count is the largest power of two with at
-// most 128 (segment, head) chains and segments of at least 512 tokens; below
-// four segments the three recurrence passes cost more than they save.  With
-// cu_seqlens the mean length stands in for the lengths, which only the device
-// knows.
-int choose_segments(int64_t B, int64_t T, int64_t H, int64_t N, bool has_cu) {
-  const int64_t len = has_cu ? (B * T) / (N > 0 ? N : 1) : T;
-  int64_t S = 1;
-  while (2 * S * N * H <= 128 && len / (2 * S) >= 512 && 2 * S <= 4096) S *= 2;
-  return S >= 4 ? (int)S : 1;
-}
-
-}  // namespace
 
 int kda_fwd_segments(int64_t B, int64_t T, int64_t H, int64_t num_seqs, int has_cu_seqlens) {
   int64_t N = 0;

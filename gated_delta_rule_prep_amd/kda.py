@@ -288,9 +288,8 @@ def fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state
                 raise KDAValueError(KDA_EINVAL, "bad sizes for the workspace: B=%d T=%d H=%d segments=%d" % (
                     B, T, H, segments))
             workspace = torch.empty(n, dtype=torch.uint8, device=dev)
-    elif workspace is None:   # just what this call's path needs
-        workspace = alloc_workspace(B, T, H, N, cu_seqlens is not None, dev, chunk, parts,
-                                    "auto" if path is None else path)
+    elif workspace is None:   # what this call's path needs (kda_fwd: every form it may take)
+        workspace = alloc_workspace(B, T, H, N, cu_seqlens is not None, dev, chunk, parts, path)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(out),
             _ptr(A_log), _ptr(dt_bias), float(lower_bound), _ptr(initial_state),
             _state_code(initial_state), _ptr(final_state), _state_code(final_state),

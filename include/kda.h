@@ -107,6 +107,12 @@ extern "C" {
  * and the 16 x 16 unit-lower-triangular inverse) and the chunk recurrence (the
  * chunk-by-chunk delta-rule state update and the output).  kda_fwd leaves
  * the execution path to the library (KDA_PATH_AUTO); kda_fwd_ex selects it.
+ * Without cu_seqlens (B sequences of T tokens, lengths known on the host)
+ * kda_fwd also cuts the sequences into segments (kda_fwd_segmented with
+ * kda_fwd_segments' count) when that count is above 1 -- few heads and long
+ * sequences, where one chain per (sequence, head) leaves the chip idle -- and
+ * the workspace holds the segmented layout; kda_fwd_workspace_bytes sizes for
+ * it.  With a smaller workspace the sequences run uncut.
  *
  * initial_state / final_state: NULL with dtype KDA_DTYPE_NONE, or a pointer
  * with KDA_DTYPE_BF16 / KDA_DTYPE_FP32.  When both are given their dtypes must
@@ -118,7 +124,8 @@ extern "C" {
  * workspace: device memory, 256-byte aligned, of at least
  * kda_fwd_workspace_bytes_ex(B, T, H, num_seqs, cu != NULL, 0, 0, KDA_PATH_AUTO)
  * bytes (tables and the chunk records, about 864 B per token-head) --
- * kda_fwd_workspace_bytes gives a size that suits every path.  Its contents
+ * kda_fwd_workspace_bytes gives a size that suits every path (and the
+ * segmented form kda_fwd may take).  Its contents
  * are scratch between calls except for the status word.
  * stream: a hipStream_t (NULL = the default stream).
  *
@@ -316,8 +323,9 @@ int kda_decode(const void* q, const void* k, const void* v, const void* g, const
                int64_t N, int64_t H, int64_t K, int64_t V, hipStream_t stream);
 
 /*
- * Workspace bytes that suit kda_fwd and every kda_fwd_ex path and chunk size
- * for these sizes (0 if the sizes are invalid).  num_seqs is ignored when
+ * Workspace bytes that suit kda_fwd (the segmented form it may take
+ * included) and every kda_fwd_ex path and chunk size for these sizes (0 if
+ * the sizes are invalid).  num_seqs is ignored when
  * has_cu_seqlens is 0 (then N = B).
  */
 size_t kda_fwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t num_seqs,

@@ -335,3 +335,22 @@ def test_precision_study_rejects_bad_variants():
     a[0] = FAKE
     a[22] = 700
     assert kda.lib().kda_fwd_precision(*a, 7) == kda.KDA_EWORKSPACE
+
+
+def test_kda_fwd_workspace_covers_its_segmented_form():
+    """kda_fwd cuts B sequences of T tokens into kda_fwd_segments' count of
+    segments when that is above 1 and the workspace allows; its all-paths size
+    covers that layout, and stays the plain one when the count is 1."""
+    for B, T, H in ((1, 8192, 4), (2, 4096, 8), (1, 65536, 2)):
+        S = kda.segments_for(B, T, H)
+        assert S > 1
+        seg = kda.segmented_workspace_bytes(B, T, H, 0, False, S)
+        assert kda.workspace_bytes(B, T, H) == max(seg, kda.workspace_layout(B, T, H, chunk=16)["total"],
+                                                   kda.workspace_layout(B, T, H, chunk=32)["total"])
+    for B, T, H in ((1, 8192, 96), (1, 1024, 4)):
+        assert kda.segments_for(B, T, H) == 1
+        assert kda.workspace_bytes(B, T, H) == max(kda.workspace_layout(B, T, H, chunk=16)["total"],
+                                                   kda.workspace_layout(B, T, H, chunk=32)["total"])
+    # with cu_seqlens the lengths are the device's: no cut, plain sizes
+    assert kda.workspace_bytes(1, 8192, 4, 1, True) == max(kda.workspace_layout(1, 8192, 4, 1, True, chunk=16)["total"],
+                                                            kda.workspace_layout(1, 8192, 4, 1, True, chunk=32)["total"])

@@ -129,3 +129,24 @@ def test_segmented_bad_cu_seqlens_sets_status_and_touches_nothing():
     ws = torch.empty(kda.segmented_workspace_bytes(1, 64, 2, 2, True, 3), dtype=torch.uint8, device="cuda")
     run_seg(inp, 3, d=d, workspace=ws)
     assert kda.check_status(ws) == kda.KDA_STATUS_OK
+
+
+def test_kda_fwd_takes_the_segmented_form_when_the_workspace_allows():
+    """Without cu_seqlens and with few heads, kda_fwd runs kda_fwd_segmented
+    with the library's count (bitwise the same result); with a workspace sized
+    only for the uncut call it runs uncut (bitwise kda_fwd_ex's library choice)."""
+    from gated_delta_rule_prep_amd import kda
+    inp = make_inputs(1, 8192, 4, seed=412, state_dtype="fp32")
+    say("case kda_fwd cut / uncut, T8192 H4")
+    d = device_inputs(inp)
+    o_fwd, f_fwd = run_gpu(inp, d=d)                      # kda_fwd, all-paths workspace
+    o_seg, f_seg = run_seg(inp, kda.segments_for(1, 8192, 4), d=d)
+    small = kda.alloc_workspace(1, 8192, 4, 1, False, "cuda", None, None, "auto")
+    o_unc, f_unc = run_gpu(inp, d=d, workspace=small)     # kda_fwd, too small to cut
+    o_ex, f_ex = run_gpu(inp, d=d, path="auto")           # kda_fwd_ex, the library's path
+    torch.cuda.synchronize()
+    assert torch.equal(o_fwd.view(torch.int16), o_seg.view(torch.int16)) and torch.equal(f_fwd, f_seg)
+    assert torch.equal(o_unc.view(torch.int16), o_ex.view(torch.int16)) and torch.equal(f_unc, f_ex)
+    ref_o, ref_f = oracle_run(inp)
+    assert_close(to_f64(o_fwd), ref_o, "out")
+    assert_close(to_f64(f_fwd), ref_f, "final_state", "fp32")
