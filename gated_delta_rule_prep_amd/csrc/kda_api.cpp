@@ -358,7 +358,17 @@ static int fwd_impl(const void* q, const void* k, const void* v, const void* g, 
       return fail(KDA_EINVAL, "kda: path %d cannot run chunk=%d with parts=%d (the fused path takes 16-token "
                   "chunks and one part)", path_req, chunk_req, parts_req);
     const bool fused = path == KDA_PATH_FUSED;   // fused kernel only
-    const bool both = path == KDA_PATH_AUTO;     // both paths enqueued, the scheduler picks
+    const bool both = path == KDA_PATH_AUTO;     // the library's choice
+    // With cu_seqlens only the device knows the lengths: both paths are
+    // enqueued and the scheduler kernel picks (the other path's kernels exit
+    // at once).  B sequences of T tokens: the host picks and enqueues one.
+    int host_pick = -1;
+    if (both && cu_seqlens == nullptr) {
+      const int64_t nc = (T + kda::C - 1) / kda::C;
+      host_pick = kda::choose_path(H, B, B * nc, nc);
+    }
+    const bool run_split = !both || host_pick != KDA_PATH_FUSED;
+    const bool run_fused = both && host_pick != KDA_PATH_SPLIT;
     const int chunk = chunk_req == 0 ? kda::default_chunk() : chunk_req;
     kda::Layout L;
     int64_t N = 0;
@@ -424,7 +434,8 @@ static int fwd_impl(const void* q, const void* k, const void* v, const void* g, 
     rec(0, stream);
     rec4(0);
     if (e == hipSuccess) {
-      kda::SchedArgs sa{cu_seqlens, N, B, T, H, P, part_rows, both ? KDA_PATH_AUTO : KDA_PATH_SPLIT, ws, L};
+      kda::SchedArgs sa{cu_seqlens, N, B, T, H, P, part_rows,
+                        both ? (host_pick >= 0 ? host_pick : KDA_PATH_AUTO) : KDA_PATH_SPLIT, ws, L};
       e = kda::launch_sched(sa, stream);
     }
     rec(1, stream);
@@ -438,7 +449,7 @@ static int fwd_impl(const void* q, const void* k, const void* v, const void* g, 
                        static_cast<const uint16_t*>(g), static_cast<const uint16_t*>(beta), A_log, dt_bias,
                        scale, lower_bound, H, p, bound, ws, L};
       rec(2 + 2 * p, stream);
-      if (e == hipSuccess) e = kda::launch_prep(pa, stream);
+      if (e == hipSuccess && run_split) e = kda::launch_prep(pa, stream);
       rec(3 + 2 * p, stream);
       if (p == P - 1) rec4(2);   // after the last chunk prep
       if (P > 1 && e == hipSuccess) {
@@ -450,7 +461,7 @@ static int fwd_impl(const void* q, const void* k, const void* v, const void* g, 
                         sdt, N, H, p, lo, hi, ws, L};
       ra.precision = precision;
       rec(2 + 2 * P + 2 * p, rstream);
-      if (e == hipSuccess) e = kda::launch_recur(ra, rstream);
+      if (e == hipSuccess && run_split) e = kda::launch_recur(ra, rstream);
       rec(3 + 2 * P + 2 * p, rstream);
     }
     if (P > 1 && e == hipSuccess) {
@@ -459,7 +470,7 @@ static int fwd_impl(const void* q, const void* k, const void* v, const void* g, 
     }
     if (both) {   // exits at once unless the scheduler chose it (then prep and recurrence exited)
       rec(6, stream);
-      if (e == hipSuccess) {
+      if (e == hipSuccess && run_fused) {
         kda::FusedArgs fa{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                           static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(g),
                           static_cast<const uint16_t*>(beta), static_cast<uint16_t*>(out), A_log, dt_bias, scale,

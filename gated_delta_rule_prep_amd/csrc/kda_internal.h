@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/kda.h"   // the KDA_PATH_* codes of the path choice
+
 namespace kda {
 
 constexpr int C = 16;     // chunk size of the 16-token kernels (tokens per chunk)
@@ -100,6 +102,31 @@ struct SchedArgs {
 // Fused-kernel value-column tiling: 64 columns per workgroup (two per
 // (sequence, head)) while two tiles per pair fit on the CUs at once, else 128.
 inline __host__ __device__ bool fused_two_tiles(int64_t pairs) { return 2 * pairs <= 512; }
+
+// The library's path choice: estimated time (us) of each path on MI355X for H
+// heads, `total` chunks over all sequences, the longest sequence's `maxc`
+// chunks and N sequences (the scheduler kernel evaluates it for cu_seqlens;
+// for B sequences of T tokens the host does).  The
+// constants are measured on the box at K = V = 128 (T = 8192, H = 64 and 96,
+// fixed length, 8 x 1024 and 12 ragged sequences):
+//   split: the prep kernel streams inputs and records at about 5.2 ns per
+//     (chunk, head); the recurrence is either the longest chain (0.59 us per
+//     chunk step) or, with many pairs, throughput (0.65 us per 64-column tile
+//     step per CU, 256 CUs);
+//   fused: one 16-token step of a workgroup takes about 1.8 us (two 64-column
+//     tiles per pair) or 2.15 us (one 128-column tile), each sequence takes
+//     five pipeline steps more than its chunk count, and the work spreads
+//     over 256 CUs, one workgroup per CU.
+__host__ __device__ inline int choose_path(int64_t H, int64_t N, int64_t total, int64_t maxc) {
+  const double chunk_heads = (double)total * (double)H;
+  const double split = 5.2e-3 * chunk_heads + fmax(0.59 * (double)maxc, 0.65 * 2.0 * chunk_heads / 256.0);
+  const bool two = fused_two_tiles(N * H);
+  const double step = two ? 1.8 : 2.15;
+  const double wg_steps = ((double)total + 5.0 * (double)N) * (double)H * (two ? 2.0 : 1.0);
+  const double fused = fmax(step * (double)(maxc + 5), step * wg_steps / 256.0);
+  return fused < split ? KDA_PATH_FUSED : KDA_PATH_SPLIT;
+}
+
 
 struct PrepArgs {
   const uint16_t* q;

@@ -90,10 +90,11 @@ extern "C" {
      it, so the records never reach HBM (16-token chunks, one part);
    KDA_PATH_AUTO: the library's choice.  On MI355X the fused kernel is
      faster for batches of many short sequences and the split path whenever
-     a sequence is long; the lengths are known only on the device, so both
-     paths are enqueued and the scheduler kernel picks one from the chunk
-     counts (the other path's kernels exit at once).  The workspace is the
-     split path's. */
+     a sequence is long.  With cu_seqlens the lengths are known only on the
+     device, so both paths are enqueued and the scheduler kernel picks one
+     from the chunk counts (the other path's kernels exit at once); for B
+     sequences of T tokens the host applies the same estimate and enqueues
+     only the path it picks.  The workspace is the split path's. */
 #define KDA_PATH_AUTO 0
 #define KDA_PATH_SPLIT 1
 #define KDA_PATH_FUSED 2
