@@ -87,9 +87,10 @@ def test_fused_many_pairs_parity():
 @pytest.mark.parametrize("lens,H,expect", [([2048], 8, "split"), ([512] * 8, 64, "fused")],
                          ids=["one-long", "many-short"])
 def test_library_choice_picks_a_path_and_matches_it_bitwise(lens, H, expect):
-    """kda_fwd enqueues both paths and the scheduler kernel picks one from the
-    chunk counts: a single long sequence runs the split path, many short ones
-    the fused kernel; the result is bit for bit the chosen path's."""
+    """The library's path choice from the chunk counts (on the host for the
+    one fixed-length sequence, by the scheduler kernel with cu_seqlens): a
+    single long sequence runs the split path, many short ones the fused kernel;
+    the result is bit for bit the chosen path's."""
     from gated_delta_rule_prep_amd import kda
     inp = make_inputs(1, sum(lens), H, seed=111, state_dtype="bf16", seq_lens=lens if len(lens) > 1 else None)
     d = device_inputs(inp)
@@ -102,6 +103,27 @@ def test_library_choice_picks_a_path_and_matches_it_bitwise(lens, H, expect):
     assert torch.equal(out.view(torch.int16), o2.view(torch.int16))
     assert torch.equal(fin.view(torch.int16), f2.view(torch.int16))
     hs = [0, H // 2, H - 1]
+    ref_o, ref_f = oracle_run(inp, hs)
+    assert_close(to_f64(out)[:, :, hs], ref_o, "out")
+    assert_close(to_f64(fin)[:, hs], ref_f, "final_state", "bf16")
+
+
+def test_host_choice_for_fixed_lengths_picks_fused_for_many_short():
+    """B sequences of T tokens: the host evaluates the path estimate itself and
+    enqueues only the chosen path; 8 x 512 tokens at H = 64 runs the fused
+    kernel, bit for bit as kda_fwd_ex(fused)."""
+    from gated_delta_rule_prep_amd import kda
+    inp = make_inputs(8, 512, 64, seed=112, state_dtype="bf16")
+    d = device_inputs(inp)
+    say("case host choice B=8 T=512 H=64 (expect fused)")
+    ws = kda.alloc_workspace(8, 512, 64, 8, False, "cuda", None, None, "auto")
+    out, fin = run_gpu(inp, d=d, workspace=ws, path="auto")
+    assert kda.path_taken(ws) == "fused"
+    o2, f2 = run_gpu(inp, d=d, path="fused")
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(fin.view(torch.int16), f2.view(torch.int16))
+    hs = [0, 63]
     ref_o, ref_f = oracle_run(inp, hs)
     assert_close(to_f64(out)[:, :, hs], ref_o, "out")
     assert_close(to_f64(fin)[:, hs], ref_f, "final_state", "bf16")
