@@ -25,7 +25,10 @@
  * the current HIP device; q, k, g, v, out and the states must be 16-byte aligned.  The caller owns every buffer, including the
  * workspace; the library never allocates or frees device memory.  kda_fwd only
  * enqueues work on `stream` (no host synchronisation, no device reads on the
- * host); buffers must stay alive until the stream has passed the call.
+ * host); buffers must stay alive until the stream has passed the call.  It
+ * enqueues kernel launches only (no memsets or copies), so a call can be
+ * captured into a HIP graph and replayed with the same buffers; so can
+ * kda_fwd_ex without events or parts, kda_fwd_segmented and kda_decode.
  *
  * Shapes (P2 Kernel API), with N = B without cu_seqlens, len(cu_seqlens) - 1 with:
  *   q, k, g        bf16  [B, T, H, K]
