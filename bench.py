@@ -288,7 +288,8 @@ def main():
                          "kernel of known size that scales the HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build measures one GPU only; run it with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: the forward runs on one GPU's share of the heads and sequences, "
+              "which shard across GPUs with no communication; run it with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -354,3 +354,15 @@ def test_kda_fwd_workspace_covers_its_segmented_form():
     # with cu_seqlens the lengths are the device's: no cut, plain sizes
     assert kda.workspace_bytes(1, 8192, 4, 1, True) == max(kda.workspace_layout(1, 8192, 4, 1, True, chunk=16)["total"],
                                                             kda.workspace_layout(1, 8192, 4, 1, True, chunk=32)["total"])
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU; asked for more it exits with status 2 and a
+    message, before touching a device."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "--gpus 1" in r.stderr and r.stdout == ""
