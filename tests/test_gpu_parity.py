@@ -74,6 +74,29 @@ def test_config_parity(ci, path, chunk):
     check(inp, heads, tag="config%d %s" % (ci, cfg.name), chunk=chunk, path=path)
 
 
+@pytest.mark.parametrize("ci", range(5))
+def test_config_parity_library_choice(ci):
+    """The five workloads as bench.py times them: kda_fwd_ex with the library's
+    path choice (the fixed 8192-token headline runs the split path, the 8 x 1024
+    varlen batch the fused kernel), sampled heads against the oracle."""
+    from gated_delta_rule_prep_amd import kda
+    cfg = configs()[ci]
+    inp = cfg.make()
+    heads = None if inp.H <= 4 else sorted({0, 1, inp.H // 2, inp.H - 1})
+    say("case config%d %s path=auto" % (ci, cfg.name))
+    ws = kda.alloc_workspace(inp.B, inp.T, inp.H, inp.N, inp.cu_seqlens is not None, "cuda", None, None, "auto")
+    out, fin = run_gpu(inp, workspace=ws, path="auto")
+    torch.cuda.synchronize()
+    taken = kda.path_taken(ws)
+    assert taken in ("split", "fused")
+    if ci in (2, 3):
+        assert taken == ("split" if ci == 2 else "fused")
+    ref_o, ref_f = oracle_run(inp, heads)
+    hs = list(range(inp.H)) if heads is None else heads
+    assert_close(to_f64(out)[:, :, hs], ref_o, "out")
+    assert_close(to_f64(fin)[:, hs], ref_f, "final_state", inp.state_dtype)
+
+
 def test_fused_many_pairs_parity():
     """More (sequence, head) pairs than two 64-column tiles each can place on
     the 256 CUs at once: the fused path then runs one workgroup per pair
