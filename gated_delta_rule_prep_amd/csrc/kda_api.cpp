@@ -460,6 +460,7 @@ static int fwd_impl(const void* q, const void* k, const void* v, const void* g, 
       kda::RecurArgs ra{static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out), initial_state, final_state,
                         sdt, N, H, p, lo, hi, ws, L};
       ra.precision = precision;
+      ra.tiles = kda::recur_tiles(N * H, cu_seqlens == nullptr);
       rec(2 + 2 * P + 2 * p, rstream);
       if (e == hipSuccess && run_split) e = kda::launch_recur(ra, rstream);
       rec(3 + 2 * P + 2 * p, rstream);

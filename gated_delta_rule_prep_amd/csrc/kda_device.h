@@ -50,8 +50,10 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_floa
 __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
   return __builtin_bit_cast(uint16_t, (__bf16)x);   // (not a read through a uint16_t pointer: that aliasing is undefined)
 }
+// Two fp32 -> two bf16 in one word (lo in the low half), round to nearest even
+// (one v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
 }
 
 __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {

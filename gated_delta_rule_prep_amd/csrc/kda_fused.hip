@@ -445,7 +445,7 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
       uint16_t* const out_seq = a.out + ((int64_t)se.row0 * H + h) * V + col0;
       const int64_t out_chunk = (int64_t)C * H * V;
       const int out_lane = (int)((lc * H) * V) + 4 * lg;
-      u32x2 o_prev[NT];
+      f32x4 o_prev[NT];
 #pragma unroll
       for (int s = -kLead; s < -kLead + D - 1; ++s)   // groups -5 .. D - 7 in flight
         issue_group<NT, D>(g0 + (s + kLead) * F::kGroupBytes, pl, x, s, wave);
@@ -467,7 +467,7 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
         if (s > 0) {   // output of chunk s - 1, a full chunk (only the last chunk is partial)
           uint16_t* const ob = out_seq + (int64_t)(s - 1) * out_chunk;
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt) *reinterpret_cast<u32x2*>(ob + out_lane + 16 * nt) = o_prev[nt];
+          for (int nt = 0; nt < NT; ++nt) *reinterpret_cast<u32x2*>(ob + out_lane + 16 * nt) = pack_out(o_prev[nt]);
         }
         // T of chunk s + 1 (L^T completed at step s - 1), independent of this
         // step's chain; past the last chunk it lands in a record slot that no
@@ -485,7 +485,7 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
       if (lc < pr.len) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
-          *reinterpret_cast<u32x2*>(a.out + ((pr.row0 + lc) * H + h) * V + col0 + 16 * nt + 4 * lg) = o_prev[nt];
+          *reinterpret_cast<u32x2*>(a.out + ((pr.row0 + lc) * H + h) * V + col0 + 16 * nt + 4 * lg) = pack_out(o_prev[nt]);
       }
     } else {
       PrepCtx pc;

@@ -166,7 +166,17 @@ struct RecurArgs {
   // Precision variant of the chunk step (KDA_PREC_*, 16-token chunks only);
   // 0 is the library's own arithmetic.
   int precision;
+  // Value tiles per (sequence, head) for 16-token chunks: 1, 2 or 4 (128, 64
+  // or 32 columns per workgroup), or 0 for recur_tiles(pairs, false).
+  int tiles;
 };
+
+// The recurrence's value tiles per (sequence, head) for `pairs` chains (the
+// sequence-head pairs of the launch): 4 while that still gives one workgroup
+// per CU, else 2; 1 when the sequences are known to be of equal length and
+// two tiles per pair would not fit on the CUs at once (then throughput, not
+// the longest chain, bounds the launch).
+int recur_tiles(int64_t pairs, bool equal_lengths);
 
 // Fused chunk prep + recurrence (one kernel, records kept in LDS): the
 // inputs and outputs of kda_fwd, the scheduler's tables in `ws`.

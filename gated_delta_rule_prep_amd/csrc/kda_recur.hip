@@ -3,46 +3,55 @@
 // The second stage of the split the pages describe (P1 §二 2.2: chunk-by-chunk
 // delta-rule recurrence, output projection, rolling state).  The state's value
 // columns never interact (every step acts on each value column of the state
-// separately), so a (sequence, head) pair is cut into V-tiles, one workgroup
-// of four waves per tile, and each wave owns 16 (or, when built for it, 32) of
-// the tile's columns.  Nothing is exchanged between workgroups.  The 128 x 16
-// fp32 state slice of a wave lives in registers as 8 MFMA accumulator tiles
-// for the whole sequence; two workgroups share a pair, so each wave's serial
-// per-chunk work is half of what a whole pair would need (see launch_recur).
+// separately), so a (sequence, head) pair is cut into value tiles of 32, 64 or
+// 128 columns, one workgroup per tile, and nothing is exchanged between
+// workgroups.
 //
 // P1 = blog post "FlashKDA：月之暗面开源的 Kimi Delta Attention 高性能内核".
 //
-// Per chunk (records from the prep kernel, Z = chunk-start state, K x V; T,
-// Mqk, Kbar^T and V reach their MFMA operand layouts through transposing LDS
-// reads of token-major tiles):
-//   U = T V                      fp16 MFMA 16x16x16
-//   E = U + (-W) Z               fp16 MFMA 16x16x32 chain over the 128 channels
-//   O^T = Z^T Qhat^T + E^T Mqk^T fp16 MFMA; the same register operands as
-//                                O = Qhat Z + Mqk E with A and B swapped, so
-//                                each lane ends up with four consecutive value
-//                                columns of one token and stores them directly
-//   Z = diag(gam) Z + Kbar^T E   fp16 MFMA 16x16x16, accumulating onto gam * Z
-// Z is converted to fp16 per step for the two products that read it; the state
-// itself stays fp32.  The channel order of Qhat / -W in the record matches the
-// rows a lane holds in its two accumulator tiles (kPermCh), so the conversion
-// needs no lane exchange.  The decay factors reach the lanes by DPP row
-// broadcast from a permuted copy of gamma (kGamSlot): two LDS words per lane
-// instead of 32.
+// Per chunk (records from the prep kernel, Z = chunk-start state, K x V), on
+// the 16-column state slice of each compute wave (kda_step16.h):
+//   R = V + (-Khat) Z              fp16 MFMA 16x16x32 chain over the channels
+//   E = T R                        fp16 MFMA 16x16x16
+//   O^T = Z^T Qhat^T + E^T Mqk^T   fp16 MFMA (each lane ends up with four
+//                                  consecutive value columns of one token)
+//   Z = diag(gam) Z + Kbar^T E     fp16 MFMA 16x16x16 onto the decayed state
+// with the state itself in fp32 registers for the whole sequence.
 //
-// Memory pipeline: a ring of kDepth chunk slots in LDS, filled by direct
-// buffer-to-LDS loads (buffer_load_dwordx4 ... lds) issued kDepth - 1 chunks
-// ahead, so no VGPRs or LDS write instructions are spent on staging and up to
-// kDepth - 1 chunks are in flight from HBM.  Each slot holds the tile's value
-// rows (raw bf16) and the chunk record.  Every 16-byte piece of a slot may come
-// from any 16-byte piece of HBM, so the pieces are stored XOR-swizzled by row
-// (rather than padded), which keeps the operand reads free of bank conflicts.
-// One barrier per chunk: a wave waits for its own loads of the chunk (vmcnt),
-// then the barrier makes every wave's loads visible, and only then is the slot
-// of the previous chunk (read by every wave before the barrier) refilled.
+// Workgroup = compute waves (16 value columns each) + kLoaders loader waves.
+//   * Loader waves own every load.  Chunk c of the launch belongs to loader
+//     c mod kLoaders, which streams the chunk's record (13.8 KB) and the
+//     tile's value rows into LDS slot c mod kSlots with buffer-to-LDS loads,
+//     kSlots - 2 steps ahead, and waits for them (vmcnt(0)) just before the
+//     barrier of step c.  A loader issues its next chunk only after that wait,
+//     so it never has more than one chunk in flight and each wait covers
+//     exactly the loads of that chunk, whatever order loads complete in.
+//   * Compute waves take one barrier per step, read the step's operands from
+//     the slot (with fixed per-lane addresses plus immediates: the slot pads
+//     rows instead of swizzling them -- Qhat and -Khat rows 272 bytes apart,
+//     Kbar rows 288, value rows 2 x columns + 32 -- which also keeps the 16-byte
+//     and transposing 8-byte reads on distinct banks) and run the step.  They
+//     issue no loads and keep no load bookkeeping, so their instruction stream
+//     is the step itself (18 MFMA, 32 decay multiplies, 20 fp16 conversions,
+//     20 LDS reads and little else).
 //
-// Work placement: consecutive workgroup ids go round-robin to the 8 XCDs, and
-// the V-tiles of one pair are given ids that land on the same XCD, so the
-// pair's records come from HBM once per XCD L2 rather than once per tile.
+// What a step costs on MI355X (measured with probes shaped like this kernel,
+// 192 workgroups, 512 steps): the chain of one 16-column wave alone issues
+// one instruction per 4 cycles and takes 0.24 us; reading the 13 KB of
+// operands from LDS adds 0.17 us when four waves read them at once (every wave
+// needs the whole record; about 128 B per clock of LDS reads), and the
+// loaders' LDS writes a little more.  So a CU's step time grows with the
+// number of waves that read each record: 0.41 us per step with two compute
+// waves (32-column tiles) against 0.60 us with four (64-column tiles).  Waves
+// of 32 columns each (half the reads per column) double each wave's issue
+// time and measured slower.
+//
+// Tiles (recur_tiles): 32 columns while four tiles per pair still give one
+// workgroup per CU, else 64, else (equal lengths and many pairs: throughput,
+// not the longest chain, decides) 128.  Work placement: consecutive workgroup
+// ids go round-robin to the 8 XCDs, and the tiles of one pair get ids on the
+// same XCD, so the pair's records come from HBM once per L2 rather than once
+// per tile.
 #include "kda_device.h"
 #include "kda_internal.h"
 #include "kda_lds_pipe.h"
@@ -52,33 +61,39 @@
 namespace kda {
 namespace {
 
-constexpr int kRecPieces = REC_BYTES / 16;   // 864 16-byte pieces per record
+// ---- LDS slot layout --------------------------------------------------------
+// 16-byte positions: the tile's value rows first (row stride kValStride), then
+// the record fields at padded row strides; each region a whole number of
+// 64-position load instructions.  Offsets in bytes within the record region:
+constexpr int kQkStride = 2 * K + 16;                // Qhat / -Khat row stride
+constexpr int kKbStride = 2 * K + 32;                // Kbar row stride
+constexpr int kSlotQh = 0;                           // Qhat  [16][272]
+constexpr int kSlotNk = C * kQkStride;               // -Khat [16][272]
+constexpr int kSlotKb = 2 * C * kQkStride;           // Kbar  [16][288]
+constexpr int kSlotTail = kSlotKb + C * kKbStride;   // T^T, Mqk^T, gamma as in the record
+constexpr int kRecRegion = kSlotTail + (REC_BYTES - REC_T);
+constexpr int kRecLoads = (kRecRegion / 16 + 63) / 64;   // load instructions of the record region
+constexpr int kLoaders = 4;
+constexpr int kSlots = kLoaders + 2;                 // the loads of a chunk are issued kSlots - 2 steps ahead
+constexpr int kFar = 0x7ffffff0;                     // an offset past every descriptor's range: reads 0
+static_assert(REC_NK == REC_QH + C * 2 * K && REC_KB == REC_NK + C * 2 * K && REC_T == REC_KB + C * 2 * K,
+              "Qhat, -Khat and Kbar are three consecutive [16][128] fp16 arrays");
+static_assert(REC_MQK == REC_T + 512 && REC_GAM == REC_MQK + 512 && REC_BYTES == REC_GAM + 512,
+              "T^T, Mqk^T and gamma end the record");
 
-// NT: 16-column MFMA tiles per wave; D: ring depth; W: waves per workgroup.
-template <int NT, int D, int W>
-struct Cfg {
-  static constexpr int kWaves = W;
-  static constexpr int kThreads = 64 * W;
-  static constexpr int kWaveCols = 16 * NT;             // value columns per wave
-  static constexpr int kCols = kWaveCols * W;           // value columns per workgroup
-  static constexpr int kTiles = V / kCols;              // workgroups per (sequence, head)
-  static constexpr int kRowPieces = kCols / 8;          // 16-byte pieces per value row of the tile
-  static constexpr int kValBlocks = C * kRowPieces / 64;             // 64-piece blocks of values
-  static constexpr int kBlocks = kValBlocks + (kRecPieces + 63) / 64;   // 1 KB blocks of a slot
-  static constexpr int kMaxLoads = (kBlocks + W - 1) / W;   // load instructions per wave per chunk (at most)
-  static constexpr bool kEven = kBlocks % W == 0;           // every wave issues kMaxLoads
-  static constexpr int kSlotBytes = kBlocks * 1024;     // one ring slot
-  // byte offsets of the fields inside a slot
-  static constexpr int kVal = 0;
-  static constexpr int kRec = kValBlocks * 1024;
-  static_assert(C * kRowPieces % 64 == 0, "value rows fill whole blocks");
-  // The value rows are swizzled as piece p ^ 2 (r % 4) (see make_plan): with
-  // fewer than 8 pieces per row that index leaves the tile, and for the last
-  // tile of the last head it reads past the end of v (a 32-column build did,
-  // and faulted).  So tiles are at least 64 columns wide.
-  static_assert(kRowPieces >= 8, "the value swizzle needs at least 8 pieces (64 columns) per tile row");
-  static_assert(D >= 3 && (D - 2) * kMaxLoads <= 63, "ring depth within the vmcnt range");
-  static_assert(V % kCols == 0, "tile shape");
+// WC compute waves of 16 value columns each.
+template <int WC>
+struct Tile {
+  static constexpr int kThreads = 64 * (WC + kLoaders);
+  static constexpr int kCols = 16 * WC;                   // value columns per workgroup
+  static constexpr int kTiles = V / kCols;                // workgroups per (sequence, head)
+  static constexpr int kValStride = 2 * kCols + 32;
+  static constexpr int kRowPieces = kCols / 8;            // 16-byte pieces per value row
+  static constexpr int kValPos = (C * kValStride / 16 + 63) / 64 * 64;
+  static constexpr int kValLoads = kValPos / 64;
+  static constexpr int kRecBase = 16 * kValPos;           // record region within a slot
+  static constexpr int kSlotBytes = kRecBase + 64 * 16 * kRecLoads;
+  static_assert(kSlots * kSlotBytes <= 159 * 1024, "the ring fits the LDS");
 };
 
 // Chunk j of a sequence: first flattened token row and length (1..16).
@@ -91,102 +106,53 @@ __device__ __forceinline__ Rows chunk_rows(const SeqEntry& se, int j) {
   return Rows{(int64_t)se.row0 + C * j, rem < C ? rem : C};
 }
 
-// ---- swizzled slot layout -------------------------------------------------
-// Qhat and -W: token row r, 16-byte piece p (8 channels in record order) at
-// piece position p ^ r of the row.  Kbar and the value tile: piece p of row r
-// at position p ^ 2 (r % 4).  T^T, Mqk^T and gamma are stored as in the record.
-
-// Byte offset (within the record) of the piece that record piece position `s`
-// of a slot holds.
-__device__ __forceinline__ int rec_source(int s) {
-  if (s >= kRecPieces) return 0;   // padding: any valid piece
-  const int r = (s >> 4) & 15, p = s & 15;
-  if (s < 512) return 16 * ((s & ~15) | (p ^ r));
-  if (s < 768) return 16 * ((s & ~15) | (p ^ (2 * (r & 3))));
-  return 16 * s;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_r;
+__device__ __forceinline__ s16x4 tr16(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_r*)p);
 }
 
-// Where this lane's load instruction j of a chunk reads from.  Slot block
-// b = W j + wave (64 pieces, one per lane); blocks below kValBlocks hold the
-// value tile, the rest the record.
-template <int NT, int D, int W>
-struct LoadPlan {
-  int32_t off[Cfg<NT, D, W>::kMaxLoads];   // record byte offset, or value byte offset within the token row
-  int32_t row[Cfg<NT, D, W>::kMaxLoads];   // value blocks: byte offset of the piece within the chunk's rows
-};
-
-template <int NT, int D, int W>
-__device__ __forceinline__ void make_plan(LoadPlan<NT, D, W>& pl, int wave, int lane, int row_bytes) {
-  using Cf = Cfg<NT, D, W>;
+// The operands of one chunk step of a 16-column wave (wc = its first tile
+// column): the record region `rec` and the value rows `val` of a slot.  Lane
+// (lc, lg) = (lane % 16, lane / 16).  The transposing reads: lane j of 16-lane
+// group g fetches the 8 bytes at row 4g + j / 4, columns 4 (j % 4) .. +3 of a
+// token-major tile, and receives column j of rows 4g .. 4g + 3 (see
+// lds_read_tr).
+template <int VS>
+__device__ __forceinline__ void read_slot(Ops<1>& o, const char* rec, const char* val, int wc, int lane) {
+  const int lg = lane >> 4, lc = lane & 15;
+  const int tr_row = 4 * lg + (lc >> 2), tr_col = 4 * (lc & 3);
+  const char* tm = rec + kSlotTail + tr_row * 2 * C + 2 * tr_col;
+  o.aT = __builtin_bit_cast(f16x4, tr16(tm));
+  o.am = __builtin_bit_cast(f16x4, tr16(tm + 2 * C * C));
+  const s16x4 raw = tr16(val + tr_row * VS + 2 * (wc + tr_col));
 #pragma unroll
-  for (int j = 0; j < Cf::kMaxLoads; ++j) {
-    const int b = W * j + wave;
-    if (b < Cf::kValBlocks) {
-      const int s = 64 * b + lane, r = s / Cf::kRowPieces, p = s % Cf::kRowPieces;
-      pl.off[j] = 16 * (p ^ (2 * (r & 3)));
-      pl.row[j] = r * row_bytes + pl.off[j];
-    } else {
-      pl.row[j] = 0;
-      pl.off[j] = rec_source(64 * (b - Cf::kValBlocks) + lane);
-    }
-  }
-}
-
-// Issue the loads of chunk min(c, clast) into the ring slot at LDS address
-// `slot_lds` (all lanes, no waits); clast is the last chunk of the part, so
-// loads never run ahead into records that the next part's prep may still be
-// writing.  `vseq` is the sequence's first value row at this tile's first
-// column; everything but the per-lane offsets of the load plan is
-// wave-uniform, so the per-chunk bookkeeping stays in scalar registers.
-// Value rows past the end of a partial chunk repeat the last row: the
-// record gives them zero weight (their T rows and columns and their -W, Qhat
-// and Kbar rows are exactly zero), so any finite values are harmless.
-template <int NT, int D, int W>
-__device__ __forceinline__ void issue_chunk(uint32_t slot_lds, const LoadPlan<NT, D, W>& pl, const char* recs,
-                                            const char* vseq, const SeqEntry& se, int c, int clast, int row_bytes,
-                                            int wave) {
-  using Cf = Cfg<NT, D, W>;
-  c = min(c, clast);
-  const int len = min(se.len - C * c, C);
-  const i32x4 rrec = buf_rsrc(recs + (int64_t)c * REC_BYTES, REC_BYTES);
-  const i32x4 rval = buf_rsrc(vseq + (int64_t)c * C * row_bytes, C * row_bytes);
-  const int last = (len - 1) * row_bytes;   // byte offset of the chunk's last value row
+  for (int i = 0; i < 4; ++i) o.v[0][i] = bf16_to_f32((uint16_t)raw[i]);
+  const char* qk = rec + lc * kQkStride + 16 * lg;
 #pragma unroll
-  for (int j = 0; j < Cf::kMaxLoads; ++j) {
-    const int b = W * j + wave;   // wave-uniform
-    if (b >= Cf::kBlocks) break;
-    if (b < Cf::kValBlocks) {
-      load_lds16(rval, slot_lds + 1024 * b, min(pl.row[j], last + pl.off[j]));
-    } else {
-      load_lds16(rrec, slot_lds + 1024 * b, pl.off[j]);
-    }
+  for (int s = 0; s < 4; ++s) {
+    o.aw[s] = *reinterpret_cast<const f16x8*>(qk + kSlotNk + 64 * s);
+    o.aq[s] = *reinterpret_cast<const f16x8*>(qk + kSlotQh + 64 * s);
   }
+  const char* kb = rec + kSlotKb + tr_row * kKbStride + 2 * tr_col;
+#pragma unroll
+  for (int m = 0; m < 8; ++m) o.ak[m] = __builtin_bit_cast(f16x4, tr16(kb + 32 * m));
+  o.g2 = *reinterpret_cast<const f32x2*>(rec + kSlotTail + 4 * C * C + 8 * lane);
 }
 
-// Wait until this wave's loads of chunk ci have landed: at most the loads of
-// the D - 2 later chunks may still be in flight (loads complete in issue
-// order; the output stores, also counted, only make the wait stricter).
-template <int NT, int D, int W>
-__device__ __forceinline__ void wait_chunk(int wave) {
-  using Cf = Cfg<NT, D, W>;
-  if constexpr (Cf::kEven) {
-    wait_vmcnt<(D - 2) * Cf::kMaxLoads>();
-  } else {
-    if (wave < Cf::kBlocks % W) wait_vmcnt<(D - 2) * Cf::kMaxLoads>();
-    else wait_vmcnt<(D - 2) * (Cf::kMaxLoads - 1)>();
-  }
-}
-
-template <int NT, int D, int W, int PV>
-__global__ __launch_bounds__(64 * W) void recur_kernel(RecurArgs a) {
-  using Cf = Cfg<NT, D, W>;
-  __shared__ __align__(1024) char ring[D][Cf::kSlotBytes];
+template <int WC, int PV>
+__global__ __launch_bounds__(Tile<WC>::kThreads) void recur_kernel(RecurArgs a) {
+  using Tl = Tile<WC>;
+  __shared__ __align__(1024) char ring[kSlots * Tl::kSlotBytes];
   const int64_t H = a.H;
+  const WsHeader* hdr = reinterpret_cast<const WsHeader*>(a.ws);
+  // Nothing is touched (no output, no state) unless the scheduler accepted
+  // cu_seqlens; the fused kernel runs instead when the scheduler chose it.
+  if (hdr->status != KDA_STATUS_OK || hdr->path == KDA_PATH_FUSED) return;
   // XCD-aware placement: id b runs on XCD b % 8; the kTiles tiles of pair
   // 8 * g + x get ids 8 * (kTiles * g + tile) + x.
   const int64_t bid = blockIdx.x, x = bid & 7, q = bid >> 3;
-  const int64_t pairs = a.N * H, pair2 = 8 * (q / Cf::kTiles) + x;
-  const int tile = (int)(q % Cf::kTiles);
+  const int64_t pairs = a.N * H, pair2 = 8 * (q / Tl::kTiles) + x;
+  const int tile = (int)(q % Tl::kTiles);
   if (pair2 >= (a.sets == 2 ? 2 * pairs : pairs)) return;
   const bool alt = pair2 >= pairs;   // the second set: the transition (zero values, identity start)
   const int64_t pair = alt ? pair2 - pairs : pair2;
@@ -194,12 +160,10 @@ __global__ __launch_bounds__(64 * W) void recur_kernel(RecurArgs a) {
   const void* const s_in = alt ? nullptr : a.s_in;
   void* const s_out = alt ? static_cast<void*>(a.s_out2) : a.s_out;   // (alt: written below as fp16)
   const int sdt = alt ? KDA_DTYPE_FP32 : a.state_dtype;
-  if (reinterpret_cast<const WsHeader*>(a.ws)->path == KDA_PATH_FUSED) return;   // the fused kernel runs instead
   const int64_t slot_id = pair / H;
   const int h = (int)(pair - slot_id * H);
-  const int v0 = tile * Cf::kCols;
-  const int32_t* order = reinterpret_cast<const int32_t*>(a.ws + a.lay.order);
-  const int n = order[slot_id];
+  const int v0 = tile * Tl::kCols;
+  const int n = reinterpret_cast<const int32_t*>(a.ws + a.lay.order)[slot_id];
   const SeqEntry se = reinterpret_cast<const SeqEntry*>(a.ws + a.lay.seq_table)[n];
   const char* recs = a.ws + a.lay.records + ((int64_t)h * a.lay.max_chunks + se.first_chunk) * REC_BYTES;
   const int nch = se.nchunks;
@@ -215,160 +179,196 @@ __global__ __launch_bounds__(64 * W) void recur_kernel(RecurArgs a) {
   };
   const int ci_lo = first_at(a.row_lo), ci_hi = first_at(a.row_hi);
   if (nch > 0 ? ci_lo >= ci_hi : a.part != 0) return;
+  const int steps = ci_hi - ci_lo;
   const bool from_caller = ci_lo == 0, to_caller = ci_hi == nch;
   float* const ws_state = reinterpret_cast<float*>(a.ws + a.lay.state);
 
   const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, lg = lane >> 4, lc = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int row_bytes = (int)(H * V * 2);
+
+  if (wave >= WC) {
+    // ---------------- loader wave ----------------
+    // Chunk c (step c of the launch) goes to slot c mod kSlots, which last held
+    // chunk c - kSlots: the compute waves are done with that one at barrier
+    // c - kSlots + 1.  So chunk c is issued after that barrier, in iteration
+    // c - kSlots + 2 (iteration i ends with barrier i; chunks 0 .. kSlots - 3
+    // before the loop), and waited for in iteration c, before barrier c.
+    static_assert(kLoaders == kSlots - 2, "one chunk in flight per loader");
+    const int j = wave - WC;
+    // Source offset of this lane's 16-byte position in each load instruction.
+    // Pads, and the value rows of a partial chunk past its end, lie past the
+    // descriptor's range and read as zeros (the record gives those rows zero
+    // weight); the transition set reads no values at all.
+    int32_t vsrc[Tl::kValLoads], rsrc[kRecLoads];
+#pragma unroll
+    for (int i = 0; i < Tl::kValLoads; ++i) {
+      const int P = 64 * i + lane, r = P / (Tl::kValStride / 16), p = P % (Tl::kValStride / 16);
+      vsrc[i] = (r < C && p < Tl::kRowPieces) ? r * row_bytes + 16 * p : kFar;
+    }
+#pragma unroll
+    for (int i = 0; i < kRecLoads; ++i) {
+      const int P = 64 * i + lane;
+      int src = kFar;
+      if (P < kSlotNk / 16) {
+        const int r = P / (kQkStride / 16), p = P % (kQkStride / 16);
+        if (p < 16) src = REC_QH + 16 * (16 * r + p);
+      } else if (P < kSlotKb / 16) {
+        const int r = (P - kSlotNk / 16) / (kQkStride / 16), p = (P - kSlotNk / 16) % (kQkStride / 16);
+        if (p < 16) src = REC_NK + 16 * (16 * r + p);
+      } else if (P < kSlotTail / 16) {
+        const int r = (P - kSlotKb / 16) / (kKbStride / 16), p = (P - kSlotKb / 16) % (kKbStride / 16);
+        if (p < 16) src = REC_KB + 16 * (16 * r + p);
+      } else if (P < kRecRegion / 16) {
+        src = REC_T + 16 * (P - kSlotTail / 16);
+      }
+      rsrc[i] = src;
+    }
+    const char* vseq = reinterpret_cast<const char*>(a.v + ((int64_t)se.row0 * H + h) * V + v0);
+    const uint32_t ring0 = lds_addr(ring);
+    const auto issue = [&](int st) {
+      const int c = ci_lo + st;
+      const int len = min(se.len - C * c, C);
+      const i32x4 rrec = buf_rsrc(recs + (int64_t)c * REC_BYTES, REC_BYTES);
+      const i32x4 rval = buf_rsrc(vseq + (int64_t)c * C * row_bytes, alt ? 0 : (len - 1) * row_bytes + 2 * Tl::kCols);
+      const uint32_t slot = ring0 + (uint32_t)((st % kSlots) * Tl::kSlotBytes);
+#pragma unroll
+      for (int i = 0; i < Tl::kValLoads; ++i) load_lds16(rval, slot + 1024 * i, vsrc[i]);
+#pragma unroll
+      for (int i = 0; i < kRecLoads; ++i) load_lds16(rrec, slot + Tl::kRecBase + 1024 * i, rsrc[i]);
+    };
+    for (int c = j; c < min(steps, kSlots - 2); c += kLoaders) issue(c);
+    for (int i = 0; i < steps; ++i) {
+      if ((i & (kLoaders - 1)) == j) wait_vmcnt<0>();   // chunk i has landed in its slot
+      const int c = i + kSlots - 2;
+      if (c < steps && (c & (kLoaders - 1)) == j) issue(c);
+      barrier();
+    }
+    return;
+  }
+
+  // ---------------- compute wave ----------------
+  const int lg = lane >> 4, lc = lane & 15;
   const int64_t sbase = ((int64_t)n * H + h) * V * K;   // state [n][h][v][k]
-  const int wc = Cf::kWaveCols * wave;                   // first tile column of this wave
+  const int wc = 16 * wave;                              // first tile column of this wave
   const int col0 = v0 + wc;                              // first state column of this wave
 
-  // ---- state slice: Z[m][nt] holds rows 16m + 4lg + i, column col0 + 16nt + lc
-  f32x4 Z[8][NT];
+  // ---- state slice: Z[m][0] holds rows 16m + 4lg + i, column col0 + lc
+  f32x4 Z[8][1];
 #pragma unroll
-  for (int m = 0; m < 8; ++m)
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int64_t idx = sbase + (int64_t)(col0 + 16 * nt + lc) * K + 16 * m + 4 * lg;
-      if (!from_caller) {
-        Z[m][nt] = *reinterpret_cast<const f32x4*>(ws_state + idx);
-      } else if (alt) {   // stored [v][k] = (v == k); this lane holds k = 16 m + 4 lg + i, v = col0 + 16 nt + lc
-        const int kv = col0 + 16 * nt + lc - 16 * m - 4 * lg;
-        Z[m][nt] = f32x4{kv == 0 ? 1.f : 0.f, kv == 1 ? 1.f : 0.f, kv == 2 ? 1.f : 0.f, kv == 3 ? 1.f : 0.f};
-      } else if (s_in == nullptr) {
-        Z[m][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      } else if (sdt == KDA_DTYPE_FP32) {
-        Z[m][nt] = *reinterpret_cast<const f32x4*>(static_cast<const float*>(s_in) + idx);
-      } else {
-        const u32x2 w = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(s_in) + idx);
-        Z[m][nt] = f32x4{bf16_lo(w[0]), bf16_hi(w[0]), bf16_lo(w[1]), bf16_hi(w[1])};
-      }
+  for (int m = 0; m < 8; ++m) {
+    const int64_t idx = sbase + (int64_t)(col0 + lc) * K + 16 * m + 4 * lg;
+    if (!from_caller) {
+      Z[m][0] = *reinterpret_cast<const f32x4*>(ws_state + idx);
+    } else if (alt) {   // stored [v][k] = (v == k); this lane holds k = 16 m + 4 lg + i, v = col0 + lc
+      const int kv = col0 + lc - 16 * m - 4 * lg;
+      Z[m][0] = f32x4{kv == 0 ? 1.f : 0.f, kv == 1 ? 1.f : 0.f, kv == 2 ? 1.f : 0.f, kv == 3 ? 1.f : 0.f};
+    } else if (s_in == nullptr) {
+      Z[m][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+    } else if (sdt == KDA_DTYPE_FP32) {
+      Z[m][0] = *reinterpret_cast<const f32x4*>(static_cast<const float*>(s_in) + idx);
+    } else {
+      const u32x2 w = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(s_in) + idx);
+      Z[m][0] = f32x4{bf16_lo(w[0]), bf16_hi(w[0]), bf16_lo(w[1]), bf16_hi(w[1])};
     }
+  }
 
-  if (ci_lo < ci_hi) {
-    const int row_bytes = (int)(H * V * 2);
-    LoadPlan<NT, D, W> pl;
-    make_plan<NT, D, W>(pl, wave, lane, row_bytes);
-    const int clast = ci_hi - 1;
-    const char* vseq = reinterpret_cast<const char*>(a.v + ((int64_t)se.row0 * H + h) * V + v0);
-    const uint32_t ring0 = (uint32_t)reinterpret_cast<uintptr_t>((lds_void*)ring[0]);
+  if (steps > 0) {
     // Output rows of a full chunk: a wave-uniform base per chunk plus this
-    // lane's fixed offset (token lc, columns 16 nt + 4 lg .. +3).
-    uint16_t* const out_seq = outp + ((int64_t)se.row0 * H + h) * V + col0;
+    // lane's fixed offset (token lc, columns 4 lg .. +3 of the wave).
+    uint16_t* const out_seq = outp != nullptr ? outp + ((int64_t)(se.row0 + C * ci_lo) * H + h) * V + col0 : nullptr;
     const int64_t out_chunk = (int64_t)C * H * V;
     const int out_lane = (int)((lc * H) * V) + 4 * lg;
-    // Chunks ci_lo .. ci_lo + D-2 in flight before the first step.  Loads past
-    // the part's last chunk repeat it into slots that are never read.
-#pragma unroll
-    for (int c = 0; c < D - 1; ++c)
-      issue_chunk<NT, D, W>(ring0 + c * Cf::kSlotBytes, pl, recs, vseq, se, ci_lo + c, clast, row_bytes, wave);
-    u32x2 o_prev[NT];
-    int slot = 0;   // ring slot of chunk ci
-    for (int ci = ci_lo; ci < ci_hi; ++ci) {
-      // At most the D - 2 chunks issued after chunk ci may still be in flight
-      // (loads complete in issue order); the output stores of the step
-      // before, also counted, have had a whole step to complete.
-      wait_chunk<NT, D, W>(wave);
-      wait_lgkm0();
+    // The output of a step is rounded and stored in the next step, well after
+    // the MFMAs that produce it: a vector read of an MFMA result issued
+    // shortly after it, with more MFMAs issued in between, has returned the
+    // register's old contents on gfx950 although the compiler's wait states
+    // were in place (a form of this loop unrolled by two, whose second copy
+    // rounded its output right after computing it, got half of every lane's
+    // values stale).  A scheduling barrier before every step barrier keeps
+    // each step's instructions on their side of it.
+    f32x4 o_prev[1];
+    for (int s = 0; s < steps; ++s) {
+      __builtin_amdgcn_sched_barrier(0);
       barrier();
-      // Every wave is done with chunk ci - 1, whose slot is refilled now, and
-      // every wave's loads of chunk ci have landed.
-      const int refill = slot == 0 ? D - 1 : slot - 1;
-      issue_chunk<NT, D, W>(ring0 + refill * Cf::kSlotBytes, pl, recs, vseq, se, ci + D - 1, clast, row_bytes, wave);
-      if (ci > ci_lo && outp != nullptr) {   // output of chunk ci - 1, a full chunk (only a sequence's last chunk is partial)
-        uint16_t* const ob = out_seq + (int64_t)(ci - 1) * out_chunk;
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) *reinterpret_cast<u32x2*>(ob + out_lane + 16 * nt) = o_prev[nt];
-      }
-      Ops<NT> ops;
-      read_ops<NT>(ops, ring[slot] + Cf::kRec, ring[slot] + Cf::kVal, 2 * Cf::kCols, wc, lane);
-      if (alt) {
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) ops.v[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-      compute<NT, PV>(Z, ops, o_prev);
-      slot = slot == D - 1 ? 0 : slot + 1;
+      const char* slot = ring + (s % kSlots) * Tl::kSlotBytes;
+      Ops<1> ops;
+      read_slot<Tl::kValStride>(ops, slot + Tl::kRecBase, slot, wc, lane);
+      if (s > 0 && outp != nullptr)   // output of step s - 1, a full chunk (only a sequence's last chunk is partial)
+        *reinterpret_cast<u32x2*>(out_seq + (int64_t)(s - 1) * out_chunk + out_lane) = pack_out(o_prev[0]);
+      compute<1, PV>(Z, ops, o_prev);
+      wait_lgkm0();   // every read of this slot is done before the next barrier
     }
-    wait_vmcnt<0>();   // no load into the ring outlives the workgroup
-    const Rows pr = chunk_rows(se, clast);
-    if (lc < pr.len && outp != nullptr) {
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        *reinterpret_cast<u32x2*>(outp + ((pr.row0 + lc) * H + h) * V + col0 + 16 * nt + 4 * lg) = o_prev[nt];
-    }
+    __builtin_amdgcn_sched_barrier(0);
+    const Rows pr = chunk_rows(se, ci_hi - 1);
+    if (lc < pr.len && outp != nullptr)
+      *reinterpret_cast<u32x2*>(outp + ((pr.row0 + lc) * H + h) * V + col0 + 4 * lg) = pack_out(o_prev[0]);
   }
 
   // ---- state out
   if (!to_caller || s_out != nullptr) {
 #pragma unroll
-    for (int m = 0; m < 8; ++m)
+    for (int m = 0; m < 8; ++m) {
+      const int64_t idx = sbase + (int64_t)(col0 + lc) * K + 16 * m + 4 * lg;
+      if (!to_caller) {
+        *reinterpret_cast<f32x4*>(ws_state + idx) = Z[m][0];
+      } else if (alt) {   // the transition, fp16 in math layout [k][v]
+        uint16_t* const at = a.s_out2 + sbase + (int64_t)(16 * m + 4 * lg) * V + col0 + lc;
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const int64_t idx = sbase + (int64_t)(col0 + 16 * nt + lc) * K + 16 * m + 4 * lg;
-        if (!to_caller) {
-          *reinterpret_cast<f32x4*>(ws_state + idx) = Z[m][nt];
-        } else if (alt) {   // the transition, fp16 in math layout [k][v]
-          uint16_t* const at = a.s_out2 + sbase + (int64_t)(16 * m + 4 * lg) * V + col0 + 16 * nt + lc;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) at[i * V] = __builtin_bit_cast(uint16_t, (_Float16)Z[m][nt][i]);
-        } else if (sdt == KDA_DTYPE_FP32) {
-          *reinterpret_cast<f32x4*>(static_cast<float*>(s_out) + idx) = Z[m][nt];
-        } else {
-          u32x2 w;
-          w[0] = pack_bf16(Z[m][nt][0], Z[m][nt][1]);
-          w[1] = pack_bf16(Z[m][nt][2], Z[m][nt][3]);
-          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(s_out) + idx) = w;
-        }
+        for (int i = 0; i < 4; ++i) at[i * V] = __builtin_bit_cast(uint16_t, (_Float16)Z[m][0][i]);
+      } else if (sdt == KDA_DTYPE_FP32) {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(s_out) + idx) = Z[m][0];
+      } else {
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(s_out) + idx) = pack_out(Z[m][0]);
       }
-  }
-}
-
-// Launches recur_kernel<..., PV> for PV = a.precision, PV running over 0 .. 7.
-template <int NT, int D, int W, int PV>
-void launch_variant(const RecurArgs& a, int64_t grid, hipStream_t s) {
-  if constexpr (PV < 8) {
-    if (a.precision == PV) {
-      hipLaunchKernelGGL((recur_kernel<NT, D, W, PV>), dim3((unsigned)grid), dim3(64 * W), 0, s, a);
-      return;
     }
-    launch_variant<NT, D, W, PV + 1>(a, grid, s);
   }
 }
 
-template <int NT, int D, int W>
-hipError_t launch_tiles(const RecurArgs& a, hipStream_t s) {
-  const int64_t pairs = a.N * a.H * (a.sets == 2 ? 2 : 1);
-  const int64_t grid = 8 * Cfg<NT, D, W>::kTiles * ((pairs + 7) / 8);
+template <int WC, int PV>
+hipError_t launch_tiles(const RecurArgs& a, int64_t pairs, hipStream_t s) {
+  using Tl = Tile<WC>;
+  const int64_t grid = 8 * Tl::kTiles * ((pairs + 7) / 8);
   if (grid > INT32_MAX) return hipErrorInvalidValue;
-  // the study's variants (kda_fwd_precision): any combination of the three bits
-  if (a.precision < 0 || a.precision > 7) return hipErrorInvalidValue;
-  launch_variant<NT, D, W, 0>(a, grid, s);
+  hipLaunchKernelGGL((recur_kernel<WC, PV>), dim3((unsigned)grid), dim3(Tl::kThreads), 0, s, a);
   return hipGetLastError();
+}
+
+// The precision study's variants (kda_fwd_precision) run on 64-column tiles.
+template <int PV>
+hipError_t launch_variant(const RecurArgs& a, int64_t pairs, hipStream_t s) {
+  if constexpr (PV < 8) {
+    if (a.precision == PV) return launch_tiles<4, PV>(a, pairs, s);
+    return launch_variant<PV + 1>(a, pairs, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-// Value columns per recurrence workgroup: 64.  Each wave takes 16 columns and
-// a pair is split over two workgroups, so the per-step VALU work (state
-// conversion and decay) and MFMA work of a wave are half of a whole pair's
-// and the longest chain of the batch (the critical path) runs twice as fast
-// per chunk.  One workgroup of eight 16-column waves per pair (W = 8: each
-// record streamed once per pair, two recurrence waves per SIMD) measured
-// slower: 0.43 ms against 0.33 at T = 8192, H = 96 fixed, 0.44 against 0.34 on
-// the ragged batch, 0.26 against 0.27 at 8 x 1024.  Whole pairs per workgroup (32 columns per wave, NT = 2) read
-// each record once instead of twice but measured faster only with many short
-// sequences of equal length (3 % at 8 x 1024 tokens, H = 96) and 25 % slower
-// with one long sequence among short ones.  A 4-chunk ring (64 KB) covers the
-// HBM latency (deeper rings measured no faster).
-#ifndef KDA_RECUR_DEPTH
-#define KDA_RECUR_DEPTH 4
-#endif
+// Measured on MI355X (recurrence kernel alone, ms): T = 8192 H = 64 fixed:
+// 0.212 with 4 tiles, 0.266 with 2; T = 8192 H = 96 fixed: 0.306 with 2 tiles,
+// 0.395 with 4 (384 workgroups > 256 CUs), 0.402 with 1; 12 ragged sequences,
+// H = 96 (one of ~6000 tokens): 0.307 with 2, 0.396 with 1; 8 x 1024, H = 96:
+// 0.239 with 1, 0.278 with 2.
+int recur_tiles(int64_t pairs, bool equal_lengths) {
+  if (4 * pairs <= 256) return 4;
+  if (2 * pairs <= 256 || !equal_lengths) return 2;
+  return 1;
+}
 
 hipError_t launch_recur(const RecurArgs& a, hipStream_t s) {
   if (a.lay.chunk == C32) return a.sets == 2 || a.precision != 0 ? hipErrorInvalidValue : launch_recur32(a, s);
-  if (a.N * a.H == 0) return hipSuccess;
-  return launch_tiles<1, KDA_RECUR_DEPTH, 4>(a, s);
+  const int64_t pairs = a.N * a.H * (a.sets == 2 ? 2 : 1);
+  if (pairs == 0) return hipSuccess;
+  if (a.precision < 0 || a.precision > 7) return hipErrorInvalidValue;
+  if (a.precision != 0) return launch_variant<1>(a, pairs, s);
+  switch (a.tiles > 0 ? a.tiles : recur_tiles(pairs, false)) {
+    case 4: return launch_tiles<2, 0>(a, pairs, s);
+    case 2: return launch_tiles<4, 0>(a, pairs, s);
+    case 1: return launch_tiles<8, 0>(a, pairs, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace kda

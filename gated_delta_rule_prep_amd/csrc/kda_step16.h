@@ -144,10 +144,14 @@ __device__ __forceinline__ bf16x8 bf8_of(f16x8 h) {
 }
 
 // One chunk step from operands in registers: updates Z and returns the output
-// tile as O^T (lane (lc, lg): token lc, value columns 16nt + 4lg .. +3 of the
-// wave), rounded to bf16 and packed.
+// tile as O^T in fp32 (lane (lc, lg): token lc, value columns 16nt + 4lg .. +3
+// of the wave).  Callers round and store it a step later (pack_out), well
+// after the MFMA that produces it: a vector read of an MFMA result soon after
+// it issues, with further MFMAs queued behind it, has been measured on gfx950
+// to return the register's old contents, although the compiler's wait states
+// were in place (see the recurrence kernel's notes).
 template <int NT, int PV = kPrecDefault>
-__device__ __forceinline__ void compute(f32x4 (&Z)[8][NT], const Ops<NT>& o, u32x2 (&out)[NT]) {
+__device__ __forceinline__ void compute(f32x4 (&Z)[8][NT], const Ops<NT>& o, f32x4 (&out)[NT]) {
   // ---- R = V + (-Khat) Z ; O^T = Z^T Qhat^T
   f32x4 R[NT], O[NT];
 #pragma unroll
@@ -213,8 +217,12 @@ __device__ __forceinline__ void compute(f32x4 (&Z)[8][NT], const Ops<NT>& o, u32
   }
 
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) out[nt] = u32x2{pack_bf16(O[nt][0], O[nt][1]), pack_bf16(O[nt][2], O[nt][3])};
+  for (int nt = 0; nt < NT; ++nt) out[nt] = O[nt];
 }
+
+// The output tile of a step, rounded to bf16 (nearest even) and packed for one
+// 8-byte store per 16 columns.
+__device__ __forceinline__ u32x2 pack_out(f32x4 o) { return u32x2{pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3])}; }
 
 // State slice of a wave: Z[m][nt] holds rows 16m + 4lg + i, column
 // col0 + 16nt + lc of the state of one (sequence, head), read from `s_in`
