@@ -365,7 +365,7 @@ static int fwd_impl(const void* q, const void* k, const void* v, const void* g, 
     int host_pick = -1;
     if (both && cu_seqlens == nullptr) {
       const int64_t nc = (T + kda::C - 1) / kda::C;
-      host_pick = kda::choose_path(H, B, B * nc, nc);
+      host_pick = kda::choose_path(H, B, B * nc, nc, true);
     }
     const bool run_split = !both || host_pick != KDA_PATH_FUSED;
     const bool run_fused = both && host_pick != KDA_PATH_SPLIT;

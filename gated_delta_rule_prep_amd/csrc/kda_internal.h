@@ -103,23 +103,37 @@ struct SchedArgs {
 // (sequence, head)) while two tiles per pair fit on the CUs at once, else 128.
 inline __host__ __device__ bool fused_two_tiles(int64_t pairs) { return 2 * pairs <= 512; }
 
+// The recurrence's value tiles per (sequence, head) for `pairs` chains (the
+// sequence-head pairs of the launch): 4 while that still gives one workgroup
+// per CU, else 2; 1 when the sequences are known to be of equal length and
+// two tiles per pair would not fit on the CUs at once (then throughput, not
+// the longest chain, bounds the launch).
+__host__ __device__ inline int recur_tiles(int64_t pairs, bool equal_lengths) {
+  if (4 * pairs <= 256) return 4;
+  if (2 * pairs <= 256 || !equal_lengths) return 2;
+  return 1;
+}
+
 // The library's path choice: estimated time (us) of each path on MI355X for H
 // heads, `total` chunks over all sequences, the longest sequence's `maxc`
 // chunks and N sequences (the scheduler kernel evaluates it for cu_seqlens;
-// for B sequences of T tokens the host does).  The
-// constants are measured on the box at K = V = 128 (T = 8192, H = 64 and 96,
-// fixed length, 8 x 1024 and 12 ragged sequences):
-//   split: the prep kernel streams inputs and records at about 5.2 ns per
-//     (chunk, head); the recurrence is either the longest chain (0.59 us per
-//     chunk step) or, with many pairs, throughput (0.65 us per 64-column tile
-//     step per CU, 256 CUs);
+// for B sequences of T tokens the host does).  The constants are measured on
+// the box at K = V = 128 (T = 8192, H = 64 and 96, fixed length, 8 x 1024 and
+// 12 ragged sequences):
+//   split: the prep kernel streams inputs and records at about 5.0 ns per
+//     (chunk, head); a recurrence workgroup step takes about 0.41 us with
+//     32-column tiles and 0.58 us with 64-column ones (recur_tiles), and the
+//     recurrence is either the longest chain or, with many pairs, throughput
+//     (one workgroup per CU at a time, 256 CUs);
 //   fused: one 16-token step of a workgroup takes about 1.8 us (two 64-column
 //     tiles per pair) or 2.15 us (one 128-column tile), each sequence takes
 //     five pipeline steps more than its chunk count, and the work spreads
 //     over 256 CUs, one workgroup per CU.
-__host__ __device__ inline int choose_path(int64_t H, int64_t N, int64_t total, int64_t maxc) {
+__host__ __device__ inline int choose_path(int64_t H, int64_t N, int64_t total, int64_t maxc, bool equal_lengths) {
   const double chunk_heads = (double)total * (double)H;
-  const double split = 5.2e-3 * chunk_heads + fmax(0.59 * (double)maxc, 0.65 * 2.0 * chunk_heads / 256.0);
+  const int tiles = recur_tiles(N * H, equal_lengths);
+  const double rstep = tiles == 4 ? 0.41 : tiles == 2 ? 0.58 : 1.24;
+  const double split = 5.0e-3 * chunk_heads + fmax(rstep * (double)maxc, rstep * tiles * chunk_heads / 256.0);
   const bool two = fused_two_tiles(N * H);
   const double step = two ? 1.8 : 2.15;
   const double wg_steps = ((double)total + 5.0 * (double)N) * (double)H * (two ? 2.0 : 1.0);
@@ -170,13 +184,6 @@ struct RecurArgs {
   // or 32 columns per workgroup), or 0 for recur_tiles(pairs, false).
   int tiles;
 };
-
-// The recurrence's value tiles per (sequence, head) for `pairs` chains (the
-// sequence-head pairs of the launch): 4 while that still gives one workgroup
-// per CU, else 2; 1 when the sequences are known to be of equal length and
-// two tiles per pair would not fit on the CUs at once (then throughput, not
-// the longest chain, bounds the launch).
-int recur_tiles(int64_t pairs, bool equal_lengths);
 
 // Fused chunk prep + recurrence (one kernel, records kept in LDS): the
 // inputs and outputs of kda_fwd, the scheduler's tables in `ws`.

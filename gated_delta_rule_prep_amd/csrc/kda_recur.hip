@@ -21,11 +21,12 @@
 // Workgroup = compute waves (16 value columns each) + kLoaders loader waves.
 //   * Loader waves own every load.  Chunk c of the launch belongs to loader
 //     c mod kLoaders, which streams the chunk's record (13.8 KB) and the
-//     tile's value rows into LDS slot c mod kSlots with buffer-to-LDS loads,
-//     kSlots - 2 steps ahead, and waits for them (vmcnt(0)) just before the
-//     barrier of step c.  A loader issues its next chunk only after that wait,
-//     so it never has more than one chunk in flight and each wait covers
-//     exactly the loads of that chunk, whatever order loads complete in.
+//     tile's value rows into LDS slot c mod kSlots (kSlots = kLoaders + 2)
+//     with buffer-to-LDS loads, issued kSlots - 2 steps ahead, and waits for
+//     them (vmcnt(0)) just before the barrier of step c.  A loader issues its
+//     next chunk only after that wait, so it never has more than one chunk in
+//     flight and each wait covers exactly the loads of that chunk, whatever
+//     order loads complete in.
 //   * Compute waves take one barrier per step, read the step's operands from
 //     the slot (with fixed per-lane addresses plus immediates: the slot pads
 //     rows instead of swizzling them -- Qhat and -Khat rows 272 bytes apart,
@@ -73,8 +74,6 @@ constexpr int kSlotKb = 2 * C * kQkStride;           // Kbar  [16][288]
 constexpr int kSlotTail = kSlotKb + C * kKbStride;   // T^T, Mqk^T, gamma as in the record
 constexpr int kRecRegion = kSlotTail + (REC_BYTES - REC_T);
 constexpr int kRecLoads = (kRecRegion / 16 + 63) / 64;   // load instructions of the record region
-constexpr int kLoaders = 4;
-constexpr int kSlots = kLoaders + 2;                 // the loads of a chunk are issued kSlots - 2 steps ahead
 constexpr int kFar = 0x7ffffff0;                     // an offset past every descriptor's range: reads 0
 static_assert(REC_NK == REC_QH + C * 2 * K && REC_KB == REC_NK + C * 2 * K && REC_T == REC_KB + C * 2 * K,
               "Qhat, -Khat and Kbar are three consecutive [16][128] fp16 arrays");
@@ -84,6 +83,11 @@ static_assert(REC_MQK == REC_T + 512 && REC_GAM == REC_MQK + 512 && REC_BYTES ==
 // WC compute waves of 16 value columns each.
 template <int WC>
 struct Tile {
+  // loader waves: six for 32-column tiles, whose shorter steps need the loads
+  // issued further ahead (T = 8192, H = 64: 0.210 against 0.227 ms with
+  // four), four otherwise (H = 96, 64 columns: 0.302 against 0.308 with six)
+  static constexpr int kLoaders = WC == 2 ? 6 : 4;
+  static constexpr int kSlots = kLoaders + 2;            // the loads of a chunk are issued kSlots - 2 steps ahead
   static constexpr int kThreads = 64 * (WC + kLoaders);
   static constexpr int kCols = 16 * WC;                   // value columns per workgroup
   static constexpr int kTiles = V / kCols;                // workgroups per (sequence, head)
@@ -142,7 +146,7 @@ __device__ __forceinline__ void read_slot(Ops<1>& o, const char* rec, const char
 template <int WC, int PV>
 __global__ __launch_bounds__(Tile<WC>::kThreads) void recur_kernel(RecurArgs a) {
   using Tl = Tile<WC>;
-  __shared__ __align__(1024) char ring[kSlots * Tl::kSlotBytes];
+  __shared__ __align__(1024) char ring[Tl::kSlots * Tl::kSlotBytes];
   const int64_t H = a.H;
   const WsHeader* hdr = reinterpret_cast<const WsHeader*>(a.ws);
   // Nothing is touched (no output, no state) unless the scheduler accepted
@@ -189,12 +193,12 @@ __global__ __launch_bounds__(Tile<WC>::kThreads) void recur_kernel(RecurArgs a) 
 
   if (wave >= WC) {
     // ---------------- loader wave ----------------
-    // Chunk c (step c of the launch) goes to slot c mod kSlots, which last held
-    // chunk c - kSlots: the compute waves are done with that one at barrier
-    // c - kSlots + 1.  So chunk c is issued after that barrier, in iteration
-    // c - kSlots + 2 (iteration i ends with barrier i; chunks 0 .. kSlots - 3
-    // before the loop), and waited for in iteration c, before barrier c.
-    static_assert(kLoaders == kSlots - 2, "one chunk in flight per loader");
+    // Chunk c (step c of the launch) goes to slot c mod kSlots, which last
+    // held chunk c - kSlots: the compute waves are done with that one at
+    // barrier c - kSlots + 1.  So chunk c is issued right after barrier
+    // c - kSlots + 2 (chunks 0 .. kSlots - 3 before the loop) and waited for
+    // before barrier c.
+    static_assert(Tl::kLoaders == Tl::kSlots - 2, "one chunk in flight per loader");
     const int j = wave - WC;
     // Source offset of this lane's 16-byte position in each load instruction.
     // Pads, and the value rows of a partial chunk past its end, lie past the
@@ -231,18 +235,21 @@ __global__ __launch_bounds__(Tile<WC>::kThreads) void recur_kernel(RecurArgs a) 
       const int len = min(se.len - C * c, C);
       const i32x4 rrec = buf_rsrc(recs + (int64_t)c * REC_BYTES, REC_BYTES);
       const i32x4 rval = buf_rsrc(vseq + (int64_t)c * C * row_bytes, alt ? 0 : (len - 1) * row_bytes + 2 * Tl::kCols);
-      const uint32_t slot = ring0 + (uint32_t)((st % kSlots) * Tl::kSlotBytes);
+      const uint32_t slot = ring0 + (uint32_t)((st % Tl::kSlots) * Tl::kSlotBytes);
 #pragma unroll
       for (int i = 0; i < Tl::kValLoads; ++i) load_lds16(rval, slot + 1024 * i, vsrc[i]);
 #pragma unroll
       for (int i = 0; i < kRecLoads; ++i) load_lds16(rrec, slot + Tl::kRecBase + 1024 * i, rsrc[i]);
     };
-    for (int c = j; c < min(steps, kSlots - 2); c += kLoaders) issue(c);
+    for (int c = j; c < min(steps, Tl::kSlots - 2); c += Tl::kLoaders) issue(c);
     for (int i = 0; i < steps; ++i) {
-      if ((i & (kLoaders - 1)) == j) wait_vmcnt<0>();   // chunk i has landed in its slot
-      const int c = i + kSlots - 2;
-      if (c < steps && (c & (kLoaders - 1)) == j) issue(c);
+      const bool mine = i % Tl::kLoaders == j;
+      if (mine) wait_vmcnt<0>();   // chunk i has landed in its slot
       barrier();
+      // the next chunk of this loader, i + kSlots - 2, is issued after the
+      // barrier, while the compute waves work on chunk i: issuing its loads
+      // takes a while, and before the barrier it would hold them up
+      if (mine && i + Tl::kSlots - 2 < steps) issue(i + Tl::kSlots - 2);
     }
     return;
   }
@@ -291,7 +298,7 @@ __global__ __launch_bounds__(Tile<WC>::kThreads) void recur_kernel(RecurArgs a) 
     for (int s = 0; s < steps; ++s) {
       __builtin_amdgcn_sched_barrier(0);
       barrier();
-      const char* slot = ring + (s % kSlots) * Tl::kSlotBytes;
+      const char* slot = ring + (s % Tl::kSlots) * Tl::kSlotBytes;
       Ops<1> ops;
       read_slot<Tl::kValStride>(ops, slot + Tl::kRecBase, slot, wc, lane);
       if (s > 0 && outp != nullptr)   // output of step s - 1, a full chunk (only a sequence's last chunk is partial)
@@ -346,17 +353,11 @@ hipError_t launch_variant(const RecurArgs& a, int64_t pairs, hipStream_t s) {
 
 }  // namespace
 
-// Measured on MI355X (recurrence kernel alone, ms): T = 8192 H = 64 fixed:
-// 0.212 with 4 tiles, 0.266 with 2; T = 8192 H = 96 fixed: 0.306 with 2 tiles,
-// 0.395 with 4 (384 workgroups > 256 CUs), 0.402 with 1; 12 ragged sequences,
-// H = 96 (one of ~6000 tokens): 0.307 with 2, 0.396 with 1; 8 x 1024, H = 96:
-// 0.239 with 1, 0.278 with 2.
-int recur_tiles(int64_t pairs, bool equal_lengths) {
-  if (4 * pairs <= 256) return 4;
-  if (2 * pairs <= 256 || !equal_lengths) return 2;
-  return 1;
-}
-
+// recur_tiles (kda_internal.h), measured on MI355X (recurrence kernel alone,
+// ms): T = 8192 H = 64 fixed: 0.210 with 4 tiles, 0.266 with 2; T = 8192
+// H = 96 fixed: 0.302 with 2 tiles, 0.395 with 4 (384 workgroups > 256 CUs),
+// 0.402 with 1; 12 ragged sequences, H = 96 (one of ~6000 tokens): 0.297 with
+// 2, 0.396 with 1; 8 x 1024, H = 96: 0.239 with 1, 0.278 with 2.
 hipError_t launch_recur(const RecurArgs& a, hipStream_t s) {
   if (a.lay.chunk == C32) return a.sets == 2 || a.precision != 0 ? hipErrorInvalidValue : launch_recur32(a, s);
   const int64_t pairs = a.N * a.H * (a.sets == 2 ? 2 : 1);
