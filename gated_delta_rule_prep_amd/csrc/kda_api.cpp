@@ -307,8 +307,8 @@ static int validate_common(const void* q, const void* k, const void* g, const vo
   if (B * T > 0 && (!q || !k || !g || !beta))
     return fail(KDA_EINVAL, "kda: a required input pointer is NULL");
   if (!A_log || !dt_bias) return fail(KDA_EINVAL, "kda: A_log or dt_bias is NULL");
-  if (misaligned(q) || misaligned(k) || misaligned(g))
-    return fail(KDA_EINVAL, "kda: q, k and g must be 16-byte aligned");
+  if (misaligned(q) || misaligned(k) || misaligned(g) || misaligned(dt_bias))
+    return fail(KDA_EINVAL, "kda: q, k, g and dt_bias must be 16-byte aligned");
   if (!std::isfinite(scale)) return fail(KDA_EINVAL, "kda: scale is not finite");
   if (!std::isfinite(lower_bound) || lower_bound < -5.0f || lower_bound > 0.0f)
     return fail(KDA_EINVAL, "kda: lower_bound must lie in [-5, 0] (got %g)", (double)lower_bound);

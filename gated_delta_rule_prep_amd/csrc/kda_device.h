@@ -56,6 +56,10 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
 }
 
+// Four fp32 values rounded to bf16 (nearest even) and packed for one 8-byte
+// store.
+__device__ __forceinline__ u32x2 pack_out(f32x4 o) { return u32x2{pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3])}; }
+
 __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
   typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
   const f16x2 v = {(_Float16)lo, (_Float16)hi};

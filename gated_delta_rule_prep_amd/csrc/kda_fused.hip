@@ -3,32 +3,34 @@
 //
 // The FlashKDA blog post ("FlashKDA：月之暗面开源的 Kimi Delta Attention 高性能内核",
 // §二 2.2) splits the forward pass into a token-parallel prep stage and a
-// chunk-recurrent stage, joined by per-chunk records in global memory.  On
-// MI355X the recurrence is bound by how fast each CU can stream its operands
-// (records and values, about 16 KB per 16-token step per workgroup), not by
-// its arithmetic; the raw inputs a chunk's record is made from (q, k, g, beta:
-// 12.3 KB) are smaller than the record (13.8 KB), so building the record next
-// to the recurrence costs no extra bytes per CU and removes the record's
-// round trip through HBM (about 1.6 GB per call at T = 8192, H = 96) and the
-// separate prep launch.
+// chunk-recurrent stage, joined by per-chunk records in global memory.  The
+// raw inputs a chunk's record is made from (q, k, g, beta: 12.3 KB per chunk
+// and head) are smaller than the record (13.8 KB), so building the record next
+// to the recurrence that consumes it removes the record's round trip through
+// HBM (written by the prep, read back by the recurrence) and the separate prep
+// launch.  The price is that every workgroup builds its records itself: with
+// two workgroups per (sequence, head) each record is built twice.
 //
 // One workgroup per (sequence, head, V-tile), eight waves:
 //   * waves 0-3 run the recurrence (kda_step16.h) on 16 NT value columns each,
-//     with the fp32 state slice in registers for the whole sequence;
+//     with the fp32 state slice in registers for the whole sequence; they
+//     issue no loads;
 //   * waves 4-7 build the records: prep wave p owns the chunks c = p mod 4 and
-//     builds the record of chunk c during the four steps before step c, one
-//     phase per step (0: inputs, norms, channels 0-31; 1: channels 32-63;
-//     2: channels 64-95; 3: channels 96-127, L, Mqk and the 16 x 16 inverse).
-//     At every step each prep wave runs one phase, of four different chunks,
-//     so the per-step work is close to even, and each SIMD holds one wave of
-//     each kind: the prep wave's ALU work fills the recurrence wave's stalls.
-// Step s (s = -4 .. nchunks - 1) has one barrier.  Before it, every wave waits
-// for its own loads of group s; a group is the raw q, k, g, beta of chunk s + 4
-// (read by the phase-0 wave of step s) and the value rows of chunk s (read by
-// the recurrence at step s), streamed HBM -> LDS with buffer_load ... lds
-// D - 1 groups ahead into a ring of D group slots.  Records live in a ring of
-// five slots (chunks s .. s + 4).  The record layout in LDS is the swizzled
-// one kda_step16.h reads.
+//     builds the record of chunk c during the four steps before step c - 1,
+//     one phase per step (0: inputs, norms, channels 0-31; 1: channels 32-63;
+//     2: channels 64-95; 3: channels 96-127, L and Mqk); the recurrence waves
+//     invert I + L of chunk c at step c - 1.  At every step each prep wave
+//     runs one phase, of four different chunks, so the per-step work is close
+//     to even, and each SIMD holds one wave of each kind: the prep wave's ALU
+//     work fills the recurrence wave's stalls.
+// Step s (s = -5 .. nchunks - 1) has one barrier.  Group s -- the raw q, k,
+// g, beta of chunk s + 5 (read by the phase-0 wave of step s) and the value
+// rows of chunk s (read by the recurrence at step s) -- is streamed HBM -> LDS
+// with buffer_load ... lds into a ring of D group slots by the prep wave that
+// reads its raw inputs, issued D - 1 steps ahead; that wave has no other
+// group in flight and waits for it (vmcnt(0)) before barrier s.  Records live
+// in a ring of six slots (chunks s .. s + 5).  The record layout in LDS is the
+// swizzled one kda_step16.h reads.
 //
 // Per chunk, as in the split prep kernel (kda_prep.hip), with a2 the gate in
 // log2 units, G its in-chunk inclusive cumulative sum, P = 2^G, Pinv = 2^-G,
@@ -71,10 +73,12 @@ struct FCfg {
   // 1 KB blocks of a group slot: q, k, g (4 each: 16 rows x 256 B), beta, values
   static constexpr int kQ = 0, kK = 4, kG = 8, kB = 12, kV = 13;
   static constexpr int kBlocks = kV + kVBlocks;
-  static constexpr int kMaxLoads = (kBlocks + kAllWaves - 1) / kAllWaves;   // per wave per group
   static constexpr int kGroupBytes = kBlocks * 1024;
   static_assert(C * kRowPieces % 64 == 0, "value rows fill whole blocks");
-  static_assert(D >= 3 && (D - 2) * kMaxLoads <= 63, "ring depth within the vmcnt range");
+  // group s is issued after barrier s - D + 1 and waited for before barrier s
+  // by prep wave (s + kLead) mod 4, whose next group, s + 4, is issued after
+  // barrier s + 5 - D: at most one group in flight per wave needs D <= 5
+  static_assert(D >= 3 && D <= 5, "ring depth");
   static_assert(V % kCols == 0, "tile shape");
 };
 
@@ -97,39 +101,6 @@ __device__ __forceinline__ Rows chunk_rows(const SeqEntry& se, int j) {
   return Rows{(int64_t)se.row0 + C * j, rem < C ? rem : C};
 }
 
-// Where this lane's load j of a group reads from.  Group block b = 8 j + wave
-// (64 pieces, one per lane).  q / k / g blocks: slot piece s of the tensor's
-// 16 x 16-piece tile is row s / 16, position s % 16, and holds source piece
-// position ^ row (XOR swizzle: the phase-0 reads of 16 rows at one piece
-// index hit distinct banks).  Value blocks: as in kda_step16.h.  The beta
-// block: lane l fetches the 16-byte piece holding beta of token row l % 16.
-template <int NT, int D>
-struct GroupPlan {
-  int32_t row[FCfg<NT, D>::kMaxLoads];   // token row 0..15 in the chunk
-  int32_t off[FCfg<NT, D>::kMaxLoads];   // byte offset of the piece within the row (not beta)
-};
-
-template <int NT, int D>
-__device__ __forceinline__ void make_plan(GroupPlan<NT, D>& pl, int wave, int lane) {
-  using F = FCfg<NT, D>;
-#pragma unroll
-  for (int j = 0; j < F::kMaxLoads; ++j) {
-    const int b = kAllWaves * j + wave;
-    if (b < F::kB) {
-      const int s = 64 * (b & 3) + lane, r = s >> 4, pos = s & 15;
-      pl.row[j] = r;
-      pl.off[j] = 16 * (pos ^ r);
-    } else if (b == F::kB) {
-      pl.row[j] = lane & 15;
-      pl.off[j] = 0;
-    } else {
-      const int s = 64 * (b - F::kV) + lane, r = s / F::kRowPieces, pos = s % F::kRowPieces;
-      pl.row[j] = r;
-      pl.off[j] = 16 * (pos ^ (2 * (r & 3)));
-    }
-  }
-}
-
 struct Seq {
   const uint16_t* q;       // q, k, g at (sequence row 0, head h)
   const uint16_t* k;
@@ -143,11 +114,15 @@ struct Seq {
 // Issue the loads of group s into the group slot at LDS address `slot_lds`:
 // q, k, g, beta of chunk s + kLead and the value rows of chunk s, each chunk
 // index clamped into the sequence (clamped loads land in parts of slots that
-// are never read).  Rows past the end of a partial chunk repeat its last row;
-// the prep gives them zero weight.  All lanes, no waits.
+// are never read).  One wave issues the whole group, all lanes, no waits.
+// q / k / g: slot piece s of the tensor's 16 x 16-piece tile is row s / 16,
+// position s % 16, and holds source piece position ^ row (XOR swizzle: the
+// phase-0 reads of 16 rows at one piece index hit distinct banks).  Values:
+// the swizzle kda_step16.h reads.  Beta: lane l fetches the 16-byte piece
+// holding beta of token row l % 16.  Rows past the end of a partial chunk
+// repeat its last row; the prep gives them zero weight.
 template <int NT, int D>
-__device__ __forceinline__ void issue_group(uint32_t slot_lds, const GroupPlan<NT, D>& pl, const Seq& x, int s,
-                                            int wave) {
+__device__ __forceinline__ void issue_group(uint32_t slot_lds, const Seq& x, int s, int lane) {
   using F = FCfg<NT, D>;
   const int nch = x.se.nchunks;
   const int cq = min(max(s + kLead, 0), nch - 1), cv = min(max(s, 0), nch - 1);
@@ -156,31 +131,35 @@ __device__ __forceinline__ void issue_group(uint32_t slot_lds, const GroupPlan<N
   const int rs = (int)(H * K * 2);   // bytes between token rows (q, k, g, v alike: K = V)
   const int64_t eq = (rq.row0 - x.se.row0) * H * K, ev = (rv.row0 - x.se.row0) * H * V;
   const int qbytes = (rq.len - 1) * rs + K * 2;
+  const int lr = lane >> 4, lp = lane & 15;
+  int qoff[4];
 #pragma unroll
-  for (int j = 0; j < F::kMaxLoads; ++j) {
-    const int b = kAllWaves * j + wave;   // wave-uniform
-    if (b >= F::kBlocks) break;
-    const uint32_t dst = slot_lds + 1024 * b;
-    if (b < F::kB) {
-      // integer select (wave-uniform b): a pointer select here became an
-      // indexed private array with a full memory wait
-      const uintptr_t base = (b < F::kK ? reinterpret_cast<uintptr_t>(x.q)
-                              : b < F::kG ? reinterpret_cast<uintptr_t>(x.k)
-                                          : reinterpret_cast<uintptr_t>(x.g)) + 2 * eq;
-      load_lds16(buf_rsrc(reinterpret_cast<const void*>(base), qbytes), dst,
-                 min(pl.row[j], rq.len - 1) * rs + pl.off[j]);
-    } else if (b == F::kB) {
-      // 16-byte piece holding beta[row][h]; the descriptor starts at the piece
-      // holding the chunk's first beta, so every offset is a multiple of 16
-      const uintptr_t first = reinterpret_cast<uintptr_t>(x.beta + 2 * (rq.row0 - x.se.row0) * H);
-      const uintptr_t mine = first + (uintptr_t)(2 * (int64_t)min(pl.row[j], rq.len - 1) * H);
-      const uintptr_t base16 = first & ~(uintptr_t)15;
-      load_lds16(buf_rsrc(reinterpret_cast<const void*>(base16), (rq.len - 1) * 2 * (int)H + 32), dst,
-                 (int)((mine & ~(uintptr_t)15) - base16));
-    } else {
-      load_lds16(buf_rsrc(x.v + ev, (rv.len - 1) * rs + F::kCols * 2), dst,
-                 min(pl.row[j], rv.len - 1) * rs + pl.off[j]);
-    }
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * i + lr;
+    qoff[i] = min(r, rq.len - 1) * rs + 16 * (lp ^ r);
+  }
+  const uint16_t* const src[3] = {x.q, x.k, x.g};
+#pragma unroll
+  for (int t = 0; t < 3; ++t) {
+    const i32x4 rsrc = buf_rsrc(src[t] + eq, qbytes);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) load_lds16(rsrc, slot_lds + 1024 * (4 * t + i), qoff[i]);
+  }
+  static_assert(F::kQ == 0 && F::kK == 4 && F::kG == 8, "q, k, g blocks");
+  {
+    // 16-byte piece holding beta[row][h]; the descriptor starts at the piece
+    // holding the chunk's first beta, so every offset is a multiple of 16
+    const uintptr_t first = reinterpret_cast<uintptr_t>(x.beta + 2 * (rq.row0 - x.se.row0) * H);
+    const uintptr_t mine = first + (uintptr_t)(2 * (int64_t)min(lp, rq.len - 1) * H);
+    const uintptr_t base16 = first & ~(uintptr_t)15;
+    load_lds16(buf_rsrc(reinterpret_cast<const void*>(base16), (rq.len - 1) * 2 * (int)H + 32),
+               slot_lds + 1024 * F::kB, (int)((mine & ~(uintptr_t)15) - base16));
+  }
+  const i32x4 rval = buf_rsrc(x.v + ev, (rv.len - 1) * rs + F::kCols * 2);
+#pragma unroll
+  for (int i = 0; i < F::kVBlocks; ++i) {
+    const int sp = 64 * i + lane, r = sp / F::kRowPieces, pos = sp % F::kRowPieces;
+    load_lds16(rval, slot_lds + 1024 * (F::kV + i), min(r, rv.len - 1) * rs + 16 * (pos ^ (2 * (r & 3))));
   }
 }
 
@@ -365,19 +344,6 @@ __device__ __forceinline__ void chunk_inverse(const float (*lt)[C + 4], char* re
   *reinterpret_cast<_Float16*>(rec + REC_T + (j * C + m) * 2) = (_Float16)(x * bj);   // T^T[j][m] = T[m][j]
 }
 
-// Top of a step: wait until this wave's loads of the current group have
-// landed (at most the loads of the D - 2 later groups may still be in flight;
-// loads complete in issue order, and the output stores, also counted, only
-// make the wait stricter), then the barrier that makes every wave's loads and
-// record writes visible.
-template <int kMax, int D>
-__device__ __forceinline__ void step_sync(int nload) {
-  if (nload == kMax) wait_vmcnt<(D - 2) * kMax>();
-  else wait_vmcnt<(D - 2) * (kMax - 1)>();
-  wait_lgkm0();
-  barrier();
-}
-
 template <int NT, int D>
 __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
   using F = FCfg<NT, D>;
@@ -393,7 +359,10 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
   const int64_t pair = 8 * (qb / F::kTiles) + xcd;
   const int tile = (int)(qb % F::kTiles);
   if (pair >= a.N * H) return;
-  if (reinterpret_cast<const WsHeader*>(a.ws)->path == KDA_PATH_SPLIT) return;   // the split kernels run instead
+  const WsHeader* hdr = reinterpret_cast<const WsHeader*>(a.ws);
+  // Nothing is touched (no output, no state) unless the scheduler accepted
+  // cu_seqlens; the split kernels run instead when the scheduler chose them.
+  if (hdr->status != KDA_STATUS_OK || hdr->path == KDA_PATH_SPLIT) return;
   const int64_t slot_id = pair / H;
   const int h = (int)(pair - slot_id * H);
   const int v0 = tile * F::kCols;
@@ -434,36 +403,35 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
     x.v = a.v + ((int64_t)se.row0 * H + h) * V + v0;
     x.H = H;
     x.se = se;
-    GroupPlan<NT, D> pl;
-    make_plan<NT, D>(pl, wave, lane);
-    const int nload = (F::kBlocks - wave + kAllWaves - 1) / kAllWaves;   // this wave's loads per group
     const uint32_t g0 = lds_addr(groups[0]);
 
     // The two kinds of wave run separate loops over the same steps (one
     // barrier each per step), so that neither carries the other's registers.
     if (rec_wave) {
+      // The recurrence waves issue no loads: they wait for their LDS traffic
+      // (reads of the step's operands, T written by the inverse) and meet the
+      // others at the barrier.  The output of a step is rounded and stored in
+      // the next step, well after the MFMAs that produce it, and a scheduling
+      // barrier keeps each step's instructions on their side of the barrier.
       uint16_t* const out_seq = a.out + ((int64_t)se.row0 * H + h) * V + col0;
       const int64_t out_chunk = (int64_t)C * H * V;
       const int out_lane = (int)((lc * H) * V) + 4 * lg;
       f32x4 o_prev[NT];
-#pragma unroll
-      for (int s = -kLead; s < -kLead + D - 1; ++s)   // groups -5 .. D - 7 in flight
-        issue_group<NT, D>(g0 + (s + kLead) * F::kGroupBytes, pl, x, s, wave);
-      int gslot = 0;   // group slot of group s
+      int gslot = kLead % D;   // group slot of group s (group g sits in slot (g + kLead) mod D)
       // steps -5 .. -1: the prep waves start the first records; at step -1 the
       // inverse of chunk 0
       for (int s = -kLead; s < 0; ++s) {
-        step_sync<F::kMaxLoads, D>(nload);
-        issue_group<NT, D>(g0 + (gslot == 0 ? D - 1 : gslot - 1) * F::kGroupBytes, pl, x, s + D - 1, wave);
+        wait_lgkm0();
+        barrier();
         if (s == -1) chunk_inverse(lts[0], recs[0], wave, lane);
-        gslot = gslot == D - 1 ? 0 : gslot + 1;
       }
       int rs = 0;   // record slot of chunk s
       for (int s = 0; s < nch; ++s) {
-        step_sync<F::kMaxLoads, D>(nload);
+        __builtin_amdgcn_sched_barrier(0);
+        wait_lgkm0();
+        barrier();
         // every wave is done with group s - 1 and with the record of chunk
         // s - 1; group s has landed; the record of chunk s is complete
-        issue_group<NT, D>(g0 + (gslot == 0 ? D - 1 : gslot - 1) * F::kGroupBytes, pl, x, s + D - 1, wave);
         if (s > 0) {   // output of chunk s - 1, a full chunk (only the last chunk is partial)
           uint16_t* const ob = out_seq + (int64_t)(s - 1) * out_chunk;
 #pragma unroll
@@ -480,7 +448,7 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
         gslot = gslot == D - 1 ? 0 : gslot + 1;
         rs = rs1;
       }
-      wait_vmcnt<0>();   // no load into the ring outlives the workgroup
+      __builtin_amdgcn_sched_barrier(0);
       const Rows pr = chunk_rows(se, nch - 1);
       if (lc < pr.len) {
 #pragma unroll
@@ -498,24 +466,35 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
       pc.lane = lane;
       Carry cr;
       const int pw = wave - kRecWaves;   // this prep wave builds the chunks c = pw mod 4
-
-#pragma unroll
-      for (int s = -kLead; s < -kLead + D - 1; ++s)
-        issue_group<NT, D>(g0 + (s + kLead) * F::kGroupBytes, pl, x, s, wave);
-      int gslot = 0;
+      // Group g (steps g = -5 .. nch - 1) belongs to the prep wave that reads
+      // its raw inputs (phase 0 of chunk g + 5), pw = (g + 5) mod 4.  That wave
+      // issues it right after barrier g - D + 1, when every wave is done with
+      // group g - D, the slot's previous contents, and waits for it (vmcnt(0))
+      // just before barrier g.  The wave's next group, g + 4, is issued after
+      // barrier g + 5 - D >= g, so a prep wave never has more than one group in
+      // flight and each wait covers exactly that group's loads, whatever order
+      // loads complete in.  Prep waves issue no other global loads or stores in
+      // the loop.
+      const auto mine = [&](int g) { return ((g + kLead) & 3) == pw; };
+      for (int g = -kLead; g < min(-kLead + D - 1, nch); ++g)
+        if (mine(g)) issue_group<NT, D>(g0 + (g + kLead) * F::kGroupBytes, x, g, lane);
+      int gslot = 0;   // group slot of group s
       for (int s = -kLead; s < nch; ++s) {
-        step_sync<F::kMaxLoads, D>(nload);
-        issue_group<NT, D>(g0 + (gslot == 0 ? D - 1 : gslot - 1) * F::kGroupBytes, pl, x, s + D - 1, wave);
+        if (mine(s)) wait_vmcnt<0>();   // group s has landed in its slot
+        wait_lgkm0();
+        barrier();
+        // The lane id passes through an empty asm each step, so that the
+        // lane-dependent addresses and constants of the group loads and of the
+        // four phases are computed where they are used instead of being
+        // hoisted out of the loop and held (or spilled) across it.
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        if (s + D - 1 < nch && mine(s + D - 1))
+          issue_group<NT, D>(g0 + (gslot == 0 ? D - 1 : gslot - 1) * F::kGroupBytes, x, s + D - 1, ln);
         // chunk c (c = pw mod 4) is built in phases 0..3 at steps c - 5 .. c - 2
         const int ph = (s + kLead - pw) & 3;
         const int c = s + kLead - ph;
         if (c >= 0 && c < nch) {
-          // The lane id passes through an empty asm each step, so that the
-          // lane-dependent addresses and constants of the four phases are
-          // computed where they are used instead of being hoisted out of the
-          // loop and held (or spilled) across it.
-          int ln = lane;
-          asm volatile("" : "+v"(ln));
           pc.r = ln & 15;
           pc.cq = ln >> 4;
           pc.lane = ln;
@@ -532,7 +511,7 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
         }
         gslot = gslot == D - 1 ? 0 : gslot + 1;
       }
-      wait_vmcnt<0>();
+      wait_vmcnt<0>();   // (nothing is in flight here: every group issued was waited for)
     }
   }
 

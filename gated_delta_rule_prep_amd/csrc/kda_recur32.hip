@@ -32,19 +32,21 @@ namespace {
 
 constexpr int CC = C32;
 constexpr int kRecPieces = REC32_BYTES / 16;   // 1824 16-byte pieces per record
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
+constexpr int kWaves = 4;                      // compute waves
+constexpr int kLoaders = 2;                    // loader waves
+constexpr int kSlots = kLoaders + 2;           // ring slots: a chunk is issued kSlots - 2 steps ahead
+constexpr int kThreads = 64 * (kWaves + kLoaders);
+constexpr int kFar = 0x7ffffff0;               // an offset past every descriptor's range: reads 0
 
-template <int NT, int D>
+template <int NT>
 struct Cfg {
   static constexpr int kWaveCols = 16 * NT;             // value columns per wave
   static constexpr int kCols = kWaveCols * kWaves;      // value columns per workgroup
   static constexpr int kTiles = V / kCols;              // workgroups per (sequence, head)
   static constexpr int kRowPieces = kCols / 8;          // 16-byte pieces per value row of the tile
   static constexpr int kValBlocks = CC * kRowPieces / 64;            // 64-piece blocks of values
-  static constexpr int kBlocks = (kValBlocks + (kRecPieces + 63) / 64 + kWaves - 1) / kWaves * kWaves;
-  static constexpr int kLoads = kBlocks / kWaves;       // load instructions per wave per chunk
-  static constexpr int kSlotBytes = kBlocks * 1024;     // one ring slot
+  static constexpr int kRecBlocks = (kRecPieces + 63) / 64;          // 64-piece blocks of the record
+  static constexpr int kSlotBytes = (kValBlocks + kRecBlocks) * 1024;   // one ring slot
   static constexpr int kVal = 0;
   static constexpr int kRec = kValBlocks * 1024;
   static constexpr int kQh = kRec + REC32_QH, kNw = kRec + REC32_NW, kKb = kRec + REC32_KB;
@@ -52,8 +54,7 @@ struct Cfg {
   static_assert(CC * kRowPieces % 64 == 0, "value rows fill whole blocks");
   // the value swizzle p ^ 2 (r % 4) stays inside a row of at least 8 pieces
   static_assert(kRowPieces >= 8, "the value swizzle needs at least 8 pieces (64 columns) per tile row");
-  static_assert(D >= 3 && (D - 2) * kLoads <= 63, "ring depth within the vmcnt range");
-  static_assert(D * kSlotBytes <= 160 * 1024, "ring fits the LDS of a CU");
+  static_assert(kSlots * kSlotBytes <= 159 * 1024, "the ring fits the LDS");
   static_assert(V % kCols == 0, "tile shape");
 };
 
@@ -74,7 +75,7 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 // the row.  Kbar and the value tile: piece p of row r at p ^ 2 (r % 4).  T,
 // Mqk and gamma are stored as in the record.
 __device__ __forceinline__ int rec_source(int s) {
-  if (s >= kRecPieces) return 0;   // padding: any valid piece
+  if (s >= kRecPieces) return kFar;   // padding: reads zeros
   const int r = (s >> 4) & 31, p = s & 15;
   if (s < 1024) return 16 * ((s & ~15) | (p ^ (r & 15)));
   if (s < 1536) return 16 * ((s & ~15) | (p ^ (2 * (r & 3))));
@@ -119,9 +120,9 @@ __device__ __forceinline__ f16x8 bf16_to_f16x8(s16x4 lo, s16x4 hi) {
   return r;
 }
 
-template <int NT, int D>
+template <int NT>
 __device__ __forceinline__ void read_ops(Ops<NT>& o, const char* slot, int wc, int lane) {
-  using Cf = Cfg<NT, D>;
+  using Cf = Cfg<NT>;
   const int lg = lane >> 4, lc = lane & 15;
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
@@ -164,10 +165,10 @@ __device__ __forceinline__ f32x4 decay(f32x4 z, f32x2 g2) {
 
 // One chunk step from operands in registers: updates Z and returns the two
 // output tiles as O^T (lane (lc, lg): token 16t + lc, value columns 16nt +
-// 4lg .. +3 of the wave), rounded to bf16 and packed.
+// 4lg .. +3 of the wave) in fp32; the caller rounds them a step later.
 template <int NT>
-__device__ __forceinline__ void compute(f32x4 (&Z)[8][NT], const Ops<NT>& o, u32x2 (&out)[2][NT]) {
-  f32x4 E[2][NT], O[2][NT];
+__device__ __forceinline__ void compute(f32x4 (&Z)[8][NT], const Ops<NT>& o, f32x4 (&O)[2][NT]) {
+  f32x4 E[2][NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
@@ -218,83 +219,29 @@ __device__ __forceinline__ void compute(f32x4 (&Z)[8][NT], const Ops<NT>& o, u32
     Z[6][nt] = mfma_f16_k32(o.ak[6], eb[nt], decay<6>(Z[6][nt], o.g2));
     Z[7][nt] = mfma_f16_k32(o.ak[7], eb[nt], decay<7>(Z[7][nt], o.g2));
   }
-
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-      out[t][nt] = u32x2{pack_bf16(O[t][nt][0], O[t][nt][1]), pack_bf16(O[t][nt][2], O[t][nt][3])};
 }
-
-// Where this lane's load instruction j of a chunk reads from.  Slot block
-// b = kWaves j + wave (64 pieces, one per lane); blocks below kValBlocks hold
-// the value tile, the rest the record.
-template <int NT, int D>
-struct LoadPlan {
-  int32_t off[Cfg<NT, D>::kLoads];   // record byte offset, or value byte offset within the token row
-  int32_t row[Cfg<NT, D>::kLoads];   // value blocks: byte offset of the piece within the chunk's rows
-};
-
-template <int NT, int D>
-__device__ __forceinline__ void make_plan(LoadPlan<NT, D>& pl, int wave, int lane, int row_bytes) {
-  using Cf = Cfg<NT, D>;
-#pragma unroll
-  for (int j = 0; j < Cf::kLoads; ++j) {
-    const int b = kWaves * j + wave;
-    if (b < Cf::kValBlocks) {
-      const int s = 64 * b + lane, r = s / Cf::kRowPieces, p = s % Cf::kRowPieces;
-      pl.off[j] = 16 * (p ^ (2 * (r & 3)));
-      pl.row[j] = r * row_bytes + pl.off[j];
-    } else {
-      pl.row[j] = 0;
-      pl.off[j] = rec_source(64 * (b - Cf::kValBlocks) + lane);
-    }
-  }
-}
-
-// Issue the loads of chunk min(c, clast) into the ring slot at LDS address
-// `slot_lds` (all lanes, no waits; wave-uniform bookkeeping).  Value rows past
-// the end of a partial chunk repeat the last row: the record gives them zero
-// weight.
-template <int NT, int D>
-__device__ __forceinline__ void issue_chunk(uint32_t slot_lds, const LoadPlan<NT, D>& pl, const char* recs,
-                                            const char* vseq, const SeqEntry& se, int c, int clast, int row_bytes,
-                                            int wave) {
-  using Cf = Cfg<NT, D>;
-  c = min(c, clast);
-  const int len = min(se.len - CC * c, CC);
-  const i32x4 rrec = buf_rsrc(recs + (int64_t)c * REC32_BYTES, REC32_BYTES);
-  const i32x4 rval = buf_rsrc(vseq + (int64_t)c * CC * row_bytes, CC * row_bytes);
-  const int last = (len - 1) * row_bytes;   // byte offset of the chunk's last value row
-#pragma unroll
-  for (int j = 0; j < Cf::kLoads; ++j) {
-    const int b = kWaves * j + wave;   // wave-uniform
-    if (b < Cf::kValBlocks) {
-      load_lds16(rval, slot_lds + 1024 * b, min(pl.row[j], last + pl.off[j]));
-    } else {
-      load_lds16(rrec, slot_lds + 1024 * b, pl.off[j]);
-    }
-  }
-}
-
 
 template <int NT>
 __device__ __forceinline__ void store_out(uint16_t* out, const Rows& pr, int64_t H, int h, int col0, int lc, int lg,
-                                          const u32x2 (&o)[2][NT]) {
+                                          const f32x4 (&o)[2][NT]) {
 #pragma unroll
   for (int t = 0; t < 2; ++t)
     if (16 * t + lc < pr.len) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
-        *reinterpret_cast<u32x2*>(out + ((pr.row0 + 16 * t + lc) * H + h) * V + col0 + 16 * nt + 4 * lg) = o[t][nt];
+        *reinterpret_cast<u32x2*>(out + ((pr.row0 + 16 * t + lc) * H + h) * V + col0 + 16 * nt + 4 * lg) =
+            pack_out(o[t][nt]);
     }
 }
 
-template <int NT, int D>
+template <int NT>
 __global__ __launch_bounds__(kThreads) void recur32_kernel(RecurArgs a) {
-  using Cf = Cfg<NT, D>;
-  __shared__ __align__(1024) char ring[D][Cf::kSlotBytes];
+  using Cf = Cfg<NT>;
+  __shared__ __align__(1024) char ring[kSlots * Cf::kSlotBytes];
   const int64_t H = a.H;
+  // Nothing is touched (no output, no state) unless the scheduler accepted
+  // cu_seqlens.
+  if (reinterpret_cast<const WsHeader*>(a.ws)->status != KDA_STATUS_OK) return;
   // XCD-aware placement: id b runs on XCD b % 8; the kTiles tiles of pair
   // 8 * g + x get ids 8 * (kTiles * g + tile) + x.
   const int64_t bid = blockIdx.x, x = bid & 7, q = bid >> 3;
@@ -317,11 +264,62 @@ __global__ __launch_bounds__(kThreads) void recur32_kernel(RecurArgs a) {
   };
   const int ci_lo = first_at(a.row_lo), ci_hi = first_at(a.row_hi);
   if (nch > 0 ? ci_lo >= ci_hi : a.part != 0) return;
+  const int steps = ci_hi - ci_lo;
   const bool from_caller = ci_lo == 0, to_caller = ci_hi == nch;
   float* const ws_state = reinterpret_cast<float*>(a.ws + a.lay.state);
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, lg = lane >> 4, lc = lane & 15;
+  const int row_bytes = (int)(H * V * 2);
+
+  if (wave >= kWaves) {
+    // ---------------- loader wave ----------------
+    // Chunk c of the launch goes to slot c mod kSlots and belongs to loader
+    // c mod kLoaders, which issues it right after barrier c - kSlots + 2 (the
+    // compute waves are then done with chunk c - kSlots, the slot's previous
+    // contents) and waits for it (vmcnt(0)) just before barrier c.  Its next
+    // chunk, c + kLoaders = c + kSlots - 2, is issued only after that wait, so
+    // a loader never has more than one chunk in flight and each wait covers
+    // exactly that chunk's loads, whatever order loads complete in.
+    static_assert(kLoaders == kSlots - 2, "one chunk in flight per loader");
+    const int j = wave - kWaves;
+    // Source offset of this lane's 16-byte position in each load instruction:
+    // value row r, piece position p holds piece p ^ 2 (r % 4) of the row; rows
+    // past the end of a partial chunk lie past the descriptor's range and read
+    // as zeros (the record gives them zero weight), and so do the record's
+    // padding pieces.
+    int32_t vsrc[Cf::kValBlocks], rsrc[Cf::kRecBlocks];
+#pragma unroll
+    for (int i = 0; i < Cf::kValBlocks; ++i) {
+      const int s = 64 * i + lane, r = s / Cf::kRowPieces, p = s % Cf::kRowPieces;
+      vsrc[i] = r * row_bytes + 16 * (p ^ (2 * (r & 3)));
+    }
+#pragma unroll
+    for (int i = 0; i < Cf::kRecBlocks; ++i) rsrc[i] = rec_source(64 * i + lane);
+    const char* vseq = reinterpret_cast<const char*>(a.v + ((int64_t)se.row0 * H + h) * V + v0);
+    const uint32_t ring0 = lds_addr(ring);
+    const auto issue = [&](int st) {
+      const int c = ci_lo + st;
+      const int len = min(se.len - CC * c, CC);
+      const i32x4 rrec = buf_rsrc(recs + (int64_t)c * REC32_BYTES, REC32_BYTES);
+      const i32x4 rval = buf_rsrc(vseq + (int64_t)c * CC * row_bytes, (len - 1) * row_bytes + 2 * Cf::kCols);
+      const uint32_t slot = ring0 + (uint32_t)((st % kSlots) * Cf::kSlotBytes);
+#pragma unroll
+      for (int i = 0; i < Cf::kValBlocks; ++i) load_lds16(rval, slot + Cf::kVal + 1024 * i, vsrc[i]);
+#pragma unroll
+      for (int i = 0; i < Cf::kRecBlocks; ++i) load_lds16(rrec, slot + Cf::kRec + 1024 * i, rsrc[i]);
+    };
+    for (int c = j; c < min(steps, kSlots - 2); c += kLoaders) issue(c);
+    for (int i = 0; i < steps; ++i) {
+      const bool mine = i % kLoaders == j;
+      if (mine) wait_vmcnt<0>();   // chunk i has landed in its slot
+      barrier();
+      if (mine && i + kSlots - 2 < steps) issue(i + kSlots - 2);
+    }
+    return;
+  }
+
+  // ---------------- compute wave ----------------
   const int64_t sbase = ((int64_t)n * H + h) * V * K;   // state [n][h][v][k]
   const int wc = Cf::kWaveCols * wave;                   // first tile column of this wave
   const int col0 = v0 + wc;                              // first state column of this wave
@@ -345,35 +343,24 @@ __global__ __launch_bounds__(kThreads) void recur32_kernel(RecurArgs a) {
       }
     }
 
-  if (ci_lo < ci_hi) {
-    const int row_bytes = (int)(H * V * 2);
-    LoadPlan<NT, D> pl;
-    make_plan<NT, D>(pl, wave, lane, row_bytes);
-    const int clast = ci_hi - 1;
-    const char* vseq = reinterpret_cast<const char*>(a.v + ((int64_t)se.row0 * H + h) * V + v0);
-    const uint32_t ring0 = (uint32_t)reinterpret_cast<uintptr_t>((lds_void*)ring[0]);
-#pragma unroll
-    for (int c = 0; c < D - 1; ++c)
-      issue_chunk<NT, D>(ring0 + c * Cf::kSlotBytes, pl, recs, vseq, se, ci_lo + c, clast, row_bytes, wave);
-    u32x2 o_prev[2][NT];
-    int slot = 0;   // ring slot of chunk ci
-    for (int ci = ci_lo; ci < ci_hi; ++ci) {
-      // At most the D - 2 chunks issued after chunk ci may still be in flight
-      // (loads complete in issue order); the output stores of the step
-      // before, also counted, have had a whole step to complete.
-      wait_vmcnt<(D - 2) * Cf::kLoads>();
-      wait_lgkm0();
+  if (steps > 0) {
+    // The output of a step is rounded and stored in the next step, well after
+    // the MFMAs that produce it (as in the 16-token kernel: a vector read of an
+    // MFMA result shortly after it, with more MFMAs issued in between, is not
+    // relied on), and a scheduling barrier keeps each step's instructions on
+    // their side of the step barrier.
+    f32x4 o_prev[2][NT];
+    for (int s = 0; s < steps; ++s) {
+      __builtin_amdgcn_sched_barrier(0);
       barrier();
-      const int refill = slot == 0 ? D - 1 : slot - 1;
-      issue_chunk<NT, D>(ring0 + refill * Cf::kSlotBytes, pl, recs, vseq, se, ci + D - 1, clast, row_bytes, wave);
-      if (ci > ci_lo) store_out<NT>(a.out, chunk_rows(se, ci - 1), H, h, col0, lc, lg, o_prev);
       Ops<NT> ops;
-      read_ops<NT, D>(ops, ring[slot], wc, lane);
+      read_ops<NT>(ops, ring + (s % kSlots) * Cf::kSlotBytes, wc, lane);
+      if (s > 0) store_out<NT>(a.out, chunk_rows(se, ci_lo + s - 1), H, h, col0, lc, lg, o_prev);
       compute<NT>(Z, ops, o_prev);
-      slot = slot == D - 1 ? 0 : slot + 1;
+      wait_lgkm0();   // every read of this slot is done before the next barrier
     }
-    wait_vmcnt<0>();   // no load into the ring outlives the workgroup
-    store_out<NT>(a.out, chunk_rows(se, clast), H, h, col0, lc, lg, o_prev);
+    __builtin_amdgcn_sched_barrier(0);
+    store_out<NT>(a.out, chunk_rows(se, ci_hi - 1), H, h, col0, lc, lg, o_prev);
   }
 
   // ---- state out
@@ -388,34 +375,28 @@ __global__ __launch_bounds__(kThreads) void recur32_kernel(RecurArgs a) {
         } else if (a.state_dtype == KDA_DTYPE_FP32) {
           *reinterpret_cast<f32x4*>(static_cast<float*>(a.s_out) + idx) = Z[m][nt];
         } else {
-          u32x2 w;
-          w[0] = pack_bf16(Z[m][nt][0], Z[m][nt][1]);
-          w[1] = pack_bf16(Z[m][nt][2], Z[m][nt][3]);
-          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.s_out) + idx) = w;
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.s_out) + idx) = pack_out(Z[m][nt]);
         }
       }
   }
 }
 
-template <int NT, int D>
+template <int NT>
 hipError_t launch_tiles(const RecurArgs& a, hipStream_t s) {
   const int64_t pairs = a.N * a.H;
-  const int64_t grid = 8 * Cfg<NT, D>::kTiles * ((pairs + 7) / 8);
-  hipLaunchKernelGGL((recur32_kernel<NT, D>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  const int64_t grid = 8 * Cfg<NT>::kTiles * ((pairs + 7) / 8);
+  if (grid > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((recur32_kernel<NT>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-// 64 value columns per workgroup, as for the 16-token kernel (see
-// launch_recur); a 3-chunk ring of 36 KB slots (108 KB).
-#ifndef KDA_RECUR32_DEPTH
-#define KDA_RECUR32_DEPTH 3
-#endif
-
+// 64 value columns per workgroup (two workgroups per (sequence, head)); a
+// 4-slot ring of 33 KB slots (132 KB).
 hipError_t launch_recur32(const RecurArgs& a, hipStream_t s) {
   if (a.N * a.H == 0) return hipSuccess;
-  return launch_tiles<1, KDA_RECUR32_DEPTH>(a, s);
+  return launch_tiles<1>(a, s);
 }
 
 }  // namespace kda

@@ -220,10 +220,6 @@ __device__ __forceinline__ void compute(f32x4 (&Z)[8][NT], const Ops<NT>& o, f32
   for (int nt = 0; nt < NT; ++nt) out[nt] = O[nt];
 }
 
-// The output tile of a step, rounded to bf16 (nearest even) and packed for one
-// 8-byte store per 16 columns.
-__device__ __forceinline__ u32x2 pack_out(f32x4 o) { return u32x2{pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3])}; }
-
 // State slice of a wave: Z[m][nt] holds rows 16m + 4lg + i, column
 // col0 + 16nt + lc of the state of one (sequence, head), read from `s_in`
 // ([V][K] of that pair, bf16 or fp32; nullptr = zero state).

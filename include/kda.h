@@ -22,7 +22,8 @@
  * reading, chosen because it maps any raw gate into (lower_bound, 0).)
  *
  * All tensor pointers are DEVICE pointers to contiguous row-major buffers on
- * the current HIP device; q, k, g, v, out and the states must be 16-byte aligned.  The caller owns every buffer, including the
+ * the current HIP device; q, k, g, v, out, dt_bias and the states must be
+ * 16-byte aligned.  The caller owns every buffer, including the
  * workspace; the library never allocates or frees device memory.  kda_fwd only
  * enqueues work on `stream` (no host synchronisation, no device reads on the
  * host); buffers must stay alive until the stream has passed the call.  It
@@ -78,7 +79,8 @@ extern "C" {
 /* Device-side status word values (kda_fwd_check_status). */
 #define KDA_STATUS_OK 0
 #define KDA_STATUS_BAD_CU_SEQLENS 1 /* cu_seqlens[0] != 0, not monotone, or cu_seqlens[N] != T;
-                                       then no token was processed and out is not written */
+                                       then no token was processed and neither out nor
+                                       final_state is written, on every path */
 
 /* Chunk size of the chunked form (P1 §二 2.1 uses 16). */
 #define KDA_CHUNK 16

@@ -96,6 +96,7 @@ def call(**over):
     (dict(ws=ctypes.c_void_p(0x100010)), kda.KDA_EINVAL),     # misaligned workspace
     (dict(q=ctypes.c_void_p(0x1002)), kda.KDA_EINVAL),        # misaligned tensor
     (dict(out=ctypes.c_void_p(0x1008)), kda.KDA_EINVAL),
+    (dict(dt_bias=ctypes.c_void_p(0x1004)), kda.KDA_EINVAL),  # dt_bias is read in 16-byte vectors
     (dict(K=64), kda.KDA_EINVAL),
     (dict(V=256), kda.KDA_EINVAL),
     (dict(B=0), kda.KDA_EINVAL),

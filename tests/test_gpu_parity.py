@@ -241,22 +241,28 @@ def test_zero_tokens_passes_state_through():
     assert torch.equal(fin.cpu().view(torch.int16), torch.from_numpy(inp.initial_state.view(np.int16)))
 
 
-def test_bad_cu_seqlens_sets_status_and_touches_nothing():
+@pytest.mark.parametrize("path,chunk,parts", [("auto", None, None), ("split", 16, None), ("fused", 16, None),
+                                               ("split", 32, None), ("split", 16, 3), ("split", 32, 2)])
+def test_bad_cu_seqlens_sets_status_and_touches_nothing(path, chunk, parts):
+    """A rejected cu_seqlens leaves out and final_state exactly as they were
+    (both filled with a sentinel first), on every path."""
     from gated_delta_rule_prep_amd import kda
     inp = make_inputs(1, 64, 2, seed=206, state_dtype="fp32", seq_lens=[30, 34])
     d = device_inputs(inp)
     for bad in ([0, 40, 30], [1, 30, 64], [0, 30, 63]):
-        say("case bad cu_seqlens %s" % bad)
+        say("case bad cu_seqlens %s path %s chunk %s parts %s" % (bad, path, chunk, parts))
         cu = torch.tensor(bad, dtype=torch.int64, device="cuda")
-        out = torch.zeros(1, 64, 2, 128, dtype=torch.bfloat16, device="cuda")
-        fin = torch.zeros(2, 2, 128, 128, dtype=torch.float32, device="cuda")
-        ws = kda.alloc_workspace(1, 64, 2, 2, True, "cuda")
+        out = torch.full((1, 64, 2, 128), 3.0, dtype=torch.bfloat16, device="cuda")
+        fin = torch.full((2, 2, 128, 128), 7.0, dtype=torch.float32, device="cuda")
+        ws = kda.alloc_workspace(1, 64, 2, 2, True, "cuda", chunk=chunk, parts=parts, path=path)
         kda.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], inp.scale, out, d["A_log"], d["dt_bias"],
-                inp.lower_bound, initial_state=d["initial_state"], final_state=fin, cu_seqlens=cu, workspace=ws)
+                inp.lower_bound, initial_state=d["initial_state"], final_state=fin, cu_seqlens=cu, workspace=ws,
+                chunk=chunk, parts=parts, path=path)
         assert kda.check_status(ws) == kda.KDA_STATUS_BAD_CU_SEQLENS
-        assert torch.count_nonzero(out.view(torch.int16)) == 0
-    ws = kda.alloc_workspace(1, 64, 2, 2, True, "cuda")
-    run_gpu(inp, d=d, workspace=ws)
+        assert bool((out == 3.0).all()), "out was written"
+        assert bool((fin == 7.0).all()), "final_state was written"
+    ws = kda.alloc_workspace(1, 64, 2, 2, True, "cuda", chunk=chunk, parts=parts, path=path)
+    run_gpu(inp, d=d, workspace=ws, chunk=chunk, parts=parts, path=path)
     assert kda.check_status(ws) == kda.KDA_STATUS_OK
 
 
