@@ -99,9 +99,14 @@ struct SchedArgs {
   Layout lay;
 };
 
+constexpr int kCUs = 256;   // compute units of an MI355X
+
 // Fused-kernel value-column tiling: 64 columns per workgroup (two per
 // (sequence, head)) while two tiles per pair fit on the CUs at once, else 128.
-inline __host__ __device__ bool fused_two_tiles(int64_t pairs) { return 2 * pairs <= 512; }
+// (A workgroup takes most of a CU's LDS, so workgroups beyond the CU count
+// wait for a second round: 2 x 4096 tokens, H = 96, 0.866 ms with 384
+// workgroups of 64 columns against 0.513 with 192 of 128.)
+inline __host__ __device__ bool fused_two_tiles(int64_t pairs) { return 2 * pairs <= kCUs; }
 
 // The recurrence's value tiles per (sequence, head) for `pairs` chains (the
 // sequence-head pairs of the launch): 4 while that still gives one workgroup
@@ -109,36 +114,52 @@ inline __host__ __device__ bool fused_two_tiles(int64_t pairs) { return 2 * pair
 // two tiles per pair would not fit on the CUs at once (then throughput, not
 // the longest chain, bounds the launch).
 __host__ __device__ inline int recur_tiles(int64_t pairs, bool equal_lengths) {
-  if (4 * pairs <= 256) return 4;
-  if (2 * pairs <= 256 || !equal_lengths) return 2;
+  if (4 * pairs <= kCUs) return 4;
+  if (2 * pairs <= kCUs || !equal_lengths) return 2;
   return 1;
 }
 
 // The library's path choice: estimated time (us) of each path on MI355X for H
 // heads, `total` chunks over all sequences, the longest sequence's `maxc`
 // chunks and N sequences (the scheduler kernel evaluates it for cu_seqlens;
-// for B sequences of T tokens the host does).  The constants are measured on
-// the box at K = V = 128 (T = 8192, H = 64 and 96, fixed length, 8 x 1024 and
-// 12 ragged sequences):
-//   split: the prep kernel streams inputs and records at about 5.0 ns per
-//     (chunk, head); a recurrence workgroup step takes about 0.41 us with
-//     32-column tiles and 0.58 us with 64-column ones (recur_tiles), and the
-//     recurrence is either the longest chain or, with many pairs, throughput
-//     (one workgroup per CU at a time, 256 CUs);
-//   fused: one 16-token step of a workgroup takes about 1.8 us (two 64-column
-//     tiles per pair) or 2.15 us (one 128-column tile), each sequence takes
-//     five pipeline steps more than its chunk count, and the work spreads
-//     over 256 CUs, one workgroup per CU.
-__host__ __device__ inline int choose_path(int64_t H, int64_t N, int64_t total, int64_t maxc, bool equal_lengths) {
-  const double chunk_heads = (double)total * (double)H;
+// for B sequences of T tokens the host does).  The constants are a least-
+// squares fit to kernel times measured on the box at K = V = 128 over 36
+// batches of 8192 tokens (1 .. 128 sequences of 64 .. 8192 tokens, and 12
+// ragged ones; H = 16, 32, 64, 96), with which the choice matches the faster
+// path in all of them but one tie:
+//   split: the prep kernel streams inputs and records at about 5.7 ns per
+//     (chunk, head).  A recurrence workgroup costs about 15.6 us to start and
+//     end (tables, state, the first chunk's latency) plus 0.35 / 0.51 / 1.0 us
+//     per step with 32 / 64 / 128 columns; the recurrence is the longest chain
+//     or, with more workgroups than CUs, throughput: two 64-column workgroups
+//     share a CU, at 3.5 us of start per workgroup and 0.66 us per step and
+//     tile of CU time;
+//   fused: a workgroup step takes 1.71 us (64 columns, two workgroups per
+//     pair) or 2.08 us (128 columns), each sequence takes five pipeline steps
+//     more than its chunk count plus 3.3 us, and the work spreads over the
+//     CUs, one workgroup per CU.
+__host__ __device__ inline double recur_estimate(int64_t H, int64_t N, int64_t total, int64_t maxc,
+                                                 bool equal_lengths) {
+  const double chunk_heads = (double)total * (double)H, pairs = (double)N * (double)H;
   const int tiles = recur_tiles(N * H, equal_lengths);
-  const double rstep = tiles == 4 ? 0.41 : tiles == 2 ? 0.58 : 1.24;
-  const double split = 5.0e-3 * chunk_heads + fmax(rstep * (double)maxc, rstep * tiles * chunk_heads / 256.0);
+  const double step = tiles == 4 ? 0.35 : tiles == 2 ? 0.51 : 1.0;
+  const double chain = 15.6 + step * (double)maxc;
+  if (tiles * pairs <= kCUs) return chain;
+  if (tiles == 2) return fmax(chain, 2.0 * (3.5 * pairs + 0.66 * chunk_heads) / kCUs);
+  return fmax(chain, (15.6 * pairs + step * chunk_heads) / kCUs);
+}
+
+__host__ __device__ inline double fused_estimate(int64_t H, int64_t N, int64_t total, int64_t maxc) {
+  const double chunk_heads = (double)total * (double)H, pairs = (double)N * (double)H;
   const bool two = fused_two_tiles(N * H);
-  const double step = two ? 1.8 : 2.15;
-  const double wg_steps = ((double)total + 5.0 * (double)N) * (double)H * (two ? 2.0 : 1.0);
-  const double fused = fmax(step * (double)(maxc + 5), step * wg_steps / 256.0);
-  return fused < split ? KDA_PATH_FUSED : KDA_PATH_SPLIT;
+  const double step = two ? 1.71 : 2.08;
+  const double chain = 3.3 + step * (double)(maxc + 5);
+  return fmax(chain, (two ? 2.0 : 1.0) * (3.3 * pairs + step * (chunk_heads + 5.0 * pairs)) / kCUs);
+}
+
+__host__ __device__ inline int choose_path(int64_t H, int64_t N, int64_t total, int64_t maxc, bool equal_lengths) {
+  const double split = 5.7e-3 * (double)total * (double)H + recur_estimate(H, N, total, maxc, equal_lengths);
+  return fused_estimate(H, N, total, maxc) < split ? KDA_PATH_FUSED : KDA_PATH_SPLIT;
 }
 
 

@@ -80,13 +80,10 @@ static_assert(REC_NK == REC_QH + C * 2 * K && REC_KB == REC_NK + C * 2 * K && RE
 static_assert(REC_MQK == REC_T + 512 && REC_GAM == REC_MQK + 512 && REC_BYTES == REC_GAM + 512,
               "T^T, Mqk^T and gamma end the record");
 
-// WC compute waves of 16 value columns each.
-template <int WC>
+// WC compute waves of 16 value columns each, LD loader waves.
+template <int WC, int LD>
 struct Tile {
-  // loader waves: six for 32-column tiles, whose shorter steps need the loads
-  // issued further ahead (T = 8192, H = 64: 0.210 against 0.227 ms with
-  // four), four otherwise (H = 96, 64 columns: 0.302 against 0.308 with six)
-  static constexpr int kLoaders = WC == 2 ? 6 : 4;
+  static constexpr int kLoaders = LD;
   static constexpr int kSlots = kLoaders + 2;            // the loads of a chunk are issued kSlots - 2 steps ahead
   static constexpr int kThreads = 64 * (WC + kLoaders);
   static constexpr int kCols = 16 * WC;                   // value columns per workgroup
@@ -143,9 +140,9 @@ __device__ __forceinline__ void read_slot(Ops<1>& o, const char* rec, const char
   o.g2 = *reinterpret_cast<const f32x2*>(rec + kSlotTail + 4 * C * C + 8 * lane);
 }
 
-template <int WC, int PV>
-__global__ __launch_bounds__(Tile<WC>::kThreads) void recur_kernel(RecurArgs a) {
-  using Tl = Tile<WC>;
+template <int WC, int LD, int PV>
+__global__ __launch_bounds__((Tile<WC, LD>::kThreads)) void recur_kernel(RecurArgs a) {
+  using Tl = Tile<WC, LD>;
   __shared__ __align__(1024) char ring[Tl::kSlots * Tl::kSlotBytes];
   const int64_t H = a.H;
   const WsHeader* hdr = reinterpret_cast<const WsHeader*>(a.ws);
@@ -332,12 +329,12 @@ __global__ __launch_bounds__(Tile<WC>::kThreads) void recur_kernel(RecurArgs a) 
   }
 }
 
-template <int WC, int PV>
+template <int WC, int LD, int PV>
 hipError_t launch_tiles(const RecurArgs& a, int64_t pairs, hipStream_t s) {
-  using Tl = Tile<WC>;
+  using Tl = Tile<WC, LD>;
   const int64_t grid = 8 * Tl::kTiles * ((pairs + 7) / 8);
   if (grid > INT32_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((recur_kernel<WC, PV>), dim3((unsigned)grid), dim3(Tl::kThreads), 0, s, a);
+  hipLaunchKernelGGL((recur_kernel<WC, LD, PV>), dim3((unsigned)grid), dim3(Tl::kThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -345,7 +342,7 @@ hipError_t launch_tiles(const RecurArgs& a, int64_t pairs, hipStream_t s) {
 template <int PV>
 hipError_t launch_variant(const RecurArgs& a, int64_t pairs, hipStream_t s) {
   if constexpr (PV < 8) {
-    if (a.precision == PV) return launch_tiles<4, PV>(a, pairs, s);
+    if (a.precision == PV) return launch_tiles<4, 4, PV>(a, pairs, s);
     return launch_variant<PV + 1>(a, pairs, s);
   }
   return hipErrorInvalidValue;
@@ -353,21 +350,37 @@ hipError_t launch_variant(const RecurArgs& a, int64_t pairs, hipStream_t s) {
 
 }  // namespace
 
-// recur_tiles (kda_internal.h), measured on MI355X (recurrence kernel alone,
-// ms): T = 8192 H = 64 fixed: 0.210 with 4 tiles, 0.266 with 2; T = 8192
-// H = 96 fixed: 0.302 with 2 tiles, 0.395 with 4 (384 workgroups > 256 CUs),
-// 0.402 with 1; 12 ragged sequences, H = 96 (one of ~6000 tokens): 0.297 with
-// 2, 0.396 with 1; 8 x 1024, H = 96: 0.239 with 1, 0.278 with 2.
+// Tiles per pair (recur_tiles, kda_internal.h), measured on MI355X
+// (recurrence kernel alone, ms): T = 8192 H = 64 fixed: 0.210 with 4 tiles,
+// 0.266 with 2; T = 8192 H = 96 fixed: 0.302 with 2 tiles, 0.395 with 4 (384
+// workgroups > 256 CUs), 0.402 with 1; 12 ragged sequences, H = 96 (one of
+// ~6000 tokens): 0.297 with 2, 0.396 with 1; 8 x 1024, H = 96: 0.239 with 1,
+// 0.278 with 2.
+//
+// Loader waves and ring depth: while the launch has no more workgroups than
+// the chip has CUs, each workgroup gets a CU to itself and a deep ring (six
+// loaders and 8 slots for 32-column tiles, whose shorter steps need the loads
+// issued further ahead: T = 8192, H = 64, 0.210 against 0.227 ms with four;
+// four loaders and 6 slots otherwise: H = 96, 64 columns, 0.302 against 0.308
+// with six).  With more workgroups than CUs, two loaders and 4 slots (68 / 74
+// KB of LDS) let two workgroups share a CU, so that one's start (tables,
+// state, the first chunk's latency: about 6 us) and end overlap the other's
+// steps: 64 sequences of 128 tokens, H = 96, 0.479 -> 0.411 ms; 128 x 64,
+// 0.768 -> 0.595; 8 x 1024, 0.276 -> 0.269.  With few workgroups the shallow
+// ring is slower (T = 8192, H = 64: 0.210 -> 0.241), as two workgroups then
+// share a CU while others idle.
 hipError_t launch_recur(const RecurArgs& a, hipStream_t s) {
   if (a.lay.chunk == C32) return a.sets == 2 || a.precision != 0 ? hipErrorInvalidValue : launch_recur32(a, s);
   const int64_t pairs = a.N * a.H * (a.sets == 2 ? 2 : 1);
   if (pairs == 0) return hipSuccess;
   if (a.precision < 0 || a.precision > 7) return hipErrorInvalidValue;
   if (a.precision != 0) return launch_variant<1>(a, pairs, s);
-  switch (a.tiles > 0 ? a.tiles : recur_tiles(pairs, false)) {
-    case 4: return launch_tiles<2, 0>(a, pairs, s);
-    case 2: return launch_tiles<4, 0>(a, pairs, s);
-    case 1: return launch_tiles<8, 0>(a, pairs, s);
+  const int tiles = a.tiles > 0 ? a.tiles : recur_tiles(pairs, false);
+  const bool shared = tiles * pairs > kCUs;   // more workgroups than CUs
+  switch (tiles) {
+    case 4: return launch_tiles<2, 6, 0>(a, pairs, s);   // (4 tiles only while 4 * pairs <= 256)
+    case 2: return shared ? launch_tiles<4, 2, 0>(a, pairs, s) : launch_tiles<4, 4, 0>(a, pairs, s);
+    case 1: return launch_tiles<8, 4, 0>(a, pairs, s);
     default: return hipErrorInvalidValue;
   }
 }
