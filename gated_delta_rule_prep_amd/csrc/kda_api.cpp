@@ -558,6 +558,74 @@ int kda_fwd_ex(const void* q, const void* k, const void* v, const void* g, const
                   workspace, workspace_bytes, stream, chunk, parts, path, events, num_events, nullptr);
 }
 
+}  // extern "C"
+
+// ---- the fused path without a caller workspace ------------------------------
+
+namespace {
+
+// The fused path's workspace is only the header and the per-sequence tables
+// (layout_fused): for up to kNoAllocMaxSeqs sequences it fits in this array,
+// one copy per GPU, held until the process ends.  Host code never uses the
+// name `scratch` as an address (on the host it is a stand-in, not the device
+// copy): g_scratch[dev] holds the device address hipGetSymbolAddress gives
+// for device dev.
+constexpr int64_t kNoAllocMaxSeqs = 16384;
+constexpr size_t kScratchBytes = 256 + 16 * kNoAllocMaxSeqs + 4 * kNoAllocMaxSeqs;   // 320 KiB + 256 B
+static_assert(sizeof(kda::WsHeader) == 256 && sizeof(kda::SeqEntry) == 16, "scratch sizing");
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+char* g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of this device's scratch array (looked up once per device,
+// with the device current).
+int scratch_ptr(int dev, char** out) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(KDA_EHIP, "kda: hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch[dev] = static_cast<char*>(p);
+  }
+  *out = g_scratch[dev];
+  return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_fwd_fused_noalloc(const void* q, const void* k, const void* v, const void* g, const void* beta, float scale,
+                          void* out, const float* A_log, const float* dt_bias, float lower_bound,
+                          const void* initial_state, int initial_state_dtype, void* final_state,
+                          int final_state_dtype, const int64_t* cu_seqlens, int64_t num_seqs, int64_t B, int64_t T,
+                          int64_t H, int64_t K, int64_t V, hipStream_t stream) {
+  try {
+    int64_t N = 0;
+    int rc = check_sizes(B, T, H, K, V, cu_seqlens, num_seqs, 0, &N);
+    if (rc != KDA_OK) return rc;
+    if (N > kNoAllocMaxSeqs)
+      return fail(KDA_EINVAL, "kda: kda_fwd_fused_noalloc takes at most %lld sequences (got %lld)",
+                  (long long)kNoAllocMaxSeqs, (long long)N);
+    kda::Layout L;
+    if (!kda::layout_fused(B, T, H, N, &L) || L.total > (int64_t)kScratchBytes)
+      return fail(KDA_EINVAL, "kda: sizes do not fit the static scratch");
+    int dev = 0;
+    rc = check_device(&dev);
+    if (rc != KDA_OK) return rc;
+    char* ws = nullptr;
+    rc = scratch_ptr(dev, &ws);
+    if (rc != KDA_OK) return rc;
+    return fwd_impl(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state, initial_state_dtype,
+                    final_state, final_state_dtype, cu_seqlens, num_seqs, B, T, H, K, V, ws, kScratchBytes, stream,
+                    kda::C, 0, KDA_PATH_FUSED, nullptr, 0, nullptr);
+  } catch (...) {
+    return fail(KDA_EHIP, "kda: unexpected C++ exception");
+  }
+}
+
 int kda_fwd_num_events(int64_t B, int64_t T, int chunk, int parts, int path) {
   const int p = resolve_path(chunk, parts, path);
   if (p < 0 || B < 0 || T < 0) return 0;

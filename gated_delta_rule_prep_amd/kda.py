@@ -33,7 +33,8 @@ EXPORTS = ("kda_fwd", "kda_fwd_profiled", "kda_fwd_ex", "kda_fwd_parts", "kda_fw
            "kda_fwd_num_events", "kda_fwd_segmented", "kda_fwd_segmented_workspace_bytes",
            "kda_fwd_segments", "kda_fwd_precision",
            "kda_decode", "kda_fwd_workspace_bytes", "kda_fwd_workspace_bytes_ex", "kda_get_last_error",
-           "kda_version", "kda_fwd_check_status", "kda_workspace_layout", "kda_debug_prep")
+           "kda_version", "kda_fwd_check_status", "kda_workspace_layout", "kda_debug_prep",
+           "kda_fwd_fused_noalloc")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError("libkda.so is not built (run gated_delta_rule_prep_amd/build.py or "
@@ -85,6 +86,8 @@ _lib.kda_workspace_layout.restype = ctypes.c_int
 _lib.kda_debug_prep.argtypes = [_p, _p, _p, _p, ctypes.c_float, _p, _p, ctypes.c_float, _p, _i64, _i64,
                                 _i64, _i64, _i64, _p, ctypes.c_size_t, _p, ctypes.c_int]
 _lib.kda_debug_prep.restype = ctypes.c_int
+_lib.kda_fwd_fused_noalloc.argtypes = _lib.kda_fwd.argtypes[:21] + [_p]
+_lib.kda_fwd_fused_noalloc.restype = ctypes.c_int
 
 
 class KDAError(RuntimeError):
@@ -221,26 +224,9 @@ def parts(B: int, T: int, requested: int = 0) -> int:
     return _lib.kda_fwd_parts(B, T, requested)
 
 
-def fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state=None, final_state=None,
-        cu_seqlens=None, workspace: Optional[torch.Tensor] = None, events=None, parts: Optional[int] = None,
-        chunk: Optional[int] = None, path=None, segments: Optional[int] = None, precision: Optional[int] = None):
-    """Chunked KDA forward into the caller's ``out`` (and ``final_state``).
-
-    Shapes and dtypes as in include/kda.h.  Runs on the current stream of the
-    tensors' device.  Returns ``out``.  ``path``: None / 'auto' for the
-    library's choice, 'split' or 'fused' (kda_fwd_ex).  ``chunk``: None for
-    the library's choice, or 16 / 32 tokens per chunk (32: split path only).
-    ``parts``: None for one, or the number of overlapped ranges (split path).
-    ``events``: optional torch.cuda.Event list (enable_timing=True): with no
-    chunk / parts / path, four go through kda_fwd_profiled; otherwise
-    ``num_events(B, T, chunk, parts, path)`` go through kda_fwd_ex, which
-    records them around every kernel.  ``segments``: cut every sequence into
-    that many pieces run side by side (kda_fwd_segmented; 0 or 'auto' for the
-    library's choice); it takes none of events / parts / chunk / path.
-    ``precision``: a KDA_PREC_* combination for the precision study entry
-    point kda_fwd_precision (split path, 16-token chunks); it takes none of
-    events / parts / chunk / path / segments.
-    """
+def _fwd_shapes(q, k, v, g, beta, out, A_log, dt_bias, initial_state, final_state, cu_seqlens):
+    """Shape, dtype and device checks of the forward entry points; returns
+    (B, T, H, K, V, N, device)."""
     if q.dim() != 4:
         raise KDAValueError(KDA_EINVAL, "q must be [B, T, H, K]")
     B, T, H, K = q.shape
@@ -271,6 +257,31 @@ def fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state
             raise KDAValueError(KDA_EINVAL, "all tensors must be on %s" % dev)
     if dev.type != "cuda":
         raise KDAValueError(KDA_EINVAL, "tensors must be on a HIP device, got %s" % dev)
+    return B, T, H, K, V, N, dev
+
+
+def fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state=None, final_state=None,
+        cu_seqlens=None, workspace: Optional[torch.Tensor] = None, events=None, parts: Optional[int] = None,
+        chunk: Optional[int] = None, path=None, segments: Optional[int] = None, precision: Optional[int] = None):
+    """Chunked KDA forward into the caller's ``out`` (and ``final_state``).
+
+    Shapes and dtypes as in include/kda.h.  Runs on the current stream of the
+    tensors' device.  Returns ``out``.  ``path``: None / 'auto' for the
+    library's choice, 'split' or 'fused' (kda_fwd_ex).  ``chunk``: None for
+    the library's choice, or 16 / 32 tokens per chunk (32: split path only).
+    ``parts``: None for one, or the number of overlapped ranges (split path).
+    ``events``: optional torch.cuda.Event list (enable_timing=True): with no
+    chunk / parts / path, four go through kda_fwd_profiled; otherwise
+    ``num_events(B, T, chunk, parts, path)`` go through kda_fwd_ex, which
+    records them around every kernel.  ``segments``: cut every sequence into
+    that many pieces run side by side (kda_fwd_segmented; 0 or 'auto' for the
+    library's choice); it takes none of events / parts / chunk / path.
+    ``precision``: a KDA_PREC_* combination for the precision study entry
+    point kda_fwd_precision (split path, 16-token chunks); it takes none of
+    events / parts / chunk / path / segments.
+    """
+    B, T, H, K, V, N, dev = _fwd_shapes(q, k, v, g, beta, out, A_log, dt_bias, initial_state, final_state,
+                                        cu_seqlens)
     path_c = _path_code(path)
     if segments == "auto":
         segments = 0
@@ -309,6 +320,25 @@ def fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state
             n = 0 if events is None else len(events)
             ev = None if events is None else (ctypes.c_void_p * n)(*[e.cuda_event for e in events])
             rc = _lib.kda_fwd_ex(*args, _stream(dev), int(chunk or 0), int(parts or 0), path_c, ev, n)
+    if rc != KDA_OK:
+        _raise(rc)
+    return out
+
+
+def fwd_fused_noalloc(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state=None,
+                      final_state=None, cu_seqlens=None):
+    """kda_fwd_fused_noalloc: the fused path with the library's static
+    per-GPU scratch instead of a workspace (at most 16384 sequences; calls
+    that overlap on one GPU race).  Same arguments and results as ``fwd(...,
+    path='fused')``.  Returns ``out``."""
+    B, T, H, K, V, N, dev = _fwd_shapes(q, k, v, g, beta, out, A_log, dt_bias, initial_state, final_state,
+                                        cu_seqlens)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(out),
+            _ptr(A_log), _ptr(dt_bias), float(lower_bound), _ptr(initial_state),
+            _state_code(initial_state), _ptr(final_state), _state_code(final_state),
+            _ptr(cu_seqlens), N, B, T, H, K, V)
+    with torch.cuda.device(dev):
+        rc = _lib.kda_fwd_fused_noalloc(*args, _stream(dev))
     if rc != KDA_OK:
         _raise(rc)
     return out

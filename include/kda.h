@@ -244,6 +244,28 @@ int kda_fwd_precision(const void* q, const void* k, const void* v, const void* g
                       const int64_t* cu_seqlens, int64_t num_seqs, int64_t B, int64_t T, int64_t H, int64_t K,
                       int64_t V, void* workspace, size_t workspace_bytes, hipStream_t stream, int variant);
 
+/*
+ * kda_fwd_fused_noalloc -- for callers that cannot allocate device memory or
+ * pass a workspace (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): kda_fwd_ex on the fused path (16-token
+ * chunks, one part) with the workspace taken from a static device array of
+ * the library, 320 KiB + 256 B per GPU, held until the process ends.  At most
+ * 16384 sequences (num_seqs with cu_seqlens, else B); more returns
+ * KDA_EINVAL before any HIP call.  Arguments, checks and results otherwise as
+ * kda_fwd_ex(path = KDA_PATH_FUSED): bit for bit the same outputs.  The call
+ * allocates nothing and frees nothing; the first call on a device looks up
+ * that device's copy of the array (hipGetSymbolAddress).
+ * All calls on one GPU share its array, which keeps the last call's tables:
+ * calls that overlap on one GPU (other streams, other threads) race and give
+ * undefined results; serialise them.  A rejected cu_seqlens leaves out and
+ * final_state untouched; its status word is not readable by the caller.
+ */
+int kda_fwd_fused_noalloc(const void* q, const void* k, const void* v, const void* g, const void* beta, float scale,
+                          void* out, const float* A_log, const float* dt_bias, float lower_bound,
+                          const void* initial_state, int initial_state_dtype, void* final_state,
+                          int final_state_dtype, const int64_t* cu_seqlens, int64_t num_seqs, int64_t B, int64_t T,
+                          int64_t H, int64_t K, int64_t V, hipStream_t stream);
+
 /* Number of parts kda_fwd_ex uses for these sizes and `parts` request (0 on bad input). */
 int kda_fwd_parts(int64_t B, int64_t T, int parts);
 
