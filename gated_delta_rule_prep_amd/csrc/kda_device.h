@@ -60,6 +60,21 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 // store.
 __device__ __forceinline__ u32x2 pack_out(f32x4 o) { return u32x2{pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3])}; }
 
+// Sets `bit` in the status word at `status` (global memory) when any lane of
+// the wave holds a non-finite value among its M x NT x 4 state values: one
+// vector atomic, by the wave's first lane, and only then.
+template <int M, int NT>
+__device__ __forceinline__ void flag_nonfinite(const f32x4 (&Z)[M][NT], int32_t* status, int bit) {
+  bool bad = false;
+#pragma unroll
+  for (int m = 0; m < M; ++m)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) bad |= !__builtin_isfinite(Z[m][nt][i]);
+  if (__builtin_amdgcn_ballot_w64(bad) != 0 && (threadIdx.x & 63) == 0) atomicOr(status, bit);
+}
+
 __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
   typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
   const f16x2 v = {(_Float16)lo, (_Float16)hi};

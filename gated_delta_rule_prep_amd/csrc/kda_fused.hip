@@ -362,7 +362,7 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
   const WsHeader* hdr = reinterpret_cast<const WsHeader*>(a.ws);
   // Nothing is touched (no output, no state) unless the scheduler accepted
   // cu_seqlens; the split kernels run instead when the scheduler chose them.
-  if (hdr->status != KDA_STATUS_OK || hdr->path == KDA_PATH_SPLIT) return;
+  if ((hdr->status & KDA_STATUS_BAD_CU_SEQLENS) || hdr->path == KDA_PATH_SPLIT) return;
   const int64_t slot_id = pair / H;
   const int h = (int)(pair - slot_id * H);
   const int v0 = tile * F::kCols;
@@ -515,7 +515,12 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
     }
   }
 
-  if (rec_wave && a.s_out != nullptr) store_state<NT>(Z, a.s_out, a.state_dtype, sbase, col0, lc, lg);
+  if (rec_wave) {
+    if (a.s_out != nullptr) store_state<NT>(Z, a.s_out, a.state_dtype, sbase, col0, lc, lg);
+    // an operand beyond the fp16 range (or a non-finite input) leaves the
+    // state non-finite: reported in the status word
+    flag_nonfinite<8, NT>(Z, const_cast<int32_t*>(&hdr->status), KDA_STATUS_OVERFLOW);
+  }
 }
 
 template <int NT, int D>

@@ -51,7 +51,7 @@ constexpr int kMaxParts = 8;
 
 // Workspace header (first 256 bytes).
 struct WsHeader {
-  int32_t status;                   // KDA_STATUS_*
+  int32_t status;                   // KDA_STATUS_OK or an OR of KDA_STATUS_* bits
   int32_t chunk_count;              // number of valid chunk-table entries
   int32_t part_first[kMaxParts + 1];  // chunk-table index of the first chunk of each part; [parts] = count
   int32_t path;                     // KDA_PATH_SPLIT or KDA_PATH_FUSED: the kernels of the other path exit

@@ -148,7 +148,7 @@ __global__ __launch_bounds__((Tile<WC, LD>::kThreads)) void recur_kernel(RecurAr
   const WsHeader* hdr = reinterpret_cast<const WsHeader*>(a.ws);
   // Nothing is touched (no output, no state) unless the scheduler accepted
   // cu_seqlens; the fused kernel runs instead when the scheduler chose it.
-  if (hdr->status != KDA_STATUS_OK || hdr->path == KDA_PATH_FUSED) return;
+  if ((hdr->status & KDA_STATUS_BAD_CU_SEQLENS) || hdr->path == KDA_PATH_FUSED) return;
   // XCD-aware placement: id b runs on XCD b % 8; the kTiles tiles of pair
   // 8 * g + x get ids 8 * (kTiles * g + tile) + x.
   const int64_t bid = blockIdx.x, x = bid & 7, q = bid >> 3;
@@ -327,6 +327,9 @@ __global__ __launch_bounds__((Tile<WC, LD>::kThreads)) void recur_kernel(RecurAr
       }
     }
   }
+  // an operand beyond the fp16 range (or a non-finite input) leaves the state
+  // non-finite: reported in the status word
+  flag_nonfinite<8, 1>(Z, const_cast<int32_t*>(&hdr->status), KDA_STATUS_OVERFLOW);
 }
 
 template <int WC, int LD, int PV>

@@ -241,7 +241,7 @@ __global__ __launch_bounds__(kThreads) void recur32_kernel(RecurArgs a) {
   const int64_t H = a.H;
   // Nothing is touched (no output, no state) unless the scheduler accepted
   // cu_seqlens.
-  if (reinterpret_cast<const WsHeader*>(a.ws)->status != KDA_STATUS_OK) return;
+  if (reinterpret_cast<const WsHeader*>(a.ws)->status & KDA_STATUS_BAD_CU_SEQLENS) return;
   // XCD-aware placement: id b runs on XCD b % 8; the kTiles tiles of pair
   // 8 * g + x get ids 8 * (kTiles * g + tile) + x.
   const int64_t bid = blockIdx.x, x = bid & 7, q = bid >> 3;
@@ -379,6 +379,9 @@ __global__ __launch_bounds__(kThreads) void recur32_kernel(RecurArgs a) {
         }
       }
   }
+  // an operand beyond the fp16 range (or a non-finite input) leaves the state
+  // non-finite: reported in the status word
+  flag_nonfinite<8, NT>(Z, &reinterpret_cast<WsHeader*>(a.ws)->status, KDA_STATUS_OVERFLOW);
 }
 
 template <int NT>

@@ -92,7 +92,7 @@ __global__ __launch_bounds__(64 * kPrefixWaves) void prefix_kernel(PrefixArgs a)
   const int64_t nh = 8 * (q / 8) + x;
   const int v0 = 16 * (int)(q % 8);
   if (nh >= a.N * a.H) return;
-  if (a.hdr->status != KDA_STATUS_OK) return;   // bad cu_seqlens: leave the states alone
+  if (a.hdr->status & KDA_STATUS_BAD_CU_SEQLENS) return;   // bad cu_seqlens: leave the states alone
   const int64_t n = nh / a.H, h = nh - n * a.H;
   const int tid = threadIdx.x, lane = tid & 63, r = lane & 15, g = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);

@@ -46,7 +46,9 @@
  * Numerical range: the chunk recurrence multiplies fp16 operands with fp32
  * accumulation.  Values derived from v and the state (the state itself, the
  * per-chunk residuals) must stay below 65504 in magnitude; inputs drawn from
- * activations of O(1..1000) scale satisfy this with a wide margin.
+ * activations of O(1..1000) scale satisfy this with a wide margin.  Beyond
+ * it an operand becomes infinite, the state of that (sequence, head) ends
+ * non-finite, and the call reports KDA_STATUS_OVERFLOW in its status word.
  */
 #ifndef KDA_MI355X_H
 #define KDA_MI355X_H
@@ -76,11 +78,16 @@ extern "C" {
 #define KDA_DTYPE_BF16 1
 #define KDA_DTYPE_FP32 2
 
-/* Device-side status word values (kda_fwd_check_status). */
+/* Device-side status word (kda_fwd_check_status): KDA_STATUS_OK, or an OR of
+   these bits. */
 #define KDA_STATUS_OK 0
 #define KDA_STATUS_BAD_CU_SEQLENS 1 /* cu_seqlens[0] != 0, not monotone, or cu_seqlens[N] != T;
                                        then no token was processed and neither out nor
                                        final_state is written, on every path */
+#define KDA_STATUS_OVERFLOW 2       /* the chunk state of some (sequence, head) ended non-finite:
+                                       a value outside the fp16 operand range (see "Numerical
+                                       range" above) or a non-finite input; out and final_state
+                                       of that pair are not meaningful */
 
 /* Chunk size of the chunked form (P1 §二 2.1 uses 16). */
 #define KDA_CHUNK 16

@@ -63,3 +63,29 @@ def test_same_bits_as_kda_fwd(state):
     assert torch.equal(out.view(torch.int16), ref_o.view(torch.int16))
     assert torch.equal(fin.view(torch.int16) if fin.dtype == torch.bfloat16 else fin,
                        ref_f.view(torch.int16) if ref_f.dtype == torch.bfloat16 else ref_f)
+
+
+@pytest.mark.gpu
+@pytest.mark.skipif(not torch.cuda.is_available(), reason="no GPU")
+@pytest.mark.parametrize("varlen", [False, True])
+def test_against_the_oracle(varlen):
+    """chunk_kda with the pages' flags and the default scale (K^-1/2) against
+    the fp64 oracle, every head: the facade maps the call onto the kernels'
+    arguments without changing what is computed."""
+    import oracle
+    from gated_delta_rule_prep_amd.inputs import make_inputs
+    from tests.kda_gpu import assert_close, device_inputs, say, to_f64
+    lens = [33, 1, 90, 16] if varlen else None
+    inp = make_inputs(1 if varlen else 2, 140 if varlen else 70, 3, seed=401, state_dtype="bf16", seq_lens=lens)
+    inp.scale = 128 ** -0.5
+    say("case chunk_kda vs oracle varlen=%s" % varlen)
+    d = device_inputs(inp)
+    out, fin = chunk_kda(q=d["q"], k=d["k"], v=d["v"], g=d["g"], beta=d["beta"], initial_state=d["initial_state"],
+                         output_final_state=True, A_log=d["A_log"], dt_bias=d["dt_bias"],
+                         lower_bound=inp.lower_bound, cu_seqlens=d["cu_seqlens"], **FLAGS)
+    torch.cuda.synchronize()
+    ref_o, ref_f = oracle.kda_fwd(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.scale, inp.A_log, inp.dt_bias,
+                                  inp.lower_bound, initial_state=inp.initial_state_f64(),
+                                  output_final_state=True, cu_seqlens=inp.cu_seqlens)
+    assert_close(to_f64(out), ref_o, "out")
+    assert_close(to_f64(fin), ref_f, "final_state", "bf16")
