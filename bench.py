@@ -1,23 +1,35 @@
 """Benchmark of the chunked KDA forward on one MI355X.
 
-One step = one kda_fwd call (the scheduler, then chunk prep and chunk
-recurrence: one fused kernel by default, two kernels on the split path) over
-one batch of seeded synthetic input already resident in HBM.  Workloads:
-  * headline: T = 8192, H = 96, K = V = 128, one fixed-length sequence, bf16
-    initial and final state, lower_bound = -5;
-  * also timed: the same shape as 8 varlen sequences of 1024 tokens.
-Prints ONE JSON line (rank 0).  Per-kernel times come from HIP events that
-kda_fwd_ex records around every kernel on the stream it runs on; the roofline is computed for
-the kernel that takes the most time, with algorithmic bytes only (inputs and
-outputs of the method that kernel is responsible for), and for the whole path.
-The fp64 oracle is timed on a bounded sample of the headline workload on the
-host cores (cpu_baseline).
+One step = one forward call over one batch of seeded synthetic input already
+resident in HBM: the scheduler kernel, then chunk prep and chunk recurrence
+(two kernels on the split path, one on the fused path).  The headline is the
+library's own path choice, kda_fwd_ex(path = KDA_PATH_AUTO), on T = 8192,
+H = 96, K = V = 128, one fixed-length sequence, bf16 initial and final state,
+lower_bound = -5 (it runs the split path there).  Every one of the five
+workloads (gated_delta_rule_prep_amd.inputs.configs) gets its own entry with
+the library's choice and the explicit paths (split and fused with 16-token
+chunks, split with 32-token chunks) timed beside it.
+
+Protocol (the pages' benchmark runs 30 warmup calls, then 5 repeats of 200
+timed calls, and reports the median): W warmup steps, then R repeats of K
+timed steps each, bracketed by device synchronisation; the step time is the
+median over the repeats (min and max beside it).  Per-kernel times come from
+HIP events that kda_fwd_ex records around every kernel on the stream it runs
+on (median over K profiled calls).  The roofline is computed for the kernel
+that takes the most time, with algorithmic bytes only (the method's inputs and
+outputs that kernel is responsible for), and for the whole path; us per chunk
+step is the chain kernel's (recurrence or fused) time over the chunk steps a
+workgroup slot runs in sequence (sequential_steps).  The
+fp64 oracle is timed on a bounded sample of the headline workload on the host
+cores (cpu_baseline).
 
 Also timed (not the headline): one decode step (kda_decode) of 256
-one-token sequences x 96 heads with a bf16 state updated in place.
+one-token sequences x 96 heads with a bf16 state updated in place, and one
+long sequence with 4 heads on the segmented form.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--chunk 16|32]
-                       [--path auto|fused|split] [--only fixed|varlen|decode]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--repeats R] [--no-cpu]
+                       [--only 0|1|2|3|4|fixed|varlen|decode|segmented] [--chunk 16|32]
+                       [--path auto|fused|split]
 """
 from __future__ import annotations
 
@@ -53,9 +65,35 @@ def param_bytes(inp):
     return inp.H * 4 + inp.H * inp.K * 4
 
 
-def run_workload(cfg, steps, warmup, torch, kda, device_inputs, chunk=None, path=None, precision=None):
-    inp = cfg.make()
-    d = device_inputs(inp, "cuda")
+def timed_repeats(torch, step, steps, warmup, repeats):
+    """W warmup calls, then `repeats` runs of `steps` calls each, every run
+    bracketed by device synchronisation; returns the per-call ms of each run."""
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    out = []
+    for _ in range(repeats):
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(steps):
+            step()
+        t1.record()
+        torch.cuda.synchronize()
+        out.append(t0.elapsed_time(t1) / steps)
+    return out
+
+
+def chunk_counts(inp, chunk):
+    lens = [inp.T] * inp.B if inp.cu_seqlens is None else list(np.diff(inp.cu_seqlens))
+    return [(int(n) + chunk - 1) // chunk for n in lens]
+
+
+def run_workload(cfg, steps, warmup, torch, kda, device_inputs, chunk=None, path=None, precision=None,
+                 repeats=1, inp=None, d=None):
+    inp = cfg.make() if inp is None else inp
+    d = device_inputs(inp, "cuda") if d is None else d
     out = torch.empty((inp.B, inp.T, inp.H, inp.V), dtype=torch.bfloat16, device="cuda")
     fin = torch.empty((inp.N, inp.H, inp.V, inp.K),
                       dtype=torch.bfloat16 if inp.state_dtype == "bf16" else torch.float32, device="cuda")
@@ -75,21 +113,12 @@ def run_workload(cfg, steps, warmup, torch, kda, device_inputs, chunk=None, path
                 inp.lower_bound, initial_state=d["initial_state"], final_state=fin,
                 cu_seqlens=d["cu_seqlens"], workspace=ws, events=events, chunk=chunk, path=path)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for _ in range(steps):
-        step()
-    t1.record()
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / steps
+    reps = timed_repeats(torch, step, steps, warmup, repeats)
+    ms = float(np.median(reps))
+    th = inp.B * inp.T * inp.H
     if precision is not None:   # kda_fwd_precision records no events
-        th = inp.B * inp.T * inp.H
-        return dict(inp=inp, ms=ms, kernels={}, path=used, taken="split", token_heads=th,
-                    status=kda.check_status(ws))
+        return dict(inp=inp, ms=ms, reps=reps, kernels={}, path=used, taken="split", token_heads=th,
+                    status=kda.check_status(ws), chunk=16)
 
     # per-kernel durations: kda_fwd_ex records HIP events before and after
     # every kernel on the stream it launches that kernel on
@@ -105,20 +134,20 @@ def run_workload(cfg, steps, warmup, torch, kda, device_inputs, chunk=None, path
     torch.cuda.synchronize()
     span = lambda row, i: row[i].elapsed_time(row[i + 1])
     if used == "fused":         # [0, 1] scheduler, [2, 3] the fused kernel
-        k_ms = np.array([[span(row, 0), span(row, 2)] for row in ev]).mean(axis=0)
+        k_ms = np.median(np.array([[span(row, 0), span(row, 2)] for row in ev]), axis=0)
         kernels = {"sched": float(k_ms[0]), "fused": float(k_ms[1])}
     else:                       # [0, 1] scheduler, then prep and recurrence of each part (+ [6, 7] fused)
         P = (n_ev - 2) // 4
-        k_ms = np.array([[span(row, 0), sum(span(row, 2 + 2 * p) for p in range(P)),
-                          sum(span(row, 2 + 2 * P + 2 * p) for p in range(P))]
-                         + ([span(row, 6)] if used == "auto" else []) for row in ev]).mean(axis=0)
+        k_ms = np.median(np.array([[span(row, 0), sum(span(row, 2 + 2 * p) for p in range(P)),
+                                    sum(span(row, 2 + 2 * P + 2 * p) for p in range(P))]
+                                   + ([span(row, 6)] if used == "auto" else []) for row in ev]), axis=0)
         kernels = {"sched": float(k_ms[0]), "prep": float(k_ms[1]), "recur": float(k_ms[2])}
         if used == "auto":      # the kernels of the path not taken exit at once
             kernels["fused"] = float(k_ms[3])
     status = kda.check_status(ws)
     taken = kda.path_taken(ws)
-    th = inp.B * inp.T * inp.H
-    return dict(inp=inp, ms=ms, kernels=kernels, path=used, taken=taken, token_heads=th, status=status)
+    return dict(inp=inp, ms=ms, reps=reps, kernels=kernels, path=used, taken=taken, token_heads=th,
+                status=status, chunk=chunk or 16)
 
 
 TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "hbm_traffic_T8192_H96.md")
@@ -138,6 +167,32 @@ def load_traffic():
     return {e["workload"]: e["kernels"] for e in entries if e.get("source_hash") == cur}
 
 
+CUS = 256
+
+
+def sequential_steps(inp, res):
+    """Chunk steps one workgroup slot runs in sequence in the chain kernel:
+    the longest sequence's chunk count (plus the fused kernel's five pipeline
+    steps), or, when the launch has more workgroups than can run at once, the
+    workgroup steps per slot.  Mirrors the library's tiling (kda_internal.h:
+    recur_tiles, fused_two_tiles; two recurrence workgroups share a CU when
+    64-column tiles outnumber the CUs)."""
+    counts = chunk_counts(inp, res["chunk"])
+    pairs = inp.N * inp.H
+    if res["taken"] == "fused":
+        tiles = 2 if 2 * pairs <= CUS else 1
+        wg_steps, chain, slots = tiles * inp.H * sum(c + 5 for c in counts), max(counts) + 5, CUS
+    else:
+        if res["chunk"] == 32:
+            tiles, per_cu = 2, 1
+        else:
+            equal = inp.cu_seqlens is None
+            tiles = 4 if 4 * pairs <= CUS else (2 if 2 * pairs <= CUS or not equal else 1)
+            per_cu = 2 if tiles == 2 and tiles * pairs > CUS else 1
+        wg_steps, chain, slots = tiles * inp.H * sum(counts), max(counts), CUS * per_cu
+    return max(chain, wg_steps / min(tiles * pairs, slots))
+
+
 def roofline(res, traffic=None):
     inp, th, km = res["inp"], res["token_heads"], res["kernels"]
     prep_bytes = th * PREP_BYTES_PER_TH + param_bytes(inp)
@@ -154,6 +209,9 @@ def roofline(res, traffic=None):
     tbytes = None if t is None else int(t["fetch_bytes"] + t["write_bytes"])
     path_ms = res["ms"]
     path_ach = path_bytes / (path_ms * 1e-3) / 1e9
+    steps = sequential_steps(inp, res)
+    chain_ms = km["fused"] if res["taken"] == "fused" else km["recur"]
+    res["us_per_chunk_step"] = round(1e3 * chain_ms / steps, 4) if steps > 0 else None
     return dict(kernel=name, bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                 frac=round(ach / HBM_PEAK_GBS, 4), traffic=tbytes, kernel_ms=round(kms, 4),
                 algorithmic_bytes_per_launch=int(kbytes)), \
@@ -165,11 +223,11 @@ def roofline(res, traffic=None):
 DECODE_N, DECODE_H = 256, 96   # one decode step of a serving batch: 256 sequences, 96 heads
 
 
-def run_decode(steps, warmup, torch, kda, device_inputs):
+def run_decode(steps, warmup, torch, kda, device_inputs, repeats=1):
     """kda_decode on a batch of DECODE_N one-token sequences, bf16 state updated
     in place (the state is 805 MB, past the 256 MB Infinity Cache, so every
     step streams it from and to HBM).  Roofline: the state bytes (in + out) and
-    the token bytes per launch over the mean kernel time."""
+    the token bytes per launch over the median step time."""
     from gated_delta_rule_prep_amd.inputs import make_inputs
     inp = make_inputs(DECODE_N, 1, DECODE_H, seed=9, state_dtype="bf16", name="decode_N256_H96_bf16state")
     d = device_inputs(inp, "cuda")
@@ -180,17 +238,7 @@ def run_decode(steps, warmup, torch, kda, device_inputs):
         kda.decode(d["q"], d["k"], d["v"], d["g"], d["beta"], inp.scale, out, d["A_log"], d["dt_bias"],
                    inp.lower_bound, initial_state=st, final_state=st)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for _ in range(steps):
-        step()
-    t1.record()
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / steps
+    ms = float(np.median(timed_repeats(torch, step, steps, warmup, repeats)))
     pairs = DECODE_N * DECODE_H
     nbytes = pairs * (2 * 128 * 128 * 2 + PATH_BYTES_PER_TH) + param_bytes(inp)
     ach = nbytes / (ms * 1e-3) / 1e9
@@ -200,7 +248,7 @@ def run_decode(steps, warmup, torch, kda, device_inputs):
                          "algorithmic_bytes_per_launch": int(nbytes)}}
 
 
-def run_segmented(steps, warmup, torch, kda, device_inputs, T=8192, H=4):
+def run_segmented(steps, warmup, torch, kda, device_inputs, T=8192, H=4, repeats=1):
     """One long sequence with few heads, the case the segmented forward is for:
     kda_fwd (which cuts the sequence into the library's count of segments here)
     next to kda_fwd_ex with the library's path (one chain per head and value
@@ -217,17 +265,7 @@ def run_segmented(steps, warmup, torch, kda, device_inputs, T=8192, H=4):
         f = lambda: kda.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], inp.scale, out, d["A_log"], d["dt_bias"],
                             inp.lower_bound, initial_state=d["initial_state"], final_state=fin,
                             workspace=ws, path=path)
-        for _ in range(warmup):
-            f()
-        torch.cuda.synchronize()
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        t0.record()
-        for _ in range(steps):
-            f()
-        t1.record()
-        torch.cuda.synchronize()
-        return t0.elapsed_time(t1) / steps
+        return float(np.median(timed_repeats(torch, f, steps, warmup, repeats)))
 
     chain = timed("auto")   # kda_fwd_ex: never cuts
     seg = timed(None)       # kda_fwd
@@ -268,21 +306,48 @@ def copy_for_counters(torch, mib):
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copies": 3}))
 
 
+def workload_entry(cfg, runs, paths, traffic):
+    """One workload's entry of the JSON line: the library's choice (runs[0])
+    with its roofline, per-kernel times and us per chunk step, and every
+    timed path's median step time."""
+    res = runs[paths[0]]
+    rl, prl = roofline(res, traffic.get(cfg.name))
+    inp = res["inp"]
+    return {"workload": cfg.name, "B": inp.B, "T": inp.T, "H": inp.H, "N": inp.N,
+            "state": inp.state_dtype, "lower_bound": inp.lower_bound,
+            "path": res["path"], "path_taken": res["taken"], "chunk": res["chunk"],
+            "ms_per_step": round(res["ms"], 4),
+            "ms_repeats": {"min": round(min(res["reps"]), 4), "max": round(max(res["reps"]), 4)},
+            "value": round(res["token_heads"] / (res["ms"] * 1e-3), 1),
+            "kernels_ms": {k: round(v, 4) for k, v in res["kernels"].items()},
+            "us_per_chunk_step": res["us_per_chunk_step"],
+            "paths_ms": {p: round(runs[p]["ms"], 4) for p in paths},
+            "roofline": rl, "path_roofline": prl, "status": res["status"]}
+
+
+# (label, chunk, path) of the forms timed per workload; the first is the library's choice
+FORMS = [("auto", None, "auto"), ("split16", 16, "split"), ("fused16", 16, "fused"), ("split32", 32, "split")]
+ONLY = {"fixed": 2, "varlen": 3}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--repeats", type=int, default=5, help="timed runs of --steps calls; the median is reported")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle cpu_baseline leg")
     ap.add_argument("--cpu-heads", type=int, default=96, help="heads of the headline workload the oracle runs")
-    ap.add_argument("--only", choices=["both", "fixed", "varlen", "decode", "segmented"], default="both",
-                    help="time only one workload (for profiler runs); the JSON line needs both")
+    ap.add_argument("--only", default="all",
+                    choices=["all", "0", "1", "2", "3", "4", "fixed", "varlen", "decode", "segmented"],
+                    help="time only one workload (for profiler runs: 0-4, fixed = 2, varlen = 3); the JSON "
+                         "line needs all")
     ap.add_argument("--chunk", type=int, default=0, choices=[0, 16, 32],
-                    help="tokens per chunk (0: the library's choice)")
+                    help="with --only: tokens per chunk (0: the library's choice)")
     ap.add_argument("--path", choices=["auto", "fused", "split"], default="auto",
-                    help="execution path of kda_fwd_ex (auto: the library's choice)")
+                    help="with --only: execution path of kda_fwd_ex (auto: the library's choice)")
     ap.add_argument("--precision", type=int, default=None, choices=list(range(8)),
-                    help="with --only fixed/varlen: time kda_fwd_precision with this KDA_PREC_* variant")
+                    help="with --only 0-4: time kda_fwd_precision with this KDA_PREC_* variant")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="with --only: afterwards run 3 device-to-device copies of this many MiB, a plain copy "
                          "kernel of known size that scales the HBM byte counters")
@@ -299,72 +364,70 @@ def main():
     from tests.kda_gpu import device_inputs
 
     cfgs = configs()
+    R = max(1, args.repeats)
     if args.only == "decode":
-        print(json.dumps(run_decode(args.steps, args.warmup, torch, kda, device_inputs)))
+        print(json.dumps(run_decode(args.steps, args.warmup, torch, kda, device_inputs, R)))
         if args.copy_mib > 0:
             copy_for_counters(torch, args.copy_mib)
         return
     if args.only == "segmented":
-        print(json.dumps(run_segmented(args.steps, args.warmup, torch, kda, device_inputs)))
+        print(json.dumps(run_segmented(args.steps, args.warmup, torch, kda, device_inputs, repeats=R)))
         return
-    chunk = args.chunk or None
-    if args.only != "both":
-        res = run_workload(cfgs[2] if args.only == "fixed" else cfgs[3], args.steps, args.warmup, torch, kda,
-                           device_inputs, chunk, args.path, args.precision)
+    if args.only != "all":
+        cfg = cfgs[ONLY.get(args.only, None) if args.only in ONLY else int(args.only)]
+        res = run_workload(cfg, args.steps, args.warmup, torch, kda, device_inputs, args.chunk or None, args.path,
+                           args.precision, repeats=R)
         print(json.dumps({"workload": res["inp"].name, "path": res["path"], "path_taken": res["taken"],
-                          "precision": args.precision,
-                          "ms_per_step": round(res["ms"], 4),
+                          "chunk": res["chunk"], "precision": args.precision,
+                          "ms_per_step": round(res["ms"], 4), "ms_repeats": [round(x, 4) for x in res["reps"]],
                           "kernels_ms": {k: round(v, 4) for k, v in res["kernels"].items()}}))
         if args.copy_mib > 0:
             copy_for_counters(torch, args.copy_mib)
         return
-    # The headline numbers are the library's own choice (kda_fwd: both paths
-    # enqueued, the scheduler kernel picks one); the two explicit paths are
-    # timed beside it.
-    paths = ["auto", "split", "fused"] if args.path == "auto" and chunk in (None, 16) else [args.path]
-    runs = {}
-    for wl, cfg in (("fixed", cfgs[2]), ("varlen", cfgs[3])):
-        for pth in paths:
-            runs[wl, pth] = run_workload(cfg, args.steps, args.warmup, torch, kda, device_inputs, chunk, pth)
-    fixed, varlen = runs["fixed", paths[0]], runs["varlen", paths[0]]
-    paths_ms = lambda wl: {p: round(runs[wl, p]["ms"], 4) for p in paths}
-    decode = run_decode(args.steps, args.warmup, torch, kda, device_inputs)
-    segmented = run_segmented(args.steps, args.warmup, torch, kda, device_inputs)
+
     traffic = load_traffic()
-    t = traffic.get("decode", {}).get("decode_kernel")
+    entries = []
+    for cfg in cfgs:
+        inp = cfg.make()
+        d = device_inputs(inp, "cuda")
+        runs = {label: run_workload(cfg, args.steps, args.warmup, torch, kda, device_inputs, chunk, pth,
+                                    repeats=R, inp=inp, d=d) for label, chunk, pth in FORMS}
+        entries.append(workload_entry(cfg, runs, [f[0] for f in FORMS], traffic))
+        del d, runs
+        torch.cuda.empty_cache()
+    head = entries[2]
+    decode = run_decode(args.steps, args.warmup, torch, kda, device_inputs, R)
+    t = traffic.get(decode["workload"], {}).get("decode_kernel")
     decode["roofline"]["traffic"] = None if t is None else int(t["fetch_bytes"] + t["write_bytes"])
-    rl, path = roofline(fixed, traffic.get("fixed"))
-    rl_v, path_v = roofline(varlen, traffic.get("varlen"))
+    segmented = run_segmented(args.steps, args.warmup, torch, kda, device_inputs, repeats=R)
     cpu = None if args.no_cpu else cpu_baseline(cfgs[2], args.cpu_heads)
-    value = fixed["token_heads"] / (fixed["ms"] * 1e-3)
     line = {
         "metric": METRIC,
-        "value": round(value, 1),
+        "value": head["value"],
         "unit": "token·heads/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(fixed["ms"], 4),
+        "repeats": R,
+        "ms_per_step": head["ms_per_step"],
+        "ms_repeats": head["ms_repeats"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16 in/out, fp16 and fp32 MFMA with fp32 accumulation, fp32 state on chip",
         "data": "synthetic (seeded normal q/k/v/g/beta, A_log=log U[1,16], dt_bias~N(0,0.1), state~N(0,0.05))",
         "config": {"workload": cfgs[2].name, "B": 1, "T": 8192, "H": 96, "K": 128, "V": 128,
-                   "state": "bf16", "lower_bound": -5.0, "chunk": args.chunk or 16, "path": fixed["path"],
-                   "path_taken": fixed["taken"]},
-        "roofline": rl,
-        "path_roofline": path,
-        "kernels_ms": {k: round(v, 4) for k, v in fixed["kernels"].items()},
-        "paths_ms": paths_ms("fixed"),
-        "varlen_8x1024": {"workload": cfgs[3].name, "path": varlen["path"], "path_taken": varlen["taken"],
-                          "ms_per_step": round(varlen["ms"], 4),
-                          "value": round(varlen["token_heads"] / (varlen["ms"] * 1e-3), 1),
-                          "kernels_ms": {k: round(v, 4) for k, v in varlen["kernels"].items()},
-                          "paths_ms": paths_ms("varlen"), "roofline": rl_v, "path_roofline": path_v},
+                   "state": "bf16", "lower_bound": -5.0, "chunk": head["chunk"], "path": head["path"],
+                   "path_taken": head["path_taken"]},
+        "roofline": head["roofline"],
+        "path_roofline": head["path_roofline"],
+        "kernels_ms": head["kernels_ms"],
+        "us_per_chunk_step": head["us_per_chunk_step"],
+        "paths_ms": head["paths_ms"],
+        "workloads": entries,
         "decode_256x96": decode,
         "segmented_8192x4": segmented,
-        "status_ok": fixed["status"] == 0 and varlen["status"] == 0 and segmented["status_ok"],
+        "status_ok": all(e["status"] == 0 for e in entries) and segmented["status_ok"],
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
