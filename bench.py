@@ -150,7 +150,7 @@ def run_workload(cfg, steps, warmup, torch, kda, device_inputs, chunk=None, path
                 status=status, chunk=chunk or 16)
 
 
-TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "hbm_traffic_T8192_H96.md")
+TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "hbm_traffic.md")
 
 
 def load_traffic():

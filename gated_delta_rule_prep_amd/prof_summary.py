@@ -10,6 +10,11 @@
       copy reads and writes exactly copy_bytes), so that the figures are bytes.
       Prints one JSON object: {"workload", "scale", "kernels": {name: {fetch,
       write}}, "source_hash"}.
+  python -m gated_delta_rule_prep_amd.prof_summary counters <kernel> <units> <dir>...
+      mean per dispatch of every counter the passes under the directories
+      collected for <kernel> (short name, e.g. recur_kernel), and that mean
+      divided by <units> (the work units of one dispatch, e.g. workgroup
+      chunk steps); prints one JSON object {counter: [per dispatch, per unit]}.
 
 The source hash covers the HIP sources and headers of the kernels, so a
 reader (bench.py) can tell whether the counters still describe the current
@@ -92,6 +97,15 @@ def traffic(workload, fetch_dir, write_dir, copy_bytes):
             "kernels": kernels, "source_hash": source_hash()}
 
 
+def counters(kernel, units, dirs):
+    vals = {}
+    for d in dirs:
+        for r in counter_rows(d):
+            if short_name(r["Kernel_Name"]) == kernel:
+                vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    return {c: [statistics.mean(v), statistics.mean(v) / units] for c, v in sorted(vals.items())}
+
+
 def stats(path, title=""):
     with open(path) as fh:
         rows = list(csv.DictReader(fh))
@@ -108,6 +122,8 @@ def main(argv):
         print(stats(argv[2], argv[3] if len(argv) > 3 else ""))
     elif len(argv) == 6 and argv[1] == "traffic":
         print(json.dumps(traffic(argv[2], argv[3], argv[4], int(argv[5]))))
+    elif len(argv) >= 5 and argv[1] == "counters":
+        print(json.dumps(counters(argv[2], float(argv[3]), argv[4:])))
     elif len(argv) == 2 and argv[1] == "hash":
         print(source_hash())
     else:
