@@ -87,22 +87,28 @@ __global__ __launch_bounds__(kThreads) void sched_kernel(SchedArgs a) {
   const int32_t total = s_carry;
 
   // 3. chunk table (the fused path, whose layout has no chunk table, skips
-  // this step and the next).  Up to kThreads sequences (one scan tile, still in LDS)
-  // the threads fill each sequence's chunks together, so that one long
-  // sequence does not leave a single thread writing all of its entries;
-  // beyond that each thread fills the chunks of its own sequences.
+  // this step and the next).  Up to kThreads sequences (one scan tile, whose
+  // inclusive prefix sums are still in LDS) each thread takes chunks i = tid,
+  // tid + kThreads, ... and finds its sequence by binary search for the first
+  // prefix sum above i, so that neither one long sequence nor many short ones
+  // serialise the fill; beyond that each thread fills the chunks of its own
+  // sequences.
   const bool table = a.lay.max_chunks > 0;
   if (!table) {
   } else if (N <= kThreads) {
-    for (int64_t n = 0; n < N; ++n) {
-      const int32_t nch = bad ? 0 : s_scan[n] - (n > 0 ? s_scan[n - 1] : 0);
-      const int32_t first = s_scan[n] - nch;
+    for (int32_t i = tid; i < total; i += kThreads) {
+      int32_t lo = 0, hi = (int32_t)N - 1;
+      while (lo < hi) {
+        const int32_t mid = (lo + hi) >> 1;
+        if (s_scan[mid] > i) hi = mid;
+        else lo = mid + 1;
+      }
+      const int64_t n = lo;
+      const int32_t c = i - (n > 0 ? s_scan[n - 1] : 0);
       const int64_t row0 = a.cu ? a.cu[n] : n * a.T;
       const int64_t len = a.cu ? a.cu[n + 1] - a.cu[n] : a.T;
-      for (int32_t c = tid; c < nch; c += kThreads) {
-        const int64_t rem = len - (int64_t)c * C;
-        chunks[first + c] = ChunkEntry{(int32_t)n, (int32_t)(row0 + (int64_t)c * C), (int32_t)(rem < C ? rem : C)};
-      }
+      const int64_t rem = len - (int64_t)c * C;
+      chunks[i] = ChunkEntry{(int32_t)n, (int32_t)(row0 + (int64_t)c * C), (int32_t)(rem < C ? rem : C)};
     }
   } else {
     for (int64_t n = tid; n < N; n += kThreads) {
