@@ -431,9 +431,13 @@ static int fwd_impl(const void* q, const void* k, const void* v, const void* g, 
     char* ws = static_cast<char*>(workspace);
     const int64_t rows = B * T;
     const int64_t part_rows = P > 1 ? (rows + P - 1) / P : (rows > 0 ? rows : 1);
+    // B sequences of T tokens on the split path in one part: the tables are
+    // a function of the chunk index, so no scheduler kernel runs; the prep
+    // kernel computes the entries and writes the header.
+    const bool fixed = cu_seqlens == nullptr && P == 1 && chunk == kda::C && run_split && !run_fused;
     rec(0, stream);
     rec4(0);
-    if (e == hipSuccess) {
+    if (e == hipSuccess && !fixed) {
       kda::SchedArgs sa{cu_seqlens, N, B, T, H, P, part_rows,
                         both ? (host_pick >= 0 ? host_pick : KDA_PATH_AUTO) : KDA_PATH_SPLIT, ws, L};
       e = kda::launch_sched(sa, stream);
@@ -448,6 +452,10 @@ static int fwd_impl(const void* q, const void* k, const void* v, const void* g, 
       kda::PrepArgs pa{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                        static_cast<const uint16_t*>(g), static_cast<const uint16_t*>(beta), A_log, dt_bias,
                        scale, lower_bound, H, p, bound, ws, L};
+      if (fixed) {
+        pa.fixed_T = T;
+        pa.fixed_B = B;
+      }
       rec(2 + 2 * p, stream);
       if (e == hipSuccess && run_split) e = kda::launch_prep(pa, stream);
       rec(3 + 2 * p, stream);
@@ -461,6 +469,7 @@ static int fwd_impl(const void* q, const void* k, const void* v, const void* g, 
                         sdt, N, H, p, lo, hi, ws, L};
       ra.precision = precision;
       ra.tiles = kda::recur_tiles(N * H, cu_seqlens == nullptr);
+      if (fixed) ra.fixed_T = T;
       rec(2 + 2 * P + 2 * p, rstream);
       if (e == hipSuccess && run_split) e = kda::launch_recur(ra, rstream);
       rec(3 + 2 * P + 2 * p, rstream);

@@ -72,6 +72,19 @@ struct SeqEntry {
   int32_t len;          // tokens in the sequence
 };
 
+// B sequences of T tokens (no cu_seqlens): the scheduler's table entries
+// follow from the index, so the split path with one part runs without the
+// scheduler kernel and computes them itself.
+__host__ __device__ inline ChunkEntry fixed_chunk(int64_t T, int64_t chunk_size, int64_t i) {
+  const int64_t nc = (T + chunk_size - 1) / chunk_size, n = i / nc, c = i - n * nc;
+  const int64_t rem = T - c * chunk_size;
+  return ChunkEntry{(int32_t)n, (int32_t)(n * T + c * chunk_size), (int32_t)(rem < chunk_size ? rem : chunk_size)};
+}
+__host__ __device__ inline SeqEntry fixed_seq(int64_t T, int64_t chunk_size, int64_t n) {
+  const int64_t nc = (T + chunk_size - 1) / chunk_size;
+  return SeqEntry{(int32_t)(n * nc), (int32_t)nc, (int32_t)(n * T), (int32_t)T};
+}
+
 struct Layout {
   int64_t chunk_table;  // byte offsets into the workspace
   int64_t seq_table;
@@ -177,6 +190,10 @@ struct PrepArgs {
   int64_t grid_chunks;  // workgroup columns launched (a bound on the part's chunk count)
   char* ws;
   Layout lay;
+  // > 0: fixed_B sequences of fixed_T tokens, one part, and no scheduler
+  // kernel ran: chunk entries come from fixed_chunk, and the first workgroup
+  // writes the header (status OK, path split, chunk count, part bounds)
+  int64_t fixed_T = 0, fixed_B = 0;
 };
 
 struct RecurArgs {
@@ -204,6 +221,9 @@ struct RecurArgs {
   // Value tiles per (sequence, head) for 16-token chunks: 1, 2 or 4 (128, 64
   // or 32 columns per workgroup), or 0 for recur_tiles(pairs, false).
   int tiles;
+  // > 0: N sequences of fixed_T tokens with no scheduler tables (the prep
+  // kernel wrote the header): sequence entries from fixed_seq, order = index
+  int64_t fixed_T = 0;
 };
 
 // Fused chunk prep + recurrence (one kernel, records kept in LDS): the

@@ -86,11 +86,27 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
   const int hgrp = (int)(blockIdx.x % (unsigned)hx), cidx = (int)(blockIdx.x / (unsigned)hx);
   const int h = hgrp * kWaves + wave;
   const WsHeader* hdr = reinterpret_cast<const WsHeader*>(a.ws);
-  const int chunk = hdr->part_first[a.part] + cidx;   // this launch covers one part
-  if (chunk >= hdr->part_first[a.part + 1] || h >= H) return;   // whole waves only; no barriers below
-  if (hdr->path == KDA_PATH_FUSED) return;                      // the scheduler chose the fused kernel
+  int chunk = cidx;
+  ChunkEntry ce;
+  if (a.fixed_T > 0) {
+    const int64_t total = a.fixed_B * ((a.fixed_T + C - 1) / C);
+    if (blockIdx.x == 0 && tid == 0) {   // the header the scheduler kernel would have written
+      WsHeader* w = reinterpret_cast<WsHeader*>(a.ws);
+      w->status = KDA_STATUS_OK;
+      w->chunk_count = (int32_t)total;
+      w->path = KDA_PATH_SPLIT;
+      w->part_first[0] = 0;
+      w->part_first[1] = (int32_t)total;
+    }
+    if (chunk >= total || h >= H) return;   // whole waves only; no barriers below
+    ce = fixed_chunk(a.fixed_T, C, chunk);
+  } else {
+    chunk = hdr->part_first[a.part] + cidx;   // this launch covers one part
+    if (chunk >= hdr->part_first[a.part + 1] || h >= H) return;
+    if (hdr->path == KDA_PATH_FUSED) return;   // the scheduler chose the fused kernel
+    ce = reinterpret_cast<const ChunkEntry*>(a.ws + a.lay.chunk_table)[chunk];
+  }
   WaveSmem& sm = wsm[wave];
-  const ChunkEntry ce = reinterpret_cast<const ChunkEntry*>(a.ws + a.lay.chunk_table)[chunk];
   const int r = lane & 15, cq = lane >> 4;
   const bool valid = r < ce.len;
   const int64_t tok = (int64_t)ce.row0 + min(r, ce.len - 1);   // clamped: loads stay in the sequence

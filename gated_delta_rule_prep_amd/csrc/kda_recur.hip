@@ -148,7 +148,8 @@ __global__ __launch_bounds__((Tile<WC, LD>::kThreads)) void recur_kernel(RecurAr
   const WsHeader* hdr = reinterpret_cast<const WsHeader*>(a.ws);
   // Nothing is touched (no output, no state) unless the scheduler accepted
   // cu_seqlens; the fused kernel runs instead when the scheduler chose it.
-  if ((hdr->status & KDA_STATUS_BAD_CU_SEQLENS) || hdr->path == KDA_PATH_FUSED) return;
+  // (Without the scheduler, fixed_T > 0, neither can happen.)
+  if (a.fixed_T == 0 && ((hdr->status & KDA_STATUS_BAD_CU_SEQLENS) || hdr->path == KDA_PATH_FUSED)) return;
   // XCD-aware placement: id b runs on XCD b % 8; the kTiles tiles of pair
   // 8 * g + x get ids 8 * (kTiles * g + tile) + x.
   const int64_t bid = blockIdx.x, x = bid & 7, q = bid >> 3;
@@ -164,8 +165,9 @@ __global__ __launch_bounds__((Tile<WC, LD>::kThreads)) void recur_kernel(RecurAr
   const int64_t slot_id = pair / H;
   const int h = (int)(pair - slot_id * H);
   const int v0 = tile * Tl::kCols;
-  const int n = reinterpret_cast<const int32_t*>(a.ws + a.lay.order)[slot_id];
-  const SeqEntry se = reinterpret_cast<const SeqEntry*>(a.ws + a.lay.seq_table)[n];
+  const int n = a.fixed_T > 0 ? (int)slot_id : reinterpret_cast<const int32_t*>(a.ws + a.lay.order)[slot_id];
+  const SeqEntry se = a.fixed_T > 0 ? fixed_seq(a.fixed_T, C, n)
+                                    : reinterpret_cast<const SeqEntry*>(a.ws + a.lay.seq_table)[n];
   const char* recs = a.ws + a.lay.records + ((int64_t)h * a.lay.max_chunks + se.first_chunk) * REC_BYTES;
   const int nch = se.nchunks;
   // This launch covers the chunks whose first token row lies in [row_lo,
