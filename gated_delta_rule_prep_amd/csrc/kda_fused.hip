@@ -312,36 +312,39 @@ __device__ __forceinline__ void phase3(const PrepCtx& p, char* rec, float (*lt)[
     lv[i] = lc < rr ? beta[rr] * accL[i] : 0.f;
     mv[i] = lc <= rr ? accM[i] : 0.f;
   }
-  *reinterpret_cast<f32x4*>(&lt[lc][4 * lg]) = lv;   // lt[m][r] = L[r][m]
+#pragma unroll
+  for (int i = 0; i < 4; ++i) lt[4 * lg + i][lc] = -lv[i];   // lt[r][m] = -L[r][m] (row-major)
   *reinterpret_cast<u32x2*>(rec + REC_MQK + (lc * C + 4 * lg) * 2) = u32x2{pack_f16(mv[0], mv[1]),
                                                                           pack_f16(mv[2], mv[3])};
 }
 
 // T = (I + L)^-1 diag(beta) of one chunk, columns 4w .. 4w + 3 by recurrence
-// wave w, into the record as T^T.  Forward substitution, exact for a unit
-// lower-triangular matrix: x_r = e_j[r] - sum_{m<r} L[r][m] x_m.  Lane
-// (row j' of 16 lanes, m) owns x_m of column j = 4w + j'; each row's sum over
-// m is a 16-lane DPP reduction, so the 16 sequential rows cost a few vector
-// instructions each and no memory traffic.  L[r][m] for the lane's m comes
-// from lt[m][0..15]; beta from the record's beta area.
+// wave w, into the record as T^T.  Forward substitution by pivots, exact for
+// a unit lower-triangular matrix: lane (r, j') holds x_r of column j = 4w + j'
+// (x = e_j to start); once x_m is final (after pivots 0 .. m - 1), every row
+// takes x_r -= L[r][m] x_m, with x_m broadcast from lane m of the lane's
+// 16-lane row by DPP, one multiply-add per pivot (rows r <= m have L[r][m] = 0
+// and keep their value).  The lane's row of -L comes from lt[r][0..15]
+// (row-major, padded rows: the 16 rows' reads hit distinct banks); beta from
+// the record's beta area.
+template <int M>
+__device__ __forceinline__ float subst_from(float x, const f32x4 (&l4)[4]) {
+  // x_M from lane M of the 16-lane row (every lane of the row valid, so no
+  // old value is needed), then x_r -= L[r][M] x_M with l4 holding -L
+  const float xm = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x150 + M, 0xF, 0xF, true));
+  x = fmaf(xm, l4[M >> 2][M & 3], x);
+  if constexpr (M + 1 < C - 1) return subst_from<M + 1>(x, l4);
+  return x;
+}
+
 __device__ __forceinline__ void chunk_inverse(const float (*lt)[C + 4], char* rec, int w, int lane) {
-  const int m = lane & 15, j = 4 * w + (lane >> 4);
+  const int r = lane & 15, j = 4 * w + (lane >> 4);
   f32x4 l4[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) l4[q] = *reinterpret_cast<const f32x4*>(&lt[m][4 * q]);
-  float x = 0.f;
-#pragma unroll
-  for (int r = 0; r < C; ++r) {
-    float t = l4[r >> 2][r & 3] * x;   // L[r][m] x_m (zero unless m < r)
-    t += dpp_shr(t, 1);                // inclusive sum over the 16 lanes of the row
-    t += dpp_shr(t, 2);
-    t += dpp_shr(t, 4);
-    t += dpp_shr(t, 8);
-    const float xr = (r == j ? 1.f : 0.f) - dpp_bcast15(t);
-    x = m == r ? xr : x;
-  }
+  for (int q = 0; q < 4; ++q) l4[q] = *reinterpret_cast<const f32x4*>(&lt[r][4 * q]);
+  const float x = subst_from<0>(r == j ? 1.f : 0.f, l4);
   const float bj = reinterpret_cast<const float*>(rec + REC_BYTES)[j];
-  *reinterpret_cast<_Float16*>(rec + REC_T + (j * C + m) * 2) = (_Float16)(x * bj);   // T^T[j][m] = T[m][j]
+  *reinterpret_cast<_Float16*>(rec + REC_T + (j * C + r) * 2) = (_Float16)(x * bj);   // T^T[j][r] = T[r][j]
 }
 
 template <int NT, int D>
@@ -349,7 +352,7 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
   using F = FCfg<NT, D>;
   __shared__ __align__(1024) char groups[D][F::kGroupBytes];
   __shared__ __align__(16) char recs[kRecSlots][kSlotBytes];
-  __shared__ __align__(16) float lts[2][C][C + 4];   // L^T of chunks c (even / odd), from prep to the inverse
+  __shared__ __align__(16) float lts[2][C][C + 4];   // -L of chunks c (even / odd), from prep to the inverse
   __shared__ __align__(16) float s_adt[K];
 
   const int64_t H = a.H;
