@@ -336,6 +336,38 @@ def test_beyond_the_fp16_range_is_reported(form):
             assert not bool(torch.isfinite(fin).all())
 
 
+def test_fixed_length_call_rewrites_a_stale_header():
+    """B sequences of T tokens on the split path run without the scheduler
+    kernel; the prep kernel writes the header itself, so a workspace that a
+    previous call left marked bad (rejected cu_seqlens) or overflowed reports
+    OK and the split path after a good fixed-length call, with the right result."""
+    from gated_delta_rule_prep_amd import kda
+    inp = make_inputs(2, 40, 2, seed=212, state_dtype="fp32")
+    d = device_inputs(inp)
+    ws = kda.alloc_workspace(2, 40, 2, 2, True, "cuda")
+    say("case stale header: a rejected cu_seqlens call, then a fixed-length call")
+    bad = make_inputs(1, 80, 2, seed=213, state_dtype="fp32", seq_lens=[40, 40])
+    db = device_inputs(bad)
+    cu = torch.tensor([0, 50, 40], dtype=torch.int64, device="cuda")
+    o = torch.empty(1, 80, 2, 128, dtype=torch.bfloat16, device="cuda")
+    f = torch.empty(2, 2, 128, 128, dtype=torch.float32, device="cuda")
+    kda.fwd(db["q"], db["k"], db["v"], db["g"], db["beta"], bad.scale, o, db["A_log"], db["dt_bias"],
+            bad.lower_bound, initial_state=db["initial_state"], final_state=f, cu_seqlens=cu, workspace=ws)
+    assert kda.check_status(ws) == kda.KDA_STATUS_BAD_CU_SEQLENS
+    out, fin = run_gpu(inp, d=d, workspace=ws, path="split", chunk=16)
+    assert kda.check_status(ws) == kda.KDA_STATUS_OK
+    assert kda.path_taken(ws) == "split"
+    ref_o, ref_f = oracle_run(inp)
+    assert_close(to_f64(out), ref_o, "out")
+    assert_close(to_f64(fin), ref_f, "final_state", "fp32")
+    say("case stale header: an overflowing fixed-length call, then a good one")
+    big = _scaled(make_inputs(2, 40, 2, seed=212, state_dtype="fp32"), 1e6, 1.0)
+    run_gpu(big, workspace=ws, path="split", chunk=16)
+    assert kda.check_status(ws) == kda.KDA_STATUS_OVERFLOW
+    run_gpu(inp, d=d, workspace=ws, path="split", chunk=16)
+    assert kda.check_status(ws) == kda.KDA_STATUS_OK
+
+
 PART_CASES = [
     dict(B=2, T=300, H=3, state_dtype="fp32", lower_bound=-5.0, seed=300),
     dict(B=1, T=513, H=2, state_dtype="bf16", lower_bound=-5.0, seed=301, seq_lens=ragged_lengths(513, 9)),
