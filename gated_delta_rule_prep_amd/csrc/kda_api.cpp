@@ -176,13 +176,13 @@ namespace {
 
 // Path a kda_fwd_ex call takes: KDA_PATH_SPLIT, KDA_PATH_FUSED, KDA_PATH_AUTO
 // (both paths enqueued, the scheduler kernel picks one from the sequence
-// lengths), or -1.  Measured on MI355X (T = 8192, K = V = 128): the fused
-// kernel is faster for batches of many short sequences (8 x 1024 tokens,
-// H = 96: 0.45 ms against 0.66) but slower whenever one sequence is long (one
-// 8192-token sequence: 0.93 ms against 0.68; 12 ragged sequences with one of
-// ~6000 tokens: 0.97 against 0.71), and the lengths are only known on the
-// device.  The library chooses only where both paths can run (16-token
-// chunks, one part).
+// lengths), or -1.  Measured on MI355X (T = 8192, K = V = 128, ms per call):
+// the fused kernel is faster for batches of many short sequences (8 x 1024
+// tokens, H = 96: 0.424 against 0.526) but slower whenever one sequence is
+// long (one 8192-token sequence: 0.84 against 0.56; 12 ragged sequences with
+// one of 7359 tokens: 0.91 against 0.60), and with cu_seqlens the lengths are
+// only known on the device.  The library chooses only where both paths can run
+// (16-token chunks, one part).
 int resolve_path(int chunk, int parts, int path) {
   if (chunk != 0 && chunk != kda::C && chunk != kda::C32) return -1;
   if (parts < 0) return -1;

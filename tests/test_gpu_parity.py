@@ -344,7 +344,8 @@ def test_fixed_length_call_rewrites_a_stale_header():
     from gated_delta_rule_prep_amd import kda
     inp = make_inputs(2, 40, 2, seed=212, state_dtype="fp32")
     d = device_inputs(inp)
-    ws = kda.alloc_workspace(2, 40, 2, 2, True, "cuda")
+    n = max(kda.workspace_bytes(1, 80, 2, 2, True), kda.workspace_bytes(2, 40, 2, 2, False, 16, None, "split"))
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
     say("case stale header: a rejected cu_seqlens call, then a fixed-length call")
     bad = make_inputs(1, 80, 2, seed=213, state_dtype="fp32", seq_lens=[40, 40])
     db = device_inputs(bad)
@@ -366,6 +367,29 @@ def test_fixed_length_call_rewrites_a_stale_header():
     assert kda.check_status(ws) == kda.KDA_STATUS_OVERFLOW
     run_gpu(inp, d=d, workspace=ws, path="split", chunk=16)
     assert kda.check_status(ws) == kda.KDA_STATUS_OK
+
+
+# Launch shapes at the boundaries of the tiling rules (kda_internal.h): value
+# tiles per (sequence, head) in the recurrence (4 while 4 pairs <= 256 CUs,
+# else 2, or 1 for equal lengths past 128 pairs), two recurrence workgroups
+# per CU past 256 workgroups, and the fused kernel's 64- or 128-column tiles
+# (64 while 2 pairs <= 256).
+TILING_CASES = [
+    dict(B=1, T=37, H=64, seq_lens=[37], seed=220),               # 64 pairs: 4 tiles, 256 workgroups
+    dict(B=1, T=37, H=65, seq_lens=[37], seed=221),               # 65 pairs: 2 tiles
+    dict(B=1, T=37, H=64, seq_lens=[20, 17], seed=222),           # 128 pairs: 2 tiles, 256 workgroups; fused 64
+    dict(B=1, T=37, H=43, seq_lens=[10, 20, 7], seed=223),        # 129 pairs: 2 tiles, two per CU; fused 128
+    dict(B=43, T=37, H=3, seed=224),                              # 129 equal pairs: 1 tile of 128 columns
+    dict(B=64, T=20, H=2, seed=225),                              # 128 equal pairs: 2 tiles
+]
+
+
+@pytest.mark.parametrize("path,chunk", VARIANTS, ids=VARIANT_IDS)
+@pytest.mark.parametrize("i", range(len(TILING_CASES)))
+def test_tiling_boundaries(i, path, chunk):
+    kw = dict(TILING_CASES[i])
+    inp = make_inputs(state_dtype="bf16", **kw)
+    check(inp, tag="tiling%d" % i, chunk=chunk, path=path)
 
 
 PART_CASES = [
