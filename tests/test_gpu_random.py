@@ -1,0 +1,54 @@
+"""Seeded random sweep of the forward's arguments against the fp64 oracle:
+sequence lengths (zero-length and ragged ones included), head counts, state
+dtypes, lower bounds, gate scales, and every path / chunk size / part count,
+all small enough that the oracle checks every element."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gated_delta_rule_prep_amd.inputs import make_inputs
+from tests.kda_gpu import assert_close, run_gpu, say, to_f64
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+N_CASES = 120
+
+
+def draw(i):
+    rng = np.random.default_rng(5000 + i)
+    H = int(rng.choice([1, 2, 3, 5, 8]))
+    if rng.random() < 0.5:   # B sequences of T tokens
+        B, T, lens = int(rng.integers(1, 4)), int(rng.integers(0, 200)), None
+    else:                    # one batch of ragged sequences through cu_seqlens
+        n = int(rng.integers(1, 7))
+        lens = [int(x) for x in rng.choice([0, 1, 15, 16, 17, 31, 32, 33, int(rng.integers(1, 150))], size=n)]
+        B, T = 1, sum(lens)
+    state = str(rng.choice(["bf16", "fp32", "none"]))
+    form = str(rng.choice(["auto", "split16", "fused16", "split32", "parts"]))
+    lb = float(rng.choice([-5.0, -3.0, -1.0, 0.0]))
+    g_std = float(rng.choice([0.5, 1.0, 2.0]))
+    return dict(B=B, T=T, H=H, lens=lens, state=state, form=form, lb=lb, g_std=g_std, seed=6000 + i)
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_random_case(i):
+    c = draw(i)
+    say("case random%d %s" % (i, c))
+    inp = make_inputs(c["B"], c["T"], c["H"], seed=c["seed"], lower_bound=c["lb"], g_std=c["g_std"],
+                      state_dtype=None if c["state"] == "none" else c["state"],
+                      initial_state=c["state"] != "none", seq_lens=c["lens"])
+    kw = dict(auto={}, split16=dict(path="split", chunk=16), fused16=dict(path="fused", chunk=16),
+              split32=dict(path="split", chunk=32), parts=dict(path="split", chunk=16, parts=3))[c["form"]]
+    out, fin = run_gpu(inp, **kw)
+    torch.cuda.synchronize()
+    ref_o, ref_f = oracle.kda_fwd(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.scale, inp.A_log, inp.dt_bias,
+                                  inp.lower_bound, initial_state=inp.initial_state_f64(),
+                                  output_final_state=inp.output_final_state, cu_seqlens=inp.cu_seqlens)
+    if inp.B * inp.T > 0:
+        assert_close(to_f64(out), ref_o, "out")
+    if inp.output_final_state:
+        assert_close(to_f64(fin), ref_f, "final_state", inp.state_dtype)
