@@ -107,6 +107,32 @@ __device__ __forceinline__ Rows chunk_rows(const SeqEntry& se, int j) {
   return Rows{(int64_t)se.row0 + C * j, rem < C ? rem : C};
 }
 
+// Waits between the waves of a workgroup go through flags in LDS instead of
+// workgroup barriers.  A wait polls until its condition holds, sleeping ~64
+// cycles between polls, and gives up after kSpinLimit polls (about a tenth of
+// a second; it never happens unless a wave stops being scheduled for that
+// long), so that every wave always finishes; after one wait gave up, a wave
+// waits no more, and giving up is reported in the status word.
+constexpr int kSpinLimit = 1 << 21;
+
+
+template <int SLEEP = 1, typename Pred>
+__device__ __forceinline__ bool spin_until(Pred pred) {
+#pragma nounroll
+  for (int k = 0; k < kSpinLimit; ++k) {
+    if (pred()) return true;
+    __builtin_amdgcn_s_sleep(SLEEP);
+  }
+  return false;
+}
+
+// A flag in LDS (every lane reads the same word: the value is wave-uniform).
+typedef __attribute__((address_space(3))) volatile int lds_vint;
+__device__ __forceinline__ int lds_get(const int* p) {
+  return __builtin_amdgcn_readfirstlane(*(const lds_vint*)(p));
+}
+__device__ __forceinline__ void lds_put(int* p, int v) { *(lds_vint*)(p) = v; }
+
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_r;
 __device__ __forceinline__ s16x4 tr16(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_r*)p);
@@ -143,7 +169,16 @@ __device__ __forceinline__ void read_slot(Ops<1>& o, const char* rec, const char
 template <int WC, int LD, int PV>
 __global__ __launch_bounds__((Tile<WC, LD>::kThreads)) void recur_kernel(RecurArgs a) {
   using Tl = Tile<WC, LD>;
+  // How the waves meet: LDS flags (four or more compute waves with a CU to
+  // themselves) or a workgroup barrier per step (see the loader and compute
+  // loops).  T = 8192, H = 96 (64-column tiles), recurrence kernel alone:
+  // 0.305 ms with barriers, 0.290 with flags; with two compute waves (H = 64)
+  // and with two workgroups sharing a CU the flags were not faster (0.230
+  // against 0.228 ms; 8 x 1024 tokens on the split path 0.266 against 0.269).
+  constexpr bool kFlags = WC >= 4 && LD >= 4;
   __shared__ __align__(1024) char ring[Tl::kSlots * Tl::kSlotBytes];
+  __shared__ int ready[Tl::kSlots];   // chunk + 1 of the chunk that has landed in each slot (0: none yet)
+  __shared__ int done[WC];            // steps each compute wave has finished (its reads of them are done)
   const int64_t H = a.H;
   const WsHeader* hdr = reinterpret_cast<const WsHeader*>(a.ws);
   // Nothing is touched (no output, no state) unless the scheduler accepted
@@ -189,15 +224,22 @@ __global__ __launch_bounds__((Tile<WC, LD>::kThreads)) void recur_kernel(RecurAr
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int row_bytes = (int)(H * V * 2);
+  if (tid < Tl::kSlots) ready[tid] = 0;
+  if (tid < WC) done[tid] = 0;
+  barrier();   // the flags start cleared
+  int32_t* const status = const_cast<int32_t*>(&hdr->status);
 
   if (wave >= WC) {
     // ---------------- loader wave ----------------
-    // Chunk c (step c of the launch) goes to slot c mod kSlots, which last
-    // held chunk c - kSlots: the compute waves are done with that one at
-    // barrier c - kSlots + 1.  So chunk c is issued right after barrier
-    // c - kSlots + 2 (chunks 0 .. kSlots - 3 before the loop) and waited for
-    // before barrier c.
-    static_assert(Tl::kLoaders == Tl::kSlots - 2, "one chunk in flight per loader");
+    // Chunk c (step c of the launch) goes to slot c mod kSlots and belongs to
+    // loader c mod kLoaders, which, in the order of its chunks: waits until
+    // every compute wave is done with the slot's previous chunk, c - kSlots
+    // (done[w] >= c - kSlots + 1); issues the chunk's loads; waits for them
+    // (vmcnt(0): this loader has no other load in flight, so the wait covers
+    // exactly these, whatever order loads complete in); and marks the slot
+    // (ready = c + 1).  No cycle: a compute wave reaching step c - kSlots + 1
+    // needs only chunks up to c - kSlots + 1, all issued before chunk c.
+    static_assert(Tl::kLoaders <= Tl::kSlots, "a loader's chunks use distinct slots while in flight");
     const int j = wave - WC;
     // Source offset of this lane's 16-byte position in each load instruction.
     // Pads, and the value rows of a partial chunk past its end, lie past the
@@ -240,15 +282,36 @@ __global__ __launch_bounds__((Tile<WC, LD>::kThreads)) void recur_kernel(RecurAr
 #pragma unroll
       for (int i = 0; i < kRecLoads; ++i) load_lds16(rrec, slot + Tl::kRecBase + 1024 * i, rsrc[i]);
     };
-    for (int c = j; c < min(steps, Tl::kSlots - 2); c += Tl::kLoaders) issue(c);
-    for (int i = 0; i < steps; ++i) {
-      const bool mine = i % Tl::kLoaders == j;
-      if (mine) wait_vmcnt<0>();   // chunk i has landed in its slot
-      barrier();
-      // the next chunk of this loader, i + kSlots - 2, is issued after the
-      // barrier, while the compute waves work on chunk i: issuing its loads
-      // takes a while, and before the barrier it would hold them up
-      if (mine && i + Tl::kSlots - 2 < steps) issue(i + Tl::kSlots - 2);
+    if constexpr (kFlags) {
+      bool ok = true;
+      for (int c = j; c < steps; c += Tl::kLoaders) {
+        if (c >= Tl::kSlots && ok)   // (after one wait gave up, none of this wave's waits spins)
+          ok = spin_until<16>([&] {
+            int m = lds_get(&done[0]);
+#pragma unroll
+            for (int w = 1; w < WC; ++w) m = min(m, lds_get(&done[w]));
+            return m >= c - Tl::kSlots + 1;
+          });
+        asm volatile("" ::: "memory");
+        issue(c);
+        wait_vmcnt<0>();   // chunk c has landed in its slot
+        lds_put(&ready[c % Tl::kSlots], c + 1);
+      }
+      if (!ok && lane == 0) atomicOr(status, KDA_STATUS_SYNC_TIMEOUT);
+    } else {
+      // With barriers: chunk c is issued right after barrier c - kSlots + 2
+      // (chunks 0 .. kSlots - 3 before the loop), when the compute waves are
+      // done with the slot's previous chunk, c - kSlots (they finished it by
+      // barrier c - kSlots + 1) and this loader has waited for its previous
+      // chunk; it is waited for (vmcnt(0)) before barrier c.
+      static_assert(kFlags || Tl::kLoaders == Tl::kSlots - 2, "one chunk in flight per loader");
+      for (int c = j; c < min(steps, Tl::kSlots - 2); c += Tl::kLoaders) issue(c);
+      for (int i = 0; i < steps; ++i) {
+        const bool mine = i % Tl::kLoaders == j;
+        if (mine) wait_vmcnt<0>();   // chunk i has landed in its slot
+        barrier();
+        if (mine && i + Tl::kSlots - 2 < steps) issue(i + Tl::kSlots - 2);
+      }
     }
     return;
   }
@@ -293,18 +356,31 @@ __global__ __launch_bounds__((Tile<WC, LD>::kThreads)) void recur_kernel(RecurAr
     // rounded its output right after computing it, got half of every lane's
     // values stale).  A scheduling barrier before every step barrier keeps
     // each step's instructions on their side of it.
+    //
+    // A compute wave waits for its step's chunk (ready == s + 1) by itself
+    // and reports each finished step (done = s + 1) when its reads of the slot
+    // are over, so the waves drift apart within the ring instead of meeting
+    // at a barrier every step: their LDS reads and their MFMA chains overlap.
     f32x4 o_prev[1];
+    bool ok = true;
     for (int s = 0; s < steps; ++s) {
       __builtin_amdgcn_sched_barrier(0);
-      barrier();
+      if constexpr (kFlags) {
+        if (ok) ok = spin_until([&] { return lds_get(&ready[s % Tl::kSlots]) == s + 1; });
+        asm volatile("" ::: "memory");   // the slot's reads stay behind the wait
+      } else {
+        barrier();
+      }
       const char* slot = ring + (s % Tl::kSlots) * Tl::kSlotBytes;
       Ops<1> ops;
       read_slot<Tl::kValStride>(ops, slot + Tl::kRecBase, slot, wc, lane);
       if (s > 0 && outp != nullptr)   // output of step s - 1, a full chunk (only a sequence's last chunk is partial)
         *reinterpret_cast<u32x2*>(out_seq + (int64_t)(s - 1) * out_chunk + out_lane) = pack_out(o_prev[0]);
       compute<1, PV>(Z, ops, o_prev);
-      wait_lgkm0();   // every read of this slot is done before the next barrier
+      wait_lgkm0();   // every read of this slot is done
+      if constexpr (kFlags) lds_put(&done[wave], s + 1);
     }
+    if (!ok && lane == 0) atomicOr(status, KDA_STATUS_SYNC_TIMEOUT);
     __builtin_amdgcn_sched_barrier(0);
     const Rows pr = chunk_rows(se, ci_hi - 1);
     if (lc < pr.len && outp != nullptr)

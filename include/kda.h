@@ -84,6 +84,9 @@ extern "C" {
 #define KDA_STATUS_BAD_CU_SEQLENS 1 /* cu_seqlens[0] != 0, not monotone, or cu_seqlens[N] != T;
                                        then no token was processed and neither out nor
                                        final_state is written, on every path */
+#define KDA_STATUS_SYNC_TIMEOUT 4   /* a wait between the waves of a recurrence workgroup gave up
+                                       (about 0.1 s without progress; not expected in operation):
+                                       out and final_state are not meaningful */
 #define KDA_STATUS_OVERFLOW 2       /* the chunk state of some (sequence, head) ended non-finite:
                                        a value outside the fp16 operand range (see "Numerical
                                        range" above) or a non-finite input; out and final_state

@@ -31,7 +31,7 @@ def test_header_codes_match_binding():
     src = open(HEADER).read()
     for name, val in [("KDA_OK", 0), ("KDA_EINVAL", 1), ("KDA_EDTYPE", 2), ("KDA_EWORKSPACE", 3),
                       ("KDA_EUNSUPPORTED", 4), ("KDA_EHIP", 5), ("KDA_DTYPE_NONE", 0), ("KDA_DTYPE_BF16", 1),
-                      ("KDA_DTYPE_FP32", 2), ("KDA_STATUS_BAD_CU_SEQLENS", 1), ("KDA_STATUS_OVERFLOW", 2), ("KDA_CHUNK", 16),
+                      ("KDA_DTYPE_FP32", 2), ("KDA_STATUS_BAD_CU_SEQLENS", 1), ("KDA_STATUS_OVERFLOW", 2), ("KDA_STATUS_SYNC_TIMEOUT", 4), ("KDA_CHUNK", 16),
                       ("KDA_PATH_AUTO", 0), ("KDA_PATH_SPLIT", 1), ("KDA_PATH_FUSED", 2)]:
         m = re.search(r"#define\s+%s\s+(\d+)" % name, src)
         assert m and int(m.group(1)) == val, name
