@@ -11,6 +11,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <algorithm>
+#include <atomic>
 #include <cstdint>
 #include <cstring>
 #include <mutex>
@@ -118,6 +119,12 @@ int check_sizes(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V, const int
 }  // namespace
 
 namespace kda {
+
+namespace {
+std::atomic<int> g_spin_limit{kSpinLimit};
+}
+
+int spin_limit() { return g_spin_limit.load(std::memory_order_relaxed); }
 
 bool layout_for(int64_t B, int64_t T, int64_t H, int64_t N, int chunk, Layout* L) {
   if (B < 1 || T < 0 || H < 1 || N < 0 || (chunk != C && chunk != C32)) return false;
@@ -797,6 +804,11 @@ int kda_debug_prep(const void* q, const void* k, const void* g, const void* beta
   } catch (...) {
     return fail(KDA_EHIP, "kda: unexpected C++ exception");
   }
+}
+
+int kda_debug_set_spin_limit(int polls) {
+  kda::g_spin_limit.store(polls < 0 ? kda::kSpinLimit : polls, std::memory_order_relaxed);
+  return KDA_OK;
 }
 
 int kda_decode(const void* q, const void* k, const void* v, const void* g, const void* beta, float scale,

@@ -224,7 +224,16 @@ struct RecurArgs {
   // > 0: N sequences of fixed_T tokens with no scheduler tables (the prep
   // kernel wrote the header): sequence entries from fixed_seq, order = index
   int64_t fixed_T = 0;
+  // Polls after which a wait between the waves of a workgroup gives up (set
+  // by the launch from spin_limit()).
+  int spin_limit = 0;
 };
+
+// Waits between the waves of a recurrence workgroup give up after
+// kSpinLimit polls, or after the count a test set with
+// kda_debug_set_spin_limit (spin_limit() returns the one in force).
+constexpr int kSpinLimit = 1 << 21;
+int spin_limit();
 
 // Fused chunk prep + recurrence (one kernel, records kept in LDS): the
 // inputs and outputs of kda_fwd, the scheduler's tables in `ws`.

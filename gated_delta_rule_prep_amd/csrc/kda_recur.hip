@@ -108,18 +108,17 @@ __device__ __forceinline__ Rows chunk_rows(const SeqEntry& se, int j) {
 }
 
 // Waits between the waves of a workgroup go through flags in LDS instead of
-// workgroup barriers.  A wait polls until its condition holds, sleeping ~64
-// cycles between polls, and gives up after kSpinLimit polls (about a tenth of
-// a second; it never happens unless a wave stops being scheduled for that
+// workgroup barriers.  A wait polls until its condition holds, sleeping
+// 64 * SLEEP cycles between polls, and gives up after a limit of polls (about
+// 0.06 s for a compute wave, SLEEP = 1, and 0.9 s for a loader, SLEEP = 16, at
+// 2.4 GHz; it never happens unless a wave stops being scheduled for that
 // long), so that every wave always finishes; after one wait gave up, a wave
-// waits no more, and giving up is reported in the status word.
-constexpr int kSpinLimit = 1 << 21;
-
-
+// waits no more, and giving up is reported in the status word.  The limit
+// comes with the launch (kSpinLimit, or a test's smaller one).
 template <int SLEEP = 1, typename Pred>
-__device__ __forceinline__ bool spin_until(Pred pred) {
+__device__ __forceinline__ bool spin_until(int limit, Pred pred) {
 #pragma nounroll
-  for (int k = 0; k < kSpinLimit; ++k) {
+  for (int k = 0; k < limit; ++k) {
     if (pred()) return true;
     __builtin_amdgcn_s_sleep(SLEEP);
   }
@@ -286,7 +285,7 @@ __global__ __launch_bounds__((Tile<WC, LD>::kThreads)) void recur_kernel(RecurAr
       bool ok = true;
       for (int c = j; c < steps; c += Tl::kLoaders) {
         if (c >= Tl::kSlots && ok)   // (after one wait gave up, none of this wave's waits spins)
-          ok = spin_until<16>([&] {
+          ok = spin_until<16>(a.spin_limit, [&] {
             int m = lds_get(&done[0]);
 #pragma unroll
             for (int w = 1; w < WC; ++w) m = min(m, lds_get(&done[w]));
@@ -366,7 +365,7 @@ __global__ __launch_bounds__((Tile<WC, LD>::kThreads)) void recur_kernel(RecurAr
     for (int s = 0; s < steps; ++s) {
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (kFlags) {
-        if (ok) ok = spin_until([&] { return lds_get(&ready[s % Tl::kSlots]) == s + 1; });
+        if (ok) ok = spin_until(a.spin_limit, [&] { return lds_get(&ready[s % Tl::kSlots]) == s + 1; });
         asm volatile("" ::: "memory");   // the slot's reads stay behind the wait
       } else {
         barrier();
@@ -415,7 +414,9 @@ hipError_t launch_tiles(const RecurArgs& a, int64_t pairs, hipStream_t s) {
   using Tl = Tile<WC, LD>;
   const int64_t grid = 8 * Tl::kTiles * ((pairs + 7) / 8);
   if (grid > INT32_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((recur_kernel<WC, LD, PV>), dim3((unsigned)grid), dim3(Tl::kThreads), 0, s, a);
+  RecurArgs b = a;
+  b.spin_limit = spin_limit();
+  hipLaunchKernelGGL((recur_kernel<WC, LD, PV>), dim3((unsigned)grid), dim3(Tl::kThreads), 0, s, b);
   return hipGetLastError();
 }
 

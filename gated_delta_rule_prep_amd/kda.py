@@ -34,7 +34,7 @@ EXPORTS = ("kda_fwd", "kda_fwd_profiled", "kda_fwd_ex", "kda_fwd_parts", "kda_fw
            "kda_fwd_segments", "kda_fwd_precision",
            "kda_decode", "kda_fwd_workspace_bytes", "kda_fwd_workspace_bytes_ex", "kda_get_last_error",
            "kda_version", "kda_fwd_check_status", "kda_workspace_layout", "kda_debug_prep",
-           "kda_fwd_fused_noalloc")
+           "kda_fwd_fused_noalloc", "kda_debug_set_spin_limit")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError("libkda.so is not built (run gated_delta_rule_prep_amd/build.py or "
@@ -88,6 +88,8 @@ _lib.kda_debug_prep.argtypes = [_p, _p, _p, _p, ctypes.c_float, _p, _p, ctypes.c
 _lib.kda_debug_prep.restype = ctypes.c_int
 _lib.kda_fwd_fused_noalloc.argtypes = _lib.kda_fwd.argtypes[:21] + [_p]
 _lib.kda_fwd_fused_noalloc.restype = ctypes.c_int
+_lib.kda_debug_set_spin_limit.argtypes = [ctypes.c_int]
+_lib.kda_debug_set_spin_limit.restype = ctypes.c_int
 
 
 class KDAError(RuntimeError):
@@ -394,6 +396,12 @@ def check_status(workspace: torch.Tensor) -> int:
     if rc != KDA_OK:
         _raise(rc)
     return st.value
+
+
+def debug_set_spin_limit(polls: int) -> None:
+    """Test-only: the recurrence's waits between waves give up after `polls`
+    polls (0: at once) in the launches that follow; negative restores the default."""
+    _lib.kda_debug_set_spin_limit(int(polls))
 
 
 def debug_prep(q, k, g, beta, scale, A_log, dt_bias, lower_bound, cu_seqlens=None, workspace=None,

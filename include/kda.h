@@ -85,7 +85,7 @@ extern "C" {
                                        then no token was processed and neither out nor
                                        final_state is written, on every path */
 #define KDA_STATUS_SYNC_TIMEOUT 4   /* a wait between the waves of a recurrence workgroup gave up
-                                       (about 0.1 s without progress; not expected in operation):
+                                       (0.06 to 0.9 s without progress; not expected in operation):
                                        out and final_state are not meaningful */
 #define KDA_STATUS_OVERFLOW 2       /* the chunk state of some (sequence, head) ended non-finite:
                                        a value outside the fp16 operand range (see "Numerical
@@ -423,6 +423,17 @@ int kda_debug_prep(const void* q, const void* k, const void* g, const void* beta
                    const float* A_log, const float* dt_bias, float lower_bound,
                    const int64_t* cu_seqlens, int64_t num_seqs, int64_t B, int64_t T, int64_t H,
                    int64_t K, void* workspace, size_t workspace_bytes, hipStream_t stream, int chunk);
+
+/*
+ * kda_debug_set_spin_limit -- test-only: waits between the waves of a
+ * recurrence workgroup (the split path's recurrence at 64 or 128 value columns
+ * per workgroup) give up after `polls` polls in the launches that follow, and
+ * report KDA_STATUS_SYNC_TIMEOUT; 0 makes every such wait give up at once (the
+ * kernels still finish, with meaningless outputs).  A negative value restores
+ * the default (2^21 polls).  Process-wide, applies to every device; not meant
+ * to be called while another thread launches.  Returns KDA_OK.
+ */
+int kda_debug_set_spin_limit(int polls);
 
 #ifdef __cplusplus
 }
