@@ -22,19 +22,27 @@
 //   * Loader waves own every load.  Chunk c of the launch belongs to loader
 //     c mod kLoaders, which streams the chunk's record (13.8 KB) and the
 //     tile's value rows into LDS slot c mod kSlots (kSlots = kLoaders + 2)
-//     with buffer-to-LDS loads, issued kSlots - 2 steps ahead, and waits for
-//     them (vmcnt(0)) just before the barrier of step c.  A loader issues its
-//     next chunk only after that wait, so it never has more than one chunk in
-//     flight and each wait covers exactly the loads of that chunk, whatever
-//     order loads complete in.
-//   * Compute waves take one barrier per step, read the step's operands from
-//     the slot (with fixed per-lane addresses plus immediates: the slot pads
-//     rows instead of swizzling them -- Qhat and -Khat rows 272 bytes apart,
-//     Kbar rows 288, value rows 2 x columns + 32 -- which also keeps the 16-byte
-//     and transposing 8-byte reads on distinct banks) and run the step.  They
-//     issue no loads and keep no load bookkeeping, so their instruction stream
-//     is the step itself (18 MFMA, 32 decay multiplies, 20 fp16 conversions,
-//     20 LDS reads and little else).
+//     with buffer-to-LDS loads and waits for them (vmcnt(0)) before it
+//     reports the chunk.  A loader issues its next chunk only after that
+//     wait, so it never has more than one chunk in flight and each wait
+//     covers exactly the loads of that chunk, whatever order loads complete in.
+//   * Compute waves read the step's operands from the slot (with fixed
+//     per-lane addresses plus immediates: the slot pads rows instead of
+//     swizzling them -- Qhat and -Khat rows 272 bytes apart, Kbar rows 288,
+//     value rows 2 x columns + 32 -- which also keeps the 16-byte and
+//     transposing 8-byte reads on distinct banks) and run the step.  They
+//     issue no loads and keep no load bookkeeping, so their instruction
+//     stream is the step itself (18 MFMA, 32 decay multiplies, 20 fp16
+//     conversions, 20 LDS reads and little else).
+//   * How they meet.  Four or more compute waves with a CU to themselves:
+//     through flags in LDS.  A loader sets the slot's ready word to c + 1
+//     once chunk c has landed; a compute wave waits for it, and sets its own
+//     done word to s + 1 once its reads of step s are over; a loader refills
+//     a slot when every compute wave is done with the slot's previous chunk.
+//     The compute waves then drift apart within the ring instead of issuing
+//     their record reads at the same moment.  Otherwise (two compute waves,
+//     or two workgroups sharing a CU, where the flags measured no faster):
+//     one workgroup barrier per step, loads issued kSlots - 2 steps ahead.
 //
 // What a step costs on MI355X (measured with probes shaped like this kernel,
 // 192 workgroups, 512 steps): the chain of one 16-column wave alone issues
@@ -43,7 +51,8 @@
 // needs the whole record; about 128 B per clock of LDS reads), and the
 // loaders' LDS writes a little more.  So a CU's step time grows with the
 // number of waves that read each record: 0.41 us per step with two compute
-// waves (32-column tiles) against 0.60 us with four (64-column tiles).  Waves
+// waves (32-column tiles) against 0.60 us with four (64-column tiles) meeting
+// at a barrier every step, 0.57 through the flags.  Waves
 // of 32 columns each (half the reads per column) double each wave's issue
 // time and measured slower.
 //

@@ -16,9 +16,9 @@
       divided by <units> (the work units of one dispatch, e.g. workgroup
       chunk steps); prints one JSON object {counter: [per dispatch, per unit]}.
 
-The source hash covers the HIP sources and headers of the kernels, so a
-reader (bench.py) can tell whether the counters still describe the current
-kernels.
+The source hash covers the code of the kernels' HIP sources and headers
+(comments and layout left out), so a reader (bench.py) can tell whether the
+counters still describe the current kernels.
 """
 from __future__ import annotations
 
@@ -34,14 +34,25 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = ["csrc/kda_device.h", "csrc/kda_internal.h", "csrc/kda_lds_pipe.h", "csrc/kda_step16.h",
                   "csrc/kda_sched.hip", "csrc/kda_prep.hip", "csrc/kda_recur.hip", "csrc/kda_prep32.hip",
-                  "csrc/kda_recur32.hip", "csrc/kda_fused.hip", "csrc/kda_decode.hip", "csrc/kda_segment.hip"]
+                  "csrc/kda_recur32.hip", "csrc/kda_fused.hip", "csrc/kda_decode.hip", "csrc/kda_segment.hip",
+                  "../include/kda.h"]
+
+
+_TOKEN = re.compile(r'//[^\n]*|/\*.*?\*/|"(?:\\.|[^"\\\n])*"|\'(?:\\.|[^\'\\\n])*\'', re.S)
+
+
+def code_only(text: str) -> str:
+    """The source with its comments removed and each run of white space
+    made one space (string and character literals kept as they are)."""
+    text = _TOKEN.sub(lambda m: " " if m.group(0).startswith("/") else m.group(0), text)
+    return " ".join(text.split())
 
 
 def source_hash() -> str:
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(HERE, rel), "rb") as f:
-            h.update(rel.encode() + b"\0" + f.read())
+        with open(os.path.join(HERE, rel), encoding="utf-8") as f:
+            h.update(rel.encode() + b"\0" + code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
@@ -50,6 +61,13 @@ def short_name(name: str) -> str:
                   r"seg_cu_kernel|identity_kernel|zero_kernel|prefix_kernel|copyBuffer|elementwise_kernel)",
                   name)
     return m.group(1) if m else name[:40]
+
+
+def stats_name(name: str) -> str:
+    """short_name with the template arguments, which tell tile shapes apart
+    (recur_kernel<WC, LD, PV>)."""
+    t = re.search(r"_kernel(<[^>]*>)", name)
+    return short_name(name) + (t.group(1).replace(" ", "") if t else "")
 
 
 def counter_rows(d: str):
@@ -112,7 +130,7 @@ def stats(path, title=""):
     lines = ["| kernel | calls | avg us | min us | max us | share |", "|---|---|---|---|---|---|"]
     for r in rows:
         lines.append("| %s | %s | %.1f | %.1f | %.1f | %.1f %% |" % (
-            short_name(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+            stats_name(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
             float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
     return ("### " + title + "\n\n" if title else "") + "\n".join(lines)
 
