@@ -23,14 +23,24 @@
 //     runs one phase, of four different chunks, so the per-step work is close
 //     to even, and each SIMD holds one wave of each kind: the prep wave's ALU
 //     work fills the recurrence wave's stalls.
-// Step s (s = -5 .. nchunks - 1) has one barrier.  Group s -- the raw q, k,
-// g, beta of chunk s + 5 (read by the phase-0 wave of step s) and the value
-// rows of chunk s (read by the recurrence at step s) -- is streamed HBM -> LDS
-// with buffer_load ... lds into a ring of D group slots by the prep wave that
-// reads its raw inputs, issued D - 1 steps ahead; that wave has no other
-// group in flight and waits for it (vmcnt(0)) before barrier s.  Records live
-// in a ring of six slots (chunks s .. s + 5).  The record layout in LDS is the
+// Steps s = -5 .. nchunks - 1.  Group s -- the raw q, k, g, beta of chunk
+// s + 5 (read by the phase-0 wave of step s) and the value rows of chunk s
+// (read by the recurrence at step s) -- is streamed HBM -> LDS with
+// buffer_load ... lds into a ring of D group slots by the prep wave that reads
+// its raw inputs, issued D - 1 steps ahead; that wave has no other group in
+// flight and waits for it (vmcnt(0)) at the top of step s.  Records live in a
+// ring of six slots (chunks s .. s + 5).  The record layout in LDS is the
 // swizzled one kda_step16.h reads.
+// The waves meet through progress flags in LDS, not a barrier per step: a
+// prep wave starts step s once every recurrence wave has finished step s - 1
+// (and, before reloading a group slot, once the prep wave that read it is
+// done); a recurrence wave starts step s once every recurrence wave has
+// finished step s - 1 (T of chunk s) and group s has landed, which also
+// implies that chunks s and s + 1 are built (see the loop).  A barrier per
+// step made every step as long as its slowest phase (phase 0 is about a fifth
+// longer than phases 1 and 2); with the flags each prep wave runs its four
+// phases back to back.  Every wait is bounded and reports a time-out in the
+// status word.
 //
 // Per chunk, as in the split prep kernel (kda_prep.hip), with a2 the gate in
 // log2 units, G its in-chunk inclusive cumulative sum, P = 2^G, Pinv = 2^-G,
@@ -62,6 +72,12 @@ constexpr int kLead = 5;                     // raw inputs of chunk s + 5 arrive
 constexpr int kRecSlots = kLead + 1;         // records of chunks s .. s + 5
 constexpr int kSlotBytes = REC_BYTES + 64;   // record + the chunk's beta (fp32 [16]) in LDS
 constexpr float kEps = 1e-6f;
+// The recurrence waves spend about half of each step waiting for the record
+// builders; they poll their flags every 512 cycles (s_sleep 8), which leaves
+// the SIMD and the LDS to the builder that shares it (varlen 8 x 1024, H = 96:
+// fused kernel 0.453 ms against 0.454 polling every 64 cycles and 0.460 with a
+// barrier per step; one 8192-token sequence 0.836 / 0.849 / 0.843 ms).
+constexpr int kRecSleep = 8;
 
 template <int NT, int D>
 struct FCfg {
@@ -354,6 +370,15 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
   __shared__ __align__(16) char recs[kRecSlots][kSlotBytes];
   __shared__ __align__(16) float lts[2][C][C + 4];   // -L of chunks c (even / odd), from prep to the inverse
   __shared__ __align__(16) float s_adt[K];
+  // Progress flags (the waves meet through them instead of a barrier per
+  // step): steps are numbered s = -5 .. nch - 1 and a flag holds s + 6 once
+  // its wave has finished step s (0: none).  pdone: prep waves; rdone:
+  // recurrence waves (their reads of step s's record and value rows done, and
+  // their part of T of chunk s + 1 written); gready: group slot holds group g
+  // (g + 6), set by the wave that loaded it once the loads have landed.
+  __shared__ __align__(16) int rdone[kRecWaves];
+  __shared__ int pdone[kPrepWaves], gready[D];
+  static_assert(kRecWaves == 4, "rdone is read as one 16-byte word");
 
   const int64_t H = a.H;
   // XCD-aware placement: id b runs on XCD b % 8; the kTiles tiles of pair
@@ -381,7 +406,14 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
   // them at the first use of these values.
   float A2 = -expf(a.A_log[h]) * kLog2e;   // sigmoid(x) = 1 / (1 + 2^(-x log2 e))
   asm volatile("" : "+v"(A2));
-  if (tid < K) s_adt[tid] = A2 * a.dt_bias[(int64_t)h * K + tid];   // visible after the first barrier
+  if (tid < K) s_adt[tid] = A2 * a.dt_bias[(int64_t)h * K + tid];
+  // rdone starts at "step -2 done": the prep waves run steps -5 .. -1 (the
+  // first records) before the recurrence waves have anything to do
+  if (tid < kPrepWaves) pdone[tid] = 0;
+  if (tid < kRecWaves) rdone[tid] = 4;
+  if (tid < D) gready[tid] = 0;
+  int32_t* const status = const_cast<int32_t*>(&hdr->status);
+  bool ok = true;   // no wait of this wave gave up (after one did, it waits no more)
 
   const int64_t sbase = ((int64_t)n * H + h) * V * K;   // state [n][h][v][k]
   const int wc = F::kWaveCols * (rec_wave ? wave : 0);  // first tile column of a recurrence wave
@@ -397,6 +429,8 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
       for (int nt = 0; nt < NT; ++nt) asm volatile("" : "+v"(Z[m][nt]));
   }
 
+  barrier();   // s_adt and the flags are set; the only workgroup barrier
+
   if (nch > 0) {
     Seq x;
     x.q = a.q + ((int64_t)se.row0 * H + h) * K;
@@ -408,46 +442,57 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
     x.se = se;
     const uint32_t g0 = lds_addr(groups[0]);
 
-    // The two kinds of wave run separate loops over the same steps (one
-    // barrier each per step), so that neither carries the other's registers.
+    // The two kinds of wave run separate loops over the same steps, meeting
+    // through the progress flags, so that neither carries the other's
+    // registers.
     if (rec_wave) {
       // The recurrence waves issue no loads: they wait for their LDS traffic
-      // (reads of the step's operands, T written by the inverse) and meet the
-      // others at the barrier.  The output of a step is rounded and stored in
-      // the next step, well after the MFMAs that produce it, and a scheduling
-      // barrier keeps each step's instructions on their side of the barrier.
+      // (reads of the step's operands, T written by the inverse) before they
+      // report a step.  The output of a step is rounded and stored in the next
+      // step, well after the MFMAs that produce it, and a scheduling barrier
+      // keeps each step's instructions on their side of the waits.
       uint16_t* const out_seq = a.out + ((int64_t)se.row0 * H + h) * V + col0;
       const int64_t out_chunk = (int64_t)C * H * V;
       const int out_lane = (int)((lc * H) * V) + 4 * lg;
       f32x4 o_prev[NT];
       int gslot = kLead % D;   // group slot of group s (group g sits in slot (g + kLead) mod D)
-      // steps -5 .. -1: the prep waves start the first records; at step -1 the
-      // inverse of chunk 0
-      for (int s = -kLead; s < 0; ++s) {
-        wait_lgkm0();
-        barrier();
-        if (s == -1) chunk_inverse(lts[0], recs[0], wave, lane);
-      }
+      // step -1: the inverse of chunk 0, once its L is complete (phase 3 at
+      // step -2 by prep wave 0)
+      ok = spin_until(a.spin_limit, [&] { return lds_get(&pdone[0]) >= 4; });
+      asm volatile("" ::: "memory");
+      chunk_inverse(lts[0], recs[0], wave, lane);
+      wait_lgkm0();
+      lds_put(&rdone[wave], 5);
+      const auto rec_min = [&] { return lds_min4(rdone); };
       int rs = 0;   // record slot of chunk s
       for (int s = 0; s < nch; ++s) {
         __builtin_amdgcn_sched_barrier(0);
-        wait_lgkm0();
-        barrier();
-        // every wave is done with group s - 1 and with the record of chunk
-        // s - 1; group s has landed; the record of chunk s is complete
+        // Step s needs T of chunk s (every recurrence wave's part, written at
+        // step s - 1) and group s (the value rows) landed.  It also needs
+        // chunk s's record (phase 3 at step s - 2) and L of chunk s + 1 (phase
+        // 3 at step s - 1, for this step's inverse), which those two waits
+        // imply: the prep wave that finishes chunk s + 1 is the one that loads
+        // group s and reports it only at the top of step s, after its step
+        // s - 1; likewise group s - 1, waited for at step s - 1, came from the
+        // wave that finished chunk s at step s - 2 (for s = 0: the wait before
+        // the inverse of chunk 0).
+        if (ok) ok = spin_until<kRecSleep>(a.spin_limit, [&] { return rec_min() >= s + 5; });
+        if (ok) ok = spin_until<kRecSleep>(a.spin_limit, [&] { return lds_get(&gready[gslot]) == s + 6; });
+        asm volatile("" ::: "memory");   // the step's LDS traffic stays behind the waits
         if (s > 0) {   // output of chunk s - 1, a full chunk (only the last chunk is partial)
           uint16_t* const ob = out_seq + (int64_t)(s - 1) * out_chunk;
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt) *reinterpret_cast<u32x2*>(ob + out_lane + 16 * nt) = pack_out(o_prev[nt]);
         }
-        // T of chunk s + 1 (L^T completed at step s - 1), independent of this
-        // step's chain; past the last chunk it lands in a record slot that no
-        // chunk uses any more
+        // T of chunk s + 1, independent of this step's chain; past the last
+        // chunk it lands in a record slot that no chunk uses any more
         const int rs1 = rs == kRecSlots - 1 ? 0 : rs + 1;
         chunk_inverse(lts[(s + 1) & 1], recs[rs1], wave, lane);
         Ops<NT> ops;
         read_ops<NT>(ops, recs[rs], groups[gslot] + 1024 * F::kV, 2 * F::kCols, wc, lane);
         compute<NT>(Z, ops, o_prev);
+        wait_lgkm0();   // this step's reads are done and its part of T is written
+        lds_put(&rdone[wave], s + 6);
         gslot = gslot == D - 1 ? 0 : gslot + 1;
         rs = rs1;
       }
@@ -471,29 +516,42 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
       const int pw = wave - kRecWaves;   // this prep wave builds the chunks c = pw mod 4
       // Group g (steps g = -5 .. nch - 1) belongs to the prep wave that reads
       // its raw inputs (phase 0 of chunk g + 5), pw = (g + 5) mod 4.  That wave
-      // issues it right after barrier g - D + 1, when every wave is done with
-      // group g - D, the slot's previous contents, and waits for it (vmcnt(0))
-      // just before barrier g.  The wave's next group, g + 4, is issued after
-      // barrier g + 5 - D >= g, so a prep wave never has more than one group in
-      // flight and each wait covers exactly that group's loads, whatever order
-      // loads complete in.  Prep waves issue no other global loads or stores in
-      // the loop.
+      // issues it at step g - D + 1 into the slot of group g - D, once every
+      // wave is done with that group (the recurrence waves with step g - D, the
+      // prep wave that read it with step g - D), waits for it (vmcnt(0)) at the
+      // top of step g and reports it in gready.  The wave's next group, g + 4,
+      // is issued at step g + 5 - D >= g, so a prep wave never has more than
+      // one group in flight and each wait covers exactly that group's loads,
+      // whatever order loads complete in.  Prep waves issue no other global
+      // loads or stores in the loop.
       const auto mine = [&](int g) { return ((g + kLead) & 3) == pw; };
+      const auto rec_min = [&] { return lds_min4(rdone); };
       for (int g = -kLead; g < min(-kLead + D - 1, nch); ++g)
         if (mine(g)) issue_group<NT, D>(g0 + (g + kLead) * F::kGroupBytes, x, g, lane);
       int gslot = 0;   // group slot of group s
       for (int s = -kLead; s < nch; ++s) {
-        if (mine(s)) wait_vmcnt<0>();   // group s has landed in its slot
-        wait_lgkm0();
-        barrier();
+        if (mine(s)) {
+          wait_vmcnt<0>();   // group s has landed in its slot
+          lds_put(&gready[gslot], s + 6);
+        }
+        // Every recurrence wave is done with step s - 1: with the record slot
+        // that chunk s + 5 takes (chunk s - 1), with L of chunk s (the inverse
+        // at step s - 1), whose buffer phase 3 of chunk s + 2 takes, and with
+        // the value rows of group s - 1, whose slot group s + D - 1 takes.
+        if (ok) ok = spin_until(a.spin_limit, [&] { return rec_min() >= s + 5; });
+        asm volatile("" ::: "memory");
         // The lane id passes through an empty asm each step, so that the
         // lane-dependent addresses and constants of the group loads and of the
         // four phases are computed where they are used instead of being
         // hoisted out of the loop and held (or spilled) across it.
         int ln = lane;
         asm volatile("" : "+v"(ln));
-        if (s + D - 1 < nch && mine(s + D - 1))
+        if (s + D - 1 < nch && mine(s + D - 1)) {
+          // the prep wave that read group s - 1 (phase 0 at step s - 1) is done with it
+          if (ok) ok = spin_until(a.spin_limit, [&] { return lds_get(&pdone[(s + 4) & 3]) >= s + 5; });
+          asm volatile("" ::: "memory");
           issue_group<NT, D>(g0 + (gslot == 0 ? D - 1 : gslot - 1) * F::kGroupBytes, x, s + D - 1, ln);
+        }
         // chunk c (c = pw mod 4) is built in phases 0..3 at steps c - 5 .. c - 2
         const int ph = (s + kLead - pw) & 3;
         const int c = s + kLead - ph;
@@ -512,17 +570,20 @@ __global__ __launch_bounds__(kThreads) void fused_kernel(FusedArgs a) {
             phase3(pc, rec, lts[c & 1], cr);
           }
         }
+        wait_lgkm0();   // this step's LDS writes are done
+        lds_put(&pdone[pw], s + 6);
         gslot = gslot == D - 1 ? 0 : gslot + 1;
       }
       wait_vmcnt<0>();   // (nothing is in flight here: every group issued was waited for)
     }
   }
 
+  if (!ok && lane == 0) atomicOr(status, KDA_STATUS_SYNC_TIMEOUT);
   if (rec_wave) {
     if (a.s_out != nullptr) store_state<NT>(Z, a.s_out, a.state_dtype, sbase, col0, lc, lg);
     // an operand beyond the fp16 range (or a non-finite input) leaves the
     // state non-finite: reported in the status word
-    flag_nonfinite<8, NT>(Z, const_cast<int32_t*>(&hdr->status), KDA_STATUS_OVERFLOW);
+    flag_nonfinite<8, NT>(Z, status, KDA_STATUS_OVERFLOW);
   }
 }
 
@@ -530,7 +591,9 @@ template <int NT, int D>
 hipError_t launch_tiles(const FusedArgs& a, hipStream_t s) {
   const int64_t pairs = a.N * a.H;
   const int64_t grid = 8 * FCfg<NT, D>::kTiles * ((pairs + 7) / 8);
-  hipLaunchKernelGGL((fused_kernel<NT, D>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  FusedArgs b = a;
+  b.spin_limit = spin_limit();
+  hipLaunchKernelGGL((fused_kernel<NT, D>), dim3((unsigned)grid), dim3(kThreads), 0, s, b);
   return hipGetLastError();
 }
 

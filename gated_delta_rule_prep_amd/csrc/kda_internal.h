@@ -229,7 +229,7 @@ struct RecurArgs {
   int spin_limit = 0;
 };
 
-// Waits between the waves of a recurrence workgroup give up after
+// Waits between the waves of a recurrence or fused workgroup give up after
 // kSpinLimit polls, or after the count a test set with
 // kda_debug_set_spin_limit (spin_limit() returns the one in force).
 constexpr int kSpinLimit = 1 << 21;
@@ -254,6 +254,9 @@ struct FusedArgs {
   int64_t N, H;
   char* ws;
   Layout lay;
+  // Polls after which a wait between the waves of a workgroup gives up (set
+  // by the launch from spin_limit()).
+  int spin_limit = 0;
 };
 
 // Segmented forward: segment boundaries and the prefix over the segments'

@@ -53,4 +53,35 @@ __device__ __forceinline__ void wait_vmcnt() {
 __device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
 
+// Waits between the waves of a workgroup through flags in LDS instead of
+// workgroup barriers.  A wait polls until its condition holds, sleeping
+// 64 * SLEEP cycles between polls, and gives up after `limit` polls (2^21
+// polls: about 0.06 s at SLEEP = 1 and 0.9 s at SLEEP = 16, at 2.4 GHz; it
+// never happens unless a wave stops being scheduled for that long), so that
+// every wave always finishes.  The kernels stop waiting after one wait gave up
+// and report it in the status word; the limit comes with the launch.
+template <int SLEEP = 1, typename Pred>
+__device__ __forceinline__ bool spin_until(int limit, Pred pred) {
+#pragma nounroll
+  for (int k = 0; k < limit; ++k) {
+    if (pred()) return true;
+    __builtin_amdgcn_s_sleep(SLEEP);
+  }
+  return false;
+}
+
+// A flag in LDS (every lane reads the same word: the value is wave-uniform).
+typedef __attribute__((address_space(3))) volatile int lds_vint;
+__device__ __forceinline__ int lds_get(const int* p) {
+  return __builtin_amdgcn_readfirstlane(*(const lds_vint*)(p));
+}
+__device__ __forceinline__ void lds_put(int* p, int v) { *(lds_vint*)(p) = v; }
+// The smallest of four flags at a 16-byte aligned address, in one LDS read.
+typedef int lds_i32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) volatile lds_i32x4 lds_vi32x4;
+__device__ __forceinline__ int lds_min4(const int* p) {
+  const lds_i32x4 v = *(const lds_vi32x4*)(p);
+  return __builtin_amdgcn_readfirstlane(min(min(v[0], v[1]), min(v[2], v[3])));
+}
+
 }  // namespace kda

@@ -116,31 +116,6 @@ __device__ __forceinline__ Rows chunk_rows(const SeqEntry& se, int j) {
   return Rows{(int64_t)se.row0 + C * j, rem < C ? rem : C};
 }
 
-// Waits between the waves of a workgroup go through flags in LDS instead of
-// workgroup barriers.  A wait polls until its condition holds, sleeping
-// 64 * SLEEP cycles between polls, and gives up after a limit of polls (about
-// 0.06 s for a compute wave, SLEEP = 1, and 0.9 s for a loader, SLEEP = 16, at
-// 2.4 GHz; it never happens unless a wave stops being scheduled for that
-// long), so that every wave always finishes; after one wait gave up, a wave
-// waits no more, and giving up is reported in the status word.  The limit
-// comes with the launch (kSpinLimit, or a test's smaller one).
-template <int SLEEP = 1, typename Pred>
-__device__ __forceinline__ bool spin_until(int limit, Pred pred) {
-#pragma nounroll
-  for (int k = 0; k < limit; ++k) {
-    if (pred()) return true;
-    __builtin_amdgcn_s_sleep(SLEEP);
-  }
-  return false;
-}
-
-// A flag in LDS (every lane reads the same word: the value is wave-uniform).
-typedef __attribute__((address_space(3))) volatile int lds_vint;
-__device__ __forceinline__ int lds_get(const int* p) {
-  return __builtin_amdgcn_readfirstlane(*(const lds_vint*)(p));
-}
-__device__ __forceinline__ void lds_put(int* p, int v) { *(lds_vint*)(p) = v; }
-
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_r;
 __device__ __forceinline__ s16x4 tr16(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_r*)p);

@@ -399,7 +399,7 @@ def check_status(workspace: torch.Tensor) -> int:
 
 
 def debug_set_spin_limit(polls: int) -> None:
-    """Test-only: the recurrence's waits between waves give up after `polls`
+    """Test-only: the waits between waves (recurrence, fused kernel) give up after `polls`
     polls (0: at once) in the launches that follow; negative restores the default."""
     _lib.kda_debug_set_spin_limit(int(polls))
 

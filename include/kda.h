@@ -426,9 +426,9 @@ int kda_debug_prep(const void* q, const void* k, const void* g, const void* beta
 
 /*
  * kda_debug_set_spin_limit -- test-only: waits between the waves of a
- * recurrence workgroup (the split path's recurrence at 64 or 128 value columns
- * per workgroup) give up after `polls` polls in the launches that follow, and
- * report KDA_STATUS_SYNC_TIMEOUT; 0 makes every such wait give up at once (the
+ * workgroup (the split path's recurrence at 64 or 128 value columns per
+ * workgroup, and the fused kernel) give up after `polls` polls in the launches
+ * that follow, and report KDA_STATUS_SYNC_TIMEOUT; 0 makes every such wait give up at once (the
  * kernels still finish, with meaningless outputs).  A negative value restores
  * the default (2^21 polls).  Process-wide, applies to every device; not meant
  * to be called while another thread launches.  Returns KDA_OK.

@@ -369,33 +369,35 @@ def test_fixed_length_call_rewrites_a_stale_header():
     assert kda.check_status(ws) == kda.KDA_STATUS_OK
 
 
+@pytest.mark.parametrize("path", ["split", "fused"])
 @pytest.mark.parametrize("B", [1, 2])
-def test_wave_sync_timeout_is_reported(B):
-    """The waits between the waves of a recurrence workgroup are bounded.  With
-    the bound forced to zero polls from the host, every such wait gives up at
-    once: the kernels still finish and the status word reports the time-out.
-    With the default bound restored, the same call is clean and gives the same
-    result as before.  B = 1: 96 pairs, 64-column tiles with a CU each; B = 2:
-    192 equal pairs, 128-column tiles; 10 chunks, more than the ring's slots,
-    so the loaders wait too."""
+def test_wave_sync_timeout_is_reported(B, path):
+    """The waits between the waves of a recurrence or fused workgroup are
+    bounded.  With the bound forced to zero polls from the host, every such
+    wait gives up at once: the kernels still finish and the status word
+    reports the time-out.  With the default bound restored, the same call is
+    clean and gives the same result as before.  Split path -- B = 1: 96 pairs,
+    64-column recurrence tiles with a CU each; B = 2: 192 equal pairs,
+    128-column tiles; 10 chunks, more than the ring's slots, so the loaders
+    wait too.  Fused path -- B = 1: 64-column workgroups, B = 2: 128-column."""
     from gated_delta_rule_prep_amd import kda
     inp = make_inputs(B, 160, 96, seed=230 + B, state_dtype="fp32")
     d = device_inputs(inp)
-    ws = torch.empty(kda.workspace_bytes(B, 160, 96, B, False, 16, None, "split"), dtype=torch.uint8,
+    ws = torch.empty(kda.workspace_bytes(B, 160, 96, B, False, 16, None, path), dtype=torch.uint8,
                      device="cuda")
-    say("case sync timeout B=%d T=160 H=96 split: default bound" % B)
-    ref_out, ref_fin = run_gpu(inp, d=d, workspace=ws, path="split", chunk=16)
+    say("case sync timeout B=%d T=160 H=96 %s: default bound" % (B, path))
+    ref_out, ref_fin = run_gpu(inp, d=d, workspace=ws, path=path, chunk=16)
     assert kda.check_status(ws) == kda.KDA_STATUS_OK
-    say("case sync timeout B=%d: bound of zero polls" % B)
+    say("case sync timeout B=%d %s: bound of zero polls" % (B, path))
     try:
         kda.debug_set_spin_limit(0)
-        run_gpu(inp, d=d, workspace=ws, path="split", chunk=16)
+        run_gpu(inp, d=d, workspace=ws, path=path, chunk=16)
         st = kda.check_status(ws)
     finally:
         kda.debug_set_spin_limit(-1)
     assert st & kda.KDA_STATUS_SYNC_TIMEOUT
-    say("case sync timeout B=%d: default bound again" % B)
-    out, fin = run_gpu(inp, d=d, workspace=ws, path="split", chunk=16)
+    say("case sync timeout B=%d %s: default bound again" % (B, path))
+    out, fin = run_gpu(inp, d=d, workspace=ws, path=path, chunk=16)
     assert kda.check_status(ws) == kda.KDA_STATUS_OK
     assert torch.equal(out, ref_out) and torch.equal(fin, ref_fin)
     ref_o, ref_f = oracle_run(inp)
