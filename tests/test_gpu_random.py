@@ -52,3 +52,52 @@ def test_random_case(i):
         assert_close(to_f64(out), ref_o, "out")
     if inp.output_final_state:
         assert_close(to_f64(fin), ref_f, "final_state", inp.state_dtype)
+
+
+# Shapes where the workgroups' waves meet through LDS flags: the recurrence's
+# 64-column tiles with a CU each (65 .. 128 pairs), its 128-column tiles (more
+# than 128 pairs of equal length), and the fused kernel at both tile widths.
+N_FLAG_CASES = 48
+
+
+def draw_flag(i):
+    rng = np.random.default_rng(7000 + i)
+    kind = int(rng.integers(0, 3))
+    if kind == 0:
+        N = int(rng.integers(1, 5))
+        H = int(rng.integers(max(17, 65 // N), 128 // N + 1))
+        lens = [int(x) for x in rng.integers(0, 120, size=N)]
+        if sum(lens) == 0:
+            lens[0] = 5
+        B, T = 1, sum(lens)
+    elif kind == 1:
+        B = int(rng.integers(2, 5))
+        H = int(rng.integers(129 // B + 1, 129 // B + 30))
+        T, lens = int(rng.integers(1, 100)), None
+    else:
+        N = int(rng.integers(1, 6))
+        H = int(rng.integers(8, 70))
+        lens = [int(x) for x in rng.integers(1, 90, size=N)]
+        B, T = 1, sum(lens)
+    path = ("split", "split", "fused")[kind] if rng.random() < 0.8 else None
+    state = str(rng.choice(["bf16", "fp32", "none"]))
+    lb = float(rng.choice([-5.0, -2.0, 0.0]))
+    return dict(B=B, T=T, H=H, lens=lens, path=path, state=state, lb=lb, seed=8000 + i)
+
+
+@pytest.mark.parametrize("i", range(N_FLAG_CASES))
+def test_random_flag_case(i):
+    c = draw_flag(i)
+    say("case flag%d %s" % (i, c))
+    inp = make_inputs(c["B"], c["T"], c["H"], seed=c["seed"], lower_bound=c["lb"],
+                      state_dtype=None if c["state"] == "none" else c["state"],
+                      initial_state=c["state"] != "none", seq_lens=c["lens"])
+    out, fin = run_gpu(inp, path=c["path"], chunk=16 if c["path"] else None)
+    torch.cuda.synchronize()
+    ref_o, ref_f = oracle.kda_fwd(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.scale, inp.A_log, inp.dt_bias,
+                                  inp.lower_bound, initial_state=inp.initial_state_f64(),
+                                  output_final_state=inp.output_final_state, cu_seqlens=inp.cu_seqlens)
+    if inp.B * inp.T > 0:
+        assert_close(to_f64(out), ref_o, "out")
+    if inp.output_final_state:
+        assert_close(to_f64(fin), ref_f, "final_state", inp.state_dtype)
