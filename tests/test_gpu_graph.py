@@ -34,7 +34,7 @@ def make_call(inp, d, kind, out, fin):
         kw["segments"] = 4
         nbytes = kda.segmented_workspace_bytes(inp.B, inp.T, inp.H, inp.N, has_cu, 4)
     else:
-        path = None if kind == "auto" else kind
+        path = {"auto": None, "split_flags": "split", "fused_wide": "fused"}.get(kind, kind)
         kw["path"] = path
         nbytes = kda.workspace_bytes(inp.B, inp.T, inp.H, inp.N, has_cu, None, None, path)
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
@@ -50,6 +50,10 @@ CASES = {
     "auto": dict(B=1, T=300, H=3, state_dtype="fp32", seed=700, seq_lens=ragged_lengths(300, 5)),
     "split": dict(B=2, T=200, H=2, state_dtype="bf16", seed=701),
     "fused": dict(B=1, T=300, H=3, state_dtype="bf16", seed=702, seq_lens=ragged_lengths(300, 5)),
+    # 80 pairs: 64-column recurrence tiles whose waves meet through LDS flags
+    "split_flags": dict(B=1, T=160, H=80, state_dtype="fp32", seed=705),
+    # 150 pairs: the fused kernel's 128-column workgroups
+    "fused_wide": dict(B=1, T=120, H=50, state_dtype="bf16", seed=706, seq_lens=[40, 50, 30]),
     "segmented": dict(B=1, T=2048, H=2, state_dtype="fp32", seed=703),
     "decode": dict(B=64, T=1, H=4, state_dtype="bf16", seed=704),
 }
