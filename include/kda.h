@@ -84,13 +84,13 @@ extern "C" {
 #define KDA_STATUS_BAD_CU_SEQLENS 1 /* cu_seqlens[0] != 0, not monotone, or cu_seqlens[N] != T;
                                        then no token was processed and neither out nor
                                        final_state is written, on every path */
-#define KDA_STATUS_SYNC_TIMEOUT 4   /* a wait between the waves of a recurrence workgroup gave up
-                                       (0.06 to 0.9 s without progress; not expected in operation):
-                                       out and final_state are not meaningful */
 #define KDA_STATUS_OVERFLOW 2       /* the chunk state of some (sequence, head) ended non-finite:
                                        a value outside the fp16 operand range (see "Numerical
                                        range" above) or a non-finite input; out and final_state
                                        of that pair are not meaningful */
+#define KDA_STATUS_SYNC_TIMEOUT 4   /* a wait between the waves of a recurrence or fused workgroup
+                                       gave up (0.06 to 0.9 s without progress; not expected in
+                                       operation): out and final_state are not meaningful */
 
 /* Chunk size of the chunked form (P1 §二 2.1 uses 16). */
 #define KDA_CHUNK 16
@@ -121,8 +121,11 @@ extern "C" {
  * tables and a longest-first work order, then the two stages of P1 §二 2.2:
  * chunk prep (gate activation, L2 norm, in-chunk decay, the L / Mqk matrices
  * and the 16 x 16 unit-lower-triangular inverse) and the chunk recurrence (the
- * chunk-by-chunk delta-rule state update and the output).  kda_fwd leaves
- * the execution path to the library (KDA_PATH_AUTO); kda_fwd_ex selects it.
+ * chunk-by-chunk delta-rule state update and the output).  For B sequences
+ * of T tokens on the split path the tables are a function of the chunk index:
+ * no scheduler kernel runs, the prep kernel computes the entries and writes the
+ * workspace header itself.  kda_fwd leaves the execution path to the library
+ * (KDA_PATH_AUTO); kda_fwd_ex selects it.
  * Without cu_seqlens (B sequences of T tokens, lengths known on the host)
  * kda_fwd also cuts the sequences into segments (kda_fwd_segmented with
  * kda_fwd_segments' count) when that count is above 1 -- few heads and long
