@@ -84,13 +84,13 @@ extern "C" {
 #define KDA_STATUS_BAD_CU_SEQLENS 1 /* cu_seqlens[0] != 0, not monotone, or cu_seqlens[N] != T;
                                        then no token was processed and neither out nor
                                        final_state is written, on every path */
+#define KDA_STATUS_SYNC_TIMEOUT 4   /* a wait between the waves of a recurrence or fused workgroup
+                                       gave up (0.06 to 0.9 s without progress; not expected in
+                                       operation): out and final_state are not meaningful */
 #define KDA_STATUS_OVERFLOW 2       /* the chunk state of some (sequence, head) ended non-finite:
                                        a value outside the fp16 operand range (see "Numerical
                                        range" above) or a non-finite input; out and final_state
                                        of that pair are not meaningful */
-#define KDA_STATUS_SYNC_TIMEOUT 4   /* a wait between the waves of a recurrence or fused workgroup
-                                       gave up (0.06 to 0.9 s without progress; not expected in
-                                       operation): out and final_state are not meaningful */
 
 /* Chunk size of the chunked form (P1 §二 2.1 uses 16). */
 #define KDA_CHUNK 16
