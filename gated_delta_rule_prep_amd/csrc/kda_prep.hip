@@ -142,7 +142,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
 
   const float A2 = -expf(a.A_log[h]) * kLog2e;   // sigmoid(x) = 1 / (1 + 2^(-x log2 e))
   const float lb2 = a.lower_bound * kLog2e;
-  char* const rec_out = a.ws + a.lay.records + ((int64_t)h * a.lay.max_chunks + chunk) * REC_BYTES;
+  char* const rec_out = a.ws + a.lay.records + ((int64_t)chunk * H + h) * REC_BYTES;   // chunk-major
   // staged row r of the three arrays (element e of the current half) and the tail
   _Float16* const st_qh = reinterpret_cast<_Float16*>(sm.half[0][r]);
   _Float16* const st_nk = reinterpret_cast<_Float16*>(sm.half[1][r]);

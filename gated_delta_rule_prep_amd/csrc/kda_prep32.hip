@@ -95,7 +95,7 @@ __global__ __launch_bounds__(kThreads) void prep32_kernel(PrepArgs a) {
 
   const float A2 = -expf(a.A_log[h]) * kLog2e;   // sigmoid(x) = 1 / (1 + 2^(-x log2 e))
   const float lb2 = a.lower_bound * kLog2e;
-  char* rec = a.ws + a.lay.records + ((int64_t)h * a.lay.max_chunks + chunk) * REC32_BYTES;
+  char* rec = a.ws + a.lay.records + ((int64_t)chunk * a.H + h) * REC32_BYTES;   // chunk-major
   _Float16* rec_qh = reinterpret_cast<_Float16*>(rec + REC32_QH) + t * K;
   _Float16* rec_kb = reinterpret_cast<_Float16*>(rec + REC32_KB) + t * K;
   float* rec_gam = reinterpret_cast<float*>(rec + REC32_GAM);

@@ -186,7 +186,9 @@ __global__ __launch_bounds__((Tile<WC, LD>::kThreads)) void recur_kernel(RecurAr
   const int n = a.fixed_T > 0 ? (int)slot_id : reinterpret_cast<const int32_t*>(a.ws + a.lay.order)[slot_id];
   const SeqEntry se = a.fixed_T > 0 ? fixed_seq(a.fixed_T, C, n)
                                     : reinterpret_cast<const SeqEntry*>(a.ws + a.lay.seq_table)[n];
-  const char* recs = a.ws + a.lay.records + ((int64_t)h * a.lay.max_chunks + se.first_chunk) * REC_BYTES;
+  // Records are chunk-major: record (chunk c, head h) at (c H + h) REC_BYTES,
+  // so the chunks of one head lie H records apart.
+  const char* recs = a.ws + a.lay.records + ((int64_t)se.first_chunk * H + h) * REC_BYTES;
   const int nch = se.nchunks;
   // This launch covers the chunks whose first token row lies in [row_lo,
   // row_hi): chunks ci_lo .. ci_hi - 1 of the sequence.  The state comes from
@@ -257,7 +259,7 @@ __global__ __launch_bounds__((Tile<WC, LD>::kThreads)) void recur_kernel(RecurAr
     const auto issue = [&](int st) {
       const int c = ci_lo + st;
       const int len = min(se.len - C * c, C);
-      const i32x4 rrec = buf_rsrc(recs + (int64_t)c * REC_BYTES, REC_BYTES);
+      const i32x4 rrec = buf_rsrc(recs + (int64_t)c * H * REC_BYTES, REC_BYTES);
       const i32x4 rval = buf_rsrc(vseq + (int64_t)c * C * row_bytes, alt ? 0 : (len - 1) * row_bytes + 2 * Tl::kCols);
       const uint32_t slot = ring0 + (uint32_t)((st % Tl::kSlots) * Tl::kSlotBytes);
 #pragma unroll

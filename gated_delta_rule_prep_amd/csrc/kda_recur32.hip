@@ -254,7 +254,8 @@ __global__ __launch_bounds__(kThreads) void recur32_kernel(RecurArgs a) {
   const int32_t* order = reinterpret_cast<const int32_t*>(a.ws + a.lay.order);
   const int n = order[slot_id];
   const SeqEntry se = reinterpret_cast<const SeqEntry*>(a.ws + a.lay.seq_table)[n];
-  const char* recs = a.ws + a.lay.records + ((int64_t)h * a.lay.max_chunks + se.first_chunk) * REC32_BYTES;
+  // Records are chunk-major: record (chunk c, head h) at (c H + h) REC32_BYTES.
+  const char* recs = a.ws + a.lay.records + ((int64_t)se.first_chunk * H + h) * REC32_BYTES;
   const int nch = se.nchunks;
   // Chunks whose first token row lies in [row_lo, row_hi), with the state
   // handed over between parts as in the 16-token kernel.
@@ -301,7 +302,7 @@ __global__ __launch_bounds__(kThreads) void recur32_kernel(RecurArgs a) {
     const auto issue = [&](int st) {
       const int c = ci_lo + st;
       const int len = min(se.len - CC * c, CC);
-      const i32x4 rrec = buf_rsrc(recs + (int64_t)c * REC32_BYTES, REC32_BYTES);
+      const i32x4 rrec = buf_rsrc(recs + (int64_t)c * H * REC32_BYTES, REC32_BYTES);
       const i32x4 rval = buf_rsrc(vseq + (int64_t)c * CC * row_bytes, (len - 1) * row_bytes + 2 * Cf::kCols);
       const uint32_t slot = ring0 + (uint32_t)((st % kSlots) * Cf::kSlotBytes);
 #pragma unroll

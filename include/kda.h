@@ -396,8 +396,8 @@ int kda_fwd_check_status(const void* workspace, hipStream_t stream, int* status)
  * offsets[1] = per-sequence table (int32 quadruples {first chunk, chunk count,
  *              first token row, length}),
  * offsets[2] = work order (int32 [N], sequences longest first),
- * offsets[3] = chunk records, head-major: record (h, c) at
- *              offsets[3] + (h * offsets[5] + c) * offsets[4],
+ * offsets[3] = chunk records, chunk-major: record (chunk c, head h) at
+ *              offsets[3] + (c * H + h) * offsets[4],
  * offsets[4] = bytes per record, offsets[5] = chunk capacity (floor(B*T/chunk) + N),
  * offsets[6] = total bytes.  Returns KDA_OK or KDA_EINVAL.
  * Record layout for chunk 16 (bytes): [0, 4096) Qhat fp16 [16][128]; [4096, 8192) -Khat fp16

@@ -95,7 +95,7 @@ def test_chunk_table_and_records_match_chunked_form(C):
             kn = kk / np.sqrt((kk * kk).sum(-1, keepdims=True) + EPS)
             qn = inp.scale * qq / np.sqrt((qq * qq).sum(-1, keepdims=True) + EPS)
             P = chunked_ref.chunk_pieces(qn, kn, a, 1 / (1 + np.exp(-bf[sl, h])))
-            off = lay["records"] + (h * lay["max_chunks"] + ci) * R
+            off = lay["records"] + (ci * H + h) * R   # chunk-major
             full = decode_record(buf[off:off + R], C)
             got = {k: (v if k == "gamma" else v[:ln, :ln] if k in ("T", "M") else v[:ln]) for k, v in full.items()}
             ref = dict(Qh=P["Qh"], Kb=P["Kb"], T=P["T"], M=P["M"], gamma=P["gamma"])
