@@ -143,39 +143,41 @@ __host__ __device__ inline int recur_tiles(int64_t pairs, bool equal_lengths) {
 // squares fit to kernel times measured on the box at K = V = 128 over 36
 // batches of 8192 tokens (1 .. 128 sequences of 64 .. 8192 tokens, and 12
 // ragged ones; H = 16, 32, 64, 96), with which the choice matches the faster
-// path in all of them but one tie:
-//   split: the prep kernel streams inputs and records at about 5.7 ns per
-//     (chunk, head).  A recurrence workgroup costs about 15.6 us to start and
-//     end (tables, state, the first chunk's latency) plus 0.35 / 0.51 / 1.0 us
+// path in all of them but one tie (1.6 %).  The model is empirical: each
+// constant is what the fit gave, not a measured quantity on its own.
+//   split: the prep kernel streams inputs and records at about 5.5 ns per
+//     (chunk, head).  A recurrence workgroup costs about 13.4 us to start and
+//     end (tables, state, the first chunk's latency) plus 0.37 / 0.56 / 1.0 us
 //     per step with 32 / 64 / 128 columns; the recurrence is the longest chain
 //     or, with more workgroups than CUs, throughput: two 64-column workgroups
-//     share a CU, at 3.5 us of start per workgroup and 0.66 us per step and
-//     tile of CU time;
-//   fused: a workgroup step takes 1.71 us (64 columns, two workgroups per
-//     pair) or 2.08 us (128 columns), each sequence takes five pipeline steps
-//     more than its chunk count plus 3.3 us, and the work spreads over the
+//     share a CU, at 3.76 us of start per workgroup and 0.64 us per step and
+//     tile of CU time, the chain then at 0.47 us per step;
+//   fused: a workgroup step costs 1.75 us (64 columns, two workgroups per
+//     pair) or 2.20 us (128 columns) of CU time, and the longest sequence's
+//     chain 1.60 / 1.88 us per step; each sequence takes five pipeline steps
+//     more than its chunk count plus 1.75 us, and the work spreads over the
 //     CUs, one workgroup per CU.
 __host__ __device__ inline double recur_estimate(int64_t H, int64_t N, int64_t total, int64_t maxc,
                                                  bool equal_lengths) {
   const double chunk_heads = (double)total * (double)H, pairs = (double)N * (double)H;
   const int tiles = recur_tiles(N * H, equal_lengths);
-  const double step = tiles == 4 ? 0.35 : tiles == 2 ? 0.51 : 1.0;
-  const double chain = 15.6 + step * (double)maxc;
+  const double step = tiles == 4 ? 0.37 : tiles == 2 ? 0.56 : 1.0;
+  const double chain = 13.4 + step * (double)maxc;
   if (tiles * pairs <= kCUs) return chain;
-  if (tiles == 2) return fmax(chain, 2.0 * (3.5 * pairs + 0.66 * chunk_heads) / kCUs);
-  return fmax(chain, (15.6 * pairs + step * chunk_heads) / kCUs);
+  if (tiles == 2) return fmax(13.4 + 0.47 * (double)maxc, 2.0 * (3.76 * pairs + 0.64 * chunk_heads) / kCUs);
+  return fmax(chain, (13.4 * pairs + step * chunk_heads) / kCUs);
 }
 
 __host__ __device__ inline double fused_estimate(int64_t H, int64_t N, int64_t total, int64_t maxc) {
   const double chunk_heads = (double)total * (double)H, pairs = (double)N * (double)H;
   const bool two = fused_two_tiles(N * H);
-  const double step = two ? 1.71 : 2.08;
-  const double chain = 3.3 + step * (double)(maxc + 5);
-  return fmax(chain, (two ? 2.0 : 1.0) * (3.3 * pairs + step * (chunk_heads + 5.0 * pairs)) / kCUs);
+  const double step = two ? 1.75 : 2.20, chain_step = two ? 1.60 : 1.88;
+  const double chain = 1.75 + chain_step * (double)(maxc + 5);
+  return fmax(chain, (two ? 2.0 : 1.0) * (1.75 * pairs + step * (chunk_heads + 5.0 * pairs)) / kCUs);
 }
 
 __host__ __device__ inline int choose_path(int64_t H, int64_t N, int64_t total, int64_t maxc, bool equal_lengths) {
-  const double split = 5.7e-3 * (double)total * (double)H + recur_estimate(H, N, total, maxc, equal_lengths);
+  const double split = 5.5e-3 * (double)total * (double)H + recur_estimate(H, N, total, maxc, equal_lengths);
   return fused_estimate(H, N, total, maxc) < split ? KDA_PATH_FUSED : KDA_PATH_SPLIT;
 }
 
