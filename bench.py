@@ -167,7 +167,7 @@ def load_traffic():
     return {e["workload"]: e["kernels"] for e in entries if e.get("source_hash") == cur}
 
 
-CUS = 256
+CUS = 256   # compute units of a whole MI355X; main() reads the device's own count
 
 
 def sequential_steps(inp, res):
@@ -363,6 +363,8 @@ def main():
     sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
     from tests.kda_gpu import device_inputs
 
+    global CUS
+    CUS = torch.cuda.get_device_properties(0).multi_processor_count or CUS
     cfgs = configs()
     R = max(1, args.repeats)
     if args.only == "decode":

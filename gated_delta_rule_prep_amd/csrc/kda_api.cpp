@@ -43,6 +43,7 @@ bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) !=
 // Device capability cache: -1 unknown, 0 unsupported, 1 gfx950.
 constexpr int kMaxDevices = 64;
 int g_dev_ok[kMaxDevices];
+int g_dev_cus[kMaxDevices];   // compute units, 0 until read
 std::once_flag g_dev_once;
 
 int check_device(int* dev_out = nullptr) {
@@ -122,6 +123,17 @@ namespace kda {
 
 namespace {
 std::atomic<int> g_spin_limit{kSpinLimit};
+}
+
+int device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return kCUs;
+  int c = __atomic_load_n(&g_dev_cus[dev], __ATOMIC_ACQUIRE);
+  if (c <= 0) {
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) return kCUs;
+    __atomic_store_n(&g_dev_cus[dev], c, __ATOMIC_RELEASE);
+  }
+  return c;
 }
 
 int spin_limit() { return g_spin_limit.load(std::memory_order_relaxed); }
@@ -246,11 +258,12 @@ bool seg_layout(int64_t B, int64_t T, int64_t H, int64_t N, int S, SegLayout* L)
 // most 128 (segment, head) chains and segments of at least 512 tokens; below
 // four segments the three recurrence passes cost more than they save.  With
 // cu_seqlens the mean length stands in for the lengths, which only the device
-// knows.
+// knows.  (128 chains on the 256 CUs of a whole MI355X: half the CU count.)
 int choose_segments(int64_t B, int64_t T, int64_t H, int64_t N, bool has_cu) {
   const int64_t len = has_cu ? (B * T) / (N > 0 ? N : 1) : T;
+  const int64_t max_chains = kda::device_cus() / 2;
   int64_t S = 1;
-  while (2 * S * N * H <= 128 && len / (2 * S) >= 512 && 2 * S <= 4096) S *= 2;
+  while (2 * S * N * H <= max_chains && len / (2 * S) >= 512 && 2 * S <= 4096) S *= 2;
   return S >= 4 ? (int)S : 1;
 }
 
@@ -369,10 +382,11 @@ static int fwd_impl(const void* q, const void* k, const void* v, const void* g, 
     // With cu_seqlens only the device knows the lengths: both paths are
     // enqueued and the scheduler kernel picks (the other path's kernels exit
     // at once).  B sequences of T tokens: the host picks and enqueues one.
+    const int cus = kda::device_cus();
     int host_pick = -1;
     if (both && cu_seqlens == nullptr) {
       const int64_t nc = (T + kda::C - 1) / kda::C;
-      host_pick = kda::choose_path(H, B, B * nc, nc, true);
+      host_pick = kda::choose_path(H, B, B * nc, nc, true, cus);
     }
     const bool run_split = !both || host_pick != KDA_PATH_FUSED;
     const bool run_fused = both && host_pick != KDA_PATH_SPLIT;
@@ -401,6 +415,7 @@ static int fwd_impl(const void* q, const void* k, const void* v, const void* g, 
       rec(0);
       if (e == hipSuccess) {
         kda::SchedArgs sa{cu_seqlens, N, B, T, H, 1, B * T > 0 ? B * T : 1, KDA_PATH_FUSED, ws, L};
+        sa.cus = cus;
         e = kda::launch_sched(sa, stream);
       }
       rec(1);
@@ -412,6 +427,7 @@ static int fwd_impl(const void* q, const void* k, const void* v, const void* g, 
                           static_cast<const uint16_t*>(beta), static_cast<uint16_t*>(out), A_log, dt_bias, scale,
                           lower_bound, initial_state, final_state,
                           initial_state ? initial_state_dtype : final_state_dtype, N, H, ws, L};
+        fa.cus = cus;
         e = kda::launch_fused(fa, stream);
       }
       if (e == hipSuccess && ev) e = hipEventRecord(ev[3], stream);
@@ -447,6 +463,7 @@ static int fwd_impl(const void* q, const void* k, const void* v, const void* g, 
     if (e == hipSuccess && !fixed) {
       kda::SchedArgs sa{cu_seqlens, N, B, T, H, P, part_rows,
                         both ? (host_pick >= 0 ? host_pick : KDA_PATH_AUTO) : KDA_PATH_SPLIT, ws, L};
+      sa.cus = cus;
       e = kda::launch_sched(sa, stream);
     }
     rec(1, stream);
@@ -475,7 +492,8 @@ static int fwd_impl(const void* q, const void* k, const void* v, const void* g, 
       kda::RecurArgs ra{static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out), initial_state, final_state,
                         sdt, N, H, p, lo, hi, ws, L};
       ra.precision = precision;
-      ra.tiles = kda::recur_tiles(N * H, cu_seqlens == nullptr);
+      ra.tiles = kda::recur_tiles(N * H, cu_seqlens == nullptr, cus);
+      ra.cus = cus;
       if (fixed) ra.fixed_T = T;
       rec(2 + 2 * P + 2 * p, rstream);
       if (e == hipSuccess && run_split) e = kda::launch_recur(ra, rstream);
@@ -492,6 +510,7 @@ static int fwd_impl(const void* q, const void* k, const void* v, const void* g, 
                           static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(g),
                           static_cast<const uint16_t*>(beta), static_cast<uint16_t*>(out), A_log, dt_bias, scale,
                           lower_bound, initial_state, final_state, sdt, N, H, ws, L};
+        fa.cus = cus;
         e = kda::launch_fused(fa, stream);
       }
       rec(7, stream);
@@ -747,8 +766,10 @@ int kda_fwd_segmented(const void* q, const void* k, const void* v, const void* g
     if (e != hipSuccess) return fail(KDA_EHIP, "kda: segment launch: %s", hipGetErrorString(e));
     // The segments' chunk records: scheduler and chunk prep of the split path.
     char* const iws = ws + SL.inner;
-    e = kda::launch_sched(kda::SchedArgs{seg_cu, NS_, 1, rows, H, 1, rows > 0 ? rows : 1, KDA_PATH_SPLIT, iws, L},
-                          stream);
+    const int cus = kda::device_cus();
+    kda::SchedArgs sa{seg_cu, NS_, 1, rows, H, 1, rows > 0 ? rows : 1, KDA_PATH_SPLIT, iws, L};
+    sa.cus = cus;
+    e = kda::launch_sched(sa, stream);
     if (e == hipSuccess)
       e = kda::launch_prep(kda::PrepArgs{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                          static_cast<const uint16_t*>(g), static_cast<const uint16_t*>(beta), A_log,
@@ -760,6 +781,7 @@ int kda_fwd_segmented(const void* q, const void* k, const void* v, const void* g
     if (e == hipSuccess) {
       kda::RecurArgs ra{static_cast<const uint16_t*>(v), nullptr, nullptr, Bm, KDA_DTYPE_FP32, NS_, H, 0, 0,
                         INT64_MAX / 2, iws, L, 2, Am};
+      ra.cus = cus;
       e = kda::launch_recur(ra, stream);
     }
     if (e != hipSuccess) return fail(KDA_EHIP, "kda: launch: %s", hipGetErrorString(e));
@@ -771,6 +793,7 @@ int kda_fwd_segmented(const void* q, const void* k, const void* v, const void* g
     // the outputs, every segment from its true start
     kda::RecurArgs ro{static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out), starts, nullptr,
                       KDA_DTYPE_FP32, NS_, H, 0, 0, INT64_MAX / 2, iws, L};
+    ro.cus = cus;
     e = kda::launch_recur(ro, stream);
     if (e != hipSuccess) return fail(KDA_EHIP, "kda: recurrence launch: %s", hipGetErrorString(e));
     return KDA_OK;

@@ -606,7 +606,7 @@ hipError_t launch_tiles(const FusedArgs& a, hipStream_t s) {
 // per pair would not all fit on the 256 CUs at once.
 hipError_t launch_fused(const FusedArgs& a, hipStream_t s) {
   if (a.N * a.H == 0) return hipSuccess;
-  if (fused_two_tiles(a.N * a.H)) return launch_tiles<1, 4>(a, s);
+  if (fused_two_tiles(a.N * a.H, a.cus)) return launch_tiles<1, 4>(a, s);
   return launch_tiles<2, 3>(a, s);
 }
 

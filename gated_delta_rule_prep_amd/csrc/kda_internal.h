@@ -106,6 +106,12 @@ bool layout_for(int64_t B, int64_t T, int64_t H, int64_t N, int chunk, Layout* o
 int parts_for(int64_t rows);   // parts used for B*T token rows when the caller does not choose
 int default_chunk();           // chunk size used when the caller does not choose
 
+// Compute units of a whole MI355X.  The launch shapes and the path estimate
+// take the current device's own count (device_cus: a partitioned MI355X
+// exposes fewer), kCUs only where it cannot be read.
+constexpr int kCUs = 256;
+int device_cus();   // host only
+
 struct SchedArgs {
   const int64_t* cu;    // device, N + 1 entries, or nullptr
   int64_t N, B, T, H;
@@ -114,25 +120,24 @@ struct SchedArgs {
   int path;             // KDA_PATH_SPLIT / KDA_PATH_FUSED, or KDA_PATH_AUTO: choose from the lengths
   char* ws;
   Layout lay;
+  int cus = kCUs;       // compute units of the device (for the path estimate)
 };
-
-constexpr int kCUs = 256;   // compute units of an MI355X
 
 // Fused-kernel value-column tiling: 64 columns per workgroup (two per
 // (sequence, head)) while two tiles per pair fit on the CUs at once, else 128.
 // (A workgroup takes most of a CU's LDS, so workgroups beyond the CU count
 // wait for a second round: 2 x 4096 tokens, H = 96, 0.866 ms with 384
 // workgroups of 64 columns against 0.513 with 192 of 128.)
-inline __host__ __device__ bool fused_two_tiles(int64_t pairs) { return 2 * pairs <= kCUs; }
+inline __host__ __device__ bool fused_two_tiles(int64_t pairs, int cus) { return 2 * pairs <= cus; }
 
 // The recurrence's value tiles per (sequence, head) for `pairs` chains (the
 // sequence-head pairs of the launch): 4 while that still gives one workgroup
 // per CU, else 2; 1 when the sequences are known to be of equal length and
 // two tiles per pair would not fit on the CUs at once (then throughput, not
 // the longest chain, bounds the launch).
-__host__ __device__ inline int recur_tiles(int64_t pairs, bool equal_lengths) {
-  if (4 * pairs <= kCUs) return 4;
-  if (2 * pairs <= kCUs || !equal_lengths) return 2;
+__host__ __device__ inline int recur_tiles(int64_t pairs, bool equal_lengths, int cus) {
+  if (4 * pairs <= cus) return 4;
+  if (2 * pairs <= cus || !equal_lengths) return 2;
   return 1;
 }
 
@@ -158,27 +163,28 @@ __host__ __device__ inline int recur_tiles(int64_t pairs, bool equal_lengths) {
 //     more than its chunk count plus 1.75 us, and the work spreads over the
 //     CUs, one workgroup per CU.
 __host__ __device__ inline double recur_estimate(int64_t H, int64_t N, int64_t total, int64_t maxc,
-                                                 bool equal_lengths) {
+                                                 bool equal_lengths, int cus) {
   const double chunk_heads = (double)total * (double)H, pairs = (double)N * (double)H;
-  const int tiles = recur_tiles(N * H, equal_lengths);
+  const int tiles = recur_tiles(N * H, equal_lengths, cus);
   const double step = tiles == 4 ? 0.37 : tiles == 2 ? 0.56 : 1.0;
   const double chain = 13.4 + step * (double)maxc;
-  if (tiles * pairs <= kCUs) return chain;
-  if (tiles == 2) return fmax(13.4 + 0.47 * (double)maxc, 2.0 * (3.76 * pairs + 0.64 * chunk_heads) / kCUs);
-  return fmax(chain, (13.4 * pairs + step * chunk_heads) / kCUs);
+  if (tiles * pairs <= cus) return chain;
+  if (tiles == 2) return fmax(13.4 + 0.47 * (double)maxc, 2.0 * (3.76 * pairs + 0.64 * chunk_heads) / cus);
+  return fmax(chain, (13.4 * pairs + step * chunk_heads) / cus);
 }
 
-__host__ __device__ inline double fused_estimate(int64_t H, int64_t N, int64_t total, int64_t maxc) {
+__host__ __device__ inline double fused_estimate(int64_t H, int64_t N, int64_t total, int64_t maxc, int cus) {
   const double chunk_heads = (double)total * (double)H, pairs = (double)N * (double)H;
-  const bool two = fused_two_tiles(N * H);
+  const bool two = fused_two_tiles(N * H, cus);
   const double step = two ? 1.75 : 2.20, chain_step = two ? 1.60 : 1.88;
   const double chain = 1.75 + chain_step * (double)(maxc + 5);
-  return fmax(chain, (two ? 2.0 : 1.0) * (1.75 * pairs + step * (chunk_heads + 5.0 * pairs)) / kCUs);
+  return fmax(chain, (two ? 2.0 : 1.0) * (1.75 * pairs + step * (chunk_heads + 5.0 * pairs)) / cus);
 }
 
-__host__ __device__ inline int choose_path(int64_t H, int64_t N, int64_t total, int64_t maxc, bool equal_lengths) {
-  const double split = 5.5e-3 * (double)total * (double)H + recur_estimate(H, N, total, maxc, equal_lengths);
-  return fused_estimate(H, N, total, maxc) < split ? KDA_PATH_FUSED : KDA_PATH_SPLIT;
+__host__ __device__ inline int choose_path(int64_t H, int64_t N, int64_t total, int64_t maxc, bool equal_lengths,
+                                           int cus) {
+  const double split = 5.5e-3 * (double)total * (double)H + recur_estimate(H, N, total, maxc, equal_lengths, cus);
+  return fused_estimate(H, N, total, maxc, cus) < split ? KDA_PATH_FUSED : KDA_PATH_SPLIT;
 }
 
 
@@ -225,7 +231,7 @@ struct RecurArgs {
   // 0 is the library's own arithmetic.
   int precision;
   // Value tiles per (sequence, head) for 16-token chunks: 1, 2 or 4 (128, 64
-  // or 32 columns per workgroup), or 0 for recur_tiles(pairs, false).
+  // or 32 columns per workgroup), or 0 for recur_tiles(pairs, false, cus).
   int tiles;
   // > 0: N sequences of fixed_T tokens with no scheduler tables (the prep
   // kernel wrote the header): sequence entries from fixed_seq, order = index
@@ -233,6 +239,7 @@ struct RecurArgs {
   // Polls after which a wait between the waves of a workgroup gives up (set
   // by the launch from spin_limit()).
   int spin_limit = 0;
+  int cus = kCUs;       // compute units of the device (launch shape)
 };
 
 // Waits between the waves of a recurrence or fused workgroup give up after
@@ -263,6 +270,7 @@ struct FusedArgs {
   // Polls after which a wait between the waves of a workgroup gives up (set
   // by the launch from spin_limit()).
   int spin_limit = 0;
+  int cus = kCUs;       // compute units of the device (launch shape)
 };
 
 // Segmented forward: segment boundaries and the prefix over the segments'

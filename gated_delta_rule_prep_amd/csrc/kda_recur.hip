@@ -443,8 +443,8 @@ hipError_t launch_recur(const RecurArgs& a, hipStream_t s) {
   if (pairs == 0) return hipSuccess;
   if (a.precision < 0 || a.precision > 7) return hipErrorInvalidValue;
   if (a.precision != 0) return launch_variant<1>(a, pairs, s);
-  const int tiles = a.tiles > 0 ? a.tiles : recur_tiles(pairs, false);
-  const bool shared = tiles * pairs > kCUs;   // more workgroups than CUs
+  const int tiles = a.tiles > 0 ? a.tiles : recur_tiles(pairs, false, a.cus);
+  const bool shared = tiles * pairs > a.cus;   // more workgroups than CUs
   switch (tiles) {
     case 4: return launch_tiles<2, 6, 0>(a, pairs, s);   // (4 tiles only while 4 * pairs <= 256)
     case 2: return shared ? launch_tiles<4, 2, 0>(a, pairs, s) : launch_tiles<4, 4, 0>(a, pairs, s);

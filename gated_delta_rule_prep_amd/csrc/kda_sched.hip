@@ -156,7 +156,7 @@ __global__ __launch_bounds__(kThreads) void sched_kernel(SchedArgs a) {
   if (tid == 0) {
     hdr->status = bad ? KDA_STATUS_BAD_CU_SEQLENS : KDA_STATUS_OK;
     hdr->chunk_count = total;
-    hdr->path = a.path == KDA_PATH_AUTO ? choose_path(a.H, N, total, s_maxc, a.cu == nullptr) : a.path;
+    hdr->path = a.path == KDA_PATH_AUTO ? choose_path(a.H, N, total, s_maxc, a.cu == nullptr, a.cus) : a.path;
   }
 }
 
