@@ -291,7 +291,19 @@ def cpu_baseline(cfg, heads: int):
     th = inp.B * inp.T * heads
     return dict(value=round(th / dt, 1), unit="token·heads/s", cores=threads, kind="oracle",
                 sample="%s, heads 0..%d of %d, all %d tokens (%d token-heads), fp64 token-by-token, %.2f s wall"
-                % (cfg.name, heads - 1, inp.H, inp.T, th, dt))
+                % (cfg.name, heads - 1, inp.H, inp.T, th, dt), cpu_model=cpu_model())
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (first 'model name' line of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def copy_for_counters(torch, mib):
