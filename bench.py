@@ -318,6 +318,28 @@ def copy_for_counters(torch, mib):
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copies": 3}))
 
 
+def copy_bandwidth(torch, mib=1024, reps=20):
+    """The box's device-to-device copy rate (read + written bytes per second,
+    torch's copy of `mib` MiB, median of `reps` event-timed copies): the
+    practical streaming ceiling the kernels are read against."""
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    ts = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        b.synchronize()
+        ts.append(a.elapsed_time(b))
+    ms = sorted(ts)[len(ts) // 2]
+    del src, dst
+    return {"GB_per_s": round(2 * n / ms / 1e6, 1), "bytes_copied": n, "ms": round(ms, 4)}
+
+
 def workload_entry(cfg, runs, paths, traffic):
     """One workload's entry of the JSON line: the library's choice (runs[0])
     with its roofline, per-kernel times and us per chunk step, and every
@@ -443,6 +465,7 @@ def main():
         "segmented_8192x4": segmented,
         "status_ok": all(e["status"] == 0 for e in entries) and segmented["status_ok"],
         "cpu_baseline": cpu,
+        "hbm_copy": copy_bandwidth(torch),
     }
     print(json.dumps(line), flush=True)
 
