@@ -25,7 +25,7 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-Wall", "-Wno-u
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-mllvm", "-amdgpu-mfma-vgpr-form=1",
          "-I", os.path.join(ROOT, "include"), "-I", CSRC]
-SOURCES = ["kda_api.cpp", "kda_sched.hip", "kda_prep.hip", "kda_recur.hip", "kda_prep32.hip", "kda_recur32.hip", "kda_fused.hip", "kda_segment.hip",
+SOURCES = ["kda_api.cpp", "kda_sched.hip", "kda_prep.hip", "kda_recur.hip", "kda_prep32.hip", "kda_recur32.hip", "kda_prep64.hip", "kda_recur64.hip", "kda_fused.hip", "kda_segment.hip",
            "kda_decode.hip"]
 
 

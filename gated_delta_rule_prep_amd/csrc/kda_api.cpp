@@ -139,8 +139,8 @@ int device_cus() {
 int spin_limit() { return g_spin_limit.load(std::memory_order_relaxed); }
 
 bool layout_for(int64_t B, int64_t T, int64_t H, int64_t N, int chunk, Layout* L) {
-  if (B < 1 || T < 0 || H < 1 || N < 0 || (chunk != C && chunk != C32)) return false;
-  const int64_t rec_bytes = chunk == C ? REC_BYTES : REC32_BYTES;
+  if (B < 1 || T < 0 || H < 1 || N < 0 || (chunk != C && chunk != C32 && chunk != C64)) return false;
+  const int64_t rec_bytes = chunk == C ? REC_BYTES : chunk == C32 ? REC32_BYTES : REC64_BYTES;
   const int64_t max_chunks = (B * T) / chunk + N;   // sum_n ceil(len_n / chunk) <= B*T/chunk + N
   int64_t off = sizeof(WsHeader);
   L->chunk_table = off;
@@ -203,7 +203,7 @@ namespace {
 // only known on the device.  The library chooses only where both paths can run
 // (16-token chunks, one part).
 int resolve_path(int chunk, int parts, int path) {
-  if (chunk != 0 && chunk != kda::C && chunk != kda::C32) return -1;
+  if (chunk != 0 && chunk != kda::C && chunk != kda::C32 && chunk != kda::C64) return -1;
   if (parts < 0) return -1;
   const bool fusable = (chunk == 0 || chunk == kda::C) && parts <= 1;
   if (path == KDA_PATH_AUTO) return fusable ? KDA_PATH_AUTO : KDA_PATH_SPLIT;
@@ -301,7 +301,8 @@ int kda_workspace_layout(int64_t B, int64_t T, int64_t H, int64_t num_seqs, int 
                          int64_t offsets[7]) {
   int64_t N = 0;
   if (offsets == nullptr) return fail(KDA_EINVAL, "kda: offsets is NULL");
-  if (chunk != kda::C && chunk != kda::C32) return fail(KDA_EINVAL, "kda: chunk must be 16 or 32 (got %d)", chunk);
+  if (chunk != kda::C && chunk != kda::C32 && chunk != kda::C64)
+    return fail(KDA_EINVAL, "kda: chunk must be 16, 32 or 64 (got %d)", chunk);
   int rc = check_sizes(B, T, H, kda::K, kda::V, nullptr, num_seqs, has_cu_seqlens, &N);
   if (rc != KDA_OK) return rc;
   kda::Layout L;
@@ -332,7 +333,8 @@ static int validate_common(const void* q, const void* k, const void* g, const vo
   if (!std::isfinite(scale)) return fail(KDA_EINVAL, "kda: scale is not finite");
   if (!std::isfinite(lower_bound) || lower_bound < -5.0f || lower_bound > 0.0f)
     return fail(KDA_EINVAL, "kda: lower_bound must lie in [-5, 0] (got %g)", (double)lower_bound);
-  if (chunk != kda::C && chunk != kda::C32) return fail(KDA_EINVAL, "kda: chunk must be 16 or 32 (got %d)", chunk);
+  if (chunk != kda::C && chunk != kda::C32 && chunk != kda::C64)
+    return fail(KDA_EINVAL, "kda: chunk must be 16, 32 or 64 (got %d)", chunk);
   if (!(fused ? kda::layout_fused(B, T, H, *N, L) : kda::layout_for(B, T, H, *N, chunk, L)))
     return fail(KDA_EINVAL, "kda: bad sizes");
   if (!workspace) return fail(KDA_EINVAL, "kda: workspace is NULL");
@@ -371,8 +373,8 @@ static int fwd_impl(const void* q, const void* k, const void* v, const void* g, 
     if (initial_state && final_state && initial_state_dtype != final_state_dtype)
       return fail(KDA_EDTYPE, "kda: initial_state and final_state dtypes differ");
     if (parts_req < 0) return fail(KDA_EINVAL, "kda: parts must be >= 0 (got %d)", parts_req);
-    if (chunk_req != 0 && chunk_req != kda::C && chunk_req != kda::C32)
-      return fail(KDA_EINVAL, "kda: chunk must be 0, 16 or 32 (got %d)", chunk_req);
+    if (chunk_req != 0 && chunk_req != kda::C && chunk_req != kda::C32 && chunk_req != kda::C64)
+      return fail(KDA_EINVAL, "kda: chunk must be 0, 16, 32 or 64 (got %d)", chunk_req);
     const int path = resolve_path(chunk_req, parts_req, path_req);
     if (path < 0)
       return fail(KDA_EINVAL, "kda: path %d cannot run chunk=%d with parts=%d (the fused path takes 16-token "

@@ -11,6 +11,7 @@ namespace kda {
 
 constexpr int C = 16;     // chunk size of the 16-token kernels (tokens per chunk)
 constexpr int C32 = 32;   // chunk size of the 32-token kernels
+constexpr int C64 = 64;   // chunk size of the 64-token kernels
 constexpr int K = 128;    // key channels
 constexpr int V = 128;    // value channels
 
@@ -40,6 +41,20 @@ constexpr int REC32_T = 24576;     // T     fp16 [32][32], row-major, columns in
 constexpr int REC32_MQK = 26624;   // Mqk   fp16 [32][32], row-major, columns in kPermCh order
 constexpr int REC32_GAM = 28672;   // gamma fp32 [128], channel c at slot kGamSlot(c)
 constexpr int REC32_BYTES = 29184;
+
+// Chunk record of the 64-token kernels, one per (chunk, head), chunk-major.
+// Qhat, -W and Kbar as in the 32-token record with 64 token rows.  T and Mqk
+// (64 x 64) are stored as 8 blocks of 16 rows x 32 columns, block (t, u) =
+// rows 16t .. 16t + 15, token columns 32u .. 32u + 31 in kPermCh order, at
+// (2t + u) x 1024 bytes, so the 16-byte operand pieces of one MFMA are one
+// contiguous kilobyte.  The blocks above the diagonal (t < 2u) hold zeros.
+constexpr int REC64_QH = 0;        // Qhat  fp16 [64][128], channels in kPermCh order per 32-block
+constexpr int REC64_NW = 16384;    // -W    fp16 [64][128], same channel order
+constexpr int REC64_KB = 32768;    // Kbar  fp16 [64][128], token-major, natural channel order
+constexpr int REC64_T = 49152;     // T     fp16, 8 blocks [16][32] as above
+constexpr int REC64_MQK = 57344;   // Mqk   fp16, 8 blocks [16][32] as above
+constexpr int REC64_GAM = 65536;   // gamma fp32 [128], channel c at slot kGamSlot(c)
+constexpr int REC64_BYTES = 66048;
 
 // Slot of channel c = 64 r + 16 a + 4 b + i in the stored gamma: lane
 // L = 16 b + 4 a + i of a recurrence wave reads slots 2L and 2L + 1 (r = 0, 1),
@@ -93,7 +108,7 @@ struct Layout {
   int64_t chunk_table;  // byte offsets into the workspace
   int64_t seq_table;
   int64_t order;
-  int64_t chunk;        // tokens per chunk: C or C32
+  int64_t chunk;        // tokens per chunk: C, C32 or C64
   int64_t records;
   int64_t rec_bytes;
   int64_t max_chunks;
@@ -101,7 +116,7 @@ struct Layout {
   int64_t total;
 };
 
-// Returns false if the sizes or the chunk size (C or C32) are invalid.
+// Returns false if the sizes or the chunk size (C, C32 or C64) are invalid.
 bool layout_for(int64_t B, int64_t T, int64_t H, int64_t N, int chunk, Layout* out);
 int parts_for(int64_t rows);   // parts used for B*T token rows when the caller does not choose
 int default_chunk();           // chunk size used when the caller does not choose
@@ -324,5 +339,7 @@ hipError_t launch_prep(const PrepArgs& a, hipStream_t s);
 hipError_t launch_recur(const RecurArgs& a, hipStream_t s);
 hipError_t launch_prep32(const PrepArgs& a, hipStream_t s);
 hipError_t launch_recur32(const RecurArgs& a, hipStream_t s);
+hipError_t launch_prep64(const PrepArgs& a, hipStream_t s);
+hipError_t launch_recur64(const RecurArgs& a, hipStream_t s);
 
 }  // namespace kda

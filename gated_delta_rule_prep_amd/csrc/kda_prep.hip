@@ -264,6 +264,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
 
 hipError_t launch_prep(const PrepArgs& a, hipStream_t s) {
   if (a.lay.chunk == C32) return launch_prep32(a, s);
+  if (a.lay.chunk == C64) return launch_prep64(a, s);
   if (a.grid_chunks == 0) return hipSuccess;
   const unsigned hx = (unsigned)((a.H + kWaves - 1) / kWaves);
   const int64_t grid = (int64_t)hx * a.grid_chunks;

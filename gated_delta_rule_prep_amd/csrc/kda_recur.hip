@@ -439,6 +439,7 @@ hipError_t launch_variant(const RecurArgs& a, int64_t pairs, hipStream_t s) {
 // share a CU while others idle.
 hipError_t launch_recur(const RecurArgs& a, hipStream_t s) {
   if (a.lay.chunk == C32) return a.sets == 2 || a.precision != 0 ? hipErrorInvalidValue : launch_recur32(a, s);
+  if (a.lay.chunk == C64) return a.sets == 2 || a.precision != 0 ? hipErrorInvalidValue : launch_recur64(a, s);
   const int64_t pairs = a.N * a.H * (a.sets == 2 ? 2 : 1);
   if (pairs == 0) return hipSuccess;
   if (a.precision < 0 || a.precision > 7) return hipErrorInvalidValue;

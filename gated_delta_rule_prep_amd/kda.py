@@ -270,7 +270,8 @@ def fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state
     Shapes and dtypes as in include/kda.h.  Runs on the current stream of the
     tensors' device.  Returns ``out``.  ``path``: None / 'auto' for the
     library's choice, 'split' or 'fused' (kda_fwd_ex).  ``chunk``: None for
-    the library's choice, or 16 / 32 tokens per chunk (32: split path only).
+    the library's choice, or 16 / 32 / 64 tokens per chunk (32, 64: split path
+    only).
     ``parts``: None for one, or the number of overlapped ranges (split path).
     ``events``: optional torch.cuda.Event list (enable_timing=True): with no
     chunk / parts / path, four go through kda_fwd_profiled; otherwise
@@ -410,7 +411,7 @@ def debug_prep(q, k, g, beta, scale, A_log, dt_bias, lower_bound, cu_seqlens=Non
     B, T, H, K = q.shape
     N = B if cu_seqlens is None else cu_seqlens.numel() - 1
     if workspace is None:
-        workspace = alloc_workspace(B, T, H, N, cu_seqlens is not None, q.device)
+        workspace = alloc_workspace(B, T, H, N, cu_seqlens is not None, q.device, chunk, 1, "split")
     with torch.cuda.device(q.device):
         rc = _lib.kda_debug_prep(_ptr(q), _ptr(k), _ptr(g), _ptr(beta), float(scale), _ptr(A_log),
                                  _ptr(dt_bias), float(lower_bound), _ptr(cu_seqlens), N, B, T, H, K,

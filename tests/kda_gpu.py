@@ -51,7 +51,7 @@ def state_torch_dtype(inp):
 
 
 # (path, chunk) variants of kda_fwd_ex that the parity tests cover
-VARIANTS = [("fused", 16), ("split", 16), ("split", 32)]
+VARIANTS = [("fused", 16), ("split", 16), ("split", 32), ("split", 64)]
 VARIANT_IDS = ["%s%d" % v for v in VARIANTS]
 
 

@@ -176,7 +176,7 @@ def test_fwd_ex_rejects_bad_parts_and_event_counts():
     null_ev = (ctypes.c_void_p * 10)()
     assert call_ex(2, null_ev, 10) == kda.KDA_EINVAL and "NULL" in kda.last_error()
     assert call_ex(2, None, 0, q=None) == kda.KDA_EINVAL
-    for bad in (8, 17, 64, -16):
+    for bad in (8, 17, 48, 128, -16):
         assert call_ex(1, None, 0, chunk=bad) == kda.KDA_EINVAL and "chunk" in kda.last_error()
 
 
@@ -186,9 +186,11 @@ def test_path_choice_events_and_workspace():
     assert kda.path_used() == "auto"                # both enqueued, the scheduler kernel picks
     assert kda.path_used(chunk=16) == "auto" and kda.path_used(parts=1) == "auto"
     assert kda.path_used(chunk=32) == "split" and kda.path_used(parts=2) == "split"
+    assert kda.path_used(chunk=64) == "split"
     assert kda.path_used(path="split") == "split" and kda.path_used(path="fused", chunk=16) == "fused"
     assert kda.path_used(path="fused", parts=1) == "fused"
-    for bad in (dict(path="fused", chunk=32), dict(path="fused", parts=3), dict(path=7), dict(chunk=24)):
+    for bad in (dict(path="fused", chunk=32), dict(path="fused", chunk=64), dict(path="fused", parts=3),
+                dict(path=7), dict(chunk=24), dict(chunk=128)):
         with pytest.raises(ValueError):
             kda.path_used(**bad)
     assert kda.num_events(1, 8192, path="fused") == 4 and kda.num_events(1, 8192, path="split") == 6
@@ -201,6 +203,7 @@ def test_path_choice_events_and_workspace():
     assert 0 < fused <= 4096 and fused % 256 == 0
     assert split == kda.workspace_layout(1, 8192, 96, chunk=16)["total"]
     assert kda.workspace_bytes(1, 8192, 96, chunk=32) == kda.workspace_layout(1, 8192, 96, chunk=32)["total"]
+    assert kda.workspace_bytes(1, 8192, 96, chunk=64) == kda.workspace_layout(1, 8192, 96, chunk=64)["total"]
     assert kda.workspace_bytes(1, 8192, 96) >= max(fused, split)
     assert kda.workspace_bytes(1, 8192, 96, path="auto") == split      # both paths enqueued
     assert kda.workspace_bytes(1, 8192, 96, 100000, True, path="fused") >= 100000 * 20
@@ -215,12 +218,16 @@ def test_path_choice_events_and_workspace():
     assert call_ex(0, ev, 6, path=2) == kda.KDA_EINVAL and "events" in kda.last_error()   # fused takes 4
 
 
-def test_layout_for_both_chunk_sizes():
+def test_layout_for_every_chunk_size():
     l16 = kda.workspace_layout(1, 8192, 96, chunk=16)
     l32 = kda.workspace_layout(1, 8192, 96, chunk=32)
+    l64 = kda.workspace_layout(1, 8192, 96, chunk=64)
     assert l32["max_chunks"] == 8192 // 32 + 1 and l32["rec_bytes"] == 29184
     assert l32["records"] % 256 == 0 and l32["total"] >= l32["records"] + 96 * l32["max_chunks"] * 29184
-    # the workspace query covers either chunk size
+    assert l64["max_chunks"] == 8192 // 64 + 1 and l64["rec_bytes"] == 66048
+    assert l64["records"] % 256 == 0 and l64["total"] >= l64["records"] + 96 * l64["max_chunks"] * 66048
+    # the plain workspace query covers kda_fwd's 16- and 32-token forms; the
+    # 64-token chunk (kda_fwd_ex only) takes kda_fwd_workspace_bytes_ex
     assert kda.workspace_bytes(1, 8192, 96) == max(l16["total"], l32["total"])
     with pytest.raises(ValueError):
         kda.workspace_layout(1, 64, 2, chunk=24)

@@ -307,15 +307,15 @@ def test_large_magnitude_inside_the_fp16_range(path, chunk):
     assert_close(to_f64(fin), ref_f, "final_state", "fp32")
 
 
-@pytest.mark.parametrize("form", ["fused16", "split16", "split32", "parts3", "segments4"])
+@pytest.mark.parametrize("form", ["fused16", "split16", "split32", "split64", "parts3", "segments4"])
 def test_beyond_the_fp16_range_is_reported(form):
     """v scaled by 1e6: the residuals leave the fp16 operand range, the state
     ends non-finite, and every path reports KDA_STATUS_OVERFLOW in the status
     word; the next in-range call on the same workspace reports OK again."""
     from gated_delta_rule_prep_amd import kda
     kw = dict(fused16=dict(path="fused", chunk=16), split16=dict(path="split", chunk=16),
-              split32=dict(path="split", chunk=32), parts3=dict(path="split", chunk=16, parts=3),
-              segments4=dict(segments=4))[form]
+              split32=dict(path="split", chunk=32), split64=dict(path="split", chunk=64),
+              parts3=dict(path="split", chunk=16, parts=3), segments4=dict(segments=4))[form]
     for scale, expect in ((1e6, kda.KDA_STATUS_OVERFLOW), (1.0, kda.KDA_STATUS_OK)):
         inp = _scaled(make_inputs(1, 256, 2, seed=211, state_dtype="fp32"), scale, 1.0)
         say("case beyond fp16 range form=%s v x %g" % (form, scale))
@@ -436,7 +436,7 @@ PART_CASES = [
 ]
 
 
-@pytest.mark.parametrize("chunk", [16, 32])
+@pytest.mark.parametrize("chunk", [16, 32, 64])
 @pytest.mark.parametrize("i", range(len(PART_CASES)))
 def test_parts_bitwise_equal_one_part(i, chunk):
     """Cutting the rows into parts (prep of part p + 1 overlapped with the

@@ -1,5 +1,5 @@
-"""GPU unit test of the scheduler and chunk-prep kernels alone, for 16- and
-32-token chunks: the chunk table and every chunk record are decoded from the
+"""GPU unit test of the scheduler and chunk-prep kernels alone, for 16-, 32-
+and 64-token chunks: the chunk table and every chunk record are decoded from the
 workspace and compared with the fp64 chunked-form intermediates of
 tests/chunked_ref.py."""
 import numpy as np
@@ -42,15 +42,25 @@ def decode_record(rec, C):
     if C == 16:   # the 16-token record holds -Khat (the recurrence forms T (V - Khat Z))
         return dict(Qh=unpermute(f16(0, (16, 128))), Kh=-unpermute(f16(4096, (16, 128))), Kb=f16(8192, (16, 128)),
                     T=f16(12288, (16, 16)).T, M=f16(12800, (16, 16)).T, gamma=gam(13312))
-    return dict(Qh=unpermute(f16(0, (32, 128))), W=-unpermute(f16(8192, (32, 128))), Kb=f16(16384, (32, 128)),
-                T=unpermute(f16(24576, (32, 32)), PERM32), M=unpermute(f16(26624, (32, 32)), PERM32),
-                gamma=gam(28672))
+    if C == 32:
+        return dict(Qh=unpermute(f16(0, (32, 128))), W=-unpermute(f16(8192, (32, 128))), Kb=f16(16384, (32, 128)),
+                    T=unpermute(f16(24576, (32, 32)), PERM32), M=unpermute(f16(26624, (32, 32)), PERM32),
+                    gamma=gam(28672))
+
+    def blocked(o):   # 8 blocks of 16 rows x 32 token columns (kPermCh order), block (t, u) at (2t + u) KB
+        m = np.empty((64, 64))
+        for t in range(4):
+            for u in range(2):
+                m[16 * t:16 * t + 16, 32 * u:32 * u + 32] = unpermute(f16(o + (2 * t + u) * 1024, (16, 32)), PERM32)
+        return m
+    return dict(Qh=unpermute(f16(0, (64, 128))), W=-unpermute(f16(16384, (64, 128))), Kb=f16(32768, (64, 128)),
+                T=blocked(49152), M=blocked(57344), gamma=gam(65536))
 
 
-@pytest.mark.parametrize("C", [16, 32])
+@pytest.mark.parametrize("C", [16, 32, 64])
 def test_chunk_table_and_records_match_chunked_form(C):
     from gated_delta_rule_prep_amd import kda
-    lens = [1, 15, 17, 40, 0, 33, 64]
+    lens = [1, 15, 17, 40, 0, 33, 64] + ([50, 130] if C == 64 else [])
     T = sum(lens)
     H = 3
     inp = make_inputs(1, T, H, seed=300, lower_bound=-5.0, seq_lens=lens)
@@ -60,7 +70,7 @@ def test_chunk_table_and_records_match_chunked_form(C):
                         cu_seqlens=d["cu_seqlens"], chunk=C)
     torch.cuda.synchronize()
     lay = kda.workspace_layout(1, T, H, len(lens), True, chunk=C)
-    assert lay["rec_bytes"] == (13824 if C == 16 else 29184)
+    assert lay["rec_bytes"] == {16: 13824, 32: 29184, 64: 66048}[C]
     buf = ws.cpu().numpy()
     hdr = buf[:8].view(np.int32)
     assert hdr[0] == kda.KDA_STATUS_OK
