@@ -360,7 +360,8 @@ def workload_entry(cfg, runs, paths, traffic):
 
 
 # (label, chunk, path) of the forms timed per workload; the first is the library's choice
-FORMS = [("auto", None, "auto"), ("split16", 16, "split"), ("fused16", 16, "fused"), ("split32", 32, "split")]
+FORMS = [("auto", None, "auto"), ("split16", 16, "split"), ("fused16", 16, "fused"), ("split32", 32, "split"),
+         ("split64", 64, "split")]
 ONLY = {"fixed": 2, "varlen": 3}
 
 
@@ -376,7 +377,7 @@ def main():
                     choices=["all", "0", "1", "2", "3", "4", "fixed", "varlen", "decode", "segmented"],
                     help="time only one workload (for profiler runs: 0-4, fixed = 2, varlen = 3); the JSON "
                          "line needs all")
-    ap.add_argument("--chunk", type=int, default=0, choices=[0, 16, 32],
+    ap.add_argument("--chunk", type=int, default=0, choices=[0, 16, 32, 64],
                     help="with --only: tokens per chunk (0: the library's choice)")
     ap.add_argument("--path", choices=["auto", "fused", "split"], default="auto",
                     help="with --only: execution path of kda_fwd_ex (auto: the library's choice)")

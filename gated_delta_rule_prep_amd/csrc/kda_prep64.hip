@@ -45,36 +45,56 @@ __device__ __forceinline__ int pos64(int c) { return 32 * (c >> 5) + kPermPos(c 
 
 typedef float Blk[CH][CH + 4];
 
+// Regions that are never live at the same time share storage: Kbar' is read
+// by the coupling products and the rescale, Khat and the substitution scratch
+// are written only after the barrier that ends them; L_ww is dead once T_ww
+// is formed, before the X blocks are written.  65.8 KB: two workgroups per CU.
 struct __align__(16) Smem {
-  __align__(16) _Float16 kh[C64][K + 8];   // Khat relative to the chunk start (fp16), 272-byte rows
-  __align__(16) float kbp[NB - 1][32][64]; // Kbar'_m of blocks 0..2, [channel slot 8 j + e][lane]
   union {
-    Blk L[NB];                             // L_ww of each block (until the first block barrier)
-    Blk X[NB * (NB - 1) / 2];              // X_im, i > m (after it)
+    float kbp[NB - 1][32][64];             // Kbar'_m of blocks 0..2, [channel slot 8 j + e][lane]
+    struct {
+      __align__(16) _Float16 kh[C64][K + 8];   // Khat relative to the chunk start (fp16), 272-byte rows
+      Blk S[NB];                               // per-wave scratch of the block substitution
+    } c;
+  } u;
+  union {
+    Blk L[NB];                             // L_ww of each block
+    Blk X[NB * (NB - 1) / 2];              // X_im, i > m
   } lx;
   Blk T[NB * (NB + 1) / 2];                // T_ij, i >= j, fp32
-  Blk S[NB];                               // per-wave scratch of the block substitution
   __align__(16) _Float16 tp[C64][C64 + 8]; // T, row-major, columns at pos64 (fp16)
   __align__(16) _Float16 mp[C64][C64 + 8]; // Mqk, row-major, columns at pos64 (fp16)
-  float gam[NB][K];                        // gam of each block
+  __align__(16) float gam[NB][K];          // gam of each block
   float beta[C64];
 };
 
 __device__ __forceinline__ void sync_block() { __syncthreads(); }
 
-__global__ __launch_bounds__(kThreads) void prep64_kernel(PrepArgs a) {
-  __shared__ Smem sm;
-  const int tid = threadIdx.x;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+// gam of blocks 0..3 at the lane's 8 channels c0 .. c0 + 7.
+struct Gam8 {
+  f32x4 lo[NB], hi[NB];
+  __device__ __forceinline__ float at(int l, int e) const { return e < 4 ? lo[l][e] : hi[l][e - 4]; }
+};
+__device__ __forceinline__ Gam8 gam8(const Smem& sm, int c0) {
+  Gam8 g;
+#pragma unroll
+  for (int l = 0; l < NB; ++l) {
+    g.lo[l] = *reinterpret_cast<const f32x4*>(&sm.gam[l][c0]);
+    g.hi[l] = *reinterpret_cast<const f32x4*>(&sm.gam[l][c0 + 4]);
+  }
+  return g;
+}
+
+// The work of wave W (block W, tokens 16W .. 16W + 15) of one (chunk, head).
+// Every wave passes the same sequence of workgroup barriers.
+template <int W>
+__device__ __forceinline__ void prep64_wave(const PrepArgs& a, Smem& sm, const ChunkEntry& ce, int chunk, int h,
+                                            int tid) {
+  const int lane = tid & 63;
   const int64_t H = a.H;
-  const int h = blockIdx.y;
-  const WsHeader* hdr = reinterpret_cast<const WsHeader*>(a.ws);
-  const int chunk = hdr->part_first[a.part] + (int)blockIdx.x;
-  if (chunk >= hdr->part_first[a.part + 1]) return;   // the same for every wave: barriers below are safe
-  const ChunkEntry ce = reinterpret_cast<const ChunkEntry*>(a.ws + a.lay.chunk_table)[chunk];
   const int r = lane & 15, cq = lane >> 4;
   const int lc = lane & 15, lg = lane >> 4;
-  const int t = CH * w + r;                                     // token within the chunk
+  const int t = CH * W + r;                                     // token within the chunk
   const bool valid = t < ce.len;
   const int64_t tok = (int64_t)ce.row0 + min(t, ce.len - 1);   // clamped: loads stay in the sequence
   const int64_t base = (tok * H + h) * K + 8 * cq;
@@ -117,7 +137,7 @@ __global__ __launch_bounds__(kThreads) void prep64_kernel(PrepArgs a) {
 
   // ---- per channel slot of the own block: gate, scan, decay factors, L / Mqk
   f32x4 accL = {0.f, 0.f, 0.f, 0.f}, accM = {0.f, 0.f, 0.f, 0.f};
-  float khv[32], qhv[32];   // Khat'_w, Qhat'_w of the lane's token at its 32 channel slots
+  float khv[32], qhv[32];   // Khat'_W, Qhat'_W of the lane's token at its 32 channel slots
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int c0 = 32 * j + 8 * cq;
@@ -149,10 +169,10 @@ __global__ __launch_bounds__(kThreads) void prep64_kernel(PrepArgs a) {
       kb[e] = kI * gam;
       gm[e] = gam;
     }
-    if (w < NB - 1) {
-      // Kbar'_w waits for the later blocks' gam and feeds the coupling products
+    if constexpr (W < NB - 1) {
+      // Kbar'_W waits for the later blocks' gam and feeds the coupling products
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sm.kbp[w][8 * j + e][lane] = kb[e];
+      for (int e = 0; e < 8; ++e) sm.u.kbp[W][8 * j + e][lane] = kb[e];
     } else {
       // the last block's Kbar' is already relative to the chunk end
       u32x4 wkb;
@@ -161,121 +181,131 @@ __global__ __launch_bounds__(kThreads) void prep64_kernel(PrepArgs a) {
       *reinterpret_cast<u32x4*>(rec_kb + c0) = wkb;
     }
     if (r == 0) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sm.gam[w][c0 + e] = gm[e];
+      *reinterpret_cast<f32x4*>(&sm.gam[W][c0]) = f32x4{gm[0], gm[1], gm[2], gm[3]};
+      *reinterpret_cast<f32x4*>(&sm.gam[W][c0 + 4]) = f32x4{gm[4], gm[5], gm[6], gm[7]};
     }
   }
 
-  // ---- L_ww (to LDS) and Mqk_ww (into the fp16 tile, zeros to its right);
+  // ---- L_WW (to LDS) and Mqk_WW (into the fp16 tile, zeros to its right);
   // lane (c, g) holds rows 4g..4g+3 of column c of the 16 x 16 block
   if (cq == 0) sm.beta[t] = beta;
   __builtin_amdgcn_wave_barrier();
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int rr = 4 * lg + i;
-    sm.lx.L[w][rr][lc] = lc < rr ? sm.beta[CH * w + rr] * accL[i] : 0.f;
-    sm.mp[CH * w + rr][pos64(CH * w + lc)] = (_Float16)(lc <= rr ? accM[i] : 0.f);
-    for (int jb = w + 1; jb < NB; ++jb) sm.mp[CH * w + rr][pos64(CH * jb + lc)] = (_Float16)0.f;
+    sm.lx.L[W][rr][lc] = lc < rr ? sm.beta[CH * W + rr] * accL[i] : 0.f;
+    sm.mp[CH * W + rr][pos64(CH * W + lc)] = (_Float16)(lc <= rr ? accM[i] : 0.f);
+#pragma unroll
+    for (int jb = W + 1; jb < NB; ++jb) sm.mp[CH * W + rr][pos64(CH * jb + lc)] = (_Float16)0.f;
   }
   __builtin_amdgcn_wave_barrier();
 
-  // ---- T_ww column jc = column jc of (I + L_ww)^-1 times beta_jc (lanes 0..15)
+  // ---- T_WW column jc = column jc of (I + L_WW)^-1 times beta_jc (lanes 0..15)
   if (lane < CH) {
     const int jc = lane;
     float x[CH];
 #pragma unroll
     for (int rr = 0; rr < CH; ++rr) {
-      float s = rr == jc ? 1.f : 0.f;
+      float sacc = rr == jc ? 1.f : 0.f;
 #pragma unroll
-      for (int m = 0; m < rr; ++m) s = fmaf(-sm.lx.L[w][rr][m], x[m], s);
-      x[rr] = s;
+      for (int m = 0; m < rr; ++m) sacc = fmaf(-sm.lx.L[W][rr][m], x[m], sacc);
+      x[rr] = sacc;
     }
-    const float bj = sm.beta[CH * w + jc];
+    const float bj = sm.beta[CH * W + jc];
 #pragma unroll
     for (int rr = 0; rr < CH; ++rr) {
       const float tv = x[rr] * bj;
-      sm.T[tri(w, w)][rr][jc] = tv;
-      sm.tp[CH * w + rr][pos64(CH * w + jc)] = (_Float16)tv;
-      for (int jb = w + 1; jb < NB; ++jb) sm.tp[CH * w + rr][pos64(CH * jb + jc)] = (_Float16)0.f;
+      sm.T[tri(W, W)][rr][jc] = tv;
+      sm.tp[CH * W + rr][pos64(CH * W + jc)] = (_Float16)tv;
+#pragma unroll
+      for (int jb = W + 1; jb < NB; ++jb) sm.tp[CH * W + rr][pos64(CH * jb + jc)] = (_Float16)0.f;
     }
   }
   sync_block();   // every block's L, T_ww, gam, beta and Kbar' are visible; L is dead
 
-  // ---- coupling blocks of the own block row: X_wm and Mqk_wm for m < w
-  for (int m = 0; m < w; ++m) {
-    f32x4 accX = {0.f, 0.f, 0.f, 0.f}, accQ = {0.f, 0.f, 0.f, 0.f};
+  // ---- coupling blocks of the own block row, X_Wm and Mqk_Wm for m < W, and
+  // the rescale of the own rows to the chunk start / end
+  f32x4 accX[NB - 1], accQ[NB - 1];
 #pragma unroll
-    for (int s = 0; s < 32; ++s) {
-      const int ch = 32 * (s >> 3) + 8 * cq + (s & 7);
-      float dmid = 1.f;   // decay of the whole blocks strictly between m and w
-      for (int l = m + 1; l < w; ++l) dmid *= sm.gam[l][ch];
-      const float kbv = sm.kbp[m][s][lane];   // the same (token, channel) slot as this lane's own values
-      accX = mfma_f32_k4(khv[s] * dmid, kbv, accX);
-      accQ = mfma_f32_k4(qhv[s] * dmid, kbv, accQ);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sm.lx.X[lowx(w, m)][4 * lg + i][lc] = accX[i];
-      sm.mp[CH * w + 4 * lg + i][pos64(CH * m + lc)] = (_Float16)accQ[i];
-    }
+  for (int m = 0; m < NB - 1; ++m) {
+    accX[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    accQ[m] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-
-  // ---- Khat_w and Qhat_w relative to the chunk start, Kbar_w relative to its end
+  u32x4 khw[4];   // Khat_W (fp16), written to LDS once Kbar' is dead
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int c0 = 32 * j + 8 * cq;
-    float kv[8], qv[8];
+    const Gam8 g = gam8(sm, c0);
+    float kv[8], qv[8], kb[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      float pre = 1.f;
-      for (int l = 0; l < w; ++l) pre *= sm.gam[l][c0 + e];
-      kv[e] = khv[8 * j + e] * pre;
-      qv[e] = qhv[8 * j + e] * pre;
-    }
-    u32x4 wkh;
+      const int sl = 8 * j + e;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) wkh[e] = pack_f16(kv[2 * e], kv[2 * e + 1]);
-    *reinterpret_cast<u32x4*>(&sm.kh[t][c0]) = wkh;
+      for (int m = 0; m < W; ++m) {
+        float dmid = 1.f;   // decay of the whole blocks strictly between m and W
+#pragma unroll
+        for (int l = m + 1; l < W; ++l) dmid *= g.at(l, e);
+        const float kbv = sm.u.kbp[m][sl][lane];   // the same (token, channel) slot as this lane's own values
+        accX[m] = mfma_f32_k4(khv[sl] * dmid, kbv, accX[m]);
+        accQ[m] = mfma_f32_k4(qhv[sl] * dmid, kbv, accQ[m]);
+      }
+      float pre = 1.f, post = 1.f;
+#pragma unroll
+      for (int l = 0; l < W; ++l) pre *= g.at(l, e);
+#pragma unroll
+      for (int l = W + 1; l < NB; ++l) post *= g.at(l, e);
+      kv[e] = khv[sl] * pre;
+      qv[e] = qhv[sl] * pre;
+      if constexpr (W < NB - 1) kb[e] = sm.u.kbp[W][sl][lane] * post;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) khw[j][e] = pack_f16(kv[2 * e], kv[2 * e + 1]);
     const int p0 = 32 * j + kPermPos(8 * cq), p1 = 32 * j + kPermPos(8 * cq + 4);
     *reinterpret_cast<u32x2*>(rec_qh + p0) = u32x2{pack_f16(qv[0], qv[1]), pack_f16(qv[2], qv[3])};
     *reinterpret_cast<u32x2*>(rec_qh + p1) = u32x2{pack_f16(qv[4], qv[5]), pack_f16(qv[6], qv[7])};
-    if (w < NB - 1) {
-      float kb[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float post = 1.f;
-        for (int l = w + 1; l < NB; ++l) post *= sm.gam[l][c0 + e];
-        kb[e] = sm.kbp[w][8 * j + e][lane] * post;
-      }
+    if constexpr (W < NB - 1) {
       u32x4 wkb;
 #pragma unroll
       for (int e = 0; e < 4; ++e) wkb[e] = pack_f16(kb[2 * e], kb[2 * e + 1]);
       *reinterpret_cast<u32x4*>(rec_kb + c0) = wkb;
     }
   }
-  if (w == 0) {
+#pragma unroll
+  for (int m = 0; m < W; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sm.lx.X[lowx(W, m)][4 * lg + i][lc] = accX[m][i];
+      sm.mp[CH * W + 4 * lg + i][pos64(CH * m + lc)] = (_Float16)accQ[m][i];
+    }
+  if constexpr (W == 0) {
     for (int c = lane; c < K; c += 64)
       rec_gam[kGamSlot(c)] = sm.gam[0][c] * sm.gam[1][c] * sm.gam[2][c] * sm.gam[3][c];
   }
-  sync_block();   // the X blocks, Khat rows and coupling blocks of Mqk are in place
+  sync_block();   // the X blocks and coupling blocks of Mqk are in place; Kbar' is dead
+
+#pragma unroll
+  for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4*>(&sm.u.c.kh[t][32 * j + 8 * cq]) = khw[j];
 
   // ---- block forward substitution, one block row at a time (row i by wave i)
+#pragma unroll
   for (int i = 1; i < NB; ++i) {
-    if (w == i) {
+    if (i == W) {
+#pragma unroll
       for (int j = 0; j < i; ++j) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
         for (int m = j; m < i; ++m) {
 #pragma unroll
           for (int q4 = 0; q4 < 4; ++q4)
             acc = mfma_f32_k4(sm.lx.X[lowx(i, m)][lc][4 * q4 + lg], sm.T[tri(m, j)][4 * q4 + lg][lc], acc);
         }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sm.S[w][4 * lg + e][lc] = acc[e];
+        for (int e = 0; e < 4; ++e) sm.u.c.S[W][4 * lg + e][lc] = acc[e];
         __builtin_amdgcn_wave_barrier();
         f32x4 tt = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4)
-          tt = mfma_f32_k4(sm.T[tri(i, i)][lc][4 * q4 + lg], sm.S[w][4 * q4 + lg][lc], tt);
+          tt = mfma_f32_k4(sm.T[tri(i, i)][lc][4 * q4 + lg], sm.u.c.S[W][4 * q4 + lg][lc], tt);
         __builtin_amdgcn_wave_barrier();
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -284,29 +314,28 @@ __global__ __launch_bounds__(kThreads) void prep64_kernel(PrepArgs a) {
         }
       }
     }
-    sync_block();   // block row i of T is visible to the later rows
+    sync_block();   // block row i of T (and, the first time, every Khat row) is visible
   }
 
   // ---- -W rows of the own block: W^T tile n (channels 16n..16n+15) =
   // Khat^T T^T over the chunk's tokens, one 32-token half per MFMA, k in
   // kPermCh order (tokens 4g..4g+3 and 16+4g..16+4g+3 of the half in lane group g)
   {
-    const int halves = w >= 2 ? 2 : 1;   // T row block w has no tokens past its own half
-    f16x8 bT[2];
+    constexpr int halves = W >= 2 ? 2 : 1;   // T row block W has no tokens past its own half
+    f16x8 bT[halves];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) bT[u] = *reinterpret_cast<const f16x8*>(&sm.tp[CH * w + lc][32 * u + 8 * lg]);
-    _Float16* rec_nw = reinterpret_cast<_Float16*>(rec + REC64_NW) + (CH * w + lc) * K;
+    for (int u = 0; u < halves; ++u)
+      bT[u] = *reinterpret_cast<const f16x8*>(&sm.tp[CH * W + lc][32 * u + 8 * lg]);
+    _Float16* rec_nw = reinterpret_cast<_Float16*>(rec + REC64_NW) + (CH * W + lc) * K;
 #pragma unroll
     for (int n = 0; n < 8; ++n) {
       f32x4 w4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        if (u < halves) {
-          const f16x4 k0 = lds_read_tr(&sm.kh[32 * u][16 * n], K + 8, lane);
-          const f16x4 k1 = lds_read_tr(&sm.kh[32 * u + CH][16 * n], K + 8, lane);
-          const f16x8 aK = {k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]};
-          w4 = mfma_f16_k32(aK, bT[u], w4);
-        }
+      for (int u = 0; u < halves; ++u) {
+        const f16x4 k0 = lds_read_tr(&sm.u.c.kh[32 * u][16 * n], K + 8, lane);
+        const f16x4 k1 = lds_read_tr(&sm.u.c.kh[32 * u + CH][16 * n], K + 8, lane);
+        const f16x8 aK = {k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]};
+        w4 = mfma_f16_k32(aK, bT[u], w4);
       }
       const int c = 16 * n + 4 * lg;
       *reinterpret_cast<u32x2*>(rec_nw + (c & ~31) + kPermPos(c & 31)) =
@@ -322,6 +351,23 @@ __global__ __launch_bounds__(kThreads) void prep64_kernel(PrepArgs a) {
         *reinterpret_cast<const u32x4*>(&sm.tp[CH * tt + row][32 * u + 8 * piece]);
     *reinterpret_cast<u32x4*>(rec + REC64_MQK + blk * 1024 + row * 64 + piece * 16) =
         *reinterpret_cast<const u32x4*>(&sm.mp[CH * tt + row][32 * u + 8 * piece]);
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void prep64_kernel(PrepArgs a) {
+  __shared__ Smem sm;
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = blockIdx.y;
+  const WsHeader* hdr = reinterpret_cast<const WsHeader*>(a.ws);
+  const int chunk = hdr->part_first[a.part] + (int)blockIdx.x;
+  if (chunk >= hdr->part_first[a.part + 1]) return;   // the same for every wave: barriers below are safe
+  const ChunkEntry ce = reinterpret_cast<const ChunkEntry*>(a.ws + a.lay.chunk_table)[chunk];
+  switch (w) {
+    case 0: prep64_wave<0>(a, sm, ce, chunk, h, tid); break;
+    case 1: prep64_wave<1>(a, sm, ce, chunk, h, tid); break;
+    case 2: prep64_wave<2>(a, sm, ce, chunk, h, tid); break;
+    default: prep64_wave<3>(a, sm, ce, chunk, h, tid); break;
   }
 }
 

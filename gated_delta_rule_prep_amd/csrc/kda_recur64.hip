@@ -31,7 +31,7 @@ namespace {
 constexpr int CC = C64;
 constexpr int kRecPieces = REC64_BYTES / 16;   // 4128 16-byte pieces per record
 constexpr int kWaves = 4;                      // compute waves, 16 value columns each
-constexpr int kLoaders = 2;                    // loader waves, each loads every other 64-piece block
+constexpr int kLoaders = 4;                    // loader waves, each loads every fourth 64-piece block
 constexpr int kSlots = 2;                      // ring slots: chunk c + 1 loads while c is computed
 constexpr int kThreads = 64 * (kWaves + kLoaders);
 constexpr int kFar = 0x7ffffff0;               // an offset past every descriptor's range: reads 0
@@ -50,7 +50,14 @@ constexpr int kTt = kRec + REC64_T, kMt = kRec + REC64_MQK, kGam = kRec + REC64_
 static_assert(CC * kRowPieces % 64 == 0, "value rows fill whole blocks");
 static_assert(kRowPieces >= 8, "the value swizzle needs at least 8 pieces (64 columns) per tile row");
 static_assert(kSlots * kSlotBytes <= 159 * 1024, "the ring fits the LDS");
-static_assert((kBlocks + 1) / 2 <= 60, "a loader's loads of one chunk fit the vmcnt counter");
+constexpr int kPerLoader = (kBlocks + kLoaders - 1) / kLoaders;   // 64-piece blocks per loader and chunk
+static_assert(kPerLoader <= 60, "a loader's loads of one chunk fit the vmcnt counter");
+// The T and Mqk blocks above the diagonal, (t, u) = (0, 1) and (1, 1), hold
+// zeros that no step reads: slot blocks left unloaded.
+__device__ __forceinline__ bool unread_block(int i) {
+  const int tb = (kRec + REC64_T) / 1024, mb = (kRec + REC64_MQK) / 1024;
+  return i == tb + 1 || i == tb + 3 || i == mb + 1 || i == mb + 3;
+}
 
 // Chunk j of a sequence: first flattened token row and length (1..64).
 struct Rows {
@@ -250,20 +257,30 @@ __global__ __launch_bounds__(kThreads) void recur64_kernel(RecurArgs a) {
     const int j = wave - kWaves;
     const char* vseq = reinterpret_cast<const char*>(a.v + ((int64_t)se.row0 * H + h) * V + v0);
     const uint32_t ring0 = lds_addr(ring);
+    // Source offset of this lane's 16-byte position in each of the loader's
+    // load instructions (slot blocks j, j + kLoaders, ...): value row r, piece
+    // position p holds piece p ^ 2 (r % 4) of the row.
+    int32_t off[kPerLoader];
+#pragma unroll
+    for (int k = 0; k < kPerLoader; ++k) {
+      const int i = j + kLoaders * k;
+      if (i < kValBlocks) {
+        const int s = 64 * i + lane, r = s / kRowPieces, p = s % kRowPieces;
+        off[k] = r * row_bytes + 16 * (p ^ (2 * (r & 3)));
+      } else {
+        off[k] = rec_source(64 * (i - kValBlocks) + lane);
+      }
+    }
     const auto issue = [&](int st) {
       const int c = ci_lo + st;
       const int len = min(se.len - CC * c, CC);
       const i32x4 rrec = buf_rsrc(recs + (int64_t)c * H * REC64_BYTES, REC64_BYTES);
       const i32x4 rval = buf_rsrc(vseq + (int64_t)c * CC * row_bytes, (len - 1) * row_bytes + 2 * kCols);
       const uint32_t slot = ring0 + (uint32_t)((st % kSlots) * kSlotBytes);
-      for (int i = j; i < kBlocks; i += kLoaders) {
-        if (i < kValBlocks) {
-          const int s = 64 * i + lane, r = s / kRowPieces, p = s % kRowPieces;
-          load_lds16(rval, slot + kVal + 1024 * i, r * row_bytes + 16 * (p ^ (2 * (r & 3))));
-        } else {
-          const int ib = i - kValBlocks;
-          load_lds16(rrec, slot + kRec + 1024 * ib, rec_source(64 * ib + lane));
-        }
+#pragma unroll
+      for (int k = 0; k < kPerLoader; ++k) {
+        const int i = j + kLoaders * k;
+        if (i < kBlocks && !unread_block(i)) load_lds16(i < kValBlocks ? rval : rrec, slot + 1024 * i, off[k]);
       }
     };
     if (steps > 0) issue(0);

@@ -34,8 +34,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = ["csrc/kda_device.h", "csrc/kda_internal.h", "csrc/kda_lds_pipe.h", "csrc/kda_step16.h",
                   "csrc/kda_sched.hip", "csrc/kda_prep.hip", "csrc/kda_recur.hip", "csrc/kda_prep32.hip",
-                  "csrc/kda_recur32.hip", "csrc/kda_fused.hip", "csrc/kda_decode.hip", "csrc/kda_segment.hip",
-                  "../include/kda.h"]
+                  "csrc/kda_recur32.hip", "csrc/kda_prep64.hip", "csrc/kda_recur64.hip", "csrc/kda_fused.hip",
+                  "csrc/kda_decode.hip", "csrc/kda_segment.hip", "../include/kda.h"]
 
 
 _TOKEN = re.compile(r'//[^\n]*|/\*.*?\*/|"(?:\\.|[^"\\\n])*"|\'(?:\\.|[^\'\\\n])*\'', re.S)
@@ -57,7 +57,7 @@ def source_hash() -> str:
 
 
 def short_name(name: str) -> str:
-    m = re.search(r"(sched_kernel|prep32_kernel|prep_kernel|recur32_kernel|recur_kernel|fused_kernel|decode_kernel|"
+    m = re.search(r"(sched_kernel|prep32_kernel|prep64_kernel|prep_kernel|recur32_kernel|recur64_kernel|recur_kernel|fused_kernel|decode_kernel|"
                   r"seg_cu_kernel|identity_kernel|zero_kernel|prefix_kernel|copyBuffer|elementwise_kernel)",
                   name)
     return m.group(1) if m else name[:40]

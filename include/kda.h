@@ -98,8 +98,8 @@ extern "C" {
 /* Execution paths (kda_fwd_ex).  Both compute the same chunked form; their
    results differ only in rounding.
    KDA_PATH_SPLIT: the two stages of P1 §二 2.2 as two kernels, the chunk
-     records handed over through the workspace in HBM (16- or 32-token chunks,
-     optional overlap of the stages by parts);
+     records handed over through the workspace in HBM (16-, 32- or 64-token
+     chunks, optional overlap of the stages by parts);
    KDA_PATH_FUSED: one kernel per (sequence, head, value tile) that builds each
      chunk's record in LDS a few chunks ahead of the recurrence that consumes
      it, so the records never reach HBM (16-token chunks, one part);
@@ -182,20 +182,23 @@ int kda_fwd_profiled(const void* q, const void* k, const void* v, const void* g,
  * overlap of the two stages under the caller's control, and optional
  * per-kernel events.
  *
- * path: KDA_PATH_AUTO (the library's choice; with a 32-token chunk or more
- * than one part, the split path), KDA_PATH_SPLIT or KDA_PATH_FUSED (chunk 0 or
+ * path: KDA_PATH_AUTO (the library's choice; with a 32- or 64-token chunk or
+ * more than one part, the split path), KDA_PATH_SPLIT or KDA_PATH_FUSED (chunk 0 or
  * 16 and parts 0 or 1 only; otherwise KDA_EINVAL).  The workspace
  * must hold kda_fwd_workspace_bytes_ex(..., chunk, parts, path) bytes: the
- * split path keeps its chunk records there (about 864 B per token-head at
- * chunk 16), the fused path only the per-sequence tables.
+ * split path keeps its chunk records there (about 864, 912 and 1032 B per
+ * token-head at chunk 16, 32 and 64), the fused path only the per-sequence
+ * tables.  (kda_fwd_workspace_bytes covers the 16- and 32-token forms only.)
  *
- * chunk: 0 (the library's choice, as kda_fwd), 16 or 32 tokens per chunk.
+ * chunk: 0 (the library's choice, as kda_fwd), 16, 32 or 64 tokens per chunk.
  * The pages use 16 (P1 §二 2.1) so that the in-chunk decay factors stay in
- * range; the 32-token kernels build each chunk from two 16-token halves whose
- * coupling block needs only bounded factors, and step the state half as
- * often.  Both compute the same chunked form (any chunk size gives the exact
- * recurrence up to rounding); their results differ only in rounding.  Any
- * other value returns KDA_EINVAL.
+ * range, against the 64 of Flash Linear Attention; the 32- and 64-token
+ * kernels build each chunk from two or four 16-token blocks whose coupling
+ * blocks need only bounded factors (the 64 x 64 inverse by block forward
+ * substitution), and step the state a half or a quarter as often.  All
+ * compute the same chunked form (any chunk size gives the exact recurrence up
+ * to rounding); their results differ only in rounding.  Any other value
+ * returns KDA_EINVAL.
  *
  * The token rows (B * T, flattened) are cut into `parts` consecutive ranges of
  * equal size.  The chunk-prep kernel of range p + 1 runs on `stream` while the
