@@ -34,9 +34,12 @@ def make_call(inp, d, kind, out, fin):
         kw["segments"] = 4
         nbytes = kda.segmented_workspace_bytes(inp.B, inp.T, inp.H, inp.N, has_cu, 4)
     else:
-        path = {"auto": None, "split_flags": "split", "fused_wide": "fused"}.get(kind, kind)
+        path = {"auto": None, "split_flags": "split", "fused_wide": "fused", "split64": "split"}.get(kind, kind)
         kw["path"] = path
-        nbytes = kda.workspace_bytes(inp.B, inp.T, inp.H, inp.N, has_cu, None, None, path)
+        chunk = 64 if kind == "split64" else None
+        if chunk:
+            kw["chunk"] = chunk
+        nbytes = kda.workspace_bytes(inp.B, inp.T, inp.H, inp.N, has_cu, chunk, None, path)
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
 
     def call():
@@ -54,6 +57,8 @@ CASES = {
     "split_flags": dict(B=1, T=160, H=80, state_dtype="fp32", seed=705),
     # 150 pairs: the fused kernel's 128-column workgroups
     "fused_wide": dict(B=1, T=120, H=50, state_dtype="bf16", seed=706, seq_lens=[40, 50, 30]),
+    # 64-token chunks on a varlen batch
+    "split64": dict(B=1, T=300, H=3, state_dtype="fp32", seed=707, seq_lens=ragged_lengths(300, 5)),
     "segmented": dict(B=1, T=2048, H=2, state_dtype="fp32", seed=703),
     "decode": dict(B=64, T=1, H=4, state_dtype="bf16", seed=704),
 }

@@ -101,3 +101,43 @@ def test_random_flag_case(i):
         assert_close(to_f64(out), ref_o, "out")
     if inp.output_final_state:
         assert_close(to_f64(fin), ref_f, "final_state", inp.state_dtype)
+
+
+# 64-token chunks (split path, one or more parts): lengths around the chunk and
+# its 16- and 32-token blocks, so partial chunks end inside every block.
+N_C64_CASES = 32
+
+
+def draw_c64(i):
+    rng = np.random.default_rng(9000 + i)
+    H = int(rng.choice([1, 2, 3, 4, 6]))
+    if rng.random() < 0.4:
+        B, T, lens = int(rng.integers(1, 4)), int(rng.integers(0, 300)), None
+    else:
+        n = int(rng.integers(1, 7))
+        lens = [int(x) for x in rng.choice([0, 1, 16, 17, 31, 32, 33, 48, 63, 64, 65, 127, 128, 129,
+                                            int(rng.integers(1, 260))], size=n)]
+        B, T = 1, sum(lens)
+    state = str(rng.choice(["bf16", "fp32", "none"]))
+    parts = int(rng.choice([1, 1, 1, 2, 3]))
+    lb = float(rng.choice([-5.0, -3.0, -1.0, 0.0]))
+    g_std = float(rng.choice([0.5, 1.0, 2.0]))
+    return dict(B=B, T=T, H=H, lens=lens, state=state, parts=parts, lb=lb, g_std=g_std, seed=10000 + i)
+
+
+@pytest.mark.parametrize("i", range(N_C64_CASES))
+def test_random_chunk64_case(i):
+    c = draw_c64(i)
+    say("case c64-%d %s" % (i, c))
+    inp = make_inputs(c["B"], c["T"], c["H"], seed=c["seed"], lower_bound=c["lb"], g_std=c["g_std"],
+                      state_dtype=None if c["state"] == "none" else c["state"],
+                      initial_state=c["state"] != "none", seq_lens=c["lens"])
+    out, fin = run_gpu(inp, path="split", chunk=64, parts=c["parts"])
+    torch.cuda.synchronize()
+    ref_o, ref_f = oracle.kda_fwd(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.scale, inp.A_log, inp.dt_bias,
+                                  inp.lower_bound, initial_state=inp.initial_state_f64(),
+                                  output_final_state=inp.output_final_state, cu_seqlens=inp.cu_seqlens)
+    if inp.B * inp.T > 0:
+        assert_close(to_f64(out), ref_o, "out")
+    if inp.output_final_state:
+        assert_close(to_f64(fin), ref_f, "final_state", inp.state_dtype)
