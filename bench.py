@@ -381,7 +381,7 @@ def main():
                     help="with --only: tokens per chunk (0: the library's choice)")
     ap.add_argument("--path", choices=["auto", "fused", "split"], default="auto",
                     help="with --only: execution path of kda_fwd_ex (auto: the library's choice)")
-    ap.add_argument("--precision", type=int, default=None, choices=list(range(8)),
+    ap.add_argument("--precision", type=int, default=None, choices=list(range(16)),
                     help="with --only 0-4: time kda_fwd_precision with this KDA_PREC_* variant")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="with --only: afterwards run 3 device-to-device copies of this many MiB, a plain copy "

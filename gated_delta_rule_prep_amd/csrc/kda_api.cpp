@@ -482,6 +482,7 @@ static int fwd_impl(const void* q, const void* k, const void* v, const void* g, 
         pa.fixed_T = T;
         pa.fixed_B = B;
       }
+      pa.precision = precision & KDA_PREC_NEUMANN_FP16;
       rec(2 + 2 * p, stream);
       if (e == hipSuccess && run_split) e = kda::launch_prep(pa, stream);
       rec(3 + 2 * p, stream);
@@ -493,7 +494,7 @@ static int fwd_impl(const void* q, const void* k, const void* v, const void* g, 
       const int64_t lo = p * part_rows, hi = p == P - 1 ? (INT64_MAX / 2) : (p + 1) * part_rows;
       kda::RecurArgs ra{static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out), initial_state, final_state,
                         sdt, N, H, p, lo, hi, ws, L};
-      ra.precision = precision;
+      ra.precision = precision & ~KDA_PREC_NEUMANN_FP16;   // the recurrence's own bits
       ra.tiles = kda::recur_tiles(N * H, cu_seqlens == nullptr, cus);
       ra.cus = cus;
       if (fixed) ra.fixed_T = T;
@@ -568,7 +569,8 @@ int kda_fwd_precision(const void* q, const void* k, const void* v, const void* g
                       const void* initial_state, int initial_state_dtype, void* final_state, int final_state_dtype,
                       const int64_t* cu_seqlens, int64_t num_seqs, int64_t B, int64_t T, int64_t H, int64_t K,
                       int64_t V, void* workspace, size_t workspace_bytes, hipStream_t stream, int variant) {
-  const int all = KDA_PREC_BF16_STATE | KDA_PREC_BF16_INVERSE | KDA_PREC_BF16_STATE_PRODUCTS;
+  const int all = KDA_PREC_BF16_STATE | KDA_PREC_BF16_INVERSE | KDA_PREC_BF16_STATE_PRODUCTS |
+                  KDA_PREC_NEUMANN_FP16;
   if (variant < 0 || (variant & ~all) != 0)
     return fail(KDA_EINVAL, "kda: precision variant must be a combination of KDA_PREC_* bits (got %d)", variant);
   return fwd_impl(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state, initial_state_dtype,

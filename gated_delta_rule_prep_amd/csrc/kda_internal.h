@@ -221,6 +221,8 @@ struct PrepArgs {
   // kernel ran: chunk entries come from fixed_chunk, and the first workgroup
   // writes the header (status OK, path split, chunk count, part bounds)
   int64_t fixed_T = 0, fixed_B = 0;
+  // KDA_PREC_NEUMANN_FP16 set: the precision study's form of the inverse
+  int precision = 0;
 };
 
 struct RecurArgs {

@@ -59,6 +59,8 @@ struct __align__(16) WaveSmem {
   __align__(16) char half[3][C][kHalfBytes];   // Qhat, -Khat, Kbar: the current half of every row
   __align__(16) char tail[kTailBytes];         // T^T, Mqk^T, gamma as in the record
 };
+static_assert(sizeof(WaveSmem::half) >= 4 * sizeof(float) * C * (C + 4),
+              "the staged halves hold the four scratch matrices of the precision study's inverse");
 
 // Writes the staged half `hf` of the three row arrays: 3 x 16 rows x 8 pieces.
 __device__ __forceinline__ void flush_half(const WaveSmem& sm, char* rec_out, int hf, int lane) {
@@ -74,6 +76,61 @@ __device__ __forceinline__ void flush_half(const WaveSmem& sm, char* rec_out, in
   asm volatile("" ::: "memory");   // the next half's LDS writes stay behind these reads
 }
 
+// The inverse in the form the pages give it (P1 §二 2.1, 2.3), for the
+// precision study only: (I + L)^-1 = (I - L)(I + L^2)(I + L^4)(I + L^8),
+// exact because L is strictly lower (L^16 = 0).  Every factor and product is
+// an fp16 operand of a 16x16x16 MFMA with fp32 accumulation, each result
+// rounded to fp16 before it is used again.  Lane (c, g) of an MFMA holds
+// rows 4g..4g+3 of column c of the result; the 16 x 16 matrices pass between
+// the products through LDS (fp32 rows of 20).
+typedef float Mat16[C][C + 4];
+
+// A operand of s M + d I: lane (c, g) holds row c, columns 4g..4g+3.
+__device__ __forceinline__ f16x4 nm_a(const Mat16& m, float sc, float d, int lc, int lg) {
+  f16x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = (_Float16)(sc * m[lc][4 * lg + i] + (lc == 4 * lg + i ? d : 0.f));
+  return r;
+}
+// B operand of s M + d I: lane (c, g) holds rows 4g..4g+3 of column c.
+__device__ __forceinline__ f16x4 nm_b(const Mat16& m, float sc, float d, int lc, int lg) {
+  f16x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = (_Float16)(sc * m[4 * lg + i][lc] + (lc == 4 * lg + i ? d : 0.f));
+  return r;
+}
+__device__ __forceinline__ void nm_store(Mat16& m, f32x4 acc, int lc, int lg) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) m[4 * lg + i][lc] = (float)(_Float16)acc[i];
+  __builtin_amdgcn_wave_barrier();
+}
+
+// T^T of the chunk (row j = column j of (I + L)^-1 times beta_j) into the
+// record tail, from L and beta in LDS; `scratch` holds four matrices.
+__device__ __forceinline__ void neumann_inverse(const Mat16& L, const float* beta, Mat16* scratch, char* tail,
+                                                int lane) {
+  const int lc = lane & 15, lg = lane >> 4;
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  nm_store(scratch[0], mfma_f16_k16(nm_a(L, 1.f, 0.f, lc, lg), nm_b(L, 1.f, 0.f, lc, lg), z), lc, lg);   // L^2
+  nm_store(scratch[1], mfma_f16_k16(nm_a(scratch[0], 1.f, 0.f, lc, lg), nm_b(scratch[0], 1.f, 0.f, lc, lg), z),
+           lc, lg);                                                                                        // L^4
+  nm_store(scratch[2], mfma_f16_k16(nm_a(scratch[1], 1.f, 0.f, lc, lg), nm_b(scratch[1], 1.f, 0.f, lc, lg), z),
+           lc, lg);                                                                                        // L^8
+  nm_store(scratch[3], mfma_f16_k16(nm_a(L, -1.f, 1.f, lc, lg), nm_b(scratch[0], 1.f, 1.f, lc, lg), z),
+           lc, lg);                                                          // (I - L)(I + L^2)
+  nm_store(scratch[0], mfma_f16_k16(nm_a(scratch[3], 1.f, 0.f, lc, lg), nm_b(scratch[1], 1.f, 1.f, lc, lg), z),
+           lc, lg);                                                          //   (I + L^4)
+  const f32x4 n = mfma_f16_k16(nm_a(scratch[0], 1.f, 0.f, lc, lg), nm_b(scratch[2], 1.f, 1.f, lc, lg), z);   // (I + L^8)
+  const float bj = beta[lc];
+  u32x2 w;
+  w[0] = pack_f16(n[0] * bj, n[1] * bj);
+  w[1] = pack_f16(n[2] * bj, n[3] * bj);
+  *reinterpret_cast<u32x2*>(tail + (lc * C + 4 * lg) * 2) = w;   // T^T[c][4g..4g+3] = T[4g..4g+3][c]
+}
+
+// INV = 0: the inverse by forward substitution in fp32 (the library's);
+// INV = 1: the fp16 Neumann product above (kda_fwd_precision only).
+template <int INV>
 __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
   __shared__ WaveSmem wsm[kWaves];
   const int tid = threadIdx.x;
@@ -227,7 +284,11 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
   __builtin_amdgcn_wave_barrier();
 
   // ---- T^T row j = column j of (I + L)^-1 times beta_j (lanes 0..15)
-  if (lane < C) {
+  if constexpr (INV == 1) {
+    wait_lgkm0();   // the staged halves are read out: their LDS serves as scratch
+    __builtin_amdgcn_wave_barrier();
+    neumann_inverse(sm.L, sm.beta, reinterpret_cast<Mat16*>(&sm.half[0][0][0]), tail, lane);
+  } else if (lane < C) {
     const int jc = lane;
     float x[C];
 #pragma unroll
@@ -269,7 +330,10 @@ hipError_t launch_prep(const PrepArgs& a, hipStream_t s) {
   const unsigned hx = (unsigned)((a.H + kWaves - 1) / kWaves);
   const int64_t grid = (int64_t)hx * a.grid_chunks;
   if (grid > INT32_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(prep_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  if (a.precision & KDA_PREC_NEUMANN_FP16)
+    hipLaunchKernelGGL(prep_kernel<1>, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(prep_kernel<0>, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

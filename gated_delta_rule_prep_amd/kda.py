@@ -25,6 +25,7 @@ KDA_DTYPE_NONE, KDA_DTYPE_BF16, KDA_DTYPE_FP32 = 0, 1, 2
 KDA_STATUS_OK, KDA_STATUS_BAD_CU_SEQLENS, KDA_STATUS_OVERFLOW, KDA_STATUS_SYNC_TIMEOUT = 0, 1, 2, 4
 KDA_PATH_AUTO, KDA_PATH_SPLIT, KDA_PATH_FUSED = 0, 1, 2
 KDA_PREC_DEFAULT, KDA_PREC_BF16_STATE, KDA_PREC_BF16_INVERSE, KDA_PREC_BF16_STATE_PRODUCTS = 0, 1, 2, 4
+KDA_PREC_NEUMANN_FP16 = 8
 PATHS = {None: KDA_PATH_AUTO, "auto": KDA_PATH_AUTO, "split": KDA_PATH_SPLIT, "fused": KDA_PATH_FUSED,
          KDA_PATH_AUTO: KDA_PATH_AUTO, KDA_PATH_SPLIT: KDA_PATH_SPLIT, KDA_PATH_FUSED: KDA_PATH_FUSED}
 CHUNK = 16

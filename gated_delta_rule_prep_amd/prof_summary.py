@@ -106,8 +106,8 @@ def traffic(workload, fetch_dir, write_dir, copy_bytes):
     fs = copy_bytes / copy_value(f, kib)   # bytes per counter unit
     ws = copy_bytes / copy_value(w, kib)
     kernels = {}
-    for k in ("sched_kernel", "prep_kernel", "recur_kernel", "prep32_kernel", "recur32_kernel", "fused_kernel",
-              "decode_kernel"):
+    for k in ("sched_kernel", "prep_kernel", "recur_kernel", "prep32_kernel", "recur32_kernel", "prep64_kernel",
+              "recur64_kernel", "fused_kernel", "decode_kernel"):
         if k in f and k in w:
             kernels[k] = {"fetch_bytes": int(statistics.median(f[k]) * fs),
                           "write_bytes": int(statistics.median(w[k]) * ws), "dispatches": len(f[k])}

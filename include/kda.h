@@ -234,9 +234,9 @@ int kda_fwd_ex(const void* q, const void* k, const void* v, const void* g, const
 
 /*
  * kda_fwd_precision -- a study entry point, not the hot path: kda_fwd on the
- * split path (16-token chunks, one part) with the chunk recurrence's
- * arithmetic changed to one of the alternatives P1 §二 2.3 weighs, so their
- * accuracy against an exact reference can be measured.
+ * split path (16-token chunks, one part) with the chunk recurrence's or the
+ * chunk prep's arithmetic changed to one of the alternatives P1 §二 2.1 and
+ * 2.3 weigh, so their accuracy against an exact reference can be measured.
  *   KDA_PREC_DEFAULT: the library's arithmetic (state fp32 on chip, fp16
  *     MFMA operands with fp32 accumulation); equal to kda_fwd_ex(path = split).
  *   KDA_PREC_BF16_STATE: the state rounded to bf16 after every chunk update,
@@ -246,6 +246,11 @@ int kda_fwd_ex(const void* q, const void* k, const void* v, const void* g, const
  *     in fp16 for its precision.
  *   KDA_PREC_BF16_STATE_PRODUCTS: Khat Z and Qhat Z with the state copy and
  *     the record's -Khat and Qhat in bf16 instead of fp16.
+ *   KDA_PREC_NEUMANN_FP16: the chunk prep forms the 16 x 16 inverse as the
+ *     pages do (P1 §二 2.1, 2.3), the Neumann product (I - L)(I + L^2)(I + L^4)
+ *     (I + L^8), exact since L is strictly lower, with every factor and
+ *     product an fp16 matrix-core operand (fp32 accumulation), instead of
+ *     forward substitution in fp32.
  * variant: any combination of these bits; anything else returns KDA_EINVAL.
  * Arguments, workspace (kda_fwd_workspace_bytes_ex(..., 16, 1,
  * KDA_PATH_SPLIT) bytes or more) and checks otherwise as kda_fwd.
@@ -254,6 +259,7 @@ int kda_fwd_ex(const void* q, const void* k, const void* v, const void* g, const
 #define KDA_PREC_BF16_STATE 1
 #define KDA_PREC_BF16_INVERSE 2
 #define KDA_PREC_BF16_STATE_PRODUCTS 4
+#define KDA_PREC_NEUMANN_FP16 8
 int kda_fwd_precision(const void* q, const void* k, const void* v, const void* g, const void* beta, float scale,
                       void* out, const float* A_log, const float* dt_bias, float lower_bound,
                       const void* initial_state, int initial_state_dtype, void* final_state, int final_state_dtype,

@@ -335,7 +335,7 @@ def test_segmented_segments_and_workspace():
 def test_precision_study_rejects_bad_variants():
     a = [FAKE, FAKE, FAKE, FAKE, FAKE, 0.088, FAKE, FAKE, FAKE, -5.0, None, 0, None, 0, None, 0, 1, 64, 2, 128,
          128, WS, 1 << 40, None]
-    for bad in (-1, 8, 9, 16):
+    for bad in (-1, 16, 17, 32):
         assert kda.lib().kda_fwd_precision(*a, bad) == kda.KDA_EINVAL and "precision" in kda.last_error()
     # the remaining checks are kda_fwd's, made before any HIP call
     a[0] = None
@@ -343,6 +343,7 @@ def test_precision_study_rejects_bad_variants():
     a[0] = FAKE
     a[22] = 700
     assert kda.lib().kda_fwd_precision(*a, 7) == kda.KDA_EWORKSPACE
+    assert kda.lib().kda_fwd_precision(*a, kda.KDA_PREC_NEUMANN_FP16 | 1) == kda.KDA_EWORKSPACE
 
 
 def test_kda_fwd_workspace_covers_its_segmented_form():

@@ -1,7 +1,8 @@
 """The precision study of kda_fwd_precision against the fp64 oracle: the
 library's arithmetic next to the alternatives the FlashKDA blog post weighs in
-§二 2.3 (the state stored in bf16 between chunk updates; the inverse stage
-E = T R in bf16 instead of fp16; the state products in bf16).
+§二 2.1 and 2.3 (the state stored in bf16 between chunk updates; the inverse stage
+E = T R in bf16 instead of fp16; the state products in bf16; the 16 x 16 inverse
+as the fp16 Neumann product the pages describe instead of fp32 substitution).
 
 The default variant must equal the split path bitwise and meet the contract's
 tolerance.  The alternatives are measurements, not contracts: each is checked
@@ -23,7 +24,7 @@ if not torch.cuda.is_available():
 
 VARIANTS = {0: "default (fp32 state, fp16 operands)", 1: "bf16 state between updates", 2: "bf16 inverse stage",
             4: "bf16 state products", 3: "state + inverse", 5: "state + products", 6: "inverse + products",
-            7: "all three"}
+            7: "all three", 8: "fp16 Neumann inverse (the pages')", 9: "Neumann inverse + bf16 state"}
 
 
 def run_variant(inp, d, variant):
