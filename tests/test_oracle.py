@@ -196,6 +196,7 @@ def test_gate_range_and_claimed_bf16_headroom():
     (128, 128, 37, 16, -5.0, "bf16", 5),
     (128, 128, 300, 16, -0.5, "fp32", 6),
     (128, 128, 64, 32, -2.0, "fp32", 7),
+    (128, 128, 150, 64, -5.0, "fp32", 8),
 ])
 def test_oracle_matches_chunked_form(K, V, T, C, lb, state, seed):
     inp = make_inputs(1, T, 2, K=K, V=V, seed=seed, lower_bound=lb, state_dtype=state)
