@@ -216,7 +216,7 @@ int resolve_path(int chunk, int parts, int path) {
 
 extern "C" {
 
-int kda_version(void) { return 200; }  // 0.2.0
+int kda_version(void) { return 300; }  // 0.3.0: 64-token chunks, the Neumann precision variant
 
 const char* kda_get_last_error(void) { return g_last_error.c_str(); }
 
