@@ -52,7 +52,7 @@ def chunk_kda(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
     final_state)``: out bf16 [B, T, H, V]; final_state [N, H, V, K] in the
     dtype of initial_state (``final_state_dtype`` when there is none, fp32 by
     default) if ``output_final_state``, else None.  ``chunk``: None for the
-    library's chunk size, or 16 / 32.  Runs on the current stream.
+    library's chunk size, or 16 / 32 / 64.  Runs on the current stream.
     """
     if not use_gate_in_kernel:
         _reject("use_gate_in_kernel=False (the kernels take the raw gate g)")

@@ -336,7 +336,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_fused(const FusedArgs& a, hipStream_t s);
 hipError_t launch_seg_cu(const SegArgs& a, hipStream_t s);
 hipError_t launch_prefix(const PrefixArgs& a, hipStream_t s);
-// The launchers pick the 16- or 32-token kernels by a.lay.chunk.
+// The launchers pick the 16-, 32- or 64-token kernels by a.lay.chunk.
 hipError_t launch_prep(const PrepArgs& a, hipStream_t s);
 hipError_t launch_recur(const RecurArgs& a, hipStream_t s);
 hipError_t launch_prep32(const PrepArgs& a, hipStream_t s);

@@ -2,7 +2,7 @@
 //
 // Turns the sequence boundaries into
 //   * a chunk table: chunk i -> {sequence n, first flattened token row, length},
-//     chunks of at most lay.chunk (16 or 32) tokens that restart at every sequence start (so a
+//     chunks of at most lay.chunk (16, 32 or 64) tokens that restart at every sequence start (so a
 //     chunk never straddles two sequences; the pages batch variable-length
 //     sequences through cu_seqlens: README mirror "内核 API", cu_seqlens row);
 //   * a per-sequence table {first chunk, chunk count, first token row, length};

@@ -400,7 +400,7 @@ int kda_version(void);
 int kda_fwd_check_status(const void* workspace, hipStream_t stream, int* status);
 
 /*
- * Workspace layout for chunk = 16 or 32, for tests that decode the chunk records:
+ * Workspace layout for chunk = 16, 32 or 64, for tests that decode the chunk records:
  * offsets[0] = chunk table (int32 triples {sequence, first token row, length}),
  * offsets[1] = per-sequence table (int32 quadruples {first chunk, chunk count,
  *              first token row, length}),
@@ -421,6 +421,13 @@ int kda_fwd_check_status(const void* workspace, hipStream_t stream, int* status)
  * [26624, 28672) Mqk fp16 [32][32], both row-major with the columns of each row
  * in the order {0-3, 16-19, 4-7, 20-23, 8-11, 24-27, 12-15, 28-31};
  * [28672, 29184) gamma fp32 [128] as above.
+ * Record layout for chunk 64 (bytes): [0, 16384) Qhat fp16 [64][128] and
+ * [16384, 32768) -W fp16 [64][128], channels as above; [32768, 49152) Kbar fp16
+ * [64][128] (token-major, natural order); [49152, 57344) T and [57344, 65536)
+ * Mqk, fp16, each as eight blocks of 16 rows x 32 columns, block (t, u) (rows
+ * 16t .. 16t + 15, token columns 32u .. 32u + 31 in the order above) at
+ * (2t + u) * 1024 bytes, the blocks above the diagonal zero; [65536, 66048)
+ * gamma fp32 [128] as above.
  */
 int kda_workspace_layout(int64_t B, int64_t T, int64_t H, int64_t num_seqs, int has_cu_seqlens, int chunk,
                          int64_t offsets[7]);
@@ -428,7 +435,7 @@ int kda_workspace_layout(int64_t B, int64_t T, int64_t H, int64_t num_seqs, int 
 /*
  * kda_debug_prep -- test-only: enqueue the scheduler and the split path's chunk-prep kernels
  * alone (same arguments as kda_fwd minus v, out and the states, plus the
- * chunk size, 16 or 32), leaving the chunk table and records in `workspace`
+ * chunk size, 16, 32 or 64), leaving the chunk table and records in `workspace`
  * for inspection.
  */
 int kda_debug_prep(const void* q, const void* k, const void* g, const void* beta, float scale,
