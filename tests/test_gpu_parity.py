@@ -253,7 +253,8 @@ def test_zero_tokens_passes_state_through():
 
 
 @pytest.mark.parametrize("path,chunk,parts", [("auto", None, None), ("split", 16, None), ("fused", 16, None),
-                                               ("split", 32, None), ("split", 16, 3), ("split", 32, 2)])
+                                               ("split", 32, None), ("split", 16, 3), ("split", 32, 2),
+                                               ("split", 64, None), ("split", 64, 2)])
 def test_bad_cu_seqlens_sets_status_and_touches_nothing(path, chunk, parts):
     """A rejected cu_seqlens leaves out and final_state exactly as they were
     (both filled with a sentinel first), on every path."""
