@@ -429,11 +429,14 @@ def test_tiling_boundaries(i, path, chunk):
     check(inp, tag="tiling%d" % i, chunk=chunk, path=path)
 
 
+_MANY = [int(x) for x in np.random.default_rng(305).integers(0, 13, size=1100)]
 PART_CASES = [
     dict(B=2, T=300, H=3, state_dtype="fp32", lower_bound=-5.0, seed=300),
     dict(B=1, T=513, H=2, state_dtype="bf16", lower_bound=-5.0, seed=301, seq_lens=ragged_lengths(513, 9)),
     dict(B=1, T=200, H=2, state_dtype="fp32", lower_bound=-1.0, seed=302, seq_lens=[0, 3, 0, 150, 1, 46, 0]),
     dict(B=1, T=40, H=4, state_dtype=None, lower_bound=-5.0, seed=303),
+    # more sequences than one scheduler scan tile (1024): the parts' bounds from the written table
+    dict(B=1, T=sum(_MANY), H=1, state_dtype="fp32", lower_bound=-3.0, seed=305, seq_lens=_MANY),
 ]
 
 

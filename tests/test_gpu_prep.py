@@ -57,6 +57,53 @@ def decode_record(rec, C):
                 T=blocked(49152), M=blocked(57344), gamma=gam(65536))
 
 
+def check_tables(buf, lay, lens, cu, C):
+    """The scheduler's chunk table, sequence table and work order, exactly;
+    returns the chunk table's entries."""
+    hdr = buf[:8].view(np.int32)
+    nch = sum((l + C - 1) // C for l in lens)
+    assert hdr[1] == nch
+    table = buf[lay["chunk_table"]:lay["chunk_table"] + 12 * nch].view(np.int32).reshape(nch, 3)
+    want = []
+    for n, l in enumerate(lens):
+        for c in range(0, l, C):
+            want.append((n, int(cu[n]) + c, min(C, l - c)))
+    assert [tuple(r) for r in table] == want
+    seqs = buf[lay["seq_table"]:lay["seq_table"] + 16 * len(lens)].view(np.int32).reshape(-1, 4)
+    order = buf[lay["order"]:lay["order"] + 4 * len(lens)].view(np.int32)
+    assert list(seqs[:, 1]) == [(l + C - 1) // C for l in lens]
+    assert list(seqs[:, 2]) == [int(x) for x in cu[:-1]] and list(seqs[:, 3]) == list(lens)
+    assert list(seqs[:, 0]) == [sum((l + C - 1) // C for l in lens[:n]) for n in range(len(lens))]
+    assert sorted(order) == list(range(len(lens)))
+    counts = [seqs[n, 1] for n in order]
+    assert counts == sorted(counts, reverse=True)               # longest first
+    if len(lens) <= 2048:                                        # ties in index order
+        keyed = [(-seqs[n, 1], n) for n in order]
+        assert keyed == sorted(keyed)
+    return want
+
+
+@pytest.mark.parametrize("N", [40, 300, 1300])
+def test_scheduler_tables_many_sequences(N):
+    """The scheduler's tables for one wave's worth of sequences, one block's
+    and more than one scan tile (1024 sequences per tile), with empty
+    sequences among them."""
+    from gated_delta_rule_prep_amd import kda
+    rng = np.random.default_rng(320 + N)
+    lens = [int(x) for x in rng.integers(0, 40, size=N)]
+    T = sum(lens)
+    inp = make_inputs(1, T, 1, seed=321, lower_bound=-5.0, seq_lens=lens)
+    say("case scheduler tables N=%d T=%d" % (N, T))
+    d = device_inputs(inp)
+    ws = kda.debug_prep(d["q"], d["k"], d["g"], d["beta"], inp.scale, d["A_log"], d["dt_bias"], inp.lower_bound,
+                        cu_seqlens=d["cu_seqlens"], chunk=16)
+    torch.cuda.synchronize()
+    lay = kda.workspace_layout(1, T, 1, N, True, chunk=16)
+    buf = ws.cpu().numpy()
+    assert buf[:4].view(np.int32)[0] == kda.KDA_STATUS_OK
+    check_tables(buf, lay, lens, inp.cu_seqlens, 16)
+
+
 @pytest.mark.parametrize("C", [16, 32, 64])
 def test_chunk_table_and_records_match_chunked_form(C):
     from gated_delta_rule_prep_amd import kda
@@ -74,23 +121,8 @@ def test_chunk_table_and_records_match_chunked_form(C):
     buf = ws.cpu().numpy()
     hdr = buf[:8].view(np.int32)
     assert hdr[0] == kda.KDA_STATUS_OK
-    nch = sum((l + C - 1) // C for l in lens)
     cu = inp.cu_seqlens
-    assert hdr[1] == nch
-    table = buf[lay["chunk_table"]:lay["chunk_table"] + 12 * nch].view(np.int32).reshape(nch, 3)
-    want = []
-    for n, l in enumerate(lens):
-        for c in range(0, l, C):
-            want.append((n, int(cu[n]) + c, min(C, l - c)))
-    assert [tuple(r) for r in table] == want
-    seqs = buf[lay["seq_table"]:lay["seq_table"] + 16 * len(lens)].view(np.int32).reshape(-1, 4)
-    order = buf[lay["order"]:lay["order"] + 4 * len(lens)].view(np.int32)
-    assert list(seqs[:, 1]) == [(l + C - 1) // C for l in lens]
-    assert list(seqs[:, 2]) == [int(x) for x in cu[:-1]] and list(seqs[:, 3]) == lens
-    assert list(seqs[:, 0]) == [sum((l + C - 1) // C for l in lens[:n]) for n in range(len(lens))]
-    assert sorted(order) == list(range(len(lens)))
-    counts = [seqs[n, 1] for n in order]
-    assert counts == sorted(counts, reverse=True)               # longest first
+    want = check_tables(buf, lay, lens, cu, C)
 
     f = chunked_ref.decode_bf16
     qf, kf, gf, bf = f(inp.q)[0], f(inp.k)[0], f(inp.g)[0], f(inp.beta)[0]
