@@ -5,8 +5,9 @@ E = T R in bf16 instead of fp16; the state products in bf16; the 16 x 16 inverse
 as the fp16 Neumann product the pages describe instead of fp32 substitution).
 
 The default variant must equal the split path bitwise and meet the contract's
-tolerance.  The alternatives are measurements, not contracts: each is checked
-to be finite, and its scores are printed for the table of the study.
+tolerance, and so must the pages' fp16 Neumann inverse (the study found it as
+accurate).  The other alternatives are measurements, not contracts: each is
+checked to be finite, and its scores are printed for the table of the study.
 """
 import numpy as np
 import pytest
@@ -63,6 +64,9 @@ def test_precision_variants(ci):
             assert torch.equal(o.view(torch.int16), base_o.view(torch.int16))
             assert torch.equal(f.view(torch.int16) if f.dtype == torch.bfloat16 else f,
                                base_f.view(torch.int16) if f.dtype == torch.bfloat16 else base_f)
+            assert_close(to_f64(o)[:, :, hs], ref_o, "out")
+            assert_close(to_f64(f)[:, hs], ref_f, "final_state", inp.state_dtype)
+        if v == 8:   # the pages' fp16 Neumann inverse: as accurate as the library's substitution
             assert_close(to_f64(o)[:, :, hs], ref_o, "out")
             assert_close(to_f64(f)[:, hs], ref_f, "final_state", inp.state_dtype)
         for s in (so, sf):
