@@ -8,11 +8,11 @@ H = 96, K = V = 128, one fixed-length sequence, bf16 initial and final state,
 lower_bound = -5 (it runs the split path there).  Every one of the five
 workloads (gated_delta_rule_prep_amd.inputs.configs) gets its own entry with
 the library's choice and the explicit paths (split and fused with 16-token
-chunks, split with 32-token chunks) timed beside it.
+chunks, split with 32- and 64-token chunks) timed beside it.
 
 Protocol (the pages' benchmark runs 30 warmup calls, then 5 repeats of 200
-timed calls, and reports the median): W warmup steps, then R repeats of K
-timed steps each, bracketed by device synchronisation; the step time is the
+timed calls, and reports the median; these are the defaults): W warmup steps,
+then R repeats of K timed steps each, bracketed by device synchronisation; the step time is the
 median over the repeats (min and max beside it).  Per-kernel times come from
 HIP events that kda_fwd_ex records around every kernel on the stream it runs
 on (median over K profiled calls).  The roofline is computed for the kernel
@@ -28,7 +28,7 @@ one-token sequences x 96 heads with a bf16 state updated in place, and one
 long sequence with 4 heads on the segmented form.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--repeats R] [--no-cpu]
-                       [--only 0|1|2|3|4|fixed|varlen|decode|segmented] [--chunk 16|32]
+                       [--only 0|1|2|3|4|fixed|varlen|decode|segmented] [--chunk 16|32|64]
                        [--path auto|fused|split]
 """
 from __future__ import annotations
@@ -368,8 +368,8 @@ ONLY = {"fixed": 2, "varlen": 3}
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--repeats", type=int, default=5, help="timed runs of --steps calls; the median is reported")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle cpu_baseline leg")
     ap.add_argument("--cpu-heads", type=int, default=96, help="heads of the headline workload the oracle runs")
